@@ -1,0 +1,275 @@
+"""Reference work-map builder (oracle; test infrastructure only).
+
+What the method does before every inference step, as the pages describe it
+([P3] §3.1 "方案", steps 1-5; [P4] §二.1; [P1] §3.1):
+
+1. cut every request's KV range into tiles of one uniform size;
+2. concatenate all requests' tiles into one task stream;
+3. give every worker (a CTA on the pages' GPU, a workgroup here) the same, or
+   nearly the same, budget of tiles from the global tile count;
+4. fill each worker greedily from the stream up to its budget, so that a long
+   request may span several workers; the resulting task map is built once per
+   step and read by the attention kernel of every layer;
+5. (kernel side) each split writes a partial result and a combine merges them.
+
+The budget arithmetic is the one in [P2] §二.1 ``dynamic_tile_scheduler``:
+``base = total // workers`` and the first ``total % workers`` workers get one
+extra tile.  [P3]'s worked example: lengths 1024, 5120 and 2048 with 512-token
+tiles give 2, 10 and 4 tiles, and 4 workers receive 4 tiles each.
+
+Readings where the pages are silent (each one is also listed in the design doc):
+
+* tile count is a ceiling (a partial last tile is still a tile; a floor, as in
+  [P2]'s pseudocode, would drop tokens and make attention wrong);
+* the task stream is in batch order, tiles in ascending KV order;
+* "greedy bin-packing" is a contiguous fill: worker w takes the next budget_w
+  tiles of the stream ([P3]'s "long request spans CTAs" and "4 tiles each"
+  hold under it);
+* consecutive tiles of one request inside one worker form one split
+  ("segment"), which owns one partial slot;
+* every tile costs one budget unit, a partial last tile included.
+
+Work-map layout (int32 words, one flat buffer; the GPU planner must produce
+exactly these words)::
+
+    [0] version (=1)     [1] B (requests)   [2] W (workers)   [3] kv_tile
+    [4] S (segments)     [5] T (tiles)      [6] q_tile (1 for decode)
+    [7] U (query units)
+    worker_ptr[W + 1]               segments of worker w: [worker_ptr[w], worker_ptr[w+1])
+    unit_ptr[U + 1]                 segments of unit u:   [unit_ptr[u],  unit_ptr[u+1])
+    unit[U][2]   = (b, q_tile_index)
+    seg[S][4]    = (b, q_tile_index, kv_begin, kv_end)   (KV token range, end exclusive)
+
+A decode unit is one request (q_tile_index 0).  A prefill unit is one
+q_tile-row block of one request's query chunk.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Sequence, Tuple
+
+import numpy as np
+
+MAP_VERSION = 1
+HEADER_WORDS = 8
+
+
+@dataclass
+class Unit:
+    b: int            # request index
+    qt: int           # q-tile index inside the request (0 for decode)
+    extent: int       # number of KV tokens this unit attends to (its KV range is [0, extent))
+
+
+@dataclass
+class Segment:
+    b: int
+    qt: int
+    kv_begin: int
+    kv_end: int
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def tiles_of(extent: int, tile: int) -> int:
+    """Step 1, tile cut: number of uniform tiles covering ``extent`` tokens (ceiling)."""
+    return ceil_div(extent, tile) if extent > 0 else 0
+
+
+def budgets(total_tiles: int, workers: int) -> List[int]:
+    """Step 3, equal budgets: ``base = T // W``; the first ``T % W`` workers get one more."""
+    base, rem = divmod(total_tiles, workers)
+    return [base + (1 if w < rem else 0) for w in range(workers)]
+
+
+def _check_common(num_workers: int, tile: int) -> None:
+    if num_workers < 1:
+        raise ValueError("num_workers must be >= 1")
+    if tile < 1:
+        raise ValueError("tile must be >= 1")
+
+
+def _greedy_fill(units: Sequence[Unit], num_workers: int, tile: int) -> Tuple[List[List[Segment]], int]:
+    """Steps 2-4: one stream of (unit, tile) in unit order; contiguous fill per worker budget."""
+    # step 2: the task stream, unit (batch) order, ascending tile index inside a unit
+    stream = []
+    for ui, u in enumerate(units):
+        for t in range(tiles_of(u.extent, tile)):
+            stream.append((ui, t))
+    total = len(stream)
+    # step 3
+    budget = budgets(total, num_workers)
+    # step 4: worker w takes the next budget[w] tiles; runs of one unit become one segment
+    lists: List[List[Segment]] = []
+    cursor = 0
+    for w in range(num_workers):
+        taken = stream[cursor:cursor + budget[w]]
+        cursor += budget[w]
+        segs: List[Segment] = []
+        run_start = 0
+        for i in range(1, len(taken) + 1):
+            if i == len(taken) or taken[i][0] != taken[run_start][0]:
+                ui, t_first = taken[run_start]
+                t_last = taken[i - 1][1]
+                u = units[ui]
+                segs.append(Segment(u.b, u.qt, t_first * tile, min(u.extent, (t_last + 1) * tile)))
+                run_start = i
+        lists.append(segs)
+    assert cursor == total
+    return lists, total
+
+
+def _serialise(B: int, units: Sequence[Unit], lists: Sequence[Sequence[Segment]],
+               kv_tile: int, q_tile: int, total_tiles: int) -> np.ndarray:
+    W = len(lists)
+    U = len(units)
+    segs = [s for lst in lists for s in lst]
+    S = len(segs)
+    worker_ptr = [0]
+    for lst in lists:
+        worker_ptr.append(worker_ptr[-1] + len(lst))
+    # segments are in stream order, which is unit-major, so each unit's segments are contiguous
+    unit_index = {(u.b, u.qt): i for i, u in enumerate(units)}
+    counts = [0] * U
+    last = -1
+    for s in segs:
+        ui = unit_index[(s.b, s.qt)]
+        if ui < last:
+            raise AssertionError("segments are not unit-major")
+        last = ui
+        counts[ui] += 1
+    unit_ptr = [0]
+    for c in counts:
+        unit_ptr.append(unit_ptr[-1] + c)
+    words = [MAP_VERSION, B, W, kv_tile, S, total_tiles, q_tile, U]
+    words += worker_ptr
+    words += unit_ptr
+    for u in units:
+        words += [u.b, u.qt]
+    for s in segs:
+        words += [s.b, s.qt, s.kv_begin, s.kv_end]
+    return np.asarray(words, dtype=np.int32)
+
+
+def decode_units(seq_lens: Sequence[int]) -> List[Unit]:
+    """Decode: one unit per request; a single query token at position L_b - 1 sees keys [0, L_b)."""
+    for L in seq_lens:
+        if L < 0:
+            raise ValueError("negative sequence length")
+    return [Unit(b, 0, int(L)) for b, L in enumerate(seq_lens)]
+
+
+def ref_plan(seq_lens: Sequence[int], num_workers: int, tile: int) -> np.ndarray:
+    """Dynamic (load-balanced) decode work map, [P3] §3.1 方案 steps 1-4, [P2] budget formula."""
+    _check_common(num_workers, tile)
+    units = decode_units(seq_lens)
+    lists, total = _greedy_fill(units, num_workers, tile)
+    return _serialise(len(seq_lens), units, lists, tile, 1, total)
+
+
+def ref_plan_static(seq_lens: Sequence[int], num_splits: int, tile: int) -> np.ndarray:
+    """Static split-KV baseline ([P3] §3.1 问题; [P4] §二.1): one fixed split count for the batch.
+
+    Request b is cut into k_b = min(num_splits, n_b) tile-aligned chunks whose tile counts
+    differ by at most one (the larger chunks first); every chunk is a worker of its own with one
+    segment, so the worker count is sum(k_b) and depends on the batch.
+    """
+    if num_splits < 1:
+        raise ValueError("num_splits must be >= 1")
+    _check_common(1, tile)
+    units = decode_units(seq_lens)
+    lists: List[List[Segment]] = []
+    total = 0
+    for u in units:
+        n = tiles_of(u.extent, tile)
+        total += n
+        k = min(num_splits, n)
+        if k == 0:
+            continue
+        small, big_count = divmod(n, k)
+        t0 = 0
+        for c in range(k):
+            size = small + (1 if c < big_count else 0)
+            lists.append([Segment(u.b, 0, t0 * tile, min(u.extent, (t0 + size) * tile))])
+            t0 += size
+        assert t0 == n
+    return _serialise(len(seq_lens), units, lists, tile, 1, total)
+
+
+def prefill_units(q_lens: Sequence[int], kv_lens: Sequence[int], q_tile: int, causal: bool) -> List[Unit]:
+    """Chunked prefill over a cached prefix: units are q_tile-row blocks of each request's chunk.
+
+    Query row j of request b sits at absolute position kv_len_b - q_len_b + j (the chunk is the
+    last q_len_b tokens of the context); under the causal mask it sees keys [0, that position].
+    A unit's KV extent is therefore set by its last row.
+    """
+    if len(q_lens) != len(kv_lens):
+        raise ValueError("q_lens and kv_lens differ in length")
+    if q_tile < 1:
+        raise ValueError("q_tile must be >= 1")
+    units = []
+    for b, (ql, kl) in enumerate(zip(q_lens, kv_lens)):
+        if ql < 0 or kl < 0 or ql > kl:
+            raise ValueError("need 0 <= q_len <= kv_len")
+        for i in range(tiles_of(ql, q_tile)):
+            if causal:
+                extent = kl - ql + min(ql, (i + 1) * q_tile)
+            else:
+                extent = kl
+            units.append(Unit(b, i, extent))
+    return units
+
+
+def ref_plan_prefill(q_lens: Sequence[int], kv_lens: Sequence[int], num_workers: int,
+                     q_tile: int, kv_tile: int, causal: bool) -> np.ndarray:
+    """Same greedy equal-budget fill, over (request, q-tile) units instead of requests."""
+    _check_common(num_workers, kv_tile)
+    units = prefill_units(q_lens, kv_lens, q_tile, causal)
+    lists, total = _greedy_fill(units, num_workers, kv_tile)
+    return _serialise(len(q_lens), units, lists, kv_tile, q_tile, total)
+
+
+# ----------------------------------------------------------------------------------------------
+# Reading a map back (used by tests and by the attention oracle's split helpers)
+
+@dataclass
+class WorkMap:
+    version: int
+    B: int
+    W: int
+    kv_tile: int
+    S: int
+    T: int
+    q_tile: int
+    U: int
+    worker_ptr: np.ndarray
+    unit_ptr: np.ndarray
+    units: np.ndarray      # [U, 2]
+    segs: np.ndarray       # [S, 4]
+
+    def worker_segments(self, w: int) -> np.ndarray:
+        return self.segs[self.worker_ptr[w]:self.worker_ptr[w + 1]]
+
+    def unit_segments(self, u: int) -> np.ndarray:
+        return self.segs[self.unit_ptr[u]:self.unit_ptr[u + 1]]
+
+
+def parse_map(words: np.ndarray) -> WorkMap:
+    words = np.asarray(words, dtype=np.int64)
+    version, B, W, kv_tile, S, T, q_tile, U = (int(x) for x in words[:HEADER_WORDS])
+    o = HEADER_WORDS
+    worker_ptr = words[o:o + W + 1]; o += W + 1
+    unit_ptr = words[o:o + U + 1]; o += U + 1
+    units = words[o:o + 2 * U].reshape(U, 2); o += 2 * U
+    segs = words[o:o + 4 * S].reshape(S, 4); o += 4 * S
+    if o != len(words):
+        raise ValueError(f"map has {len(words)} words, layout implies {o}")
+    return WorkMap(version, B, W, kv_tile, S, T, q_tile, U, worker_ptr, unit_ptr, units, segs)
+
+
+def map_words(num_units: int, num_workers: int, num_segments: int) -> int:
+    """Exact word count of a map with the given counts."""
+    return HEADER_WORDS + (num_workers + 1) + (num_units + 1) + 2 * num_units + 4 * num_segments

@@ -1,0 +1,276 @@
+"""Pins for the oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` function takes the oracle function(s) under test as arguments and
+raises AssertionError when they disagree with what the pages or the mathematics
+fix.  ``test_oracle_*.py`` runs every pin on the real oracle; ``test_oracle_mutations.py``
+runs them on copies of the oracle with a planted mistake and requires that some
+pin fails for each.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ------------------------------------------------------------------------------------------------
+# Brute force: a pure-Python softmax with exact summation (math.fsum), written from the definition.
+
+def brute_attention(q, k, v, scale, q_len, kv_len, causal, first_row=0):
+    """q: nested [R][Hq][D] floats, k/v: [L][Hkv][D].  Returns [R][Hq][D]."""
+    R = len(q)
+    Hq = len(q[0])
+    D = len(q[0][0])
+    Hkv = len(k[0]) if kv_len else 1
+    per = Hq // Hkv
+    out = []
+    for j in range(R):
+        row = []
+        last = (kv_len - q_len + first_row + j) if causal else kv_len - 1
+        for h in range(Hq):
+            g = h // per
+            keys = [t for t in range(kv_len) if t <= last]
+            if not keys:
+                row.append([0.0] * D)
+                continue
+            s = [scale * math.fsum(q[j][h][d] * k[t][g][d] for d in range(D)) for t in keys]
+            mx = max(s)
+            p = [math.exp(x - mx) for x in s]
+            den = math.fsum(p)
+            row.append([math.fsum(p[i] * v[t][g][d] for i, t in enumerate(keys)) / den for d in range(D)])
+        out.append(row)
+    return out
+
+
+def _bf16_np(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(*shape, generator=g).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def pin_bruteforce_decode(ref_attention, trials=12):
+    """Decode rows (one query at position L-1) against the fsum brute force, Hq=4, Hkv=2."""
+    for t in range(trials):
+        L = 1 + (t * 5) % 12
+        D = 1 + t % 4
+        q = _bf16_np((1, 4, D), 10 + t)
+        k = _bf16_np((L, 2, D), 20 + t)
+        v = _bf16_np((L, 2, D), 30 + t)
+        scale = 1.0 / math.sqrt(D) * (1.0 + 0.37 * t)
+        got = ref_attention(q, k, v, scale, causal=True)
+        exp = np.array(brute_attention(q.tolist(), k.tolist(), v.tolist(), scale, 1, L, True))
+        assert np.allclose(got, exp, rtol=1e-13, atol=1e-13), f"decode trial {t}"
+
+
+def pin_bruteforce_prefill(ref_attention, trials=8):
+    """Causal chunk rows after a cached prefix, and the non-causal case, against brute force."""
+    for t in range(trials):
+        prefix = t % 5
+        R = 1 + (t * 3) % 6
+        L = prefix + R
+        D = 2 + t % 3
+        q = _bf16_np((R, 4, D), 40 + t)
+        k = _bf16_np((L, 2, D), 50 + t)
+        v = _bf16_np((L, 2, D), 60 + t)
+        scale = 0.5 + 0.1 * t
+        for causal in (True, False):
+            got = ref_attention(q, k, v, scale, causal=causal)
+            exp = np.array(brute_attention(q.tolist(), k.tolist(), v.tolist(), scale, R, L, causal))
+            assert np.allclose(got, exp, rtol=1e-13, atol=1e-13), f"prefill trial {t} causal={causal}"
+
+
+def pin_closed_forms(ref_attention):
+    """Closed forms that any exact softmax attention must satisfy."""
+    rng = np.random.default_rng(7)
+    L, Hq, Hkv, D = 37, 8, 2, 16
+    q = rng.standard_normal((1, Hq, D))
+    k = rng.standard_normal((L, Hkv, D))
+    # all value rows equal c -> output c
+    c = rng.standard_normal(D)
+    v = np.broadcast_to(c, (L, Hkv, D)).copy()
+    out = ref_attention(q, k, v, 0.3)
+    assert np.allclose(out, np.broadcast_to(c, out.shape), atol=1e-12)
+    # q = 0 -> uniform weights -> mean of the value rows
+    v = rng.standard_normal((L, Hkv, D))
+    out = ref_attention(np.zeros_like(q), k, v, 0.3)
+    for h in range(Hq):
+        assert np.allclose(out[0, h], v[:, h // (Hq // Hkv)].mean(axis=0), atol=1e-12)
+    # one key -> its value row
+    out = ref_attention(q, k[:1], v[:1], 0.3)
+    for h in range(Hq):
+        assert np.allclose(out[0, h], v[0, h // (Hq // Hkv)], atol=1e-12)
+    # a single dominant key: softmax puts (almost) all weight on it
+    k2 = k.copy()
+    k2[11] = 40.0 * q[0, 0] / np.linalg.norm(q[0, 0])          # head 0 aligns with key 11
+    out = ref_attention(q, k2, v, 1.0)
+    assert np.allclose(out[0, 0], v[11, 0], atol=1e-9)
+    # heads of one group with equal queries give equal outputs; heads of another group differ
+    q3 = np.repeat(q[:, :1], Hq, axis=1)
+    out = ref_attention(q3, k, v, 0.3)
+    per = Hq // Hkv
+    for h in range(Hq):
+        assert np.allclose(out[0, h], out[0, (h // per) * per], atol=1e-14)
+    assert not np.allclose(out[0, 0], out[0, per])
+
+
+def pin_gqa_head_map(ref_attention):
+    """Changing KV head g changes exactly the query heads g*per .. g*per+per-1."""
+    rng = np.random.default_rng(8)
+    L, Hq, Hkv, D = 9, 8, 4, 8
+    q = rng.standard_normal((1, Hq, D))
+    k = rng.standard_normal((L, Hkv, D))
+    v = rng.standard_normal((L, Hkv, D))
+    base = ref_attention(q, k, v, 0.5)
+    per = Hq // Hkv
+    for g in range(Hkv):
+        v2 = v.copy()
+        v2[:, g] += 1.0
+        out = ref_attention(q, k, v2, 0.5)
+        changed = [h for h in range(Hq) if not np.allclose(out[0, h], base[0, h])]
+        assert changed == list(range(g * per, (g + 1) * per)), (g, changed)
+
+
+def pin_library_sdpa(ref_attention):
+    """With no cached prefix the causal chunk is textbook causal attention: compare against
+    torch's scaled_dot_product_attention in float64 (GQA expanded by repeating KV heads)."""
+    g = torch.Generator().manual_seed(3)
+    for (R, Hq, Hkv, D, prefix) in [(13, 8, 2, 16, 0), (7, 4, 4, 8, 0), (5, 8, 1, 32, 0)]:
+        q = torch.randn(R, Hq, D, generator=g, dtype=torch.float64)
+        k = torch.randn(R + prefix, Hkv, D, generator=g, dtype=torch.float64)
+        v = torch.randn(R + prefix, Hkv, D, generator=g, dtype=torch.float64)
+        per = Hq // Hkv
+        kk = k.repeat_interleave(per, dim=1).permute(1, 0, 2)
+        vv = v.repeat_interleave(per, dim=1).permute(1, 0, 2)
+        exp = torch.nn.functional.scaled_dot_product_attention(
+            q.permute(1, 0, 2), kk, vv, is_causal=True, scale=0.25).permute(1, 0, 2).numpy()
+        got = ref_attention(q.numpy(), k.numpy(), v.numpy(), 0.25, causal=True)
+        assert np.allclose(got, exp, rtol=1e-12, atol=1e-12)
+        exp_nc = torch.nn.functional.scaled_dot_product_attention(
+            q.permute(1, 0, 2), kk, vv, is_causal=False, scale=0.25).permute(1, 0, 2).numpy()
+        got_nc = ref_attention(q.numpy(), k.numpy(), v.numpy(), 0.25, causal=False)
+        assert np.allclose(got_nc, exp_nc, rtol=1e-12, atol=1e-12)
+
+
+def pin_combine_invariance(ref_attention, ref_partial, ref_combine, trials=30):
+    """Any partition of the KV range, merged by combine, equals the unsplit result (fp64)."""
+    rng = np.random.default_rng(11)
+    for t in range(trials):
+        L = int(rng.integers(1, 200))
+        R = int(rng.integers(1, 5))
+        causal = bool(t % 2)
+        Lctx = L + (R if causal else 0)
+        q = rng.standard_normal((R, 4, 8)) * 2.0
+        k = rng.standard_normal((Lctx, 2, 8))
+        v = rng.standard_normal((Lctx, 2, 8))
+        cuts = sorted(set([0, Lctx] + rng.integers(0, Lctx + 1, size=int(rng.integers(0, 8))).tolist()))
+        # include a one-token piece and an empty piece
+        parts = [ref_partial(q, k, v, 0.4, a, e, causal) for a, e in zip(cuts[:-1], cuts[1:])]
+        parts.append(ref_partial(q, k, v, 0.4, Lctx, Lctx, causal))
+        got = ref_combine(parts)
+        exp = ref_attention(q, k, v, 0.4, causal=causal)
+        assert np.allclose(got, exp, rtol=1e-13, atol=1e-13), f"trial {t}"
+
+
+def pin_partial_definition(ref_partial):
+    """(m, l, o) of a piece against the fsum brute force of its own definition."""
+    rng = np.random.default_rng(12)
+    L, D = 10, 3
+    q = rng.standard_normal((1, 2, D))
+    k = rng.standard_normal((L, 1, D))
+    v = rng.standard_normal((L, 1, D))
+    a, e = 3, 8
+    m, l, o = ref_partial(q, k, v, 0.7, a, e, True)
+    for h in range(2):
+        s = [0.7 * math.fsum(q[0, h, d] * k[t, 0, d] for d in range(D)) for t in range(a, e)]
+        mx = max(s)
+        assert abs(m[0, h] - mx) < 1e-14
+        assert abs(l[0, h] - math.fsum(math.exp(x - mx) for x in s)) < 1e-13
+        for d in range(D):
+            ref = math.fsum(math.exp(s[i] - mx) * v[a + i, 0, d] for i in range(e - a))
+            assert abs(o[0, h, d] - ref) < 1e-13
+    # a piece with no visible key
+    m, l, o = ref_partial(q, k, v, 0.7, 5, 5, True)
+    assert np.all(np.isneginf(m)) and np.all(l == 0) and np.all(o == 0)
+
+
+# ------------------------------------------------------------------------------------------------
+# Planner pins
+
+def load_worked_example():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        return json.load(f)
+
+
+def pin_worked_example(ref_plan, parse_map):
+    """The pages' worked example: tiles 2/10/4, 4 tiles per worker, the long request spans workers."""
+    ex = load_worked_example()
+    mp = parse_map(ref_plan(ex["seq_lens"], ex["num_workers"], ex["tile"]))
+    assert mp.T == sum(ex["tiles_per_request"])
+    per_req = [0] * len(ex["seq_lens"])
+    per_worker = []
+    for w in range(mp.W):
+        n = 0
+        for b, _, a, e in mp.worker_segments(w):
+            t = -(-(int(e) - int(a)) // ex["tile"])
+            per_req[b] += t
+            n += t
+        per_worker.append(n)
+    assert per_req == ex["tiles_per_request"]
+    assert per_worker == ex["tiles_per_worker"]
+    workers_of = {}
+    for w in range(mp.W):
+        for b, *_ in mp.worker_segments(w):
+            workers_of.setdefault(int(b), set()).add(w)
+    assert ex["long_request_spans_workers"] == (len(workers_of[1]) > 1)
+
+
+def _worker_of_stream_index(j, T, W):
+    """Closed form of the contiguous fill: the first rem workers own base+1 consecutive indices."""
+    base, rem = divmod(T, W)
+    if j < rem * (base + 1):
+        return j // (base + 1)
+    return rem + (j - rem * (base + 1)) // base
+
+
+def pin_fill_closed_form(ref_plan, parse_map, trials=400, seed=5):
+    """Rebuild every segment from the per-tile closed form above and compare with the map."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        B = int(rng.integers(0, 9))
+        tile = int(rng.choice([1, 3, 64, 512]))
+        lens = [int(x) for x in rng.integers(0, 6 * tile + 2, size=B)]
+        W = int(rng.integers(1, 12))
+        mp = parse_map(ref_plan(lens, W, tile))
+        stream = [(b, t) for b, L in enumerate(lens) for t in range(-(-L // tile))]
+        T = len(stream)
+        assert mp.T == T and mp.W == W and mp.U == B and mp.B == B
+        expect = [[] for _ in range(W)]
+        for j, (b, t) in enumerate(stream):
+            w = _worker_of_stream_index(j, T, W)
+            lst = expect[w]
+            if lst and lst[-1][0] == b and lst[-1][3] == t * tile:
+                lst[-1][3] = min(lens[b], (t + 1) * tile)
+            else:
+                lst.append([b, 0, t * tile, min(lens[b], (t + 1) * tile)])
+        for w in range(W):
+            assert mp.worker_segments(w).tolist() == expect[w], (lens, W, tile, w)
+
+
+def pin_budget_rule(ref_plan, parse_map, trials=300, seed=6):
+    """[P2]'s budgets: base = T // W for everyone, one extra for the first T % W workers."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        lens = [int(x) for x in rng.integers(0, 5000, size=int(rng.integers(1, 7)))]
+        W = int(rng.integers(1, 40))
+        mp = parse_map(ref_plan(lens, W, 512))
+        got = []
+        for w in range(W):
+            got.append(sum(-(-(int(e) - int(a)) // 512) for _, _, a, e in mp.worker_segments(w)))
+        T = sum(-(-L // 512) for L in lens)
+        base, rem = T // W, T % W
+        assert got == [base + 1] * rem + [base] * (W - rem), (lens, W, got)

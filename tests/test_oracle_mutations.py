@@ -1,0 +1,100 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require that the pins catch
+each one.  This checks the pins, not the oracle: a pin set that a dropped term, a wrong sign or
+index, or a transposed operand slips through would not be worth much."""
+
+import importlib.util
+import os
+import sys
+import types
+
+import pytest
+
+import oracle_pins as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _load_mutant(module: str, old: str, new: str, count: int = 1) -> types.ModuleType:
+    path = os.path.join(ROOT, "oracle", module + ".py")
+    src = open(path).read()
+    assert src.count(old) >= count, f"mutation anchor not found: {old!r}"
+    src = src.replace(old, new)
+    name = f"oracle_mutant_{module}_{abs(hash((old, new)))}"
+    spec = importlib.util.spec_from_loader(name, loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    mod.__dict__["__package__"] = "oracle"
+    sys.modules[name] = mod
+    exec(compile(src, path, "exec"), mod.__dict__)
+    return mod
+
+
+def _attention_pins(m):
+    return [
+        lambda: P.pin_bruteforce_decode(m.ref_attention),
+        lambda: P.pin_bruteforce_prefill(m.ref_attention),
+        lambda: P.pin_closed_forms(m.ref_attention),
+        lambda: P.pin_gqa_head_map(m.ref_attention),
+        lambda: P.pin_library_sdpa(m.ref_attention),
+        lambda: P.pin_combine_invariance(m.ref_attention, m.ref_partial, m.ref_combine, trials=10),
+        lambda: P.pin_partial_definition(m.ref_partial),
+    ]
+
+
+def _plan_pins(m):
+    return [
+        lambda: P.pin_worked_example(m.ref_plan, m.parse_map),
+        lambda: P.pin_fill_closed_form(m.ref_plan, m.parse_map, trials=200),
+        lambda: P.pin_budget_rule(m.ref_plan, m.parse_map, trials=100),
+    ]
+
+
+def _caught(pins) -> bool:
+    for pin in pins:
+        try:
+            pin()
+        except Exception:
+            return True
+    return False
+
+
+ATTENTION_MUTANTS = {
+    "dropped scale": ("s = scale * (qg", "s = (qg"),
+    "wrong sign in exponent": ("np.exp(s - np.where", "np.exp(s + np.where"),
+    "causal bound off by one": ("first_row + np.arange(rows) + 1", "first_row + np.arange(rows)"),
+    "mask keeps the diagonal+1": ("pos[None, :] < upto", "pos[None, :] <= upto"),
+    "interleaved GQA head map": ("g * group:(g + 1) * group", "g::Hkv"),
+    "keys used as values": ("p.reshape(-1, e - a) @ vg", "p.reshape(-1, e - a) @ kg"),
+    "dropped first term of the sum": ("= p.sum(axis=2)", "= p[:, :, 1:].sum(axis=2)"),
+    "combine without max shift weights": ("w = np.where(np.isfinite(ms), np.exp(ms - np.where(has, M, 0.0)[None]), 0.0)",
+                                          "w = np.where(np.isfinite(ms), 1.0, 0.0)"),
+    "combine divides by split count": ("Lsum = (w * ls).sum(axis=0)", "Lsum = (w * ls).sum(axis=0) * 0 + len(parts)"),
+}
+
+PLAN_MUTANTS = {
+    "floor tile count": ("return ceil_div(extent, tile) if extent > 0 else 0", "return extent // tile"),
+    "extra tiles to the last workers": ("base + (1 if w < rem else 0)", "base + (1 if w >= workers - rem else 0)"),
+    "end not clipped to the request": ("min(u.extent, (t_last + 1) * tile)", "(t_last + 1) * tile"),
+    "off-by-one segment start": ("Segment(u.b, u.qt, t_first * tile,", "Segment(u.b, u.qt, t_last * tile,"),
+    "budget ignores the remainder": ("base, rem = divmod(total_tiles, workers)", "base, rem = -(-total_tiles // workers), 0"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ATTENTION_MUTANTS))
+def test_attention_mutant_is_caught(name):
+    old, new = ATTENTION_MUTANTS[name]
+    m = _load_mutant("attention", old, new, count=1)
+    assert _caught(_attention_pins(m)), f"no pin catches: {name}"
+
+
+@pytest.mark.parametrize("name", sorted(PLAN_MUTANTS))
+def test_plan_mutant_is_caught(name):
+    old, new = PLAN_MUTANTS[name]
+    m = _load_mutant("plan", old, new, count=1)
+    assert _caught(_plan_pins(m)), f"no pin catches: {name}"
+
+
+def test_unmutated_oracle_passes_all_pins():
+    import oracle.attention as A
+    import oracle.plan as Pl
+    for pin in _attention_pins(A) + _plan_pins(Pl):
+        pin()

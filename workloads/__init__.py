@@ -1,0 +1,160 @@
+"""Seeded synthetic inputs for load-balanced split-KV attention.
+
+Shared by both sides of every parity check (the float64 oracle and the GPU
+library's harness).  This module holds random draws and the workload recipes
+only: it contains none of the method's arithmetic (no tile cut, no scheduling,
+no softmax), and it imports neither the oracle nor the GPU library.
+
+Shapes follow the model the pages describe ([P3] "Hy3 Preview AI Infra 推理优化
+精读笔记" §2: 64 attention heads, 8 KV heads, head dim 128) and the request
+length mix their workload section gives (§1 and §12.1 of the same page: inputs
+up to about 192K tokens, buckets 1K/4K/16K/64K/128K mixed in one batch; [P3] §6
+and [P1] §3.4: prefix-cache reuse, about 80% hit rate).  The pages measure on a
+private production trace that is not available; these synthetic batches stand
+in for it.
+
+Every value is drawn N(0, 1) in float32 from a seeded ``torch.Generator`` on the
+CPU and rounded to bfloat16 (round to nearest even); both sides then see the
+same bf16 values.  Seeds: ``seed_for(workload_id, stream, index)`` with streams
+0 = lengths / order, 1 = page permutation, 2 = Q, 3 = K, 4 = V; K and V are
+drawn per request so a long batch can be generated and checked one request at a
+time.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Tuple
+
+import torch
+
+HQ = 64
+HKV = 8
+HEAD_DIM = 128
+PAGE = 64
+TILE = 512
+Q_TILE = 128
+
+STREAM_LENGTHS, STREAM_PAGES, STREAM_Q, STREAM_K, STREAM_V = 0, 1, 2, 3, 4
+
+
+def seed_for(workload_id: int, stream: int, index: int = 0) -> int:
+    return workload_id * 1_000_000 + stream * 10_000 + index
+
+
+def randn_bf16(shape, seed: int) -> torch.Tensor:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    return torch.randn(*shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+
+
+@dataclass
+class Workload:
+    """One synthetic batch: KV lengths (and, for prefill, query-chunk lengths)."""
+    name: str
+    workload_id: int
+    kv_lens: List[int]
+    q_lens: List[int]                 # 1 per request for decode
+    kind: str = "decode"              # "decode" or "prefill"
+    workers: Optional[int] = None     # fixed worker count (None: from the device)
+    paged: bool = True                # False: identity block table (contiguous pages)
+    hq: int = HQ
+    hkv: int = HKV
+    head_dim: int = HEAD_DIM
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return len(self.kv_lens)
+
+    def q(self, b: Optional[int] = None) -> torch.Tensor:
+        """Decode: all queries [B, Hq, D].  Prefill: request b's chunk [q_len_b, Hq, D]."""
+        if self.kind == "decode":
+            return randn_bf16((self.batch, self.hq, self.head_dim), seed_for(self.workload_id, STREAM_Q))
+        return randn_bf16((self.q_lens[b], self.hq, self.head_dim), seed_for(self.workload_id, STREAM_Q, b))
+
+    def kv(self, b: int) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Request b's keys and values, each [L_b, Hkv, D] bf16, token-major."""
+        L = self.kv_lens[b]
+        k = randn_bf16((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_K, b))
+        v = randn_bf16((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_V, b))
+        return k, v
+
+    def page_permutation(self, num_pages: int) -> torch.Tensor:
+        """Physical page for each logical page (a seeded shuffle; identity when not paged)."""
+        if not self.paged:
+            return torch.arange(num_pages)
+        g = torch.Generator(device="cpu")
+        g.manual_seed(seed_for(self.workload_id, STREAM_PAGES))
+        return torch.randperm(num_pages, generator=g)
+
+    def kv_bytes(self) -> int:
+        return sum(self.kv_lens) * self.hkv * self.head_dim * 2 * 2
+
+
+def _shuffled(values: List[int], seed: int) -> List[int]:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    order = torch.randperm(len(values), generator=g).tolist()
+    return [values[i] for i in order]
+
+
+def tiny() -> Workload:
+    """The pages' worked example ([P3] §3.1 方案): KV lengths 1024, 5120, 2048; 4 workers."""
+    return Workload("tiny", 1, [1024, 5120, 2048], [1, 1, 1], workers=4, paged=False)
+
+
+def uniform() -> Workload:
+    """64 requests at 8192 tokens each."""
+    return Workload("uniform", 2, [8192] * 64, [1] * 64)
+
+
+def mixed() -> Workload:
+    """8 requests at each of 1K, 4K, 16K, 64K and 128K tokens (K = 1024), order shuffled."""
+    lens = [n * 1024 for n in (1, 4, 16, 64, 128) for _ in range(8)]
+    lens = _shuffled(lens, seed_for(3, STREAM_LENGTHS))
+    return Workload("mixed", 3, lens, [1] * len(lens))
+
+
+def long_tail() -> Workload:
+    """One 192K-token request followed by 15 requests of uniform length in [1024, 2048]."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_for(4, STREAM_LENGTHS))
+    tail = torch.randint(1024, 2049, (15,), generator=g).tolist()
+    lens = [196608] + tail
+    return Workload("long_tail", 4, lens, [1] * len(lens))
+
+
+def prefill(chunk: int = 2048, requests: int = 8) -> Workload:
+    """Chunked causal prefill: per request a ``chunk``-row query chunk after a cached prefix whose
+    length is log-uniform in [8K, 128K] tokens."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_for(5, STREAM_LENGTHS))
+    u = torch.rand(requests, generator=g, dtype=torch.float64).tolist()
+    lo, hi = math.log(8192), math.log(131072)
+    prefixes = [int(round(math.exp(lo + x * (hi - lo)))) for x in u]
+    kv = [p + chunk for p in prefixes]
+    return Workload("prefill", 5, kv, [chunk] * requests, kind="prefill", meta={"prefix": prefixes})
+
+
+def random_decode(seed: int, batch: int, max_len: int, min_len: int = 0, hq: int = HQ, hkv: int = HKV,
+                  head_dim: int = HEAD_DIM, paged: bool = True) -> Workload:
+    """Small seeded decode batches for parity tests (ragged lengths, empty requests allowed)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_for(100 + seed, STREAM_LENGTHS))
+    lens = torch.randint(min_len, max_len + 1, (batch,), generator=g).tolist()
+    return Workload(f"random_decode_{seed}", 100 + seed, lens, [1] * batch, hq=hq, hkv=hkv,
+                    head_dim=head_dim, paged=paged)
+
+
+def random_prefill(seed: int, batch: int, max_prefix: int, max_chunk: int) -> Workload:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_for(200 + seed, STREAM_LENGTHS))
+    prefix = torch.randint(0, max_prefix + 1, (batch,), generator=g).tolist()
+    chunk = torch.randint(1, max_chunk + 1, (batch,), generator=g).tolist()
+    return Workload(f"random_prefill_{seed}", 200 + seed, [p + c for p, c in zip(prefix, chunk)], chunk,
+                    kind="prefill", meta={"prefix": prefix})
+
+
+BY_NAME = {"tiny": tiny, "uniform": uniform, "mixed": mixed, "long_tail": long_tail, "prefill": prefill}
