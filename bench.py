@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+A step is one pass of the whole hot path for one layer: the split-KV kernel over the work map and
+the combine kernel, with the map already on the device (it is built once per inference step and
+shared by all layers).  Default workload: the mixed-length batch - 40 requests, 8 each at KV
+lengths 1K, 4K, 16K, 64K and 128K tokens, one query token each, 64 query / 8 KV heads, head dim
+128, bf16, 64-token pages in a shuffled block table, 512-token tiles.
+
+Prints one JSON line: whole-step throughput in TB/s of algorithmic bytes (KV + Q + fp32 output +
+block table + lengths), the split-KV kernel's roofline fraction, the fp64 CPU oracle timed on a
+bounded sample, the static split-KV baseline and the per-CU busy spread.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "mixed-length GQA decode attention: achieved HBM TB/s (% peak) and µs/step"
+PEAK_HBM_GBS = 8000.0
+DESCRIPTIONS = {
+    "mixed": "mixed-length decode: B=40, 8 each of KV 1K/4K/16K/64K/128K (shuffled), 1 query token, "
+             "GQA 64q/8kv, d=128, bf16, paged 64-token KV (shuffled block table), tile 512",
+    "uniform": "uniform decode: B=64 x KV 8192, 1 query token, GQA 64q/8kv, d=128, bf16, paged 64-token KV "
+               "(shuffled block table), tile 512",
+    "long_tail": "single long request plus short tail: KV 192K + 15 x U[1K,2K], 1 query token, GQA 64q/8kv, "
+                 "d=128, bf16, paged 64-token KV (shuffled block table), tile 512",
+    "tiny": "worked example: KV 1024/5120/2048, 1 query token, GQA 64q/8kv, d=128, bf16, contiguous pages, "
+            "tile 512, 4 workers",
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl, page: int) -> dict:
+    tokens = sum(wl.kv_lens)
+    pages = sum(-(-L // page) for L in wl.kv_lens)
+    kv = tokens * wl.hkv * wl.head_dim * 2 * 2
+    q = wl.batch * wl.hq * wl.head_dim * 2
+    out = wl.batch * wl.hq * wl.head_dim * 4
+    table = pages * 4
+    lens = wl.batch * 4
+    return {"kv": kv, "q": q, "out": out, "block_table": table, "seq_lens": lens,
+            "step": kv + q + out + table + lens, "splitkv": kv + q + table + lens}
+
+
+def per_cu_busy(timing) -> dict:
+    """Union of [start, end) per compute unit (HW_ID CU/SH/SE fields + XCC_ID)."""
+    import numpy as np
+    t = timing.cpu().numpy().astype(np.int64)
+    hw = t[:, 2]
+    key = (t[:, 3] & 0xF) * 4096 + ((hw >> 13) & 0x7) * 512 + ((hw >> 12) & 1) * 256 + ((hw >> 8) & 0xF)
+    busy = {}
+    for k in np.unique(key):
+        iv = sorted(zip(t[key == k, 0].tolist(), t[key == k, 1].tolist()))
+        total, cs, ce = 0, iv[0][0], iv[0][1]
+        for s, e in iv[1:]:
+            if s > ce:
+                total += ce - cs
+                cs, ce = s, e
+            else:
+                ce = max(ce, e)
+        total += ce - cs
+        busy[int(k)] = total
+    vals = np.array(list(busy.values()), dtype=np.float64)
+    span = float(t[:, 1].max() - t[:, 0].min())
+    return {"cus_seen": int(len(vals)), "max_over_mean": float(vals.max() / vals.mean()),
+            "tail_fraction": float((vals.max() - vals.mean()) / vals.max()),
+            "mean_busy_over_span": float(vals.mean() / span), "workgroups": int(t.shape[0])}
+
+
+def time_steps(fn_split, fn_combine, steps: int, warmup: int, rotate):
+    import torch
+    for i in range(warmup):
+        fn_split(i)
+        fn_combine(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        a, b, c = ev[i]
+        a.record()
+        fn_split(i)
+        b.record()
+        fn_combine(i)
+        c.record()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    split_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+    return {"total_ms": t0.elapsed_time(t1), "wall_s": wall, "split_ms": split_ms, "step_ms": step_ms}
+
+
+def cpu_oracle_baseline(wl, budget_s: float, scale: float) -> dict:
+    import numpy as np
+    import torch
+    from oracle.attention import ref_attention
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    q = wl.q().to(torch.float64).numpy()
+    # the batch's requests in order until the time budget is used (input generation and the
+    # bf16 -> fp64 widening are not timed)
+    spent, tokens, done = 0.0, 0, []
+    for b in range(wl.batch):
+        k, v = wl.kv(b)
+        kd, vd = k.to(torch.float64).numpy(), v.to(torch.float64).numpy()
+        t = time.perf_counter()
+        ref_attention(q[b:b + 1], kd, vd, scale)
+        spent += time.perf_counter() - t
+        tokens += wl.kv_lens[b]
+        done.append(wl.kv_lens[b])
+        if spent >= budget_s:
+            break
+    kv_bytes = tokens * wl.hkv * wl.head_dim * 2 * 2
+    return {"value": kv_bytes / spent / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle (numpy) on the first {len(done)} of {wl.batch} requests of the same batch "
+                      f"({tokens} KV tokens), {spent:.1f} s of CPU time; bf16 KV bytes / time",
+            "seconds": spent, "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count()}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixed", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--workers", type=int, default=None, help="work lists (default: fill the device once)")
+    ap.add_argument("--head-groups", type=int, default=8)
+    ap.add_argument("--tile", type=int, default=512)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-static", action="store_true")
+    ap.add_argument("--static-steps", type=int, default=10)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (decode attention shards by "
+              "request or KV head with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import load_balanced_split_attn_amd as lb
+    import workloads as WL
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    from load_balanced_split_attn_amd.paged import pack_paged
+
+    lb.lib()
+    dev = torch.device("cuda:0")
+    wl = WL.BY_NAME[args.workload]()
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    page = 64
+    nbytes = algorithmic_bytes(wl, page)
+    log(f"workload {wl.name}: B={wl.batch} tokens={sum(wl.kv_lens)} KV={nbytes['kv'] / 1e9:.2f} GB")
+
+    t = time.perf_counter()
+    q = wl.q().to(dev)
+    kc, vc, bt = pack_paged(wl.kv, wl.kv_lens, page, wl.hkv, wl.head_dim, wl.page_permutation, dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM ({time.perf_counter() - t:.1f} s)")
+    # below 2 GB of KV, rotate over copies so consecutive steps do not hit the 256 MB MALL
+    copies = 1 if nbytes["kv"] >= 2e9 else min(8, int(math.ceil(2e9 / max(nbytes["kv"], 1))))
+    caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(copies - 1)]
+
+    workers = args.workers or (wl.workers if wl.workers else lb.attn_query_workers(0, args.head_groups))
+    plan_t = time.perf_counter()
+    step = DecodeStep(wl.kv_lens, dev, num_workers=workers, tile=args.tile, head_groups=args.head_groups)
+    plan_s = time.perf_counter() - plan_t
+    t = time.perf_counter()
+    for _ in range(100):
+        lb.attn_plan(wl.kv_lens, workers, args.tile)
+    plan_us = (time.perf_counter() - t) / 100 * 1e6
+    out = torch.empty((wl.batch, wl.hq, wl.head_dim), dtype=torch.float32, device=dev)
+
+    def split(i):
+        k_, v_ = caches[i % copies]
+        step.splitkv(q, k_, v_, bt, scale)
+
+    def comb(i):
+        step.combine(out)
+
+    log(f"dynamic map: W={step.W} G={args.head_groups} S={step.S} T={step.T}; timing {args.steps} steps")
+    r = time_steps(split, comb, args.steps, args.warmup, copies)
+    ms_per_step = r["total_ms"] / args.steps
+    split_ms = float(np.mean(r["split_ms"]))
+    step_med = float(np.median(r["step_ms"]))
+    value = nbytes["step"] / (ms_per_step * 1e-3) / 1e12
+    achieved = nbytes["splitkv"] / (split_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us ({value:.3f} TB/s), splitkv {split_ms * 1e3:.1f} us ({achieved:.0f} GB/s)")
+
+    result = {
+        "metric": METRIC, "value": round(value, 4), "unit": "TB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": DESCRIPTIONS[wl.name], "name": wl.name, "batch": wl.batch,
+                   "kv_tokens": sum(wl.kv_lens), "q_heads": wl.hq, "kv_heads": wl.hkv, "head_dim": wl.head_dim,
+                   "page": page, "tile": args.tile, "workers": step.W, "head_groups": args.head_groups,
+                   "segments": step.S, "tiles": step.T, "cache_copies": copies},
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "us_per_step_p10_p50_p90": [round(float(np.percentile(r["step_ms"], p)) * 1e3, 2) for p in (10, 50, 90)],
+        "pct_peak_hbm": round(100 * value * 1e3 / PEAK_HBM_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "splitkv_decode_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "bytes_per_launch": nbytes["splitkv"],
+                     "avg_launch_us": round(split_ms * 1e3, 2)},
+        "combine_us": round((step_med - float(np.median(r["split_ms"]))) * 1e3, 2),
+        "plan": {"host_us": round(plan_us, 2), "map_words": int(len(step.map_host)),
+                 "first_plan_and_upload_s": round(plan_s, 4)},
+    }
+
+    # per-CU busy spread from the in-kernel timestamps (separate, instrumented run)
+    timing = torch.zeros((step.W * args.head_groups, 4), dtype=torch.int64, device=dev)
+    step.splitkv(q, kc, vc, bt, scale, timing=timing)
+    torch.cuda.synchronize()
+    result["per_cu_busy"] = per_cu_busy(timing)
+
+    if not args.no_static and wl.name != "tiny":
+        max_tiles = max(-(-L // args.tile) for L in wl.kv_lens)
+        plain = min(max(1, -(-step.W // wl.batch)), max_tiles)
+        splits = sorted(set([plain] + [s for s in (1, 2, 4, 8, 16, 32, 64) if s <= max_tiles]))
+        rows = []
+        for S in splits:
+            st = DecodeStep(wl.kv_lens, dev, tile=args.tile, head_groups=args.head_groups, static_splits=S)
+
+            def s_split(i, st=st):
+                k_, v_ = caches[i % copies]
+                st.splitkv(q, k_, v_, bt, scale)
+
+            rs = time_steps(s_split, lambda i, st=st: st.combine(out), args.static_steps, 2, copies)
+            tm = rs["total_ms"] / args.static_steps
+            timing_s = torch.zeros((st.W * args.head_groups, 4), dtype=torch.int64, device=dev)
+            st.splitkv(q, kc, vc, bt, scale, timing=timing_s)
+            torch.cuda.synchronize()
+            rows.append({"splits": S, "workgroups": st.W * args.head_groups, "us_per_step": round(tm * 1e3, 2),
+                         "per_cu_max_over_mean": round(per_cu_busy(timing_s)["max_over_mean"], 3)})
+            log(f"static S={S}: {tm * 1e3:.1f} us")
+        best = min(rows, key=lambda x: x["us_per_step"])
+        plain_row = next(x for x in rows if x["splits"] == plain)
+        result["static_baseline"] = {
+            "plain_splits": plain, "plain_us": plain_row["us_per_step"], "best_splits": best["splits"],
+            "best_us": best["us_per_step"],
+            "speedup_vs_plain": round(plain_row["us_per_step"] / (ms_per_step * 1e3), 3),
+            "speedup_vs_best": round(best["us_per_step"] / (ms_per_step * 1e3), 3), "sweep": rows}
+
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a CPU sample")
+        result["cpu_baseline"] = cpu_oracle_baseline(wl, args.cpu_seconds, scale)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,184 @@
+/*
+ * lbsa.h - load-balanced split-KV attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of liblbsa.so.  Only C types cross it: plain host or device pointers,
+ * sizes and a HIP stream passed as void*.  The library never allocates device
+ * memory, never synchronises the device and keeps no state between calls other
+ * than a cached occupancy query per device.
+ *
+ * The method (sources are web pages; cited by title and section):
+ *   [P3] "Hy3 Preview AI Infra 推理优化精读笔记", §3.1 Attention：动态切分和负载均衡
+ *        (问题 / 方案 / 收益), §2 model table, §14 glossary ("Split-KV", "Tile", "CTA").
+ *   [P4] "腾讯混元AI Infra进化：HPC-Ops推理核心算子全面升级", §二.1 Attention.
+ *   [P1] pwwt.cn explainer of the same article, §3.1 算子优化.
+ *   [P2] "大模型推理性能优化新范式：Hy3架构下的全栈优化技术拆解", §二.1 (budget pseudocode).
+ * Every request's KV range is cut into uniform tiles; the tiles of the whole
+ * batch form one stream; each worker (a workgroup here, a CTA on the pages'
+ * GPU) gets an equal or near-equal tile budget and is filled greedily from the
+ * stream, so a long request spans several workers.  This task map is built
+ * once per inference step and read by the attention kernel of every layer; each
+ * split writes a partial result and a combine kernel merges them.
+ *
+ * Status codes: every entry point returns LBSA_OK (0) or a negative code.
+ * Kernels are asynchronous on the given stream: a device-side fault surfaces at
+ * the caller's next synchronisation, not in the return code.
+ *
+ * ---------------------------------------------------------------------------
+ * Work map: one flat little-endian int32 buffer
+ *
+ *   [0] version (=1)   [1] B  (requests)     [2] W (workers)      [3] kv_tile
+ *   [4] S (segments)   [5] T  (total tiles)  [6] q_tile (1 for decode)
+ *   [7] U (query units: one per request in decode, one per q_tile rows in prefill)
+ *   worker_ptr[W+1]    segments of worker w:  [worker_ptr[w], worker_ptr[w+1])
+ *   unit_ptr[U+1]      segments of unit u:    [unit_ptr[u], unit_ptr[u+1])
+ *   unit[U][2]         (b, q_tile_index)
+ *   seg[S][4]          (b, q_tile_index, kv_begin, kv_end), KV token range, end exclusive
+ *
+ * Segment i is one split and owns partial slot i.  Segments are stored in task
+ * stream order, which is both worker-major and unit-major.  Total words:
+ * 8 + (W+1) + (U+1) + 2U + 4S.
+ *
+ * ---------------------------------------------------------------------------
+ * Tensor layouts (device memory, all caller-owned)
+ *
+ *   q        bf16 [rows, Hq, D]: decode rows = B (one query per request);
+ *                                prefill rows = sum of q_len_b, request b from row q_start[b]
+ *   k_cache  bf16 [num_pages, Hkv, page_size, D]     token-major inside a (page, head) block
+ *   v_cache  bf16 [num_pages, Hkv, D, page_size]     dim-major ("V transposed") inside a block
+ *   block_table int32 [B, block_table_stride]: physical page of logical page p of request b
+ *   part_m, part_l fp32 [S, R, Hq];  part_o fp32 [S, R, Hq, D]   (R = 1 decode, q_tile prefill)
+ *   out      fp32 or bf16 [rows, Hq, D]
+ * Query head h reads KV head h / (Hq / Hkv) (grouped-query attention; [P3] §2:
+ * 64 query heads, 8 KV heads, head dim 128).
+ * Partial (m, l, o) of a split: m = max scaled score (natural-log units),
+ * l = sum exp(s - m), o = sum exp(s - m) v, not divided by l.  A split with no
+ * visible key writes (-inf, 0, 0).
+ */
+#ifndef LBSA_H
+#define LBSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LBSA_OK 0
+#define LBSA_ERR_INVALID (-1)     /* null pointer, negative size, bad shape or alignment      */
+#define LBSA_ERR_CAPACITY (-2)    /* map buffer too small; *map_words_out holds the size needed */
+#define LBSA_ERR_UNSUPPORTED (-3) /* a shape the kernels are not built for (see each call)     */
+#define LBSA_ERR_HIP (-4)         /* HIP runtime error at launch                              */
+
+#define LBSA_MAP_VERSION 1
+#define LBSA_MAP_HEADER_WORDS 8
+
+/* Human-readable name of a status code.  Never returns NULL. */
+const char* attn_status_string(int status);
+
+/*
+ * Upper bound on the words of a map with U units, W workers and at most T tiles:
+ * 8 + (W+1) + (U+1) + 2U + 4*min(T, W+U-1).  Returns -1 if an argument is negative
+ * or the bound does not fit in int32.
+ */
+int32_t attn_map_words(int32_t num_units, int32_t num_workers, int64_t total_tiles_upper);
+
+/*
+ * Dynamic (load-balanced) decode work map ([P3] §3.1 方案 steps 1-4; [P2] budget
+ * rule: base = T / W, the first T % W workers get one more tile).
+ *   seq_lens      host int32[B], KV length of each request (>= 0); the single query of
+ *                 request b sits at position seq_lens[b]-1 and sees keys [0, seq_lens[b])
+ *   num_workers   W >= 1 work lists (one per worker; a worker may be run by several
+ *                 workgroups, one per KV-head group)
+ *   tile          tile size in KV tokens (>= 1; 512 in the pages' worked example)
+ *   map           host int32[map_capacity], written with the layout above
+ *   map_words_out optional (may be NULL): words written, or words needed on
+ *                 LBSA_ERR_CAPACITY
+ * Tile counts are ceilings; the stream is in batch order with tiles ascending;
+ * worker w takes the next budget_w tiles; consecutive tiles of one request inside
+ * one worker form one segment.  Pure host function: reentrant, deterministic,
+ * allocation-free.  Errors: LBSA_ERR_INVALID (null pointer, B < 0, W < 1,
+ * tile < 1, negative length, T beyond int32), LBSA_ERR_CAPACITY.
+ */
+int attn_plan(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile,
+              int32_t* map, int32_t map_capacity, int32_t* map_words_out);
+
+/*
+ * Static split-KV map, the imbalance baseline ([P3] §3.1 问题; [P4] §二.1: one
+ * fixed split granularity for the whole batch).  Request b is cut into
+ * k_b = min(num_splits, n_b) tile-aligned chunks whose tile counts differ by at
+ * most one, larger chunks first; each chunk is its own worker with one segment,
+ * so the map's W = sum_b k_b.  Arguments and errors as attn_plan.
+ */
+int attn_plan_static(const int32_t* seq_lens, int32_t B, int32_t num_splits, int32_t tile,
+                     int32_t* map, int32_t map_capacity, int32_t* map_words_out);
+
+/*
+ * Prefill work map for chunked prefill over a cached prefix: request b has a
+ * q_lens[b]-row query chunk that is the last q_lens[b] positions of a
+ * kv_lens[b]-token context.  Units are (b, i) blocks of q_tile rows, batch-major;
+ * under the causal mask unit (b, i) attends to keys
+ * [0, kv_lens[b] - q_lens[b] + min(q_lens[b], (i+1)*q_tile)), otherwise to all
+ * kv_lens[b] keys.  The units' kv_tile tiles are then filled exactly as in
+ * attn_plan.  Errors as attn_plan, plus q_lens[b] > kv_lens[b] or q_tile < 1.
+ */
+int attn_plan_prefill(const int32_t* q_lens, const int32_t* kv_lens, int32_t B,
+                      int32_t num_workers, int32_t q_tile, int32_t kv_tile, int32_t causal,
+                      int32_t* map, int32_t map_capacity, int32_t* map_words_out);
+
+/*
+ * Workers that fill the device with one resident wave of decode workgroups:
+ * CUs x (resident split-KV workgroups per CU) / head_groups, for the decode kernel
+ * launched with head_groups workgroups per worker.  Cached per device.
+ */
+int attn_query_workers(int device, int32_t head_groups, int32_t* num_workers_out);
+
+/*
+ * Split-KV decode kernel ([P3] §3.1 方案 step 4; [P4] §二.1): launches
+ * num_workers x head_groups workgroups; workgroup (w, g) walks worker w's segment
+ * list for the Hkv/head_groups KV heads of group g and writes one partial per
+ * segment and query head.
+ *   q, k_cache, v_cache, block_table  device, layouts above (16-byte aligned)
+ *   num_pages     pages in the caches (physical page ids are clamped into range)
+ *   seq_lens      device int32[B]; a segment's KV end is clamped to seq_lens[b]
+ *   map           device copy of an attn_plan / attn_plan_static map for this batch
+ *   num_workers, num_segments   W and S of that map
+ *   head_groups   G, a divisor of Hkv
+ *   part_m, part_l, part_o       device fp32 outputs sized by S (see layouts)
+ *   timing        optional device uint64[W*G*4] (start, end, HW_ID, XCC_ID per
+ *                 workgroup, device realtime clock); NULL disables recording
+ *   stream        hipStream_t, or NULL for the null stream
+ * Supported: head_dim 128, Hq/Hkv = 8, bf16, page_size a multiple of 32.
+ * Errors: LBSA_ERR_INVALID, LBSA_ERR_UNSUPPORTED, LBSA_ERR_HIP.
+ */
+int attn_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
+                 const int32_t* seq_lens, const int32_t* map,
+                 int32_t num_workers, int32_t num_segments, int32_t head_groups,
+                 int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                 int32_t page_size, float softmax_scale,
+                 float* part_m, float* part_l, float* part_o,
+                 uint64_t* timing, void* stream);
+
+/*
+ * Combine kernel ([P3] §3.1 方案 step 5): for every unit and query head merges the
+ * unit's partial slots: M = max m_s, w_s = exp(m_s - M), out = sum w_s o_s / sum w_s l_s;
+ * a unit without any visible key gets 0.
+ *   map           device map (as given to the split kernel)
+ *   num_units     U of the map
+ *   rows_per_unit 1 for decode, q_tile for prefill
+ *   q_lens, q_start  device int32[B] for prefill (row count and first output row of
+ *                 request b); NULL for decode, where unit b writes output row b
+ *   out_dtype     0 = fp32, 1 = bf16 (round to nearest even)
+ * Errors: LBSA_ERR_INVALID, LBSA_ERR_UNSUPPORTED (head_dim != 128), LBSA_ERR_HIP.
+ */
+int attn_combine(const float* part_m, const float* part_l, const float* part_o,
+                 const int32_t* map, int32_t num_units, int32_t rows_per_unit,
+                 const int32_t* q_lens, const int32_t* q_start,
+                 int32_t num_q_heads, int32_t head_dim,
+                 void* out, int32_t out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LBSA_H */

@@ -1,0 +1,206 @@
+"""Load-balanced split-KV attention for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``liblbsa.so`` (C ABI declared in ``include/lbsa.h``).  The functions
+here only marshal arguments: torch tensors supply device pointers and the current HIP stream,
+every step of the path runs in the library (host planner in C++, kernels in HIP).  There is no
+fallback: if the library is missing, the first call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+__all__ = [
+    "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill",
+    "attn_query_workers", "attn_splitkv", "attn_combine", "attn_status_string", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbsa.so")
+
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+_c_vp = ctypes.c_void_p
+_c_i32 = ctypes.c_int32
+
+_SIGNATURES = {
+    "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "attn_map_words": (ctypes.c_int32, [_c_i32, _c_i32, ctypes.c_int64]),
+    "attn_plan": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
+    "attn_plan_static": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
+    "attn_plan_prefill": (ctypes.c_int, [_c_i32p, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                         _c_i32p, _c_i32, _c_i32p]),
+    "attn_query_workers": (ctypes.c_int, [ctypes.c_int, _c_i32, _c_i32p]),
+    "attn_splitkv": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
+                                    _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                    ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "attn_combine": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
+                                    _c_i32, _c_i32, _c_vp, _c_i32, _c_vp]),
+}
+
+_lib = None
+
+
+class LbsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {attn_status_string(status)} ({status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblbsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m load_balanced_split_attn_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise LbsaError(status, where)
+
+
+def _i32_host(values: Sequence[int]) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(values, dtype=np.int64).astype(np.int32))
+
+
+def _ptr_i32(a: np.ndarray):
+    return a.ctypes.data_as(_c_i32p)
+
+
+def attn_map_words(num_units: int, num_workers: int, total_tiles_upper: int) -> int:
+    n = lib().attn_map_words(num_units, num_workers, total_tiles_upper)
+    if n < 0:
+        raise LbsaError(-1, "attn_map_words")
+    return n
+
+
+def _plan_call(fn, where, *args) -> np.ndarray:
+    need = _c_i32(0)
+    cap = 64
+    while True:
+        buf = np.zeros(cap, dtype=np.int32)
+        st = fn(*args, _ptr_i32(buf), cap, ctypes.byref(need))
+        if st == -2 and need.value > cap:
+            cap = need.value
+            continue
+        _check(st, where)
+        return buf[:need.value].copy()
+
+
+def attn_plan(seq_lens: Sequence[int], num_workers: int, tile: int = 512) -> np.ndarray:
+    """Dynamic work map (host int32 array)."""
+    lens = _i32_host(seq_lens)
+    return _plan_call(lib().attn_plan, "attn_plan", _ptr_i32(lens), len(lens), num_workers, tile)
+
+
+def attn_plan_static(seq_lens: Sequence[int], num_splits: int, tile: int = 512) -> np.ndarray:
+    """Static split-KV map: min(num_splits, tiles) chunks per request, one worker each."""
+    lens = _i32_host(seq_lens)
+    return _plan_call(lib().attn_plan_static, "attn_plan_static", _ptr_i32(lens), len(lens), num_splits, tile)
+
+
+def attn_plan_prefill(q_lens: Sequence[int], kv_lens: Sequence[int], num_workers: int, q_tile: int = 128,
+                      kv_tile: int = 512, causal: bool = True) -> np.ndarray:
+    ql, kl = _i32_host(q_lens), _i32_host(kv_lens)
+    if len(ql) != len(kl):
+        raise ValueError("q_lens and kv_lens differ in length")
+    return _plan_call(lib().attn_plan_prefill, "attn_plan_prefill", _ptr_i32(ql), _ptr_i32(kl), len(ql),
+                      num_workers, q_tile, kv_tile, int(bool(causal)))
+
+
+def attn_query_workers(device: int = 0, head_groups: int = 8) -> int:
+    out = _c_i32(0)
+    _check(lib().attn_query_workers(device, head_groups, ctypes.byref(out)), "attn_query_workers")
+    return out.value
+
+
+def _dptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str, dev=None) -> None:
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: need a contiguous {dtype} GPU tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name}: on {t.device}, expected {dev}")
+
+
+def map_header(map_host: np.ndarray) -> dict:
+    keys = ("version", "B", "W", "kv_tile", "S", "T", "q_tile", "U")
+    return dict(zip(keys, (int(x) for x in map_host[:8])))
+
+
+def attn_splitkv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                 seq_lens: torch.Tensor, map_dev: torch.Tensor, num_workers: int, num_segments: int,
+                 head_groups: int, softmax_scale: float, part_m: torch.Tensor, part_l: torch.Tensor,
+                 part_o: torch.Tensor, timing: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Launch the split-KV decode kernel.  Layouts: q [B, Hq, D]; k_cache [P, Hkv, page, D];
+    v_cache [P, Hkv, D, page]; block_table [B, stride]; part_m/l [S, Hq]; part_o [S, Hq, D]."""
+    dev = q.device
+    _need(q, torch.bfloat16, "q", dev)
+    _need(k_cache, torch.bfloat16, "k_cache", dev)
+    _need(v_cache, torch.bfloat16, "v_cache", dev)
+    _need(block_table, torch.int32, "block_table", dev)
+    _need(seq_lens, torch.int32, "seq_lens", dev)
+    _need(map_dev, torch.int32, "map", dev)
+    for name, t in (("part_m", part_m), ("part_l", part_l), ("part_o", part_o)):
+        _need(t, torch.float32, name, dev)
+    B, Hq, D = q.shape
+    P, Hkv, page, Dk = k_cache.shape
+    if tuple(v_cache.shape) != (P, Hkv, D, page) or Dk != D:
+        raise ValueError("k_cache/v_cache shapes do not match [P, Hkv, page, D] / [P, Hkv, D, page]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.numel() != B:
+        raise ValueError("block_table/seq_lens do not match the batch")
+    if part_m.numel() < num_segments * Hq or part_l.numel() < num_segments * Hq or \
+            part_o.numel() < num_segments * Hq * D:
+        raise ValueError("partial buffers smaller than num_segments")
+    if timing is not None:
+        _need(timing, torch.int64, "timing", dev)
+        if timing.numel() < num_workers * head_groups * 4:
+            raise ValueError("timing buffer too small")
+    st = lib().attn_splitkv(_dptr(q), _dptr(k_cache), _dptr(v_cache), _dptr(block_table), block_table.shape[1],
+                            P, _dptr(seq_lens), _dptr(map_dev), num_workers, num_segments, head_groups, B, Hq,
+                            Hkv, D, page, float(softmax_scale), _dptr(part_m), _dptr(part_l), _dptr(part_o),
+                            _dptr(timing), _stream(stream))
+    _check(st, "attn_splitkv")
+
+
+def attn_combine(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor, map_dev: torch.Tensor,
+                 num_units: int, out: torch.Tensor, rows_per_unit: int = 1, q_lens: Optional[torch.Tensor] = None,
+                 q_start: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Merge partials into out [rows, Hq, D] (fp32 or bf16)."""
+    dev = out.device
+    for name, t in (("part_m", part_m), ("part_l", part_l), ("part_o", part_o)):
+        _need(t, torch.float32, name, dev)
+    _need(map_dev, torch.int32, "map", dev)
+    if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out: need a contiguous fp32 or bf16 GPU tensor")
+    if q_lens is not None:
+        _need(q_lens, torch.int32, "q_lens", dev)
+        _need(q_start, torch.int32, "q_start", dev)
+    Hq, D = out.shape[-2], out.shape[-1]
+    st = lib().attn_combine(_dptr(part_m), _dptr(part_l), _dptr(part_o), _dptr(map_dev), num_units, rows_per_unit,
+                            _dptr(q_lens), _dptr(q_start), Hq, D, _dptr(out),
+                            1 if out.dtype == torch.bfloat16 else 0, _stream(stream))
+    _check(st, "attn_combine")

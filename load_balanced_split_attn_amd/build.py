@@ -1,0 +1,59 @@
+"""Build liblbsa.so (gfx950) in-tree with hipcc.
+
+``python -m load_balanced_split_attn_amd.build`` compiles every source under ``csrc/`` into
+``load_balanced_split_attn_amd/liblbsa.so``.  Cross-compiles without a GPU.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "liblbsa.so")
+
+SOURCES = ["plan.cpp", "splitkv_decode.hip", "combine.hip"]
+
+HIP_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    # keep hipcc from emitting packed fp32 VALU instructions (v_pk_fma_f32 and friends)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-command-line-argument",
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build liblbsa.so)")
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    tmp = LIB + ".tmp"
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-shared", "-I", INCLUDE, "-I", CSRC, *srcs,
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = "\n".join(line for line in (res.stdout + res.stderr).splitlines() if noise not in line)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,251 @@
+// Host-side task-map builder ("Task Assign"): runs once per inference step, before the
+// attention kernels of all layers ([P4] "腾讯混元AI Infra进化：HPC-Ops推理核心算子全面升级"
+// §二.1; [P3] "Hy3 Preview AI Infra 推理优化精读笔记" §3.1 方案 steps 1-4).
+//
+// Plain C++17 with no HIP dependency: the same object is linked into liblbsa.so and can be
+// built with g++ alone.  No allocation: every pass walks the units in place and writes into
+// the caller's buffer.
+//
+// The fill never materialises the tile stream.  A cursor (unit, first unused tile) advances
+// through the units; worker w consumes budget_w tiles, emitting one segment per unit it touches.
+// Budgets follow [P2] "大模型推理性能优化新范式" §二.1: base = T / W, plus one for the first
+// T % W workers.
+
+#include <climits>
+#include <cstdint>
+#include <cstring>
+
+#include "lbsa.h"
+
+namespace {
+
+inline int64_t tiles_for(int64_t extent, int64_t tile) { return extent > 0 ? (extent + tile - 1) / tile : 0; }
+
+// A unit source yields (b, q_tile_index, extent) in batch-major order.
+struct DecodeUnits {
+  const int32_t* lens;
+  int32_t B;
+  int64_t count() const { return B; }
+  template <class F> bool each(F&& f) const {
+    for (int32_t b = 0; b < B; ++b)
+      if (!f(b, 0, (int64_t)lens[b])) return false;
+    return true;
+  }
+};
+
+struct PrefillUnits {
+  const int32_t* q_lens;
+  const int32_t* kv_lens;
+  int32_t B;
+  int32_t q_tile;
+  bool causal;
+  int64_t count() const {
+    int64_t n = 0;
+    for (int32_t b = 0; b < B; ++b) n += tiles_for(q_lens[b], q_tile);
+    return n;
+  }
+  template <class F> bool each(F&& f) const {
+    for (int32_t b = 0; b < B; ++b) {
+      const int64_t ql = q_lens[b], kl = kv_lens[b];
+      const int64_t blocks = tiles_for(ql, q_tile);
+      for (int64_t i = 0; i < blocks; ++i) {
+        const int64_t last_row_end = ql < (i + 1) * q_tile ? ql : (i + 1) * q_tile;
+        const int64_t extent = causal ? kl - ql + last_row_end : kl;
+        if (!f(b, (int32_t)i, extent)) return false;
+      }
+    }
+    return true;
+  }
+};
+
+struct Writer {
+  int32_t* map;
+  int32_t W, U;
+  int64_t seg_base() const { return LBSA_MAP_HEADER_WORDS + (W + 1) + (U + 1) + 2 * (int64_t)U; }
+  int32_t* worker_ptr() const { return map + LBSA_MAP_HEADER_WORDS; }
+  int32_t* unit_ptr() const { return map + LBSA_MAP_HEADER_WORDS + W + 1; }
+  int32_t* units() const { return map + LBSA_MAP_HEADER_WORDS + W + 1 + U + 1; }
+  int32_t* seg(int64_t i) const { return map + seg_base() + 4 * i; }
+};
+
+// Greedy equal-budget fill.  With `w` null only the segment count is returned.
+template <class Units>
+int64_t fill(const Units& units, int64_t T, int32_t W, int64_t tile, const Writer* w) {
+  const int64_t base = T / W, rem = T % W;
+  int64_t segs = 0;
+  int32_t worker = 0;
+  int64_t left = W > 0 ? base + (0 < rem ? 1 : 0) : 0;  // budget left for `worker`
+  if (w) w->worker_ptr()[0] = 0;
+  // close every worker whose budget is exhausted (including zero budgets)
+  auto advance_workers = [&]() {
+    while (left == 0 && worker < W) {
+      ++worker;
+      if (w) w->worker_ptr()[worker] = (int32_t)segs;
+      if (worker < W) left = base + (worker < rem ? 1 : 0);
+    }
+  };
+  advance_workers();
+  int64_t u = 0;
+  units.each([&](int32_t b, int32_t qt, int64_t extent) {
+    if (w) {
+      w->unit_ptr()[u] = (int32_t)segs;
+      w->units()[2 * u] = b;
+      w->units()[2 * u + 1] = qt;
+    }
+    const int64_t n = tiles_for(extent, tile);
+    int64_t t = 0;
+    while (t < n) {
+      if (worker >= W) return false;  // budgets sum to T, so this cannot happen
+      const int64_t take = (n - t) < left ? (n - t) : left;
+      if (w) {
+        int32_t* s = w->seg(segs);
+        const int64_t end = (t + take) * tile;
+        s[0] = b;
+        s[1] = qt;
+        s[2] = (int32_t)(t * tile);
+        s[3] = (int32_t)(end < extent ? end : extent);
+      }
+      ++segs;
+      t += take;
+      left -= take;
+      advance_workers();
+    }
+    ++u;
+    return true;
+  });
+  if (w) w->unit_ptr()[u] = (int32_t)segs;
+  return segs;
+}
+
+template <class Units>
+int plan_units(const Units& units, int32_t B, int32_t W, int32_t kv_tile, int32_t q_tile,
+               int32_t* map, int32_t cap, int32_t* words_out) {
+  // pass 1: U, T and validation
+  int64_t U = 0, T = 0;
+  bool ok = units.each([&](int32_t, int32_t, int64_t extent) {
+    if (extent < 0) return false;
+    ++U;
+    T += tiles_for(extent, kv_tile);
+    return T <= INT32_MAX && extent <= INT32_MAX;
+  });
+  if (!ok || U > INT32_MAX / 4) return LBSA_ERR_INVALID;
+  // pass 2: S
+  Writer probe{nullptr, W, (int32_t)U};
+  const int64_t S = fill(units, T, W, kv_tile, nullptr);
+  const int64_t words = probe.seg_base() + 4 * S;
+  if (words > INT32_MAX) return LBSA_ERR_INVALID;
+  if (words_out) *words_out = (int32_t)words;
+  if (words > cap) return LBSA_ERR_CAPACITY;
+  // pass 3: write
+  Writer wr{map, W, (int32_t)U};
+  map[0] = LBSA_MAP_VERSION;
+  map[1] = B;
+  map[2] = W;
+  map[3] = kv_tile;
+  map[4] = (int32_t)S;
+  map[5] = (int32_t)T;
+  map[6] = q_tile;
+  map[7] = (int32_t)U;
+  const int64_t S2 = fill(units, T, W, kv_tile, &wr);
+  return S2 == S ? LBSA_OK : LBSA_ERR_INVALID;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case LBSA_OK: return "ok";
+    case LBSA_ERR_INVALID: return "invalid argument";
+    case LBSA_ERR_CAPACITY: return "map buffer too small";
+    case LBSA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case LBSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t attn_map_words(int32_t num_units, int32_t num_workers, int64_t total_tiles_upper) {
+  if (num_units < 0 || num_workers < 0 || total_tiles_upper < 0) return -1;
+  int64_t s_max = (int64_t)num_workers + num_units - 1;
+  if (total_tiles_upper < s_max) s_max = total_tiles_upper;
+  if (s_max < 0) s_max = 0;
+  const int64_t words = LBSA_MAP_HEADER_WORDS + (int64_t)num_workers + 1 + num_units + 1 +
+                        2 * (int64_t)num_units + 4 * s_max;
+  return words > INT32_MAX ? -1 : (int32_t)words;
+}
+
+int attn_plan(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile,
+              int32_t* map, int32_t map_capacity, int32_t* map_words_out) {
+  if (B < 0 || num_workers < 1 || tile < 1 || !map || map_capacity < 0) return LBSA_ERR_INVALID;
+  if (B > 0 && !seq_lens) return LBSA_ERR_INVALID;
+  DecodeUnits units{seq_lens, B};
+  return plan_units(units, B, num_workers, tile, 1, map, map_capacity, map_words_out);
+}
+
+int attn_plan_prefill(const int32_t* q_lens, const int32_t* kv_lens, int32_t B,
+                      int32_t num_workers, int32_t q_tile, int32_t kv_tile, int32_t causal,
+                      int32_t* map, int32_t map_capacity, int32_t* map_words_out) {
+  if (B < 0 || num_workers < 1 || q_tile < 1 || kv_tile < 1 || !map || map_capacity < 0)
+    return LBSA_ERR_INVALID;
+  if (B > 0 && (!q_lens || !kv_lens)) return LBSA_ERR_INVALID;
+  for (int32_t b = 0; b < B; ++b)
+    if (q_lens[b] < 0 || kv_lens[b] < 0 || q_lens[b] > kv_lens[b]) return LBSA_ERR_INVALID;
+  PrefillUnits units{q_lens, kv_lens, B, q_tile, causal != 0};
+  return plan_units(units, B, num_workers, kv_tile, q_tile, map, map_capacity, map_words_out);
+}
+
+int attn_plan_static(const int32_t* seq_lens, int32_t B, int32_t num_splits, int32_t tile,
+                     int32_t* map, int32_t map_capacity, int32_t* map_words_out) {
+  if (B < 0 || num_splits < 1 || tile < 1 || !map || map_capacity < 0) return LBSA_ERR_INVALID;
+  if (B > 0 && !seq_lens) return LBSA_ERR_INVALID;
+  int64_t T = 0, Wp = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (seq_lens[b] < 0) return LBSA_ERR_INVALID;
+    const int64_t n = tiles_for(seq_lens[b], tile);
+    T += n;
+    Wp += n < num_splits ? n : num_splits;
+  }
+  if (T > INT32_MAX) return LBSA_ERR_INVALID;
+  const int64_t U = B, S = Wp;
+  const int64_t words = LBSA_MAP_HEADER_WORDS + (Wp + 1) + (U + 1) + 2 * U + 4 * S;
+  if (words > INT32_MAX) return LBSA_ERR_INVALID;
+  if (map_words_out) *map_words_out = (int32_t)words;
+  if (words > map_capacity) return LBSA_ERR_CAPACITY;
+  Writer wr{map, (int32_t)Wp, (int32_t)U};
+  map[0] = LBSA_MAP_VERSION;
+  map[1] = B;
+  map[2] = (int32_t)Wp;
+  map[3] = tile;
+  map[4] = (int32_t)S;
+  map[5] = (int32_t)T;
+  map[6] = 1;
+  map[7] = (int32_t)U;
+  int64_t s = 0;
+  wr.worker_ptr()[0] = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    wr.unit_ptr()[b] = (int32_t)s;
+    wr.units()[2 * b] = b;
+    wr.units()[2 * b + 1] = 0;
+    const int64_t L = seq_lens[b];
+    const int64_t n = tiles_for(L, tile);
+    const int64_t k = n < num_splits ? n : num_splits;
+    int64_t t0 = 0;
+    for (int64_t c = 0; c < k; ++c) {
+      const int64_t size = n / k + (c < n % k ? 1 : 0);
+      int32_t* seg = wr.seg(s);
+      const int64_t end = (t0 + size) * tile;
+      seg[0] = b;
+      seg[1] = 0;
+      seg[2] = (int32_t)(t0 * tile);
+      seg[3] = (int32_t)(end < L ? end : L);
+      t0 += size;
+      ++s;
+      wr.worker_ptr()[s] = (int32_t)s;
+    }
+  }
+  wr.unit_ptr()[B] = (int32_t)s;
+  return LBSA_OK;
+}
+
+}  // extern "C"

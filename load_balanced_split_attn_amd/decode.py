@@ -1,0 +1,59 @@
+"""Decode attention for one inference step: plan once, run for every layer.
+
+The pages build the task map once per inference step and let the attention kernel of every layer
+read it ([P4] "腾讯混元AI Infra进化：HPC-Ops推理核心算子全面升级" §二.1; [P3] "Hy3 Preview AI
+Infra 推理优化精读笔记" §3.1 方案 step 4).  ``DecodeStep`` does that: the constructor calls the
+host planner and copies the map to the device once; each call launches the split-KV kernel and the
+combine kernel on the current stream, reusing the map and the partial buffers.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import torch
+
+from . import attn_combine, attn_plan, attn_plan_static, attn_query_workers, attn_splitkv, map_header
+
+
+class DecodeStep:
+    def __init__(self, seq_lens: Sequence[int], device, num_workers: Optional[int] = None, tile: int = 512,
+                 head_groups: int = 8, num_q_heads: int = 64, head_dim: int = 128,
+                 static_splits: Optional[int] = None):
+        device = torch.device(device)
+        self.seq_lens_host = [int(x) for x in seq_lens]
+        if static_splits is not None:
+            self.map_host = attn_plan_static(self.seq_lens_host, static_splits, tile)
+        else:
+            if num_workers is None:
+                num_workers = attn_query_workers(device.index or 0, head_groups)
+            self.map_host = attn_plan(self.seq_lens_host, num_workers, tile)
+        hdr = map_header(self.map_host)
+        self.W, self.S, self.U, self.T = hdr["W"], hdr["S"], hdr["U"], hdr["T"]
+        self.tile = tile
+        self.head_groups = head_groups
+        self.device = device
+        self.map = torch.from_numpy(self.map_host).to(device)
+        self.seq_lens = torch.tensor(self.seq_lens_host, dtype=torch.int32, device=device)
+        S = max(self.S, 1)
+        self.part_m = torch.empty((S, num_q_heads), dtype=torch.float32, device=device)
+        self.part_l = torch.empty((S, num_q_heads), dtype=torch.float32, device=device)
+        self.part_o = torch.empty((S, num_q_heads, head_dim), dtype=torch.float32, device=device)
+
+    def splitkv(self, q, k_cache, v_cache, block_table, scale: float, timing=None, stream=None) -> None:
+        attn_splitkv(q, k_cache, v_cache, block_table, self.seq_lens, self.map, self.W, self.S, self.head_groups,
+                     scale, self.part_m, self.part_l, self.part_o, timing=timing, stream=stream)
+
+    def combine(self, out, stream=None) -> None:
+        attn_combine(self.part_m, self.part_l, self.part_o, self.map, self.U, out, stream=stream)
+
+    def __call__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None, timing=None,
+                 stream=None) -> torch.Tensor:
+        if scale is None:
+            scale = q.shape[-1] ** -0.5
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        self.splitkv(q, k_cache, v_cache, block_table, scale, timing=timing, stream=stream)
+        self.combine(out, stream=stream)
+        return out

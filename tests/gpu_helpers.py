@@ -1,0 +1,54 @@
+"""Shared helpers for the GPU parity tests: seeded inputs in the kernels' layout, the fp64 oracle on
+the same bf16 values, and the tolerance checks."""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import workloads as WL
+from load_balanced_split_attn_amd.paged import pack_paged
+from oracle.attention import ref_attention
+
+MAX_ABS = 1e-2
+REL_RMS = 2e-3
+SCALE = 1.0 / math.sqrt(128)
+
+
+def note(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def decode_inputs(wl: WL.Workload, device="cuda", page=64, pad_value=0.0):
+    q = wl.q().to(device)
+    k_cache, v_cache, bt = pack_paged(wl.kv, wl.kv_lens, page, wl.hkv, wl.head_dim, wl.page_permutation,
+                                      device, pad_value=pad_value)
+    return q, k_cache, v_cache, bt
+
+
+def oracle_decode(wl: WL.Workload, requests=None, scale=SCALE):
+    q = wl.q().to(torch.float64).numpy()
+    out = {}
+    for b in (range(wl.batch) if requests is None else requests):
+        k, v = wl.kv(b)
+        out[b] = ref_attention(q[b:b + 1], k.to(torch.float64).numpy(), v.to(torch.float64).numpy(), scale)[0]
+    return out
+
+
+def errors(got: np.ndarray, ref: np.ndarray):
+    diff = got.astype(np.float64) - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff)) / den if den > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, what: str, max_abs=MAX_ABS, rel_rms=REL_RMS):
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    ma, rr = errors(got, ref)
+    assert ma <= max_abs and rr <= rel_rms, f"{what}: max_abs={ma:.3e} rel_rms={rr:.3e}"
+    return ma, rr

@@ -1,0 +1,131 @@
+"""C ABI on the CPU: the library loads, exports every declared symbol, and its host planner
+reproduces the oracle's work map bit for bit (no GPU calls here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as WL
+from oracle.plan import ref_plan, ref_plan_prefill, ref_plan_static
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "lbsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import load_balanced_split_attn_amd as lb
+    return lb
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared_functions()
+    assert len(names) >= 8
+    handle = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(handle, n), n
+
+
+def test_status_strings(L):
+    assert L.attn_status_string(0) == "ok"
+    assert L.attn_status_string(-2) == "map buffer too small"
+
+
+def _random_batches(n, seed):
+    rng = np.random.default_rng(seed)
+    for _ in range(n):
+        B = int(rng.integers(0, 20))
+        tile = int(rng.choice([1, 32, 64, 512]))
+        hi = int(rng.choice([1, 3, 40])) * tile
+        lens = [int(x) for x in rng.integers(0, hi + 2, size=B)]
+        W = int(rng.integers(1, 300))
+        yield lens, W, tile
+
+
+def test_plan_bit_exact_random(L):
+    for lens, W, tile in _random_batches(3000, 1):
+        got = L.attn_plan(lens, W, tile)
+        exp = ref_plan(lens, W, tile)
+        assert got.dtype == np.int32 and np.array_equal(got, exp), (lens, W, tile)
+
+
+def test_plan_static_bit_exact_random(L):
+    for lens, W, tile in _random_batches(2000, 2):
+        S = 1 + W % 17
+        assert np.array_equal(L.attn_plan_static(lens, S, tile), ref_plan_static(lens, S, tile)), (lens, S, tile)
+
+
+def test_plan_prefill_bit_exact_random(L):
+    rng = np.random.default_rng(3)
+    for _ in range(1500):
+        B = int(rng.integers(0, 8))
+        q_lens = [int(x) for x in rng.integers(0, 600, size=B)]
+        kv_lens = [q + int(rng.integers(0, 5000)) for q in q_lens]
+        W = int(rng.integers(1, 200))
+        q_tile = int(rng.choice([16, 128]))
+        kv_tile = int(rng.choice([64, 512]))
+        causal = bool(rng.integers(0, 2))
+        got = L.attn_plan_prefill(q_lens, kv_lens, W, q_tile, kv_tile, causal)
+        exp = ref_plan_prefill(q_lens, kv_lens, W, q_tile, kv_tile, causal)
+        assert np.array_equal(got, exp), (q_lens, kv_lens, W, q_tile, kv_tile, causal)
+
+
+@pytest.mark.parametrize("name", ["tiny", "uniform", "mixed", "long_tail"])
+@pytest.mark.parametrize("W", [4, 256, 384, 512, 1024])
+def test_plan_bit_exact_workloads(L, name, W):
+    wl = WL.BY_NAME[name]()
+    assert np.array_equal(L.attn_plan(wl.kv_lens, W, 512), ref_plan(wl.kv_lens, W, 512))
+    for S in (1, 2, 7, 13, 64):
+        assert np.array_equal(L.attn_plan_static(wl.kv_lens, S, 512), ref_plan_static(wl.kv_lens, S, 512))
+
+
+@pytest.mark.parametrize("W", [64, 256, 1024])
+def test_plan_prefill_bit_exact_workload(L, W):
+    wl = WL.prefill()
+    got = L.attn_plan_prefill(wl.q_lens, wl.kv_lens, W, 128, 512, True)
+    assert np.array_equal(got, ref_plan_prefill(wl.q_lens, wl.kv_lens, W, 128, 512, True))
+
+
+def test_map_words_bound(L):
+    for lens, W, tile in _random_batches(500, 4):
+        words = L.attn_plan(lens, W, tile)
+        T = int(words[5])
+        assert len(words) <= L.attn_map_words(len(lens), W, T)
+    assert L.lib().attn_map_words(-1, 3, 5) == -1
+
+
+def test_errors_and_capacity(L):
+    lib = L.lib()
+    i32 = ctypes.c_int32
+    lens = (i32 * 3)(1024, 5120, 2048)
+    buf = (i32 * 64)()
+    need = i32(0)
+    assert lib.attn_plan(lens, 3, 4, 512, buf, 10, ctypes.byref(need)) == -2
+    assert need.value == 8 + 5 + 4 + 6 + 4 * 5
+    assert lib.attn_plan(lens, 3, 4, 512, buf, need.value, ctypes.byref(need)) == 0
+    assert list(buf)[:need.value] == ref_plan([1024, 5120, 2048], 4, 512).tolist()
+    bad = (i32 * 2)(5, -1)
+    assert lib.attn_plan(bad, 2, 4, 512, buf, 64, None) == -1
+    assert lib.attn_plan(lens, 3, 0, 512, buf, 64, None) == -1
+    assert lib.attn_plan(lens, 3, 4, 0, buf, 64, None) == -1
+    assert lib.attn_plan(lens, -1, 4, 512, buf, 64, None) == -1
+    assert lib.attn_plan(None, 3, 4, 512, buf, 64, None) == -1
+    assert lib.attn_plan_static(lens, 3, 0, 512, buf, 64, None) == -1
+    ql = (i32 * 1)(10)
+    kl = (i32 * 1)(5)
+    assert lib.attn_plan_prefill(ql, kl, 1, 4, 128, 512, 1, buf, 64, None) == -1
+    # kernels reject bad shapes before touching the device
+    assert lib.attn_splitkv(None, None, None, None, 0, 1, None, None, 4, 0, 8, 1, 64, 8, 128, 64, 1.0,
+                            None, None, None, None, None) == -1
+    dummy = ctypes.c_void_p(16)
+    assert lib.attn_splitkv(dummy, dummy, dummy, dummy, 1, 1, dummy, dummy, 4, 0, 8, 1, 64, 8, 96, 64, 1.0,
+                            None, None, None, None, None) == -3
+    assert lib.attn_combine(None, None, None, dummy, 1, 1, None, None, 64, 128, None, 0, None) == -1

@@ -1,0 +1,133 @@
+"""GPU parity of the decode path (attn_plan -> attn_splitkv -> attn_combine through the C ABI)
+against the fp64 oracle, on small seeded batches that span several tiles and ragged tails."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from gpu_helpers import SCALE, assert_close, decode_inputs, errors, note, oracle_decode
+from oracle.attention import ref_split_partials
+from oracle.plan import ref_plan, ref_plan_static
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lb():
+    import load_balanced_split_attn_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.lib()
+    return m
+
+
+def _run(lb, wl, words, head_groups=8, pad_value=0.0, out_dtype=torch.float32, poison=False, inputs=None):
+    from load_balanced_split_attn_amd import map_header
+    q, kc, vc, bt = inputs if inputs is not None else decode_inputs(wl, pad_value=pad_value)
+    hdr = map_header(words)
+    dev = q.device
+    mp = torch.from_numpy(np.asarray(words, dtype=np.int32)).to(dev)
+    lens = torch.tensor(wl.kv_lens, dtype=torch.int32, device=dev)
+    S = max(hdr["S"], 1)
+    fill = float("nan") if poison else 0.0
+    pm = torch.full((S, wl.hq), fill, dtype=torch.float32, device=dev)
+    pl = torch.full((S, wl.hq), fill, dtype=torch.float32, device=dev)
+    po = torch.full((S, wl.hq, wl.head_dim), fill, dtype=torch.float32, device=dev)
+    out = torch.full(q.shape, fill, dtype=out_dtype, device=dev)
+    lb.attn_splitkv(q, kc, vc, bt, lens, mp, hdr["W"], hdr["S"], head_groups, SCALE, pm, pl, po)
+    lb.attn_combine(pm, pl, po, mp, hdr["U"], out)
+    torch.cuda.synchronize()
+    return out, (pm, pl, po)
+
+
+def test_tiny_worked_example(lb):
+    wl = WL.tiny()
+    words = lb.attn_plan(wl.kv_lens, 4, 512)
+    assert np.array_equal(words, ref_plan(wl.kv_lens, 4, 512))
+    ref = oracle_decode(wl)
+    for G in (8, 1):
+        note(f"tiny worked example, head_groups={G}")
+        out, parts = _run(lb, wl, words, head_groups=G)
+        got = out.cpu().numpy()
+        for b in range(wl.batch):
+            assert_close(got[b], ref[b], f"request {b} G={G}")
+    # partial-level diagnostics against the oracle's per-split partials
+    q = wl.q().double().numpy()
+    kvs = [wl.kv(b) for b in range(wl.batch)]
+    rparts = ref_split_partials(words, [q[b:b + 1] for b in range(wl.batch)],
+                                [k.double().numpy() for k, _ in kvs], [v.double().numpy() for _, v in kvs], SCALE)
+    pm, pl, po = (t.cpu().numpy() for t in parts)
+    for s, (m, l, o) in enumerate(rparts):
+        assert np.max(np.abs(pm[s] - m[0])) <= 1e-3, f"slot {s} m"
+        lse_got = pm[s] + np.log(pl[s])
+        lse_ref = m[0] + np.log(l[0])
+        assert np.max(np.abs(lse_got - lse_ref)) <= 1e-3, f"slot {s} lse"
+        assert_close(po[s] / pl[s][:, None], o[0] / l[0][:, None], f"slot {s} o/l")
+
+
+@pytest.mark.parametrize("seed,batch,max_len,W,G", [
+    (0, 6, 3000, 7, 8), (1, 9, 1500, 1, 8), (2, 5, 5000, 64, 4), (3, 12, 700, 100, 2),
+    (4, 4, 2600, 3, 1), (5, 7, 1100, 2000, 8),
+])
+def test_random_ragged(lb, seed, batch, max_len, W, G):
+    wl = WL.random_decode(seed, batch, max_len)
+    wl.kv_lens[0] = 0                           # an empty request
+    wl.kv_lens[-1] = max(wl.kv_lens[-1], 513)   # a ragged tail past one tile
+    note(f"random ragged seed={seed} lens={wl.kv_lens} W={W} G={G}")
+    words = lb.attn_plan(wl.kv_lens, W, 512)
+    assert np.array_equal(words, ref_plan(wl.kv_lens, W, 512))
+    out, _ = _run(lb, wl, words, head_groups=G, pad_value=float("nan"), poison=True)
+    got = out.cpu().numpy()
+    ref = oracle_decode(wl)
+    for b in range(wl.batch):
+        assert_close(got[b], ref[b], f"seed {seed} request {b} (L={wl.kv_lens[b]})")
+
+
+def test_maps_agree_and_paging_invariance(lb):
+    wl = WL.random_decode(11, 8, 4000, min_len=1)
+    note(f"map agreement lens={wl.kv_lens}")
+    inputs = decode_inputs(wl)
+    outs = []
+    for words in (lb.attn_plan(wl.kv_lens, 37, 512), lb.attn_plan(wl.kv_lens, 1, 512),
+                  lb.attn_plan_static(wl.kv_lens, 1, 512), lb.attn_plan_static(wl.kv_lens, 3, 512),
+                  lb.attn_plan(wl.kv_lens, 37, 64)):
+        out, _ = _run(lb, wl, words, inputs=inputs)
+        outs.append(out.cpu().numpy().astype(np.float64))
+    for o in outs[1:]:
+        assert errors(o, outs[0])[1] <= 1e-5
+    # same map, two runs: bitwise equal
+    words = lb.attn_plan(wl.kv_lens, 37, 512)
+    a, _ = _run(lb, wl, words, inputs=inputs)
+    b, _ = _run(lb, wl, words, inputs=inputs)
+    assert torch.equal(a, b)
+    # a different physical page order gives bitwise the same result
+    wl2 = WL.random_decode(11, 8, 4000, min_len=1)
+    wl2.page_permutation = lambda n: torch.randperm(n, generator=torch.Generator().manual_seed(99))
+    c, _ = _run(lb, wl2, words)
+    assert torch.equal(a, c)
+
+
+def test_bf16_output(lb):
+    wl = WL.random_decode(12, 4, 2000, min_len=600)
+    words = lb.attn_plan(wl.kv_lens, 16, 512)
+    out, _ = _run(lb, wl, words, out_dtype=torch.bfloat16)
+    ref = oracle_decode(wl)
+    got = out.float().cpu().numpy()
+    for b in range(wl.batch):
+        assert_close(got[b], ref[b], f"bf16 request {b}")
+
+
+def test_timing_records(lb):
+    wl = WL.random_decode(13, 4, 3000, min_len=1000)
+    q, kc, vc, bt = decode_inputs(wl)
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    step = DecodeStep(wl.kv_lens, q.device, num_workers=20, head_groups=8)
+    timing = torch.zeros((20 * 8, 4), dtype=torch.int64, device=q.device)
+    out = step(q, kc, vc, bt, timing=timing)
+    torch.cuda.synchronize()
+    t = timing.cpu().numpy()
+    assert np.all(t[:, 1] >= t[:, 0]) and np.all(t[:, 0] > 0)
+    assert np.all((t[:, 3] & 0xF) < 8)
+    ref = oracle_decode(wl)
+    for b in range(wl.batch):
+        assert_close(out[b].cpu().numpy(), ref[b], f"timed run request {b}")
