@@ -80,32 +80,74 @@ def per_cu_busy(timing) -> dict:
             "mean_busy_over_span": float(vals.mean() / span), "workgroups": int(t.shape[0])}
 
 
-def time_steps(fn_split, fn_combine, steps: int, warmup: int, rotate):
+def time_steps(fn_split, fn_combine, steps: int, warmup: int):
+    """Two timed passes on the launch stream: (1) `steps` back-to-back steps bracketed by one event
+    pair (the step rate); (2) the same steps with an event pair around every split-KV launch and
+    every combine launch (per-kernel durations)."""
     import torch
     for i in range(warmup):
         fn_split(i)
         fn_combine(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        a, b, c = ev[i]
-        a.record()
         fn_split(i)
-        b.record()
         fn_combine(i)
-        c.record()
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    split_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    step_ms = [a.elapsed_time(c) for a, _, c in ev]
-    return {"total_ms": t0.elapsed_time(t1), "wall_s": wall, "split_ms": split_ms, "step_ms": step_ms}
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        a, b, c, d = ev[i]
+        a.record()
+        fn_split(i)
+        b.record()
+        c.record()
+        fn_combine(i)
+        d.record()
+    torch.cuda.synchronize()
+    return {"total_ms": t0.elapsed_time(t1), "wall_s": wall,
+            "split_ms": [a.elapsed_time(b) for a, b, _, _ in ev],
+            "combine_ms": [c.elapsed_time(d) for _, _, c, d in ev]}
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "load_balanced_split_attn_amd", "csrc")
+    for name in ("common.h", "splitkv_decode.hip"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs, if they were taken on
+    the current kernel source (None otherwise)."""
+    path = os.path.join(ROOT, "load_balanced_split_attn_amd", "measured_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kernel, {}).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != kernel_source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def calibration_copy(dev) -> None:
+    """A plain 1 GiB device-to-device copy (torch's copy kernel): the known-size reference that
+    scales the FETCH_SIZE / WRITE_SIZE counters in the profile runs."""
+    import torch
+    src = torch.ones(2**30 // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_oracle_baseline(wl, budget_s: float, scale: float) -> dict:
@@ -161,6 +203,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-static", action="store_true")
     ap.add_argument("--static-steps", type=int, default=10)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="run one plain 1 GiB copy first (reference for the HBM byte counters)")
+    ap.add_argument("--no-probe", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -178,6 +223,8 @@ def main() -> int:
 
     lb.lib()
     dev = torch.device("cuda:0")
+    if args.calibration_copy:
+        calibration_copy(dev)
     wl = WL.BY_NAME[args.workload]()
     scale = 1.0 / math.sqrt(wl.head_dim)
     page = 64
@@ -211,10 +258,9 @@ def main() -> int:
         step.combine(out)
 
     log(f"dynamic map: W={step.W} G={args.head_groups} S={step.S} T={step.T}; timing {args.steps} steps")
-    r = time_steps(split, comb, args.steps, args.warmup, copies)
+    r = time_steps(split, comb, args.steps, args.warmup)
     ms_per_step = r["total_ms"] / args.steps
     split_ms = float(np.mean(r["split_ms"]))
-    step_med = float(np.median(r["step_ms"]))
     value = nbytes["step"] / (ms_per_step * 1e-3) / 1e12
     achieved = nbytes["splitkv"] / (split_ms * 1e-3) / 1e9
     log(f"step {ms_per_step * 1e3:.1f} us ({value:.3f} TB/s), splitkv {split_ms * 1e3:.1f} us ({achieved:.0f} GB/s)")
@@ -228,13 +274,14 @@ def main() -> int:
                    "page": page, "tile": args.tile, "workers": step.W, "head_groups": args.head_groups,
                    "segments": step.S, "tiles": step.T, "cache_copies": copies},
         "us_per_step": round(ms_per_step * 1e3, 2),
-        "us_per_step_p10_p50_p90": [round(float(np.percentile(r["step_ms"], p)) * 1e3, 2) for p in (10, 50, 90)],
+        "splitkv_us_p10_p50_p90": [round(float(np.percentile(r["split_ms"], p)) * 1e3, 2) for p in (10, 50, 90)],
         "pct_peak_hbm": round(100 * value * 1e3 / PEAK_HBM_GBS, 2),
         "roofline": {"bound": "hbm", "kernel": "splitkv_decode_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None, "bytes_per_launch": nbytes["splitkv"],
-                     "avg_launch_us": round(split_ms * 1e3, 2)},
-        "combine_us": round((step_med - float(np.median(r["split_ms"]))) * 1e3, 2),
+                     "traffic": recorded_traffic("splitkv_decode_kernel", wl.name),
+                     "bytes_per_launch": nbytes["splitkv"], "avg_launch_us": round(split_ms * 1e3, 2),
+                     "kernel_source_digest": kernel_source_digest()},
+        "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 2),
         "plan": {"host_us": round(plan_us, 2), "map_words": int(len(step.map_host)),
                  "first_plan_and_upload_s": round(plan_s, 4)},
     }
@@ -257,7 +304,7 @@ def main() -> int:
                 k_, v_ = caches[i % copies]
                 st.splitkv(q, k_, v_, bt, scale)
 
-            rs = time_steps(s_split, lambda i, st=st: st.combine(out), args.static_steps, 2, copies)
+            rs = time_steps(s_split, lambda i, st=st: st.combine(out), args.static_steps, 2)
             tm = rs["total_ms"] / args.static_steps
             timing_s = torch.zeros((st.W * args.head_groups, 4), dtype=torch.int64, device=dev)
             st.splitkv(q, kc, vc, bt, scale, timing=timing_s)
@@ -272,6 +319,25 @@ def main() -> int:
             "best_us": best["us_per_step"],
             "speedup_vs_plain": round(plain_row["us_per_step"] / (ms_per_step * 1e3), 3),
             "speedup_vs_best": round(best["us_per_step"] / (ms_per_step * 1e3), 3), "sweep": rows}
+
+    if not args.no_probe:
+        # the device's streaming-read ceiling, measured on the same run (the KV cache itself)
+        sink = torch.zeros(8192 * 256, dtype=torch.int32, device=dev)
+        best = None
+        for blocks in (2048, 4096, 8192):
+            for _ in range(2):
+                lb.attn_probe_stream_read(kc, blocks, sink)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                lb.attn_probe_stream_read(kc, blocks, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            gbs = kc.numel() * 2 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+            best = gbs if best is None else max(best, gbs)
+        result["stream_read_ceiling"] = {"GB/s": round(best, 1), "buffer_GB": round(kc.numel() * 2 / 1e9, 2),
+                                         "splitkv_frac_of_ceiling": round(achieved / best, 4)}
 
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a CPU sample")

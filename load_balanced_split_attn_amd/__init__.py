@@ -39,6 +39,7 @@ _SIGNATURES = {
                                     ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "attn_combine": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                     _c_i32, _c_i32, _c_vp, _c_i32, _c_vp]),
+    "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
 }
 
 _lib = None
@@ -204,3 +205,12 @@ def attn_combine(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tenso
                             _dptr(q_lens), _dptr(q_start), Hq, D, _dptr(out),
                             1 if out.dtype == torch.bfloat16 else 0, _stream(stream))
     _check(st, "attn_combine")
+
+
+def attn_probe_stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor, stream=None) -> None:
+    """Read all of ``buf`` once (measurement helper: the device's streaming-read ceiling)."""
+    if not buf.is_cuda or not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < blocks * 256:
+        raise ValueError("attn_probe_stream_read: need a contiguous GPU buffer and an int32 sink of blocks*256")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().attn_probe_stream_read(_dptr(buf), nbytes - nbytes % 16, blocks, _dptr(sink), _stream(stream)),
+           "attn_probe_stream_read")

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblbsa.so")
 
-SOURCES = ["plan.cpp", "splitkv_decode.hip", "combine.hip"]
+SOURCES = ["plan.cpp", "splitkv_decode.hip", "combine.hip", "probe.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
@@ -37,8 +37,8 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build liblbsa.so)")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, extra_flags=None, out: str = LIB) -> str:
+    tmp = out + ".tmp"
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-shared", "-I", INCLUDE, "-I", CSRC, *srcs,
            "-o", tmp]
@@ -51,8 +51,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -2,8 +2,7 @@
 // ([P3] "Hy3 Preview AI Infra 推理优化精读笔记" §3.1 方案 step 5; [P4] §二.1: a combine kernel
 // merges the split-KV results).
 //
-// Each thread owns four consecutive output dims of one (unit, row, query head); 32 threads
-// cover the 128 dims.  The unit's slots are walked once with a running maximum:
+// For every (unit, row, query head):
 //   M = max_s m_s,  w_s = exp(m_s - M),  out = sum_s w_s o_s / sum_s w_s l_s,
 // slots with m_s = -inf (no visible key) contribute nothing, and a unit with no visible key at
 // all gets 0.  Slots of one unit are contiguous in the map, in ascending KV order.
@@ -24,57 +23,93 @@ struct CombineParams {
   int32_t U, R, Hq, out_bf16;
 };
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, xor_lane(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += xor_lane(v, m);
+  return v;
+}
+
+// One wave per (unit, row, query head).  Pass 1 spreads the unit's slots over the lanes for the
+// maximum and the weighted sum of l; pass 2 gives each lane two output dims and walks the slots
+// with independent loads (unrolled) so the short, latency-bound loop keeps several in flight.
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t total = (int64_t)p.U * p.R * p.Hq;
+  if (gw >= total) return;
   const int W = p.map[2];
   const int32_t* unit_ptr = p.map + 8 + (W + 1);
   const int32_t* units = unit_ptr + (p.U + 1);
-  const int64_t total = (int64_t)p.U * p.R * p.Hq * 32;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int d4 = (int)(idx & 31);
-    int64_t rest = idx >> 5;
-    const int h = (int)(rest % p.Hq);
-    rest /= p.Hq;
-    const int r = (int)(rest % p.R);
-    const int u = (int)(rest / p.R);
-    const int b = units[2 * u];
-    const int qt = units[2 * u + 1];
-    int64_t orow;
-    if (p.q_lens) {
-      const int row_in_req = qt * p.R + r;
-      if (row_in_req >= p.q_lens[b]) continue;
-      orow = (int64_t)p.q_start[b] + row_in_req;
-    } else {
-      orow = b;
+  const int h = (int)(gw % p.Hq);
+  const int64_t rest = gw / p.Hq;
+  const int r = (int)(rest % p.R);
+  const int u = (int)(rest / p.R);
+  const int b = units[2 * u];
+  const int qt = units[2 * u + 1];
+  int64_t orow;
+  if (p.q_lens) {
+    const int row_in_req = qt * p.R + r;
+    if (row_in_req >= p.q_lens[b]) return;
+    orow = (int64_t)p.q_start[b] + row_in_req;
+  } else {
+    orow = b;
+  }
+  const int s0 = unit_ptr[u];
+  const int n = unit_ptr[u + 1] - s0;
+  auto slot = [&](int i) -> int64_t { return ((int64_t)(s0 + i) * p.R + r) * p.Hq + h; };
+
+  float M = -INFINITY;
+  for (int i = lane; i < n; i += 64) M = fmaxf(M, p.part_m[slot(i)]);
+  M = wave_max(M);
+  float L = 0.f;
+  if (M != -INFINITY) {
+    for (int i = lane; i < n; i += 64) {
+      const float m = p.part_m[slot(i)];
+      if (m != -INFINITY) L += fast_exp2((m - M) * kLog2e) * p.part_l[slot(i)];
     }
-    float M = -INFINITY, L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int s1 = unit_ptr[u + 1];
-    for (int s = unit_ptr[u]; s < s1; ++s) {
-      const int64_t slot = ((int64_t)s * p.R + r) * p.Hq + h;
-      const float m = p.part_m[slot];
-      if (m == -INFINITY) continue;
-      if (m > M) {
-        const float sc = fast_exp2((M - m) * kLog2e);   // M = -inf gives 0
-        acc *= sc;
-        L *= sc;
-        M = m;
+  }
+  L = wave_sum(L);
+
+  float a0 = 0.f, a1 = 0.f;
+  if (L > 0.f) {
+    int i = 0;
+    for (; i + 4 <= n; i += 4) {
+      float m[4];
+      float2 o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m[j] = p.part_m[slot(i + j)];
+        o[j] = *reinterpret_cast<const float2*>(p.part_o + slot(i + j) * 128 + 2 * lane);
       }
-      const float wgt = fast_exp2((m - M) * kLog2e);
-      L += wgt * p.part_l[slot];
-      const f32x4 o = *reinterpret_cast<const f32x4*>(p.part_o + slot * 128 + 4 * d4);
-      acc += wgt * o;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float w = (m[j] == -INFINITY) ? 0.f : fast_exp2((m[j] - M) * kLog2e);
+        a0 += w * o[j].x;
+        a1 += w * o[j].y;
+      }
     }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    acc *= inv;
-    const int64_t obase = (orow * p.Hq + h) * 128 + 4 * d4;
-    if (p.out_bf16) {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + obase);
-      dst[0] = pack_bf16(acc[0], acc[1]);
-      dst[1] = pack_bf16(acc[2], acc[3]);
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase) = acc;
+    for (; i < n; ++i) {
+      const float m = p.part_m[slot(i)];
+      const float2 o = *reinterpret_cast<const float2*>(p.part_o + slot(i) * 128 + 2 * lane);
+      const float w = (m == -INFINITY) ? 0.f : fast_exp2((m - M) * kLog2e);
+      a0 += w * o.x;
+      a1 += w * o.y;
     }
+    const float inv = 1.f / L;
+    a0 *= inv;
+    a1 *= inv;
+  }
+  const int64_t obase = (orow * p.Hq + h) * 128 + 2 * lane;
+  if (p.out_bf16) {
+    reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + obase)[0] = pack_bf16(a0, a1);
+  } else {
+    *reinterpret_cast<float2*>(static_cast<float*>(p.out) + obase) = make_float2(a0, a1);
   }
 }
 
@@ -91,14 +126,14 @@ extern "C" int attn_combine(const float* part_m, const float* part_l, const floa
   if (!q_lens && rows_per_unit != 1) return LBSA_ERR_INVALID;
   if (out_dtype != 0 && out_dtype != 1) return LBSA_ERR_INVALID;
   if (head_dim != 128) return LBSA_ERR_UNSUPPORTED;
-  if ((reinterpret_cast<uintptr_t>(part_o) | reinterpret_cast<uintptr_t>(out)) & (out_dtype ? 7 : 15))
+  if ((reinterpret_cast<uintptr_t>(part_o) | reinterpret_cast<uintptr_t>(out)) & (out_dtype ? 3 : 7))
     return LBSA_ERR_INVALID;
   if (num_units == 0) return LBSA_OK;
   CombineParams p{part_m, part_l, part_o, map, q_lens, q_start, out, num_units, rows_per_unit,
                   num_q_heads, out_dtype};
-  const int64_t total = (int64_t)num_units * rows_per_unit * num_q_heads * 32;
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
+  const int64_t waves = (int64_t)num_units * rows_per_unit * num_q_heads;
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks > INT32_MAX) return LBSA_ERR_INVALID;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0,
                      static_cast<hipStream_t>(stream), p);
   return hipGetLastError() == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;

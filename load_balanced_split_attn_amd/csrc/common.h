@@ -16,6 +16,11 @@ constexpr float kLn2 = 0.6931471805599453f;
 // 16-byte global load of 8 bf16 values (one dwordx4).
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Streaming 16-byte load: non-temporal hint for data read exactly once (the KV stream).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // v_mfma_f32_16x16x32_bf16: C[16x16] += A[16x32] * B[32x16].  Lane l supplies row (l % 16) of A
