@@ -190,6 +190,58 @@ def _cpu_model() -> str:
     return "unknown"
 
 
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def prefill_flops(wl) -> int:
+    """Algorithmic flops of causal chunked prefill: 4 * D * Hq per (row, visible key) pair."""
+    total = 0
+    for ql, kl in zip(wl.q_lens, wl.kv_lens):
+        prefix = kl - ql
+        total += ql * prefix + ql * (ql + 1) // 2
+    return 4 * wl.head_dim * wl.hq * total
+
+
+def bench_prefill(dev, workers_list, steps: int, warmup: int) -> dict:
+    """Chunked prefill over cached prefixes: 8 requests x 2048-row causal chunks after prefixes drawn
+    log-uniform in [8K, 128K]; q tiles of 128 rows x KV tiles of 512 on the same greedy planner."""
+    import numpy as np
+    import torch
+
+    import workloads as WL
+    from load_balanced_split_attn_amd.paged import pack_paged
+    from load_balanced_split_attn_amd.prefill import PrefillStep
+    wl = WL.prefill()
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    q = torch.cat([wl.q(b) for b in range(wl.batch)], dim=0).to(dev)
+    kc, vc, bt = pack_paged(wl.kv, wl.kv_lens, 64, wl.hkv, wl.head_dim, wl.page_permutation, dev)
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    flops = prefill_flops(wl)
+    rows = []
+    for W in workers_list:
+        st = PrefillStep(wl.q_lens, wl.kv_lens, dev, num_workers=W)
+        r = time_steps(lambda i, st=st: st.splitkv(q, kc, vc, bt, scale), lambda i, st=st: st.combine(out),
+                       steps, warmup)
+        split_ms = float(np.mean(r["split_ms"]))
+        rows.append({"workers": W, "segments": st.S, "us_per_step": round(r["total_ms"] / steps * 1e3, 1),
+                     "splitkv_us": round(split_ms * 1e3, 1),
+                     "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 1),
+                     "splitkv_tflops": round(flops / (split_ms * 1e-3) / 1e12, 1)})
+        log(f"prefill W={W}: splitkv {split_ms * 1e3:.0f} us ({rows[-1]['splitkv_tflops']} TFLOP/s)")
+        del st
+    best = min(rows, key=lambda x: x["us_per_step"])
+    prefix = wl.meta["prefix"]
+    cached = sum(prefix) / sum(wl.kv_lens)
+    return {"workload": "chunked prefill: 8 x 2048-row causal chunks after prefixes log-uniform in [8K, 128K] "
+                        f"({prefix}), GQA 64q/8kv, d=128, bf16, q tile 128 x KV tile 512",
+            "cached_fraction": round(cached, 4), "flops_per_step": flops,
+            "us_per_step": best["us_per_step"], "tflops_per_step": round(flops / (best["us_per_step"] * 1e-6) / 1e12, 1),
+            "roofline": {"bound": "mfma", "kernel": "splitkv_prefill_kernel",
+                         "achieved": best["splitkv_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(best["splitkv_tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None},
+            "sweep": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +258,9 @@ def main() -> int:
     ap.add_argument("--calibration-copy", action="store_true",
                     help="run one plain 1 GiB copy first (reference for the HBM byte counters)")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill report")
+    ap.add_argument("--prefill-workers", default="8,16,32")
+    ap.add_argument("--prefill-steps", type=int, default=5)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -338,6 +393,10 @@ def main() -> int:
             best = gbs if best is None else max(best, gbs)
         result["stream_read_ceiling"] = {"GB/s": round(best, 1), "buffer_GB": round(kc.numel() * 2 / 1e9, 2),
                                          "splitkv_frac_of_ceiling": round(achieved / best, 4)}
+
+    if not args.no_prefill:
+        result["prefill"] = bench_prefill(dev, [int(x) for x in args.prefill_workers.split(",")],
+                                          args.prefill_steps, 1)
 
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a CPU sample")

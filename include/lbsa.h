@@ -147,7 +147,7 @@ int attn_query_workers(int device, int32_t head_groups, int32_t* num_workers_out
  *   timing        optional device uint64[W*G*4] (start, end, HW_ID, XCC_ID per
  *                 workgroup, device realtime clock); NULL disables recording
  *   stream        hipStream_t, or NULL for the null stream
- * Supported: head_dim 128, Hq/Hkv = 8, bf16, page_size a multiple of 32.
+ * Supported: head_dim 128, Hq/Hkv = 8, bf16, page_size a multiple of 64.
  * Errors: LBSA_ERR_INVALID, LBSA_ERR_UNSUPPORTED, LBSA_ERR_HIP.
  */
 int attn_splitkv(const void* q, const void* k_cache, const void* v_cache,
@@ -158,6 +158,29 @@ int attn_splitkv(const void* q, const void* k_cache, const void* v_cache,
                  int32_t page_size, float softmax_scale,
                  float* part_m, float* part_l, float* part_o,
                  uint64_t* timing, void* stream);
+
+/*
+ * Split-KV chunked-prefill kernel over a cached prefix (the greedy map of attn_plan_prefill
+ * applied to prefill units; prefix reuse as in [P3] §6: a request's new chunk attends to its
+ * cached prefix and, causally, to itself).  Request b has q_lens[b] query rows stored from row
+ * q_start[b] of q [rows, Hq, D]; they are the last q_lens[b] positions of a kv_lens[b]-token
+ * context held in the paged caches.  Launches 8 x ceil(W x Hkv / 8) x 8 workgroups of 256
+ * threads: workgroup (w, g, h) walks worker w's segments for query head h of KV head g, 32 rows per
+ * wave.  Writes, for every segment s and row i < q_tile of its unit that lies inside the chunk,
+ * part_m/part_l [S, q_tile, Hq] and part_o [S, q_tile, Hq, D] (rows past the chunk are not
+ * written).  With causal != 0 row j sees keys [0, kv_lens[b] - q_lens[b] + j]; otherwise all keys.
+ *   q_lens, q_start, kv_lens  device int32[B]
+ *   map           device copy of the attn_plan_prefill map (same q_tile, kv_tile % 64 == 0)
+ * Supported: head_dim 128, Hq/Hkv = 8, bf16, q_tile 128, page_size a multiple of 64.
+ * Errors: LBSA_ERR_INVALID, LBSA_ERR_UNSUPPORTED, LBSA_ERR_HIP.
+ */
+int attn_splitkv_prefill(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
+                         const int32_t* q_lens, const int32_t* q_start, const int32_t* kv_lens,
+                         const int32_t* map, int32_t num_workers, int32_t num_segments, int32_t B,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                         int32_t q_tile, int32_t causal, float softmax_scale,
+                         float* part_m, float* part_l, float* part_o, void* stream);
 
 /*
  * Combine kernel ([P3] §3.1 方案 step 5): for every unit and query head merges the

@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill",
-    "attn_query_workers", "attn_splitkv", "attn_combine", "attn_status_string", "LIB_PATH",
+    "attn_query_workers", "attn_splitkv", "attn_splitkv_prefill", "attn_combine", "attn_status_string",
+    "attn_probe_stream_read", "map_header", "LIB_PATH",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbsa.so")
@@ -40,6 +41,9 @@ _SIGNATURES = {
     "attn_combine": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                     _c_i32, _c_i32, _c_vp, _c_i32, _c_vp]),
     "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
+    "attn_splitkv_prefill": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
+                                            _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                            _c_i32, _c_i32, ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp]),
 }
 
 _lib = None
@@ -185,6 +189,39 @@ def attn_splitkv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                             Hkv, D, page, float(softmax_scale), _dptr(part_m), _dptr(part_l), _dptr(part_o),
                             _dptr(timing), _stream(stream))
     _check(st, "attn_splitkv")
+
+
+def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                         q_lens: torch.Tensor, q_start: torch.Tensor, kv_lens: torch.Tensor, map_dev: torch.Tensor,
+                         num_workers: int, num_segments: int, softmax_scale: float, part_m: torch.Tensor,
+                         part_l: torch.Tensor, part_o: torch.Tensor, causal: bool = True, q_tile: int = 128,
+                         stream=None) -> None:
+    """Launch the chunked-prefill split-KV kernel.  q [rows, Hq, D]; caches as in attn_splitkv;
+    q_lens/q_start/kv_lens [B]; part_m/l [S, q_tile, Hq]; part_o [S, q_tile, Hq, D]."""
+    dev = q.device
+    _need(q, torch.bfloat16, "q", dev)
+    _need(k_cache, torch.bfloat16, "k_cache", dev)
+    _need(v_cache, torch.bfloat16, "v_cache", dev)
+    _need(block_table, torch.int32, "block_table", dev)
+    for name, t in (("q_lens", q_lens), ("q_start", q_start), ("kv_lens", kv_lens), ("map", map_dev)):
+        _need(t, torch.int32, name, dev)
+    for name, t in (("part_m", part_m), ("part_l", part_l), ("part_o", part_o)):
+        _need(t, torch.float32, name, dev)
+    rows, Hq, D = q.shape
+    P, Hkv, page, Dk = k_cache.shape
+    B = q_lens.numel()
+    if tuple(v_cache.shape) != (P, Hkv, D, page) or Dk != D:
+        raise ValueError("k_cache/v_cache shapes do not match [P, Hkv, page, D] / [P, Hkv, D, page]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or q_start.numel() != B or kv_lens.numel() != B:
+        raise ValueError("block_table/q_start/kv_lens do not match the batch")
+    if part_m.numel() < num_segments * q_tile * Hq or part_o.numel() < num_segments * q_tile * Hq * D:
+        raise ValueError("partial buffers smaller than num_segments")
+    st = lib().attn_splitkv_prefill(_dptr(q), _dptr(k_cache), _dptr(v_cache), _dptr(block_table),
+                                    block_table.shape[1], P, _dptr(q_lens), _dptr(q_start), _dptr(kv_lens),
+                                    _dptr(map_dev), num_workers, num_segments, B, Hq, Hkv, D, page, q_tile,
+                                    int(bool(causal)), float(softmax_scale), _dptr(part_m), _dptr(part_l),
+                                    _dptr(part_o), _stream(stream))
+    _check(st, "attn_splitkv_prefill")
 
 
 def attn_combine(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor, map_dev: torch.Tensor,

@@ -52,3 +52,31 @@ def assert_close(got: np.ndarray, ref: np.ndarray, what: str, max_abs=MAX_ABS, r
     ma, rr = errors(got, ref)
     assert ma <= max_abs and rr <= rel_rms, f"{what}: max_abs={ma:.3e} rel_rms={rr:.3e}"
     return ma, rr
+
+
+def prefill_inputs(wl: WL.Workload, device="cuda", page=64, pad_value=0.0):
+    q = torch.cat([wl.q(b) for b in range(wl.batch)], dim=0).to(device)
+    k_cache, v_cache, bt = pack_paged(wl.kv, wl.kv_lens, page, wl.hkv, wl.head_dim, wl.page_permutation,
+                                      device, pad_value=pad_value)
+    return q, k_cache, v_cache, bt
+
+
+def q_starts(wl: WL.Workload):
+    starts, acc = [], 0
+    for n in wl.q_lens:
+        starts.append(acc)
+        acc += n
+    return starts
+
+
+def oracle_prefill_rows(wl: WL.Workload, b: int, rows, causal=True, scale=SCALE):
+    """fp64 oracle for selected rows of request b's chunk: {row: [Hq, D]}."""
+    from oracle.attention import ref_partial
+    q = wl.q(b).to(torch.float64).numpy()
+    k, v = wl.kv(b)
+    kd, vd = k.to(torch.float64).numpy(), v.to(torch.float64).numpy()
+    out = {}
+    for j in rows:
+        m, l, o = ref_partial(q[j:j + 1], kd, vd, scale, 0, kd.shape[0], causal, first_row=j, q_len=q.shape[0])
+        out[j] = o[0] / l[0][:, None]
+    return out

@@ -1,0 +1,94 @@
+"""GPU parity of the chunked-prefill path (attn_plan_prefill -> attn_splitkv_prefill ->
+attn_combine through the C ABI) against the fp64 oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from gpu_helpers import (SCALE, assert_close, errors, note, oracle_prefill_rows, prefill_inputs, q_starts)
+from oracle.attention import ref_attention
+from oracle.plan import ref_plan_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, W, causal=True, inputs=None, poison=False, kv_tile=512):
+    from load_balanced_split_attn_amd.prefill import PrefillStep
+    q, kc, vc, bt = inputs if inputs is not None else prefill_inputs(wl, pad_value=float("nan"))
+    step = PrefillStep(wl.q_lens, wl.kv_lens, q.device, num_workers=W, causal=causal, kv_tile=kv_tile)
+    assert np.array_equal(step.map_host, ref_plan_prefill(wl.q_lens, wl.kv_lens, W, 128, kv_tile, causal))
+    if poison:
+        for t in (step.part_m, step.part_l, step.part_o):
+            t.fill_(float("nan"))
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device)
+    step(q, kc, vc, bt, scale=SCALE, out=out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), step
+
+
+def _check_all(wl, got, causal=True):
+    starts = q_starts(wl)
+    for b in range(wl.batch):
+        k, v = wl.kv(b)
+        ref = ref_attention(wl.q(b).double().numpy(), k.double().numpy(), v.double().numpy(), SCALE, causal=causal)
+        assert_close(got[starts[b]:starts[b] + wl.q_lens[b]], ref,
+                     f"{wl.name} request {b} (q_len={wl.q_lens[b]}, kv_len={wl.kv_lens[b]}, causal={causal})")
+
+
+@pytest.mark.parametrize("seed,batch,max_prefix,max_chunk,W", [
+    (0, 3, 1500, 300, 3), (1, 4, 700, 200, 1), (2, 2, 3000, 260, 8), (3, 5, 100, 140, 16),
+])
+def test_random_prefill(seed, batch, max_prefix, max_chunk, W):
+    wl = WL.random_prefill(seed, batch, max_prefix, max_chunk)
+    note(f"prefill seed={seed} q_lens={wl.q_lens} kv_lens={wl.kv_lens} W={W}")
+    got, _ = _run(wl, W, causal=True, poison=True)
+    _check_all(wl, got, causal=True)
+
+
+def test_non_causal_and_small_tiles():
+    wl = WL.random_prefill(7, 3, 900, 200)
+    note(f"non-causal q_lens={wl.q_lens} kv_lens={wl.kv_lens}")
+    got, _ = _run(wl, 5, causal=False)
+    _check_all(wl, got, causal=False)
+    got, _ = _run(wl, 5, causal=True, kv_tile=64)
+    _check_all(wl, got, causal=True)
+
+
+def test_no_prefix_is_textbook_causal():
+    wl = WL.random_prefill(8, 2, 0, 300)   # prefix 0: plain causal self-attention of the chunk
+    note(f"no prefix q_lens={wl.q_lens} kv_lens={wl.kv_lens}")
+    got, _ = _run(wl, 4)
+    _check_all(wl, got)
+
+
+def test_single_row_matches_decode():
+    """A one-row chunk is a decode query at the last position."""
+    import load_balanced_split_attn_amd as lb
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    wl = WL.random_prefill(9, 3, 2000, 1)
+    wl.q_lens = [1] * wl.batch
+    wl.kv_lens = [max(1, L) for L in wl.kv_lens]
+    q, kc, vc, bt = prefill_inputs(wl)
+    got, _ = _run(wl, 3, inputs=(q, kc, vc, bt))
+    step = DecodeStep(wl.kv_lens, q.device, num_workers=3)
+    dec = step(q, kc, vc, bt, scale=SCALE)
+    torch.cuda.synchronize()
+    assert errors(got.astype(np.float64), dec.cpu().numpy().astype(np.float64))[1] <= 1e-5
+
+
+def test_full_size_prefill_sampled():
+    """The chunked-prefill batch (8 x 2048-row chunks after log-uniform [8K, 128K] prefixes) in the
+    bench launch configuration; sampled rows of three requests against the oracle."""
+    wl = WL.prefill()
+    note(f"full-size prefill kv_lens={wl.kv_lens}")
+    W = 8
+    got, step = _run(wl, W, poison=True)
+    assert np.all(np.isfinite(got))
+    starts = q_starts(wl)
+    rows = [0, 1, 127, 128, 511, 1024, 1500, 2047]
+    for b in (0, 2, int(np.argmax(wl.kv_lens))):
+        ref = oracle_prefill_rows(wl, b, rows)
+        for j in rows:
+            ma, rr = assert_close(got[starts[b] + j], ref[j], f"prefill request {b} row {j}")
+        note(f"  request {b} kv_len={wl.kv_lens[b]}: rows {rows} ok (last rel_rms {rr:.2e})")
