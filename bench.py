@@ -259,7 +259,7 @@ def main() -> int:
                     help="run one plain 1 GiB copy first (reference for the HBM byte counters)")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill report")
-    ap.add_argument("--prefill-workers", default="8,16,32")
+    ap.add_argument("--prefill-workers", default="32,64")
     ap.add_argument("--prefill-steps", type=int, default=5)
     args = ap.parse_args()
 

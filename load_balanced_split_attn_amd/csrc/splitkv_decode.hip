@@ -140,7 +140,7 @@ __device__ __forceinline__ void compute_chunk(Chunk& ch, State& st, const u32x4 
       const int t0 = c0 + 32 * kb_i + 8 * ln.grp;
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        if (t0 + e < kv_begin || t0 + e >= kv_end) sc[kb_i][e] = -INFINITY;
+        sc[kb_i][e] = (t0 + e < kv_begin || t0 + e >= kv_end) ? -INFINITY : sc[kb_i][e];
       // masked tokens may hold any bits (NaN included), and p = 0 does not cancel a NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

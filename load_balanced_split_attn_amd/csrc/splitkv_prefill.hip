@@ -9,12 +9,16 @@
 //
 // gfx950 design.  Workgroup = (worker w, KV head g, query head h of the group), 4 waves; wave v
 // owns the 32 query rows 32v .. 32v+31 of the unit.  Each 64-key chunk of K (token-major) and V
-// (dim-major) is staged once in LDS (double-buffered; global loads for the next chunk are in flight
-// while the current one is computed) and read by all four waves: 128 query rows per K/V load, and
-// the eight query heads of a KV head run as eight workgroups on one XCD so K/V come from one L2.
+// (dim-major) goes from HBM straight into LDS with buffer->LDS loads (no registers), in XOR-swizzled
+// layouts that the MFMA fragment reads take without bank conflicts, and is read by all four waves:
+// 128 query rows per K/V load; the eight query heads of a KV head run as eight workgroups on one
+// XCD so K/V come from one L2.  Two 32 KiB LDS stages (the next chunk streams in while the current
+// one is computed) and a register budget of 256 let two workgroups share a CU, so one wave's
+// softmax VALU work overlaps another wave's MFMAs.
 // Per wave, with the query rows as the MFMA columns:
 //   S^T (keys x rows) = K . Q^T       v_mfma_f32_16x16x32_bf16, Q^T fragments held in VGPRs
-//   O^T (dims x rows) += V^T . P^T    same instruction, P as bf16 hi + lo parts
+//   O^T (dims x rows) += V^T . P^T    v_mfma_f32_16x16x32_bf16 with P as bf16 hi + lo parts
+//                                      (or fp16 operands, see LBSA_PREFILL_PV_F16)
 // so every lane holds whole columns: the softmax max/sum of a row needs only in-lane reductions and
 // two lane exchanges, exactly as in the decode kernel.  Key tiles are interleaved in 4-key groups so
 // that a lane's 8 scores per 32 keys are the 8 consecutive keys it supplies to the PV product.
@@ -44,12 +48,50 @@ constexpr int kPD = 128;          // head dim
 constexpr int kPChunk = 64;       // keys per staged chunk
 constexpr int kQTile = 128;       // query rows per unit
 constexpr int kColBlocks = 2;     // 16-row column blocks per wave (32 rows)
-constexpr int kKRow = kPD * 2;             // LDS bytes per key row of K (16-byte granules XOR-swizzled)
-constexpr int kVRow = kPChunk * 2 + 16;    // LDS bytes per dim row of V^T (padded by one granule)
-constexpr int kKBytes = kPChunk * kKRow;   // 17408
-constexpr int kVBytes = kPD * kVRow;       // 18432
-constexpr int kStage = kKBytes + kVBytes;  // one buffer
-constexpr float kPRescaleSlack = 8.0f;
+constexpr int kKRow = kPD * 2;             // LDS bytes per key row of K (16 granules, XOR-swizzled)
+constexpr int kVRow = kPChunk * 2;         // LDS bytes per dim row of V^T (8 granules, XOR-swizzled)
+constexpr int kKBytes = kPChunk * kKRow;   // 16 KiB
+constexpr int kVBytes = kPD * kVRow;       // 16 KiB
+constexpr int kStage = kKBytes + kVBytes;  // one pipeline stage: a 64-key chunk of K and V^T
+constexpr float kPRescaleSlack = 8.0f;   // log2 units
+
+// Tuning knobs (compile-time):
+//   LBSA_PREFILL_PV_F16  1: P.V on v_mfma_f32_16x16x32_f16 - each V fragment is converted to fp16
+//                        after it is read from LDS (exact for |v| in the fp16 normal range; larger
+//                        magnitudes saturate at 65504) and P is rounded to fp16 (11 significant
+//                        bits); 0: bf16 V with P split into bf16 hi + lo parts (two MFMAs)
+//   LBSA_PREFILL_WPE     waves per SIMD the register budget is fitted to (1 or 2)
+#ifndef LBSA_PREFILL_PV_F16
+#define LBSA_PREFILL_PV_F16 0
+#endif
+#ifndef LBSA_PREFILL_WPE
+#define LBSA_PREFILL_WPE 2
+#endif
+//   LBSA_PREFILL_STAGES  LDS pipeline stages of 32 KiB (3: two chunks in flight, one workgroup per
+//                        CU; 2: one chunk in flight, two workgroups per CU)
+#ifndef LBSA_PREFILL_STAGES
+#define LBSA_PREFILL_STAGES 2
+#endif
+
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                0, 0);
+}
+
+// two bf16 values (one dword) -> two fp16 values, round toward zero (exact for the values bf16 and
+// fp16 share; saturates instead of overflowing)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(x), bf16_hi(x)));
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 __device__ __forceinline__ u32x4 lds_ld16(const uint8_t* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
@@ -58,13 +100,32 @@ __device__ __forceinline__ u32x4 lds_ld16(const uint8_t* base, int off) {
 // K rows are 256 B (16 granules).  The 16 lanes of one ds_read_b128 read the same granule of keys
 // {0-3, 8-11, 16-19, 24-27} (+4): granule G of key k sits at slot G ^ swz(k), which gives those 16
 // keys 16 different bank groups.
-__device__ __forceinline__ int k_slot(int key, int granule) {
-  const int swz = (key & 3) | (((key >> 3) & 3) << 2);
-  return key * kKRow + 16 * (granule ^ swz);
-}
+__device__ __forceinline__ int k_swz(int key) { return (key & 3) | (((key >> 3) & 3) << 2); }
+__device__ __forceinline__ int k_slot(int key, int granule) { return key * kKRow + 16 * (granule ^ k_swz(key)); }
 
-__global__ __launch_bounds__(256) void splitkv_prefill_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage];
+// V^T rows are 128 B (8 granules).  The 16 lanes of one read take dims 16n + 0..15 at one key
+// granule: granule G of dim d sits at slot G ^ ((d >> 1) & 7), so the 16 reads hit 16 bank groups.
+__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
+__device__ __forceinline__ int v_slot(int d, int granule) { return kKBytes + d * kVRow + 16 * (granule ^ v_swz(d)); }
+
+#define LBSA_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
+
+// Read-only kernel inputs read at wave-uniform addresses (block table): the constant address
+// space makes them scalar loads, counted apart from the vector-memory queue the LDS DMA uses.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+
+// s_waitcnt with vmcnt <= vm and lgkmcnt <= lgkm (gfx9 encoding; expcnt left at its maximum)
+#define LBSA_WAIT_VM_LGKM(vm, lgkm) \
+  __builtin_amdgcn_s_waitcnt(((vm) & 0xF) | (((vm) >> 4) << 14) | (0x7 << 4) | (((lgkm) & 0xF) << 8))
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LBSA_PREFILL_WPE, LBSA_PREFILL_WPE)))
+void splitkv_prefill_kernel(PrefillParams p) {
+  // three pipeline stages, separate objects so the compiler can tell their DMA writes apart
+  __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
+#if LBSA_PREFILL_STAGES == 3
+  __shared__ __attribute__((aligned(16))) uint8_t stage2[kStage];
+#endif
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -85,12 +146,32 @@ __global__ __launch_bounds__(256) void splitkv_prefill_kernel(PrefillParams p) {
   const int h = g * 8 + hq;                        // query head of this workgroup
   const int rbase = 32 * wave;                     // first row (inside the unit) of this wave
 
-  const int U = p.map[7];
-  const int32_t* worker_ptr = p.map + 8;
-  const int32_t* segs = p.map + 8 + (p.W + 1) + (U + 1) + 2 * U;
+  const_i32* map = (const_i32*)p.map;
+  const int U = map[7];
+  const_i32* worker_ptr = map + 8;
+  const_i32* segs = map + 8 + (p.W + 1) + (U + 1) + 2 * U;
+  const_i32* q_lens = (const_i32*)p.q_lens;
+  const_i32* q_start = (const_i32*)p.q_start;
+  const_i32* kv_lens = (const_i32*)p.kv_lens;
   const int s_begin = worker_ptr[w];
   const int s_end = min(worker_ptr[w + 1], p.S);
   const int block_bytes = p.page * kPD * 2;
+  const float c = p.scale_log2;                 // raw score -> log2 units
+  const float slack_raw = kPRescaleSlack / c;
+
+  // DMA layout: wave v fills LDS granules 64*(4v + t) + lane, t = 0..3, of the K half and of the
+  // V^T half of a stage; the lane fetches whichever global granule belongs in that swizzled slot
+  // byte offsets inside a (page, KV head) block; the chunk's offset in the page goes in the scalar
+  // offset, so these registers stay unchanged while earlier loads that read them are in flight
+  int k_src[4], v_src[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int slot = 64 * (4 * wave + t) + lane;
+    const int key = slot >> 4;
+    k_src[t] = (key * kPD + 8 * ((slot & 15) ^ k_swz(key))) * 2;
+    const int d = slot >> 3;
+    v_src[t] = (d * p.page + 8 * ((slot & 7) ^ v_swz(d))) * 2;
+  }
 
   for (int s = s_begin; s < s_end; ++s) {
     const int b = segs[4 * s];
@@ -98,8 +179,8 @@ __global__ __launch_bounds__(256) void splitkv_prefill_kernel(PrefillParams p) {
     const int kv_begin = segs[4 * s + 2];
     int kv_end = segs[4 * s + 3];
     if (b < 0 || b >= p.B) continue;
-    const int q_len = p.q_lens[b];
-    const int kv_len = p.kv_lens[b];
+    const int q_len = q_lens[b];
+    const int kv_len = kv_lens[b];
     const int prefix = kv_len - q_len;
     kv_end = min(kv_end, kv_len);
     kv_end = min(kv_end, p.bt_stride * p.page);
@@ -115,7 +196,7 @@ __global__ __launch_bounds__(256) void splitkv_prefill_kernel(PrefillParams p) {
     for (int cb = 0; cb < kColBlocks; ++cb) {
       const int row = wave_row0 + 16 * cb + r;
       const bool ok = row < q_len;
-      const uint16_t* qp = p.q + ((size_t)(p.q_start[b] + (ok ? row : 0)) * p.Hq + h) * kPD + 8 * grp;
+      const uint16_t* qp = p.q + ((size_t)(q_start[b] + (ok ? row : 0)) * p.Hq + h) * kPD + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qf[cb][ks] = ok ? ld16(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
     }
@@ -131,14 +212,15 @@ __global__ __launch_bounds__(256) void splitkv_prefill_kernel(PrefillParams p) {
       for (int n = 0; n < 8; ++n) o[cb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int32_t* bt_row = p.block_table + (size_t)b * p.bt_stride;
+    const_i32* bt_row = (const_i32*)(p.block_table + (size_t)b * p.bt_stride);
     const int c_first = kv_begin & ~(kPChunk - 1);
-    // chunk staging: every thread loads 4 K granules (key idx/16, dims 8*(idx%16)) and 4 V^T
-    // granules (dim idx/8, keys 8*(idx%8)) into registers, computes, then stores them to LDS
-    u32x4 kreg[4], vreg[4];
-    auto load_chunk = [&](int c) {
-      const int pg = c / p.page;
-      const int off = c - pg * p.page;
+    const int n_chunks = kv_end > c_first ? (kv_end - c_first + kPChunk - 1) / kPChunk : 0;
+
+    // chunk i -> stage: each wave issues 8 buffer->LDS loads of 1 KiB (4 of K, 4 of V^T)
+    auto dma = [&](int i, uint8_t* st) {
+      const int c0 = c_first + kPChunk * i;
+      const int pg = c0 / p.page;
+      const int off = c0 - pg * p.page;
       int pid = bt_row[pg];
       pid = min(max(pid, 0), p.num_pages - 1);
       const size_t blk = ((size_t)pid * p.Hkv + g) * (size_t)p.page * kPD;
@@ -147,71 +229,38 @@ __global__ __launch_bounds__(256) void splitkv_prefill_kernel(PrefillParams p) {
       __amdgpu_buffer_rsrc_t vr =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + blk), (short)0, block_bytes, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = tid + 256 * i;
-        kreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                kr, ((off + (idx >> 4)) * kPD + 8 * (idx & 15)) * 2, 0, 0));
-        vreg[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                vr, ((idx >> 3) * p.page + off + 8 * (idx & 7)) * 2, 0, 0));
-      }
-    };
-    auto store_chunk = [&](int buf_) {
-      uint8_t* kd = smem + buf_ * kStage;
-      uint8_t* vd = kd + kKBytes;
+      for (int t = 0; t < 4; ++t)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LBSA_LDS(st + 1024 * (4 * wave + t)), 16, k_src[t],
+                                                 off * kPD * 2, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx = tid + 256 * i;
-        *reinterpret_cast<u32x4*>(kd + k_slot(idx >> 4, idx & 15)) = kreg[i];
-        *reinterpret_cast<u32x4*>(vd + (idx >> 3) * kVRow + 16 * (idx & 7)) = vreg[i];
-      }
+      for (int t = 0; t < 4; ++t)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LBSA_LDS(st + kKBytes + 1024 * (4 * wave + t)), 16, v_src[t],
+                                                 off * 2, 0, 0);
     };
 
-    if (c_first < kv_end) {
-      load_chunk(c_first);
-      store_chunk(0);
-    }
-    int buf = 0;
-    for (int c0 = c_first; c0 < kv_end; c0 += kPChunk, buf ^= 1) {
-      __syncthreads();   // chunk c0 is in LDS buffer `buf`; every wave is done with buffer buf^1
-      const bool more = c0 + kPChunk < kv_end;
-      if (more) load_chunk(c0 + kPChunk);   // in flight while chunk c0 is computed
-      if (c0 > wave_last_key) {
-        // chunk entirely past this wave's causal diagonal: only help staging
-        if (more) store_chunk(buf ^ 1);
-        continue;
-      }
-      // chunk entirely above this wave's causal diagonal: nothing to do (still joins the barriers)
-      if (c0 > wave_last_key) continue;
-      const uint8_t* kd = smem + buf * kStage;
-      const uint8_t* vd = kd + kKBytes;
+    auto compute = [&](int i, const uint8_t* st) {
+      const int c0 = c_first + kPChunk * i;
+      if (c0 > wave_last_key) return;   // chunk entirely past this wave's rows (causal) or no rows
       // mask needed: keys outside [kv_begin, kv_end), or (causal) keys after some row's position
       const bool edge = (c0 < kv_begin) || (c0 + kPChunk > kv_end) ||
                         (p.causal && c0 + kPChunk - 1 > prefix + wave_row0);
-
-#pragma unroll 1
-      for (int kb = 0; kb < 2; ++kb) {
-        const int kbase = c0 + 32 * kb;
-        // scores: sc[cb][4j+i] = key kbase + 8grp + 4j + i, column (row) r of block cb
-        float sc[kColBlocks][8];
+      // sc[kb][cb][4j+i] = key c0 + 32kb + 8grp + 4j + i, column (row) r of block cb
+      auto qk = [&](int kb, float (&scb)[kColBlocks][8]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int key = 32 * kb + 8 * (r >> 2) + 4 * j + (r & 3);
           u32x4 kf[4];
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) kf[ks] = lds_ld16(kd, k_slot(key, 4 * ks + grp));
+          for (int ks = 0; ks < 4; ++ks) kf[ks] = lds_ld16(st, k_slot(key, 4 * ks + grp));
 #pragma unroll
           for (int cb = 0; cb < kColBlocks; ++cb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(kf[ks], qf[cb][ks], acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sc[cb][4 * j + i] = acc[i] * p.scale_log2;
+            for (int e = 0; e < 4; ++e) scb[cb][4 * j + e] = acc[e];   // raw q.k; scaled inside exp2
           }
         }
-        // V^T fragments of this 32-key block: dim 16n + r, keys kbase + 8grp .. +7
-        u32x4 vf[8];
-#pragma unroll
-        for (int n = 0; n < 8; ++n) vf[n] = lds_ld16(vd, (16 * n + r) * kVRow + (32 * kb + 8 * grp) * 2);
         if (edge) {
 #pragma unroll
           for (int cb = 0; cb < kColBlocks; ++cb) {
@@ -219,66 +268,165 @@ __global__ __launch_bounds__(256) void splitkv_prefill_kernel(PrefillParams p) {
             const int last = p.causal ? prefix + row : kv_len - 1;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int t = kbase + 8 * grp + e;
-              if (t < kv_begin || t >= kv_end || t > last) sc[cb][e] = -INFINITY;
+              const int t = c0 + 32 * kb + 8 * grp + e;
+              scb[cb][e] = (t < kv_begin || t >= kv_end || t > last) ? -INFINITY : scb[cb][e];
             }
           }
+        }
+      };
+      // S^T of both 32-key blocks, then one softmax update for the whole chunk, then P.V for both
+      // blocks: the exp / split work of one tile and the P.V MFMAs of another sit in one straight
+      // line of code the scheduler can interleave
+      float sc[2][kColBlocks][8];
+      qk(0, sc[0]);
+      qk(1, sc[1]);
+      float neg_mc[kColBlocks];
+      bool any_rescale = false;
+      float mxs[kColBlocks];
+#pragma unroll
+      for (int cb = 0; cb < kColBlocks; ++cb) {
+        float mx = sc[0][cb][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[kb][cb][e]);
+        mx = fmaxf(mx, xor_lane(mx, 16));
+        mx = fmaxf(mx, xor_lane(mx, 32));
+        m_true[cb] = fmaxf(m_true[cb], mx);
+        mxs[cb] = mx;
+        any_rescale |= mx > m_ref[cb] + slack_raw;
+      }
+      if (__builtin_amdgcn_ballot_w64(any_rescale)) {
+#pragma unroll
+        for (int cb = 0; cb < kColBlocks; ++cb) {
+          const float m_new = (mxs[cb] > m_ref[cb] + slack_raw) ? mxs[cb] : m_ref[cb];
+          const float alpha = fast_exp2((m_ref[cb] - m_new) * c);   // 1 where unchanged, 0 from -inf
+          m_ref[cb] = m_new;
+          lsum[cb] *= alpha;
+#pragma unroll
+          for (int n = 0; n < 8; ++n) o[cb][n] *= alpha;
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < kColBlocks; ++cb) neg_mc[cb] = (m_ref[cb] == -INFINITY) ? 0.f : -m_ref[cb] * c;
+
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kbase = c0 + 32 * kb;
+        // V^T fragments of this 32-key block: dim 16n + r, keys kbase + 8grp .. +7
+        u32x4 vf[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) vf[n] = lds_ld16(st, v_slot(16 * n + r, 4 * kb + grp));
+        if (edge) {
           // keys outside [kv_begin, kv_end) may hold any bits; p = 0 does not cancel a NaN
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = kbase + 8 * grp + 2 * i;
+          for (int e = 0; e < 4; ++e) {
+            const int t = kbase + 8 * grp + 2 * e;
             const uint32_t keep = ((t >= kv_begin && t < kv_end) ? 0x0000ffffu : 0u) |
                                   ((t + 1 >= kv_begin && t + 1 < kv_end) ? 0xffff0000u : 0u);
 #pragma unroll
-            for (int n = 0; n < 8; ++n) vf[n][i] &= keep;
+            for (int n = 0; n < 8; ++n) vf[n][e] &= keep;
           }
         }
+#if LBSA_PREFILL_PV_F16
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vf[n][e] = bf16x2_to_f16x2(vf[n][e]);
+#endif
 #pragma unroll
         for (int cb = 0; cb < kColBlocks; ++cb) {
-          float mx = sc[cb][0];
-#pragma unroll
-          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[cb][e]);
-          mx = fmaxf(mx, xor_lane(mx, 16));
-          mx = fmaxf(mx, xor_lane(mx, 32));
-          m_true[cb] = fmaxf(m_true[cb], mx);
-          const bool need = mx > m_ref[cb] + kPRescaleSlack;
-          if (__builtin_amdgcn_ballot_w64(need)) {
-            const float m_new = need ? mx : m_ref[cb];
-            const float alpha = fast_exp2(m_ref[cb] - m_new);
-            m_ref[cb] = m_new;
-            lsum[cb] *= alpha;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) o[cb][n] *= alpha;
-          }
-          const float m_use = (m_ref[cb] == -INFINITY) ? 0.f : m_ref[cb];
           float ps[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            ps[e] = fast_exp2(sc[cb][e] - m_use);
+            ps[e] = fast_exp2(fmaf(sc[kb][cb][e], c, neg_mc[cb]));
             lsum[cb] += ps[e];
           }
+#if LBSA_PREFILL_PV_F16
+          u32x4 pf;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pf[e] = pack_f16(ps[2 * e], ps[2 * e + 1]);
+#pragma unroll
+          for (int n = 0; n < 8; ++n) o[cb][n] = mfma16x16x32_f16(vf[n], pf, o[cb][n]);
+#else
+          // P split into bf16 hi + lo parts: two MFMAs keep ~16 significant bits of each probability
           u32x4 phi, plo;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t hv = pack_bf16(ps[2 * i], ps[2 * i + 1]);
-            phi[i] = hv;
-            plo[i] = pack_bf16(ps[2 * i] - bf16_lo(hv), ps[2 * i + 1] - bf16_hi(hv));
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t hv = pack_bf16(ps[2 * e], ps[2 * e + 1]);
+            phi[e] = hv;
+            plo[e] = pack_bf16(ps[2 * e] - bf16_lo(hv), ps[2 * e + 1] - bf16_hi(hv));
           }
 #pragma unroll
           for (int n = 0; n < 8; ++n) {
             o[cb][n] = mfma16x16x32(vf[n], phi, o[cb][n]);
             o[cb][n] = mfma16x16x32(vf[n], plo, o[cb][n]);
           }
+#endif
         }
       }
-      if (more) store_chunk(buf ^ 1);
-    }
-    __syncthreads();   // all waves are done with LDS before the next segment stages into it
+    };
 
-    // write the partials of this wave's 64 rows (rows past the chunk's end are not stored)
+#if LBSA_PREFILL_STAGES == 3
+    // one pipeline step: start chunk i+2's DMA, compute chunk i, then make chunk i+1 visible to
+    // every wave (own DMA complete -> barrier).  Stage i+2 was last read by chunk i-1, which every
+    // wave finished before the previous step's barrier.
+    auto step = [&](int i, const uint8_t* cur, uint8_t* ahead) {
+      const bool more = i + 2 < n_chunks;
+      if (more) dma(i + 2, ahead);
+      compute(i, cur);
+      if (more) {
+        LBSA_WAIT_VM_LGKM(8, 0);
+      } else {
+        LBSA_WAIT_VM_LGKM(0, 0);
+      }
+      __builtin_amdgcn_s_barrier();
+    };
+
+    if (n_chunks > 0) {
+      dma(0, stage0);
+      if (n_chunks > 1) {
+        dma(1, stage1);
+        LBSA_WAIT_VM_LGKM(8, 0);
+      } else {
+        LBSA_WAIT_VM_LGKM(0, 0);
+      }
+      __builtin_amdgcn_s_barrier();
+      for (int i = 0; i < n_chunks; i += 3) {
+        step(i, stage0, stage2);
+        if (i + 1 >= n_chunks) break;
+        step(i + 1, stage1, stage0);
+        if (i + 2 >= n_chunks) break;
+        step(i + 2, stage2, stage1);
+      }
+    }
+#else
+    // one pipeline step: start chunk i+1's DMA into the other stage (last read by chunk i-1,
+    // finished by every wave before the previous barrier), compute chunk i, wait, barrier
+    auto step = [&](int i, const uint8_t* cur, uint8_t* ahead) {
+      const bool more = i + 1 < n_chunks;
+      if (more) dma(i + 1, ahead);
+      compute(i, cur);
+      LBSA_WAIT_VM_LGKM(0, 0);
+      __builtin_amdgcn_s_barrier();
+    };
+
+    if (n_chunks > 0) {
+      dma(0, stage0);
+      LBSA_WAIT_VM_LGKM(0, 0);
+      __builtin_amdgcn_s_barrier();
+      for (int i = 0; i < n_chunks; i += 2) {
+        step(i, stage0, stage1);
+        if (i + 1 >= n_chunks) break;
+        step(i + 1, stage1, stage0);
+      }
+    }
+#endif
+
+    // write the partials of this wave's rows (rows past the chunk's end are not stored)
 #pragma unroll
     for (int cb = 0; cb < kColBlocks; ++cb) {
-      const float to_true = (m_true[cb] == -INFINITY) ? 0.f : fast_exp2(m_ref[cb] - m_true[cb]);
+      const float to_true = (m_true[cb] == -INFINITY) ? 0.f : fast_exp2((m_ref[cb] - m_true[cb]) * c);
       float l = lsum[cb] * to_true;
       l += xor_lane(l, 16);
       l += xor_lane(l, 32);
@@ -286,7 +434,7 @@ __global__ __launch_bounds__(256) void splitkv_prefill_kernel(PrefillParams p) {
       if (unit_row0 + row_in_unit < q_len) {
         const size_t slot = ((size_t)s * kQTile + row_in_unit) * p.Hq + h;
         if (grp == 0) {
-          p.part_m[slot] = (m_true[cb] == -INFINITY) ? -INFINITY : m_true[cb] * kLn2;
+          p.part_m[slot] = (m_true[cb] == -INFINITY) ? -INFINITY : m_true[cb] * c * kLn2;
           p.part_l[slot] = l;
         }
         float* dst = p.part_o + slot * kPD + 4 * grp;

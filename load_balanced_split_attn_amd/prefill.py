@@ -17,7 +17,7 @@ Q_TILE = 128
 
 
 class PrefillStep:
-    def __init__(self, q_lens: Sequence[int], kv_lens: Sequence[int], device, num_workers: int = 8,
+    def __init__(self, q_lens: Sequence[int], kv_lens: Sequence[int], device, num_workers: int = 32,
                  kv_tile: int = 512, causal: bool = True, num_q_heads: int = 64, head_dim: int = 128):
         device = torch.device(device)
         self.q_lens_host = [int(x) for x in q_lens]
