@@ -259,8 +259,10 @@ def main() -> int:
                     help="run one plain 1 GiB copy first (reference for the HBM byte counters)")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill report")
-    ap.add_argument("--prefill-workers", default="32,64")
+    ap.add_argument("--prefill-workers", default="64,128")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the chunked-prefill report (profiling runs); prints its JSON")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -280,6 +282,10 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.calibration_copy:
         calibration_copy(dev)
+    if args.only_prefill:
+        print(json.dumps(bench_prefill(dev, [int(x) for x in args.prefill_workers.split(",")],
+                                       args.prefill_steps, 1)), flush=True)
+        return 0
     wl = WL.BY_NAME[args.workload]()
     scale = 1.0 / math.sqrt(wl.head_dim)
     page = 64

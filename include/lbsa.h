@@ -171,16 +171,20 @@ int attn_splitkv(const void* q, const void* k_cache, const void* v_cache,
  * written).  With causal != 0 row j sees keys [0, kv_lens[b] - q_lens[b] + j]; otherwise all keys.
  *   q_lens, q_start, kv_lens  device int32[B]
  *   map           device copy of the attn_plan_prefill map (same q_tile, kv_tile % 64 == 0)
+ *   flags         0: P.V in fp16 (V converted exactly from bf16 while staged, P rounded to 11
+ *                 significant bits; |v| above 65504 saturates); LBSA_PREFILL_EXACT_PV: bf16 V with
+ *                 P as bf16 hi + lo parts (~16 bits, no range limit, ~15% slower)
  * Supported: head_dim 128, Hq/Hkv = 8, bf16, q_tile 128, page_size a multiple of 64.
- * Errors: LBSA_ERR_INVALID, LBSA_ERR_UNSUPPORTED, LBSA_ERR_HIP.
+ * Errors: LBSA_ERR_INVALID (also unknown flag bits), LBSA_ERR_UNSUPPORTED, LBSA_ERR_HIP.
  */
+#define LBSA_PREFILL_EXACT_PV 1
 int attn_splitkv_prefill(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
                          const int32_t* q_lens, const int32_t* q_start, const int32_t* kv_lens,
                          const int32_t* map, int32_t num_workers, int32_t num_segments, int32_t B,
                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                          int32_t q_tile, int32_t causal, float softmax_scale,
-                         float* part_m, float* part_l, float* part_o, void* stream);
+                         float* part_m, float* part_l, float* part_o, int32_t flags, void* stream);
 
 /*
  * Combine kernel ([P3] §3.1 方案 step 5): for every unit and query head merges the

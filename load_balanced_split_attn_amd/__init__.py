@@ -43,7 +43,7 @@ _SIGNATURES = {
     "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
     "attn_splitkv_prefill": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
                                             _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
-                                            _c_i32, _c_i32, ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp]),
+                                            _c_i32, _c_i32, ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp]),
 }
 
 _lib = None
@@ -195,9 +195,10 @@ def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                          q_lens: torch.Tensor, q_start: torch.Tensor, kv_lens: torch.Tensor, map_dev: torch.Tensor,
                          num_workers: int, num_segments: int, softmax_scale: float, part_m: torch.Tensor,
                          part_l: torch.Tensor, part_o: torch.Tensor, causal: bool = True, q_tile: int = 128,
-                         stream=None) -> None:
+                         exact_pv: bool = False, stream=None) -> None:
     """Launch the chunked-prefill split-KV kernel.  q [rows, Hq, D]; caches as in attn_splitkv;
-    q_lens/q_start/kv_lens [B]; part_m/l [S, q_tile, Hq]; part_o [S, q_tile, Hq, D]."""
+    q_lens/q_start/kv_lens [B]; part_m/l [S, q_tile, Hq]; part_o [S, q_tile, Hq, D].
+    exact_pv: bf16 P.V with hi/lo P (no fp16 range limit on V) instead of the fp16 P.V path."""
     dev = q.device
     _need(q, torch.bfloat16, "q", dev)
     _need(k_cache, torch.bfloat16, "k_cache", dev)
@@ -220,7 +221,7 @@ def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                                     block_table.shape[1], P, _dptr(q_lens), _dptr(q_start), _dptr(kv_lens),
                                     _dptr(map_dev), num_workers, num_segments, B, Hq, Hkv, D, page, q_tile,
                                     int(bool(causal)), float(softmax_scale), _dptr(part_m), _dptr(part_l),
-                                    _dptr(part_o), _stream(stream))
+                                    _dptr(part_o), 1 if exact_pv else 0, _stream(stream))
     _check(st, "attn_splitkv_prefill")
 
 

@@ -17,8 +17,8 @@
 // softmax VALU work overlaps another wave's MFMAs.
 // Per wave, with the query rows as the MFMA columns:
 //   S^T (keys x rows) = K . Q^T       v_mfma_f32_16x16x32_bf16, Q^T fragments held in VGPRs
-//   O^T (dims x rows) += V^T . P^T    v_mfma_f32_16x16x32_bf16 with P as bf16 hi + lo parts
-//                                      (or fp16 operands, see LBSA_PREFILL_PV_F16)
+//   O^T (dims x rows) += V^T . P^T    fp16 operands (V converted in LDS), or bf16 with P as
+//                                      hi + lo parts (see "P.V precision" below)
 // so every lane holds whole columns: the softmax max/sum of a row needs only in-lane reductions and
 // two lane exchanges, exactly as in the decode kernel.  Key tiles are interleaved in 4-key groups so
 // that a lane's 8 scores per 32 keys are the 8 consecutive keys it supplies to the PV product.
@@ -56,14 +56,16 @@ constexpr int kStage = kKBytes + kVBytes;  // one pipeline stage: a 64-key chunk
 constexpr float kPRescaleSlack = 8.0f;   // log2 units
 
 // Tuning knobs (compile-time):
-//   LBSA_PREFILL_PV_F16  1: P.V on v_mfma_f32_16x16x32_f16 - each V fragment is converted to fp16
-//                        after it is read from LDS (exact for |v| in the fp16 normal range; larger
-//                        magnitudes saturate at 65504) and P is rounded to fp16 (11 significant
-//                        bits); 0: bf16 V with P split into bf16 hi + lo parts (two MFMAs)
+//
+// P.V precision (runtime, template parameter PV):
+//   kPvF16   (default) each chunk's V^T is converted to fp16 once, in LDS, by the workgroup (one
+//            extra barrier per chunk) and P is rounded to fp16 (11 significant bits); the products
+//            run on v_mfma_f32_16x16x32_f16.  The bf16 -> fp16 conversion is exact for |v| in the
+//            fp16 normal range; larger magnitudes saturate at 65504.
+//   kPvExact bf16 V with P split into bf16 hi + lo parts (two MFMAs, ~16 significant bits), no
+//            range limit.
 //   LBSA_PREFILL_WPE     waves per SIMD the register budget is fitted to (1 or 2)
-#ifndef LBSA_PREFILL_PV_F16
-#define LBSA_PREFILL_PV_F16 0
-#endif
+
 #ifndef LBSA_PREFILL_WPE
 #define LBSA_PREFILL_WPE 2
 #endif
@@ -73,6 +75,9 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 #define LBSA_PREFILL_STAGES 2
 #endif
 
+
+constexpr int kPvExact = 0;
+constexpr int kPvF16 = 2;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -118,6 +123,7 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;
 #define LBSA_WAIT_VM_LGKM(vm, lgkm) \
   __builtin_amdgcn_s_waitcnt(((vm) & 0xF) | (((vm) >> 4) << 14) | (0x7 << 4) | (((lgkm) & 0xF) << 8))
 
+template <int PV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LBSA_PREFILL_WPE, LBSA_PREFILL_WPE)))
 void splitkv_prefill_kernel(PrefillParams p) {
   // three pipeline stages, separate objects so the compiler can tell their DMA writes apart
@@ -161,6 +167,16 @@ void splitkv_prefill_kernel(PrefillParams p) {
 
   // DMA layout: wave v fills LDS granules 64*(4v + t) + lane, t = 0..3, of the K half and of the
   // V^T half of a stage; the lane fetches whichever global granule belongs in that swizzled slot
+  // LDS fragment addresses.  K: key 32kb + 4j + key0 at granule 4ks + grp; the swizzle of those keys
+  // is swz(key0) for every (kb, j), so each read is k_base[ks] + (32kb + 4j) * 256.  V^T: dim
+  // 16n + r at granule 4kb + grp; the swizzle depends on r only, so each read is v_base[kb] + 2048n.
+  const int key0 = 8 * (r >> 2) + (r & 3);
+  int k_base[4], v_base[2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) k_base[ks] = k_slot(key0, 4 * ks + grp);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) v_base[kb] = v_slot(r, 4 * kb + grp);
+
   // byte offsets inside a (page, KV head) block; the chunk's offset in the page goes in the scalar
   // offset, so these registers stay unchanged while earlier loads that read them are in flight
   int k_src[4], v_src[4];
@@ -248,10 +264,9 @@ void splitkv_prefill_kernel(PrefillParams p) {
       auto qk = [&](int kb, float (&scb)[kColBlocks][8]) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int key = 32 * kb + 8 * (r >> 2) + 4 * j + (r & 3);
           u32x4 kf[4];
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) kf[ks] = lds_ld16(st, k_slot(key, 4 * ks + grp));
+          for (int ks = 0; ks < 4; ++ks) kf[ks] = lds_ld16(st, k_base[ks] + (32 * kb + 4 * j) * kKRow);
 #pragma unroll
           for (int cb = 0; cb < kColBlocks; ++cb) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -316,7 +331,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
         // V^T fragments of this 32-key block: dim 16n + r, keys kbase + 8grp .. +7
         u32x4 vf[8];
 #pragma unroll
-        for (int n = 0; n < 8; ++n) vf[n] = lds_ld16(st, v_slot(16 * n + r, 4 * kb + grp));
+        for (int n = 0; n < 8; ++n) vf[n] = lds_ld16(st, v_base[kb] + 16 * n * kVRow);
         if (edge) {
           // keys outside [kv_begin, kv_end) may hold any bits; p = 0 does not cancel a NaN
 #pragma unroll
@@ -328,12 +343,6 @@ void splitkv_prefill_kernel(PrefillParams p) {
             for (int n = 0; n < 8; ++n) vf[n][e] &= keep;
           }
         }
-#if LBSA_PREFILL_PV_F16
-#pragma unroll
-        for (int n = 0; n < 8; ++n)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vf[n][e] = bf16x2_to_f16x2(vf[n][e]);
-#endif
 #pragma unroll
         for (int cb = 0; cb < kColBlocks; ++cb) {
           float ps[8];
@@ -342,13 +351,13 @@ void splitkv_prefill_kernel(PrefillParams p) {
             ps[e] = fast_exp2(fmaf(sc[kb][cb][e], c, neg_mc[cb]));
             lsum[cb] += ps[e];
           }
-#if LBSA_PREFILL_PV_F16
+          if constexpr (PV == kPvF16) {
           u32x4 pf;
 #pragma unroll
           for (int e = 0; e < 4; ++e) pf[e] = pack_f16(ps[2 * e], ps[2 * e + 1]);
 #pragma unroll
           for (int n = 0; n < 8; ++n) o[cb][n] = mfma16x16x32_f16(vf[n], pf, o[cb][n]);
-#else
+          } else {
           // P split into bf16 hi + lo parts: two MFMAs keep ~16 significant bits of each probability
           u32x4 phi, plo;
 #pragma unroll
@@ -362,16 +371,17 @@ void splitkv_prefill_kernel(PrefillParams p) {
             o[cb][n] = mfma16x16x32(vf[n], phi, o[cb][n]);
             o[cb][n] = mfma16x16x32(vf[n], plo, o[cb][n]);
           }
-#endif
+          }
         }
       }
     };
 
 #if LBSA_PREFILL_STAGES == 3
+    static_assert(PV == kPvExact || LBSA_PREFILL_STAGES == 2, "in-LDS V conversion needs the two-stage pipeline");
     // one pipeline step: start chunk i+2's DMA, compute chunk i, then make chunk i+1 visible to
     // every wave (own DMA complete -> barrier).  Stage i+2 was last read by chunk i-1, which every
     // wave finished before the previous step's barrier.
-    auto step = [&](int i, const uint8_t* cur, uint8_t* ahead) {
+    auto step = [&](int i, uint8_t* cur, uint8_t* ahead) {
       const bool more = i + 2 < n_chunks;
       if (more) dma(i + 2, ahead);
       compute(i, cur);
@@ -403,8 +413,21 @@ void splitkv_prefill_kernel(PrefillParams p) {
 #else
     // one pipeline step: start chunk i+1's DMA into the other stage (last read by chunk i-1,
     // finished by every wave before the previous barrier), compute chunk i, wait, barrier
-    auto step = [&](int i, const uint8_t* cur, uint8_t* ahead) {
+    auto step = [&](int i, uint8_t* cur, uint8_t* ahead) {
       const bool more = i + 1 < n_chunks;
+      if constexpr (PV == kPvF16) {
+        // V^T of chunk i to fp16, in place: each thread converts the granules its own loads wrote
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          u32x4* gp = reinterpret_cast<u32x4*>(cur + kKBytes + 1024 * (4 * wave + t) + 16 * lane);
+          u32x4 x = *gp;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
+          *gp = x;
+        }
+        LBSA_WAIT_VM_LGKM(0, 0);
+        __builtin_amdgcn_s_barrier();
+      }
       if (more) dma(i + 1, ahead);
       compute(i, cur);
       LBSA_WAIT_VM_LGKM(0, 0);
@@ -455,7 +478,7 @@ extern "C" int attn_splitkv_prefill(const void* q, const void* k_cache, const vo
                                     const int32_t* map, int32_t num_workers, int32_t num_segments, int32_t B,
                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                                     int32_t q_tile, int32_t causal, float softmax_scale, float* part_m,
-                                    float* part_l, float* part_o, void* stream) {
+                                    float* part_l, float* part_o, int32_t flags, void* stream) {
   if (num_workers < 1 || num_segments < 0 || B < 0 || num_kv_heads < 1 || num_pages < 1 ||
       block_table_stride < 0 || page_size < 1)
     return LBSA_ERR_INVALID;
@@ -467,6 +490,7 @@ extern "C" int attn_splitkv_prefill(const void* q, const void* k_cache, const vo
     return LBSA_ERR_INVALID;
   if (head_dim != kPD || num_q_heads != 8 * num_kv_heads || page_size % kPChunk != 0 || q_tile != kQTile)
     return LBSA_ERR_UNSUPPORTED;
+  if (flags & ~LBSA_PREFILL_EXACT_PV) return LBSA_ERR_INVALID;
   PrefillParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k_cache);
@@ -493,7 +517,11 @@ extern "C" int attn_splitkv_prefill(const void* q, const void* k_cache, const vo
   const int64_t pairs = (int64_t)num_workers * num_kv_heads;
   const int64_t grid = ((pairs + 7) / 8) * 8 * 8;
   if (grid > INT32_MAX) return LBSA_ERR_INVALID;
-  hipLaunchKernelGGL(splitkv_prefill_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     p);
+  if (flags & LBSA_PREFILL_EXACT_PV)
+    hipLaunchKernelGGL(splitkv_prefill_kernel<kPvExact>, dim3((unsigned)grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), p);
+  else
+    hipLaunchKernelGGL(splitkv_prefill_kernel<kPvF16>, dim3((unsigned)grid), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), p);
   return hipGetLastError() == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;
 }

@@ -17,12 +17,14 @@ Q_TILE = 128
 
 
 class PrefillStep:
-    def __init__(self, q_lens: Sequence[int], kv_lens: Sequence[int], device, num_workers: int = 32,
-                 kv_tile: int = 512, causal: bool = True, num_q_heads: int = 64, head_dim: int = 128):
+    def __init__(self, q_lens: Sequence[int], kv_lens: Sequence[int], device, num_workers: int = 128,
+                 kv_tile: int = 512, causal: bool = True, num_q_heads: int = 64, head_dim: int = 128,
+                 exact_pv: bool = False):
         device = torch.device(device)
         self.q_lens_host = [int(x) for x in q_lens]
         self.kv_lens_host = [int(x) for x in kv_lens]
         self.causal = bool(causal)
+        self.exact_pv = bool(exact_pv)
         self.map_host = attn_plan_prefill(self.q_lens_host, self.kv_lens_host, num_workers, Q_TILE, kv_tile,
                                           self.causal)
         hdr = map_header(self.map_host)
@@ -44,7 +46,7 @@ class PrefillStep:
     def splitkv(self, q, k_cache, v_cache, block_table, scale: float, stream=None) -> None:
         attn_splitkv_prefill(q, k_cache, v_cache, block_table, self.q_lens, self.q_start, self.kv_lens, self.map,
                              self.W, self.S, scale, self.part_m, self.part_l, self.part_o, causal=self.causal,
-                             stream=stream)
+                             exact_pv=self.exact_pv, stream=stream)
 
     def combine(self, out, stream=None) -> None:
         attn_combine(self.part_m, self.part_l, self.part_o, self.map, self.U, out, rows_per_unit=Q_TILE,

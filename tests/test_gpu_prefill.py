@@ -13,10 +13,11 @@ from oracle.plan import ref_plan_prefill
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, W, causal=True, inputs=None, poison=False, kv_tile=512):
+def _run(wl, W, causal=True, inputs=None, poison=False, kv_tile=512, exact_pv=False):
     from load_balanced_split_attn_amd.prefill import PrefillStep
     q, kc, vc, bt = inputs if inputs is not None else prefill_inputs(wl, pad_value=float("nan"))
-    step = PrefillStep(wl.q_lens, wl.kv_lens, q.device, num_workers=W, causal=causal, kv_tile=kv_tile)
+    step = PrefillStep(wl.q_lens, wl.kv_lens, q.device, num_workers=W, causal=causal, kv_tile=kv_tile,
+                       exact_pv=exact_pv)
     assert np.array_equal(step.map_host, ref_plan_prefill(wl.q_lens, wl.kv_lens, W, 128, kv_tile, causal))
     if poison:
         for t in (step.part_m, step.part_l, step.part_o):
@@ -36,13 +37,14 @@ def _check_all(wl, got, causal=True):
                      f"{wl.name} request {b} (q_len={wl.q_lens[b]}, kv_len={wl.kv_lens[b]}, causal={causal})")
 
 
+@pytest.mark.parametrize("exact_pv", [False, True])
 @pytest.mark.parametrize("seed,batch,max_prefix,max_chunk,W", [
     (0, 3, 1500, 300, 3), (1, 4, 700, 200, 1), (2, 2, 3000, 260, 8), (3, 5, 100, 140, 16),
 ])
-def test_random_prefill(seed, batch, max_prefix, max_chunk, W):
+def test_random_prefill(seed, batch, max_prefix, max_chunk, W, exact_pv):
     wl = WL.random_prefill(seed, batch, max_prefix, max_chunk)
-    note(f"prefill seed={seed} q_lens={wl.q_lens} kv_lens={wl.kv_lens} W={W}")
-    got, _ = _run(wl, W, causal=True, poison=True)
+    note(f"prefill seed={seed} q_lens={wl.q_lens} kv_lens={wl.kv_lens} W={W} exact_pv={exact_pv}")
+    got, _ = _run(wl, W, causal=True, poison=True, exact_pv=exact_pv)
     _check_all(wl, got, causal=True)
 
 
@@ -50,6 +52,8 @@ def test_non_causal_and_small_tiles():
     wl = WL.random_prefill(7, 3, 900, 200)
     note(f"non-causal q_lens={wl.q_lens} kv_lens={wl.kv_lens}")
     got, _ = _run(wl, 5, causal=False)
+    _check_all(wl, got, causal=False)
+    got, _ = _run(wl, 5, causal=False, exact_pv=True)
     _check_all(wl, got, causal=False)
     got, _ = _run(wl, 5, causal=True, kv_tile=64)
     _check_all(wl, got, causal=True)
@@ -62,6 +66,29 @@ def test_no_prefix_is_textbook_causal():
     _check_all(wl, got)
 
 
+def test_exact_pv_agrees_with_fp16_pv():
+    """Both P.V precisions give the same attention to well inside the tolerance."""
+    wl = WL.random_prefill(10, 3, 2500, 300)
+    inputs = prefill_inputs(wl)
+    a, _ = _run(wl, 6, inputs=inputs)
+    b, _ = _run(wl, 6, inputs=inputs, exact_pv=True)
+    assert errors(a.astype(np.float64), b.astype(np.float64))[1] <= 1e-3
+
+
+def test_flags_rejected():
+    import load_balanced_split_attn_amd as lb
+    wl = WL.random_prefill(11, 1, 100, 50)
+    q, kc, vc, bt = prefill_inputs(wl)
+    from load_balanced_split_attn_amd.prefill import PrefillStep
+    st = PrefillStep(wl.q_lens, wl.kv_lens, q.device, num_workers=2)
+    lib = lb.lib()
+    rc = lib.attn_splitkv_prefill(lb._dptr(q), lb._dptr(kc), lb._dptr(vc), lb._dptr(bt), bt.shape[1], kc.shape[0],
+                                  lb._dptr(st.q_lens), lb._dptr(st.q_start), lb._dptr(st.kv_lens), lb._dptr(st.map),
+                                  st.W, st.S, 1, 64, 8, 128, 64, 128, 1, SCALE, lb._dptr(st.part_m),
+                                  lb._dptr(st.part_l), lb._dptr(st.part_o), 4, None)
+    assert rc == -1
+
+
 def test_single_row_matches_decode():
     """A one-row chunk is a decode query at the last position."""
     import load_balanced_split_attn_amd as lb
@@ -70,11 +97,14 @@ def test_single_row_matches_decode():
     wl.q_lens = [1] * wl.batch
     wl.kv_lens = [max(1, L) for L in wl.kv_lens]
     q, kc, vc, bt = prefill_inputs(wl)
-    got, _ = _run(wl, 3, inputs=(q, kc, vc, bt))
     step = DecodeStep(wl.kv_lens, q.device, num_workers=3)
     dec = step(q, kc, vc, bt, scale=SCALE)
     torch.cuda.synchronize()
-    assert errors(got.astype(np.float64), dec.cpu().numpy().astype(np.float64))[1] <= 1e-5
+    dec = dec.cpu().numpy().astype(np.float64)
+    exact, _ = _run(wl, 3, inputs=(q, kc, vc, bt), exact_pv=True)
+    assert errors(exact.astype(np.float64), dec)[1] <= 1e-5          # same arithmetic up to fp32 order
+    fast, _ = _run(wl, 3, inputs=(q, kc, vc, bt))
+    assert errors(fast.astype(np.float64), dec)[1] <= 1e-3           # P rounded to fp16
 
 
 def test_full_size_prefill_sampled():
@@ -82,7 +112,7 @@ def test_full_size_prefill_sampled():
     bench launch configuration; sampled rows of three requests against the oracle."""
     wl = WL.prefill()
     note(f"full-size prefill kv_lens={wl.kv_lens}")
-    W = 8
+    W = 64
     got, step = _run(wl, W, poison=True)
     assert np.all(np.isfinite(got))
     starts = q_starts(wl)
