@@ -196,13 +196,16 @@ int attn_splitkv_prefill(const void* q, const void* k_cache, const void* v_cache
  *   q_lens, q_start  device int32[B] for prefill (row count and first output row of
  *                 request b); NULL for decode, where unit b writes output row b
  *   out_dtype     0 = fp32, 1 = bf16 (round to nearest even)
+ *   max_splits    largest slot count of any unit (from the host map), or 0 if unknown; above 16 a
+ *                 unit's slots are spread over four waves (a launch-shape hint, any value >= 0 is
+ *                 correct)
  * Errors: LBSA_ERR_INVALID, LBSA_ERR_UNSUPPORTED (head_dim != 128), LBSA_ERR_HIP.
  */
 int attn_combine(const float* part_m, const float* part_l, const float* part_o,
                  const int32_t* map, int32_t num_units, int32_t rows_per_unit,
                  const int32_t* q_lens, const int32_t* q_start,
                  int32_t num_q_heads, int32_t head_dim,
-                 void* out, int32_t out_dtype, void* stream);
+                 void* out, int32_t out_dtype, int32_t max_splits, void* stream);
 
 #ifdef __cplusplus
 }

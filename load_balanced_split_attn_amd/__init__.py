@@ -39,7 +39,7 @@ _SIGNATURES = {
                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                     ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "attn_combine": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
-                                    _c_i32, _c_i32, _c_vp, _c_i32, _c_vp]),
+                                    _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, _c_vp]),
     "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
     "attn_splitkv_prefill": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
                                             _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -156,6 +156,14 @@ def map_header(map_host: np.ndarray) -> dict:
     return dict(zip(keys, (int(x) for x in map_host[:8])))
 
 
+def max_splits_of(map_host: np.ndarray) -> int:
+    """Largest number of partial slots of one unit in a host work map."""
+    hdr = map_header(map_host)
+    o = 8 + hdr["W"] + 1
+    ptr = np.asarray(map_host[o:o + hdr["U"] + 1], dtype=np.int64)
+    return int(np.max(np.diff(ptr))) if hdr["U"] > 0 else 0
+
+
 def attn_splitkv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                  seq_lens: torch.Tensor, map_dev: torch.Tensor, num_workers: int, num_segments: int,
                  head_groups: int, softmax_scale: float, part_m: torch.Tensor, part_l: torch.Tensor,
@@ -227,8 +235,9 @@ def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
 
 def attn_combine(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor, map_dev: torch.Tensor,
                  num_units: int, out: torch.Tensor, rows_per_unit: int = 1, q_lens: Optional[torch.Tensor] = None,
-                 q_start: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Merge partials into out [rows, Hq, D] (fp32 or bf16)."""
+                 q_start: Optional[torch.Tensor] = None, max_splits: int = 0, stream=None) -> None:
+    """Merge partials into out [rows, Hq, D] (fp32 or bf16).  max_splits: largest slot count of a unit
+    (a launch-shape hint; see max_splits_of)."""
     dev = out.device
     for name, t in (("part_m", part_m), ("part_l", part_l), ("part_o", part_o)):
         _need(t, torch.float32, name, dev)
@@ -241,7 +250,7 @@ def attn_combine(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tenso
     Hq, D = out.shape[-2], out.shape[-1]
     st = lib().attn_combine(_dptr(part_m), _dptr(part_l), _dptr(part_o), _dptr(map_dev), num_units, rows_per_unit,
                             _dptr(q_lens), _dptr(q_start), Hq, D, _dptr(out),
-                            1 if out.dtype == torch.bfloat16 else 0, _stream(stream))
+                            1 if out.dtype == torch.bfloat16 else 0, int(max_splits), _stream(stream))
     _check(st, "attn_combine")
 
 

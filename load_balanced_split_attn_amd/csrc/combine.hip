@@ -35,19 +35,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// One wave per (unit, row, query head).  Pass 1 spreads the unit's slots over the lanes for the
-// maximum and the weighted sum of l; pass 2 gives each lane two output dims and walks the slots
-// with independent loads (unrolled) so the short, latency-bound loop keeps several in flight.
+// WPI waves per (unit, row, query head) item.  Pass 1 spreads the unit's slots over the lanes for
+// the maximum and the weighted sum of l (every wave of the item does it); pass 2 gives each lane two
+// output dims and walks the slots s = wave, wave + WPI, ... with independent loads (unrolled), so
+// the short, latency-bound loop keeps several in flight; with WPI > 1 the waves' sums meet in LDS.
+// WPI = 1 serves units with a few slots (4 items per workgroup), WPI = 4 units split over many
+// workers (one item per workgroup).
+template <int WPI>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
+  __shared__ float2 red[WPI > 1 ? WPI * 64 : 1];
   const int lane = threadIdx.x & 63;
-  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int64_t item = (int64_t)blockIdx.x * (4 / WPI) + (WPI == 1 ? wave : 0);
+  const int sub = WPI == 1 ? 0 : wave;
   const int64_t total = (int64_t)p.U * p.R * p.Hq;
-  if (gw >= total) return;
+  if (item >= total) return;
   const int W = p.map[2];
   const int32_t* unit_ptr = p.map + 8 + (W + 1);
   const int32_t* units = unit_ptr + (p.U + 1);
-  const int h = (int)(gw % p.Hq);
-  const int64_t rest = gw / p.Hq;
+  const int h = (int)(item % p.Hq);
+  const int64_t rest = item / p.Hq;
   const int r = (int)(rest % p.R);
   const int u = (int)(rest / p.R);
   const int b = units[2 * u];
@@ -78,14 +85,14 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 
   float a0 = 0.f, a1 = 0.f;
   if (L > 0.f) {
-    int i = 0;
-    for (; i + 4 <= n; i += 4) {
+    int i = sub;
+    for (; i + 3 * WPI < n; i += 4 * WPI) {
       float m[4];
       float2 o[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        m[j] = p.part_m[slot(i + j)];
-        o[j] = *reinterpret_cast<const float2*>(p.part_o + slot(i + j) * 128 + 2 * lane);
+        m[j] = p.part_m[slot(i + j * WPI)];
+        o[j] = *reinterpret_cast<const float2*>(p.part_o + slot(i + j * WPI) * 128 + 2 * lane);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -94,13 +101,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
         a1 += w * o[j].y;
       }
     }
-    for (; i < n; ++i) {
+    for (; i < n; i += WPI) {
       const float m = p.part_m[slot(i)];
       const float2 o = *reinterpret_cast<const float2*>(p.part_o + slot(i) * 128 + 2 * lane);
       const float w = (m == -INFINITY) ? 0.f : fast_exp2((m - M) * kLog2e);
       a0 += w * o.x;
       a1 += w * o.y;
     }
+  }
+  if constexpr (WPI > 1) {
+    red[wave * 64 + lane] = make_float2(a0, a1);
+    __syncthreads();
+    if (wave != 0) return;
+    a0 = 0.f;
+    a1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPI; ++w) {
+      a0 += red[w * 64 + lane].x;
+      a1 += red[w * 64 + lane].y;
+    }
+  }
+  if (L > 0.f) {
     const float inv = 1.f / L;
     a0 *= inv;
     a1 *= inv;
@@ -120,8 +141,10 @@ using namespace lbsa;
 extern "C" int attn_combine(const float* part_m, const float* part_l, const float* part_o,
                             const int32_t* map, int32_t num_units, int32_t rows_per_unit,
                             const int32_t* q_lens, const int32_t* q_start, int32_t num_q_heads,
-                            int32_t head_dim, void* out, int32_t out_dtype, void* stream) {
-  if (num_units < 0 || rows_per_unit < 1 || num_q_heads < 1 || !map || !out) return LBSA_ERR_INVALID;
+                            int32_t head_dim, void* out, int32_t out_dtype, int32_t max_splits,
+                            void* stream) {
+  if (num_units < 0 || rows_per_unit < 1 || num_q_heads < 1 || !map || !out || max_splits < 0)
+    return LBSA_ERR_INVALID;
   if ((q_lens == nullptr) != (q_start == nullptr)) return LBSA_ERR_INVALID;
   if (!q_lens && rows_per_unit != 1) return LBSA_ERR_INVALID;
   if (out_dtype != 0 && out_dtype != 1) return LBSA_ERR_INVALID;
@@ -131,10 +154,15 @@ extern "C" int attn_combine(const float* part_m, const float* part_l, const floa
   if (num_units == 0) return LBSA_OK;
   CombineParams p{part_m, part_l, part_o, map, q_lens, q_start, out, num_units, rows_per_unit,
                   num_q_heads, out_dtype};
-  const int64_t waves = (int64_t)num_units * rows_per_unit * num_q_heads;
-  const int64_t blocks = (waves + 3) / 4;
-  if (blocks > INT32_MAX) return LBSA_ERR_INVALID;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), p);
+  const int64_t items = (int64_t)num_units * rows_per_unit * num_q_heads;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (max_splits > 16) {
+    if (items > INT32_MAX) return LBSA_ERR_INVALID;
+    hipLaunchKernelGGL(combine_kernel<4>, dim3((unsigned)items), dim3(256), 0, st, p);
+  } else {
+    const int64_t blocks = (items + 3) / 4;
+    if (blocks > INT32_MAX) return LBSA_ERR_INVALID;
+    hipLaunchKernelGGL(combine_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  }
   return hipGetLastError() == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;
 }

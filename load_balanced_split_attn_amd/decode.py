@@ -13,7 +13,7 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import attn_combine, attn_plan, attn_plan_static, attn_query_workers, attn_splitkv, map_header
+from . import attn_combine, attn_plan, attn_plan_static, attn_query_workers, attn_splitkv, map_header, max_splits_of
 
 
 class DecodeStep:
@@ -30,6 +30,7 @@ class DecodeStep:
             self.map_host = attn_plan(self.seq_lens_host, num_workers, tile)
         hdr = map_header(self.map_host)
         self.W, self.S, self.U, self.T = hdr["W"], hdr["S"], hdr["U"], hdr["T"]
+        self.max_splits = max_splits_of(self.map_host)
         self.tile = tile
         self.head_groups = head_groups
         self.device = device
@@ -45,7 +46,8 @@ class DecodeStep:
                      scale, self.part_m, self.part_l, self.part_o, timing=timing, stream=stream)
 
     def combine(self, out, stream=None) -> None:
-        attn_combine(self.part_m, self.part_l, self.part_o, self.map, self.U, out, stream=stream)
+        attn_combine(self.part_m, self.part_l, self.part_o, self.map, self.U, out, max_splits=self.max_splits,
+                     stream=stream)
 
     def __call__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None, timing=None,

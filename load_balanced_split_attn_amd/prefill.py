@@ -11,7 +11,7 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import attn_combine, attn_plan_prefill, attn_splitkv_prefill, map_header
+from . import attn_combine, attn_plan_prefill, attn_splitkv_prefill, map_header, max_splits_of
 
 Q_TILE = 128
 
@@ -29,6 +29,7 @@ class PrefillStep:
                                           self.causal)
         hdr = map_header(self.map_host)
         self.W, self.S, self.U, self.T = hdr["W"], hdr["S"], hdr["U"], hdr["T"]
+        self.max_splits = max_splits_of(self.map_host)
         self.device = device
         self.map = torch.from_numpy(self.map_host).to(device)
         self.q_lens = torch.tensor(self.q_lens_host, dtype=torch.int32, device=device)
@@ -50,7 +51,7 @@ class PrefillStep:
 
     def combine(self, out, stream=None) -> None:
         attn_combine(self.part_m, self.part_l, self.part_o, self.map, self.U, out, rows_per_unit=Q_TILE,
-                     q_lens=self.q_lens, q_start=self.q_start, stream=stream)
+                     q_lens=self.q_lens, q_start=self.q_start, max_splits=self.max_splits, stream=stream)
 
     def __call__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

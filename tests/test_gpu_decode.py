@@ -107,6 +107,31 @@ def test_maps_agree_and_paging_invariance(lb):
     assert torch.equal(a, c)
 
 
+def test_combine_many_splits(lb):
+    """A long request cut over many workers: the four-waves-per-unit combine (max_splits > 16) and
+    the one-wave combine agree, and both match the oracle."""
+    wl = WL.random_decode(14, 3, 100, min_len=50)
+    wl.kv_lens[1] = 40000          # 79 tiles of 512 over 120 workers -> many one-tile splits
+    words = lb.attn_plan(wl.kv_lens, 120, 512)
+    assert lb.max_splits_of(words) > 16
+    inputs = decode_inputs(wl)
+    from load_balanced_split_attn_amd import map_header
+    hdr = map_header(words)
+    q = inputs[0]
+    mp = torch.from_numpy(words).to(q.device)
+    _, (pm, pl, po) = _run(lb, wl, words, inputs=inputs)
+    outs = []
+    for ms in (0, lb.max_splits_of(words)):
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device)
+        lb.attn_combine(pm, pl, po, mp, hdr["U"], out, max_splits=ms)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert errors(outs[0].astype(np.float64), outs[1].astype(np.float64))[1] <= 1e-6
+    ref = oracle_decode(wl)
+    for b in range(wl.batch):
+        assert_close(outs[1][b], ref[b], f"many-split request {b}")
+
+
 def test_bf16_output(lb):
     wl = WL.random_decode(12, 4, 2000, min_len=600)
     words = lb.attn_plan(wl.kv_lens, 16, 512)
