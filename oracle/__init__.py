@@ -13,6 +13,9 @@ Two parts:
 * ``oracle.attention`` - exact softmax attention in float64 (the plain
   definition), per-split partials (max, sum-exp, unnormalised output) and the
   combine that merges them.
+* ``oracle.fp8``       - the value of an element of an 8-bit (OCP E4M3) KV
+  cache with per-KV-head scales, and decode attention over such a cache
+  (dequantise, then ``oracle.attention``).
 
 Sources (the web pages this method is described on):
 
@@ -33,4 +36,4 @@ text); its pins are the worked example's tile and budget counts plus
 invariants that any contiguous equal-budget fill must satisfy.
 """
 
-from . import attention, plan  # noqa: F401
+from . import attention, fp8, plan  # noqa: F401

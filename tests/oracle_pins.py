@@ -274,3 +274,79 @@ def pin_budget_rule(ref_plan, parse_map, trials=300, seed=6):
         T = sum(-(-L // 512) for L in lens)
         base, rem = T // W, T % W
         assert got == [base + 1] * rem + [base] * (W - rem), (lens, W, got)
+
+
+# ------------------------------------------------------------------------------------------------
+# 8-bit (E4M3) KV cache.
+
+def _torch_e4m3_values():
+    """Every E4M3 code through torch's own float8_e4m3fn conversion (a library routine)."""
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def pin_e4m3_library(e4m3_table):
+    """All 256 codes agree with torch's float8_e4m3fn decoding, NaN codes included."""
+    got = np.asarray(e4m3_table(), dtype=np.float64)
+    exp = _torch_e4m3_values()
+    assert got.shape == (256,)
+    assert np.array_equal(np.isnan(got), np.isnan(exp))
+    fin = ~np.isnan(exp)
+    assert np.array_equal(got[fin], exp[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(exp[fin]))
+
+
+def pin_e4m3_closed_forms(e4m3_value):
+    """Values the OCP E4M3 definition fixes: one, the largest finite value, the smallest
+    subnormal and normal, signed zero, and the two NaN codes."""
+    fixed = {0x00: 0.0, 0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x7E: 448.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+             0x08: 2.0 ** -6, 0x30: 0.5, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+    for code, val in fixed.items():
+        assert e4m3_value(code) == val, (hex(code), e4m3_value(code), val)
+    assert math.copysign(1.0, e4m3_value(0x80)) == -1.0 and e4m3_value(0x80) == 0.0
+    assert math.isnan(e4m3_value(0x7F)) and math.isnan(e4m3_value(0xFF))
+    vals = [e4m3_value(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(vals, vals[1:])), "positive codes must increase"
+    for c in range(0x7F):
+        assert e4m3_value(c | 0x80) == -vals[c]
+
+
+def pin_fp8_decode_library(ref_decode_fp8):
+    """Decode over an FP8 cache equals torch's SDPA (float64) over torch-dequantised K and V."""
+    g = torch.Generator().manual_seed(11)
+    for (L, Hq, Hkv, D) in [(9, 8, 2, 16), (1, 4, 4, 8), (17, 8, 1, 32)]:
+        q = torch.randn(2, Hq, D, generator=g).to(torch.bfloat16).to(torch.float64)
+        kc = [torch.randint(0, 256, (L, Hkv, D), generator=g, dtype=torch.int32).to(torch.uint8) for _ in range(2)]
+        vc = [torch.randint(0, 256, (L, Hkv, D), generator=g, dtype=torch.int32).to(torch.uint8) for _ in range(2)]
+        for c in kc + vc:   # no NaN codes in a stored cache
+            c[(c & 0x7F) == 0x7F] = 0x3A
+        ks = (0.01 + torch.rand(Hkv, generator=g, dtype=torch.float64)).to(torch.float32).to(torch.float64)
+        vs = (0.01 + torch.rand(Hkv, generator=g, dtype=torch.float64)).to(torch.float32).to(torch.float64)
+        got = ref_decode_fp8(q.numpy(), [c.numpy() for c in kc], [c.numpy() for c in vc], ks.numpy(), vs.numpy(), 0.3)
+        per = Hq // Hkv
+        for b in range(2):
+            k = kc[b].view(torch.float8_e4m3fn).to(torch.float64) * ks[None, :, None]
+            v = vc[b].view(torch.float8_e4m3fn).to(torch.float64) * vs[None, :, None]
+            kk = k.repeat_interleave(per, dim=1).permute(1, 0, 2)
+            vv = v.repeat_interleave(per, dim=1).permute(1, 0, 2)
+            exp = torch.nn.functional.scaled_dot_product_attention(
+                q[b:b + 1].permute(1, 0, 2), kk, vv, scale=0.3).permute(1, 0, 2).numpy()[0]
+            assert np.allclose(got[b], exp, rtol=1e-12, atol=1e-12)
+
+
+def pin_fp8_scale_laws(ref_decode_fp8):
+    """Scaling every K scale by c equals scaling the softmax scale by c; scaling every V scale by c
+    scales the output by c; a single key returns its dequantised value row."""
+    rng = np.random.default_rng(12)
+    Hq, Hkv, D, L = 8, 2, 16, 11
+    q = rng.standard_normal((1, Hq, D))
+    kc = [rng.integers(0, 0x7F, (L, Hkv, D), dtype=np.uint8)]
+    vc = [rng.integers(0, 0x7F, (L, Hkv, D), dtype=np.uint8) | (rng.integers(0, 2, (L, Hkv, D), dtype=np.uint8) << 7)]
+    ks, vs = np.array([0.011, 0.023]), np.array([0.5, 0.125])
+    base = ref_decode_fp8(q, kc, vc, ks, vs, 0.2)
+    assert np.allclose(ref_decode_fp8(q, kc, vc, 3 * ks, vs, 0.2), ref_decode_fp8(q, kc, vc, ks, vs, 0.6),
+                       rtol=1e-12, atol=1e-14)
+    assert not np.allclose(ref_decode_fp8(q, kc, vc, 3 * ks, vs, 0.2), base, rtol=1e-6, atol=1e-9)
+    assert np.allclose(ref_decode_fp8(q, kc, vc, ks, 4 * vs, 0.2), 4 * base, rtol=1e-12, atol=1e-14)
+    one = ref_decode_fp8(q, [kc[0][:1]], [vc[0][:1]], ks, vs, 0.2)[0]
+    exp = _torch_e4m3_values()[vc[0][0]] * vs[:, None]            # [Hkv, D]
+    assert np.array_equal(one, np.repeat(exp, Hq // Hkv, axis=0))

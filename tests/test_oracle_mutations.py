@@ -48,6 +48,15 @@ def _plan_pins(m):
     ]
 
 
+def _fp8_pins(m):
+    return [
+        lambda: P.pin_e4m3_library(m.e4m3_table),
+        lambda: P.pin_e4m3_closed_forms(m.e4m3_value),
+        lambda: P.pin_fp8_decode_library(m.ref_decode_fp8),
+        lambda: P.pin_fp8_scale_laws(m.ref_decode_fp8),
+    ]
+
+
 def _caught(pins) -> bool:
     for pin in pins:
         try:
@@ -68,6 +77,18 @@ ATTENTION_MUTANTS = {
     "combine without max shift weights": ("w = np.where(np.isfinite(ms), np.exp(ms - np.where(has, M, 0.0)[None]), 0.0)",
                                           "w = np.where(np.isfinite(ms), 1.0, 0.0)"),
     "combine divides by split count": ("Lsum = (w * ls).sum(axis=0)", "Lsum = (w * ls).sum(axis=0) * 0 + len(parts)"),
+}
+
+FP8_MUTANTS = {
+    "exponent bias 8": ("E4M3_BIAS = 7", "E4M3_BIAS = 8"),
+    "subnormals given the implicit one": ("return sign * mant * 2.0 ** (1 - E4M3_BIAS - E4M3_MANT_BITS)",
+                                          "return sign * (1.0 + mant / 8.0) * 2.0 ** (1 - E4M3_BIAS)"),
+    "sign bit ignored": ("sign = -1.0 if code & 0x80 else 1.0", "sign = 1.0"),
+    "top code read as a number": ("if exp == 0xF and mant == 0x7:", "if False:"),
+    "mantissa over 16": ("(1.0 + mant / 8.0)", "(1.0 + mant / 16.0)"),
+    "values scaled with the key scale": ("v = dequantize_kv(v_codes[b], v_scale)", "v = dequantize_kv(v_codes[b], k_scale)"),
+    "keys scaled with the value scale": ("k = dequantize_kv(k_codes[b], k_scale)", "k = dequantize_kv(k_codes[b], v_scale)"),
+    "scale of the first head for all": ("vals * scale[None, :, None]", "vals * scale[0]"),
 }
 
 PLAN_MUTANTS = {
@@ -93,8 +114,16 @@ def test_plan_mutant_is_caught(name):
     assert _caught(_plan_pins(m)), f"no pin catches: {name}"
 
 
+@pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
+def test_fp8_mutant_is_caught(name):
+    old, new = FP8_MUTANTS[name]
+    m = _load_mutant("fp8", old, new, count=1)
+    assert _caught(_fp8_pins(m)), f"no pin catches: {name}"
+
+
 def test_unmutated_oracle_passes_all_pins():
     import oracle.attention as A
+    import oracle.fp8 as F
     import oracle.plan as Pl
-    for pin in _attention_pins(A) + _plan_pins(Pl):
+    for pin in _attention_pins(A) + _plan_pins(Pl) + _fp8_pins(F):
         pin()

@@ -16,9 +16,10 @@ in for it.
 Every value is drawn N(0, 1) in float32 from a seeded ``torch.Generator`` on the
 CPU and rounded to bfloat16 (round to nearest even); both sides then see the
 same bf16 values.  Seeds: ``seed_for(workload_id, stream, index)`` with streams
-0 = lengths / order, 1 = page permutation, 2 = Q, 3 = K, 4 = V; K and V are
-drawn per request so a long batch can be generated and checked one request at a
-time.
+0 = lengths / order, 1 = page permutation, 2 = Q, 3 = K, 4 = V, 5 = the per-head
+scales of an 8-bit cache; K and V are drawn per request so a long batch can be
+generated and checked one request at a time.  An 8-bit (E4M3) cache holds the
+same K and V draws, quantised per KV head (``Workload.kv_fp8``).
 """
 
 from __future__ import annotations
@@ -36,17 +37,30 @@ PAGE = 64
 TILE = 512
 Q_TILE = 128
 
-STREAM_LENGTHS, STREAM_PAGES, STREAM_Q, STREAM_K, STREAM_V = 0, 1, 2, 3, 4
+STREAM_LENGTHS, STREAM_PAGES, STREAM_Q, STREAM_K, STREAM_V, STREAM_SCALES = 0, 1, 2, 3, 4, 5
+E4M3_MAX = 448.0
 
 
 def seed_for(workload_id: int, stream: int, index: int = 0) -> int:
     return workload_id * 1_000_000 + stream * 10_000 + index
 
 
-def randn_bf16(shape, seed: int) -> torch.Tensor:
+def randn_f32(shape, seed: int) -> torch.Tensor:
     g = torch.Generator(device="cpu")
     g.manual_seed(seed)
-    return torch.randn(*shape, generator=g, dtype=torch.float32).to(torch.bfloat16)
+    return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+
+def randn_bf16(shape, seed: int) -> torch.Tensor:
+    return randn_f32(shape, seed).to(torch.bfloat16)
+
+
+def to_e4m3_codes(x: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
+    """Input recipe of an 8-bit cache (the producer's job, not the attention's): x / scale per KV
+    head (dim 1), clamped to the E4M3 range and rounded to nearest even by torch's float8_e4m3fn
+    conversion; returns the codes as uint8."""
+    y = (x / scale[None, :, None]).clamp(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
 @dataclass
@@ -80,6 +94,24 @@ class Workload:
         k = randn_bf16((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_K, b))
         v = randn_bf16((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_V, b))
         return k, v
+
+    def kv_scales(self) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Per-KV-head float32 scales of the 8-bit cache, K and V: 2^u with u ~ U[-6.5, -5.5], about
+        what an amax / 448 calibration gives for N(0, 1) values, and different for every head."""
+        g = torch.Generator(device="cpu")
+        g.manual_seed(seed_for(self.workload_id, STREAM_SCALES))
+        u = torch.rand(2, self.hkv, generator=g, dtype=torch.float32) - 6.5
+        s = torch.exp2(u)
+        return s[0].clone(), s[1].clone()
+
+    def kv_fp8(self, b: int) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Request b's keys and values as E4M3 codes [L_b, Hkv, D] uint8: the same N(0, 1) draws as
+        ``kv`` (before their bf16 rounding), quantised with ``kv_scales``."""
+        L = self.kv_lens[b]
+        ks, vs = self.kv_scales()
+        k = randn_f32((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_K, b))
+        v = randn_f32((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_V, b))
+        return to_e4m3_codes(k, ks), to_e4m3_codes(v, vs)
 
     def page_permutation(self, num_pages: int) -> torch.Tensor:
         """Physical page for each logical page (a seeded shuffle; identity when not paged)."""
