@@ -43,10 +43,12 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(wl, page: int) -> dict:
+def algorithmic_bytes(wl, page: int, kv_elem: int = 2) -> dict:
+    """Bytes the step must move: K and V (kv_elem bytes per element; an 8-bit cache adds its
+    per-head scales), Q, the fp32 output, the block table and the lengths."""
     tokens = sum(wl.kv_lens)
     pages = sum(-(-L // page) for L in wl.kv_lens)
-    kv = tokens * wl.hkv * wl.head_dim * 2 * 2
+    kv = tokens * wl.hkv * wl.head_dim * kv_elem * 2 + (2 * wl.hkv * 4 if kv_elem == 1 else 0)
     q = wl.batch * wl.hq * wl.head_dim * 2
     out = wl.batch * wl.hq * wl.head_dim * 4
     table = pages * 4
@@ -242,6 +244,56 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int) -> dict:
             "sweep": rows}
 
 
+def bench_fp8(dev, wl, args, bf16_us: float) -> dict:
+    """The same decode step over an 8-bit (E4M3) KV cache with per-head scales: the same map shape
+    and combine, half the KV bytes."""
+    import numpy as np
+    import torch
+
+    import load_balanced_split_attn_amd as lb
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    from load_balanced_split_attn_amd.paged import pack_paged
+    page = 64
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    q = wl.q().to(dev)
+    kc, vc, bt = pack_paged(wl.kv_fp8, wl.kv_lens, page, wl.hkv, wl.head_dim, wl.page_permutation, dev,
+                            dtype=torch.uint8)
+    ks, vs = (s.to(dev) for s in wl.kv_scales())
+    nb = algorithmic_bytes(wl, page, kv_elem=1)
+    copies = 1 if nb["kv"] >= 2e9 else min(8, int(math.ceil(2e9 / max(nb["kv"], 1))))
+    caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(copies - 1)]
+    workers = args.workers or (wl.workers if wl.workers else
+                               lb.attn_query_workers(0, args.head_groups, lb.KV_FP8_E4M3))
+    step = DecodeStep(wl.kv_lens, dev, num_workers=workers, tile=args.tile, head_groups=args.head_groups,
+                      kv_dtype=lb.KV_FP8_E4M3)
+    out = torch.empty((wl.batch, wl.hq, wl.head_dim), dtype=torch.float32, device=dev)
+
+    def split(i):
+        k_, v_ = caches[i % copies]
+        step.splitkv(q, k_, v_, bt, scale, kv_scales=(ks, vs))
+
+    r = time_steps(split, lambda i: step.combine(out), args.steps, args.warmup)
+    ms = r["total_ms"] / args.steps
+    split_ms = float(np.mean(r["split_ms"]))
+    achieved = nb["splitkv"] / (split_ms * 1e-3) / 1e9
+    timing = torch.zeros((step.W * args.head_groups, 4), dtype=torch.int64, device=dev)
+    step.splitkv(q, kc, vc, bt, scale, timing=timing, kv_scales=(ks, vs))
+    torch.cuda.synchronize()
+    log(f"fp8 cache: step {ms * 1e3:.1f} us, splitkv {split_ms * 1e3:.1f} us ({achieved:.0f} GB/s)")
+    return {"workload": DESCRIPTIONS[wl.name].replace("bf16, paged", "bf16 q, E4M3 KV with per-head fp32 scales, "
+                                                                     "paged"),
+            "algorithmic_bytes": nb["step"], "us_per_step": round(ms * 1e3, 2),
+            "value": round(nb["step"] / (ms * 1e-3) / 1e12, 4), "unit": "TB/s",
+            "speedup_vs_bf16_step": round(bf16_us / (ms * 1e3), 3),
+            "workers": step.W, "segments": step.S, "cache_copies": copies,
+            "roofline": {"bound": "hbm", "kernel": "splitkv_decode_kernel<KvFp8>", "achieved": round(achieved, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "traffic": recorded_traffic("splitkv_decode_kernel_fp8", wl.name),
+                         "bytes_per_launch": nb["splitkv"], "avg_launch_us": round(split_ms * 1e3, 2)},
+            "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 2),
+            "per_cu_busy": per_cu_busy(timing)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -263,6 +315,9 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the chunked-prefill report (profiling runs); prints its JSON")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit KV cache report")
+    ap.add_argument("--only-fp8", action="store_true",
+                    help="run only the 8-bit KV cache report on --workload (profiling runs); prints its JSON")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -287,6 +342,9 @@ def main() -> int:
                                        args.prefill_steps, 1)), flush=True)
         return 0
     wl = WL.BY_NAME[args.workload]()
+    if args.only_fp8:
+        print(json.dumps(bench_fp8(dev, wl, args, float("nan"))), flush=True)
+        return 0
     scale = 1.0 / math.sqrt(wl.head_dim)
     page = 64
     nbytes = algorithmic_bytes(wl, page)
@@ -399,6 +457,9 @@ def main() -> int:
             best = gbs if best is None else max(best, gbs)
         result["stream_read_ceiling"] = {"GB/s": round(best, 1), "buffer_GB": round(kc.numel() * 2 / 1e9, 2),
                                          "splitkv_frac_of_ceiling": round(achieved / best, 4)}
+
+    if not args.no_fp8:
+        result["fp8_kv"] = bench_fp8(dev, wl, args, ms_per_step * 1e3)
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(dev, [int(x) for x in args.prefill_workers.split(",")],

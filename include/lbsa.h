@@ -126,11 +126,22 @@ int attn_plan_prefill(const int32_t* q_lens, const int32_t* kv_lens, int32_t B,
                       int32_t* map, int32_t map_capacity, int32_t* map_words_out);
 
 /*
- * Workers that fill the device with one resident wave of decode workgroups:
- * CUs x (resident split-KV workgroups per CU) / head_groups, for the decode kernel
- * launched with head_groups workgroups per worker.  Cached per device.
+ * KV cache element types of the decode kernels.
+ *   LBSA_KV_BF16      bf16 k_cache / v_cache (attn_splitkv)
+ *   LBSA_KV_FP8_E4M3  8-bit OCP E4M3 codes with one fp32 scale per KV head for K and one for V
+ *                     (attn_splitkv_fp8)
  */
-int attn_query_workers(int device, int32_t head_groups, int32_t* num_workers_out);
+#define LBSA_KV_BF16 0
+#define LBSA_KV_FP8_E4M3 1
+
+/*
+ * Workers that fill the device with one resident wave of decode workgroups:
+ * CUs x (resident split-KV workgroups per CU) / head_groups, for the decode kernel of cache type
+ * kv_dtype (LBSA_KV_*) launched with head_groups workgroups per worker.  Cached per device and type.
+ * Errors: LBSA_ERR_INVALID (head_groups not a divisor of 8, unknown kv_dtype, device out of range),
+ * LBSA_ERR_HIP.
+ */
+int attn_query_workers(int device, int32_t head_groups, int32_t kv_dtype, int32_t* num_workers_out);
 
 /*
  * Split-KV decode kernel ([P3] §3.1 方案 step 4; [P4] §二.1): launches
@@ -158,6 +169,28 @@ int attn_splitkv(const void* q, const void* k_cache, const void* v_cache,
                  int32_t page_size, float softmax_scale,
                  float* part_m, float* part_l, float* part_o,
                  uint64_t* timing, void* stream);
+
+/*
+ * Split-KV decode over an 8-bit KV cache (the 8-bit cache of the pages' production precision:
+ * [P3] §1 and §14 "W8A8C8", §8 attention in FP8; [P4] §一: BF16 and FP8 formats).  Same work map,
+ * launch shape, partial layout and errors as attn_splitkv; only the cache differs:
+ *   k_cache  uint8 [num_pages, Hkv, page_size, D]   OCP E4M3 codes, token-major per block
+ *   v_cache  uint8 [num_pages, Hkv, D, page_size]   dim-major per block
+ *   k_scale, v_scale  device fp32[Hkv] (4-byte aligned): element x of KV head g stands for
+ *                 e4m3(x) * k_scale[g] (keys) or e4m3(x) * v_scale[g] (values)
+ * The codes are widened exactly to bf16 before the matrix products; q stays bf16.  Partials are in
+ * real units (the scales are applied), so attn_combine merges them as usual.
+ * Errors: as attn_splitkv, plus LBSA_ERR_INVALID for a missing or misaligned scale pointer.
+ */
+int attn_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache,
+                     const float* k_scale, const float* v_scale,
+                     const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
+                     const int32_t* seq_lens, const int32_t* map,
+                     int32_t num_workers, int32_t num_segments, int32_t head_groups,
+                     int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t page_size, float softmax_scale,
+                     float* part_m, float* part_l, float* part_o,
+                     uint64_t* timing, void* stream);
 
 /*
  * Split-KV chunked-prefill kernel over a cached prefix (the greedy map of attn_plan_prefill

@@ -17,9 +17,13 @@ import torch
 
 __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill",
-    "attn_query_workers", "attn_splitkv", "attn_splitkv_prefill", "attn_combine", "attn_status_string",
-    "attn_probe_stream_read", "map_header", "LIB_PATH",
+    "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_prefill", "attn_combine",
+    "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
 ]
+
+# cache element types (LBSA_KV_* in include/lbsa.h)
+KV_BF16 = 0
+KV_FP8_E4M3 = 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblbsa.so")
 
@@ -34,10 +38,13 @@ _SIGNATURES = {
     "attn_plan_static": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
     "attn_plan_prefill": (ctypes.c_int, [_c_i32p, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                          _c_i32p, _c_i32, _c_i32p]),
-    "attn_query_workers": (ctypes.c_int, [ctypes.c_int, _c_i32, _c_i32p]),
+    "attn_query_workers": (ctypes.c_int, [ctypes.c_int, _c_i32, _c_i32, _c_i32p]),
     "attn_splitkv": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                     ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "attn_splitkv_fp8": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
+                                        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                        ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "attn_combine": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                     _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, _c_vp]),
     "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
@@ -128,9 +135,9 @@ def attn_plan_prefill(q_lens: Sequence[int], kv_lens: Sequence[int], num_workers
                       num_workers, q_tile, kv_tile, int(bool(causal)))
 
 
-def attn_query_workers(device: int = 0, head_groups: int = 8) -> int:
+def attn_query_workers(device: int = 0, head_groups: int = 8, kv_dtype: int = KV_BF16) -> int:
     out = _c_i32(0)
-    _check(lib().attn_query_workers(device, head_groups, ctypes.byref(out)), "attn_query_workers")
+    _check(lib().attn_query_workers(device, head_groups, kv_dtype, ctypes.byref(out)), "attn_query_workers")
     return out.value
 
 
@@ -164,16 +171,12 @@ def max_splits_of(map_host: np.ndarray) -> int:
     return int(np.max(np.diff(ptr))) if hdr["U"] > 0 else 0
 
 
-def attn_splitkv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
-                 seq_lens: torch.Tensor, map_dev: torch.Tensor, num_workers: int, num_segments: int,
-                 head_groups: int, softmax_scale: float, part_m: torch.Tensor, part_l: torch.Tensor,
-                 part_o: torch.Tensor, timing: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Launch the split-KV decode kernel.  Layouts: q [B, Hq, D]; k_cache [P, Hkv, page, D];
-    v_cache [P, Hkv, D, page]; block_table [B, stride]; part_m/l [S, Hq]; part_o [S, Hq, D]."""
+def _check_decode_args(q, k_cache, v_cache, block_table, seq_lens, map_dev, num_workers, num_segments, head_groups,
+                       part_m, part_l, part_o, timing, cache_dtype):
     dev = q.device
     _need(q, torch.bfloat16, "q", dev)
-    _need(k_cache, torch.bfloat16, "k_cache", dev)
-    _need(v_cache, torch.bfloat16, "v_cache", dev)
+    _need(k_cache, cache_dtype, "k_cache", dev)
+    _need(v_cache, cache_dtype, "v_cache", dev)
     _need(block_table, torch.int32, "block_table", dev)
     _need(seq_lens, torch.int32, "seq_lens", dev)
     _need(map_dev, torch.int32, "map", dev)
@@ -192,11 +195,44 @@ def attn_splitkv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
         _need(timing, torch.int64, "timing", dev)
         if timing.numel() < num_workers * head_groups * 4:
             raise ValueError("timing buffer too small")
+    return B, Hq, D, P, Hkv, page
+
+
+def attn_splitkv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                 seq_lens: torch.Tensor, map_dev: torch.Tensor, num_workers: int, num_segments: int,
+                 head_groups: int, softmax_scale: float, part_m: torch.Tensor, part_l: torch.Tensor,
+                 part_o: torch.Tensor, timing: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Launch the split-KV decode kernel.  Layouts: q [B, Hq, D]; k_cache [P, Hkv, page, D];
+    v_cache [P, Hkv, D, page]; block_table [B, stride]; part_m/l [S, Hq]; part_o [S, Hq, D]."""
+    B, Hq, D, P, Hkv, page = _check_decode_args(q, k_cache, v_cache, block_table, seq_lens, map_dev, num_workers,
+                                                num_segments, head_groups, part_m, part_l, part_o, timing,
+                                                torch.bfloat16)
     st = lib().attn_splitkv(_dptr(q), _dptr(k_cache), _dptr(v_cache), _dptr(block_table), block_table.shape[1],
                             P, _dptr(seq_lens), _dptr(map_dev), num_workers, num_segments, head_groups, B, Hq,
                             Hkv, D, page, float(softmax_scale), _dptr(part_m), _dptr(part_l), _dptr(part_o),
                             _dptr(timing), _stream(stream))
     _check(st, "attn_splitkv")
+
+
+def attn_splitkv_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                     v_scale: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor, map_dev: torch.Tensor,
+                     num_workers: int, num_segments: int, head_groups: int, softmax_scale: float,
+                     part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor,
+                     timing: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Launch the split-KV decode kernel over an 8-bit E4M3 cache: k_cache/v_cache uint8 codes in the
+    layouts of attn_splitkv, k_scale/v_scale float32 [Hkv] (value = e4m3(code) * scale of the head)."""
+    B, Hq, D, P, Hkv, page = _check_decode_args(q, k_cache, v_cache, block_table, seq_lens, map_dev, num_workers,
+                                                num_segments, head_groups, part_m, part_l, part_o, timing,
+                                                torch.uint8)
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _need(t, torch.float32, name, q.device)
+        if t.numel() != Hkv:
+            raise ValueError(f"{name}: need one scale per KV head ({Hkv})")
+    st = lib().attn_splitkv_fp8(_dptr(q), _dptr(k_cache), _dptr(v_cache), _dptr(k_scale), _dptr(v_scale),
+                                _dptr(block_table), block_table.shape[1], P, _dptr(seq_lens), _dptr(map_dev),
+                                num_workers, num_segments, head_groups, B, Hq, Hkv, D, page, float(softmax_scale),
+                                _dptr(part_m), _dptr(part_l), _dptr(part_o), _dptr(timing), _stream(stream))
+    _check(st, "attn_splitkv_fp8")
 
 
 def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

@@ -1,21 +1,25 @@
-// Split-KV decode attention over a paged bf16 KV cache, driven by a precomputed work map.
+// Split-KV decode attention over a paged KV cache (bf16, or 8-bit E4M3 with per-head scales),
+// driven by a precomputed work map.
 //
 // Method: [P3] "Hy3 Preview AI Infra 推理优化精读笔记" §3.1 方案 step 4 and [P4]
 // "腾讯混元AI Infra进化：HPC-Ops推理核心算子全面升级" §二.1: every worker reads its own list
 // from the global task map and computes split-KV partial results for it.  GQA shape of [P3] §2
-// (8 query heads per KV head, head dim 128).
+// (8 query heads per KV head, head dim 128).  The 8-bit cache is the production precision of
+// [P3] §1 / §14 ("W8A8C8") and §8 (attention in FP8).
 //
 // gfx950 design.  A workgroup is (worker w, KV-head group g) with one 64-lane wave per KV head
 // of the group; waves are independent (no LDS, no barriers).  For each segment (b, kv_begin,
-// kv_end) of list w a wave streams the segment's KV in 32-token chunks:
+// kv_end) of list w a wave streams the segment's KV in 64-token chunks (one page of 64 tokens, or
+// a 64-token slice of a larger page):
 //
-//   * K chunk (32 tokens x 128 dims, token-major in the page) and V chunk (128 dims x 32 tokens,
-//     dim-major in the page) go straight from HBM into VGPRs with 16-byte loads laid out as MFMA
-//     operands, so no LDS round trip is needed;
+//   * K chunk (64 tokens x 128 dims, token-major in the page) and V chunk (128 dims x 64 tokens,
+//     dim-major in the page) go straight from HBM into VGPRs with 16-byte buffer loads laid out
+//     as MFMA operands, so no LDS round trip is needed; the next chunks' loads are in flight while
+//     the current chunk is computed;
 //   * S = K . Q^T with v_mfma_f32_16x16x32_bf16: rows are tokens, columns are the 8 query heads
-//     of the KV head (columns 8..15 repeat them and are ignored);  the two 16-token row tiles are
-//     interleaved so each lane ends up holding the scores of 8 consecutive tokens of one head,
-//     exactly the k-slice it must supply to the PV product;
+//     of the KV head (columns 8..15 repeat them and are ignored).  Token rows are assigned so that
+//     each lane ends up holding the scores of 8 consecutive tokens of one head, exactly the
+//     k-slice it must supply to the PV product;
 //   * online softmax in the exp2 domain per lane (head = lane % 16), the chunk maximum reduced
 //     across the four 16-lane groups with two lane exchanges;
 //   * O^T += V^T . P^T with the same MFMA; P is split into bf16 hi + lo parts (two MFMAs) so the
@@ -23,10 +27,17 @@
 //     accuracy;
 //   * at segment end the wave writes (m, l, o) for its 8 query heads to partial slot = segment id.
 //
+// 8-bit cache: the E4M3 codes are widened to bf16 in registers right before the MFMAs
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1, exact: every E4M3 value is a bf16 value); the K scale
+// of the head is folded into the softmax scale and the V scale into the partial's o at segment end,
+// so the arithmetic on the codes is the bf16 path's.  Each chunk is half the bytes of a bf16 chunk,
+// so the pipeline keeps more chunks in flight.
+//
 // The contractions are tiny (8 query heads) and the kernel is HBM-bound: MFMA work per chunk is
-// ~24 instructions against 16 KiB of loads.  The matrix cores take the dot products off the VALU,
-// whose fp32 FMA budget at full HBM rate would otherwise be nearly exhausted (about 2,300 VALU
-// lane operations per token and KV head for QK, PV and softmax, against ~2,500 available).
+// ~48 instructions against 32 KiB (bf16) or 16 KiB (8-bit) of loads.  The matrix cores take the
+// dot products off the VALU, whose fp32 FMA budget at full HBM rate would otherwise be nearly
+// exhausted (about 2,300 VALU lane operations per token and KV head for QK, PV and softmax, against
+// ~2,500 available at the bf16 byte rate and half that at the 8-bit rate).
 
 #include "common.h"
 #include "lbsa.h"
@@ -34,9 +45,11 @@
 namespace lbsa {
 
 struct DecodeParams {
-  const uint16_t* q;            // [B, Hq, 128]
-  const uint16_t* k;            // [pages, Hkv, page, 128]
-  const uint16_t* v;            // [pages, Hkv, 128, page]
+  const uint16_t* q;            // [B, Hq, 128] bf16
+  const uint8_t* k;             // [pages, Hkv, page, 128] elements of the cache type
+  const uint8_t* v;             // [pages, Hkv, 128, page]
+  const float* k_scale;         // [Hkv] for the 8-bit cache, else null
+  const float* v_scale;         // [Hkv] for the 8-bit cache, else null
   const int32_t* block_table;   // [B, bt_stride]
   const int32_t* seq_lens;      // [B]
   const int32_t* map;
@@ -49,65 +62,127 @@ struct DecodeParams {
 };
 
 constexpr int kD = 128;
-
-// Tuning knobs (compile-time):
-//   LBSA_DECODE_KB    32-token k-blocks per loop iteration (1: half a 64-token page, 2: a page)
-//   LBSA_DECODE_PIPE  1: double-buffer the K/V registers so the next chunk's loads are in flight
-//                     while the current chunk is computed
-//   LBSA_DECODE_NT    1: non-temporal hint on the KV stream loads
-#ifndef LBSA_DECODE_KB
-#define LBSA_DECODE_KB 2
-#endif
-#ifndef LBSA_DECODE_PIPE
-#define LBSA_DECODE_PIPE 1
-#endif
-#ifndef LBSA_DECODE_NT
-#define LBSA_DECODE_NT 0
-#endif
-
-constexpr int kKB = LBSA_DECODE_KB;
-constexpr int kChunk = 32 * kKB;   // tokens per loop iteration
+constexpr int kKB = 2;             // 32-token k-blocks per chunk
+constexpr int kChunk = 32 * kKB;   // tokens per chunk
 constexpr int kMinPage = kChunk;   // a chunk never straddles two pages
 
-#if LBSA_DECODE_NT
-constexpr int kKvAux = 2;   // buffer-load cache policy: non-temporal
-#else
-constexpr int kKvAux = 0;
+// Tuning knobs (compile-time): chunks in the register pipeline (2: the next chunk is in flight
+// while the current one is computed; 3: the next two), per cache type.
+#ifndef LBSA_DECODE_DEPTH
+#define LBSA_DECODE_DEPTH 2
+#endif
+#ifndef LBSA_FP8_DEPTH
+#define LBSA_FP8_DEPTH 3
 #endif
 
-// K/V registers of one chunk, laid out as MFMA operands.
-struct Chunk {
-  u32x4 k[kKB][2][4];   // k-block, S-tile, dim block of 32: token row tok0 + 4j, dims 32c + 8grp
-  u32x4 v[kKB][8];      // k-block, dim tile of 16: dim 16n + r, tokens 8grp .. 8grp+7
-};
-
 struct Lane {
-  int r, grp, tok0;
+  int r, grp;
   int k_off;   // byte offset of this lane's K fragment inside a (page, head) block
   int v_off;   // byte offset of this lane's V fragment inside a (page, head) block
 };
 
 __device__ __forceinline__ u32x4 buf_load(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kKvAux));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
 }
 
-// One chunk = tokens [off, off + kChunk) of one (page, KV head) block.  Buffer descriptors bound
-// each load to its 16 KiB block (a load outside it would return zeros, never fault); the lane's
-// offset is one VGPR and the per-load offsets are scalar.
-__device__ __forceinline__ void load_chunk(Chunk& ch, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int off,
-                                           int page, const Lane& ln) {
+// ---- cache element types --------------------------------------------------------------------
+//
+// A type fixes how a lane's 16-byte loads map onto the MFMA operands.  For k-block kb (32 tokens)
+// S-tile j (16 token rows) the lane supplies A-row r = one token and, for the four MFMAs c = 0..3
+// over the 128 dims, eight dims each; the Q^T fragments use the same dims.  C rows 4grp + i of the
+// tile land in lane (r, grp), so the lane's eight scores per k-block are the tokens
+// first_token(kb) + e, e = 0..7, and its V operand of that k-block must hold the same tokens.
+
+// bf16 cache: K row r of S-tile (kb, j) is token 32kb + 8(r/4) + 4j + r%4; MFMA c takes dims
+// 32c + 8grp .. +7; V fragment = 8 consecutive tokens (16 bytes) of dim 16n + r.
+struct KvBf16 {
+  static constexpr int kElem = 2;
+  struct Chunk {
+    u32x4 k[kKB][2][4];   // k-block, S-tile, MFMA c
+    u32x4 v[kKB][8];      // k-block, dim tile n: dim 16n + r, tokens first_token(kb) .. +7
+  };
+  __device__ static int first_token(int kb, const Lane& ln) { return 32 * kb + 8 * ln.grp; }
+  __device__ static int q_dim(int c, const Lane& ln) { return 32 * c + 8 * ln.grp; }
+  __device__ static void setup(Lane& ln, int page) {
+    const int tok0 = 8 * (ln.r >> 2) + (ln.r & 3);
+    ln.k_off = (tok0 * kD + 8 * ln.grp) * 2;
+    ln.v_off = (ln.r * page + 8 * ln.grp) * 2;
+  }
+  __device__ static void load(Chunk& ch, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int off, int page,
+                              const Lane& ln) {
 #pragma unroll
-  for (int kb_i = 0; kb_i < kKB; ++kb_i)
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        ch.k[kb_i][j][c] = buf_load(kr, ln.k_off + (4 * j * kD + 32 * c) * 2, (off + 32 * kb_i) * kD * 2);
+        for (int c = 0; c < 4; ++c)
+          ch.k[kb][j][c] = buf_load(kr, ln.k_off + (4 * j * kD + 32 * c) * 2, (off + 32 * kb) * kD * 2);
 #pragma unroll
-  for (int kb_i = 0; kb_i < kKB; ++kb_i)
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-    for (int n = 0; n < 8; ++n) ch.v[kb_i][n] = buf_load(vr, ln.v_off, (16 * n * page + off + 32 * kb_i) * 2);
+      for (int n = 0; n < 8; ++n) ch.v[kb][n] = buf_load(vr, ln.v_off, (16 * n * page + off + 32 * kb) * 2);
+  }
+  __device__ static u32x4 k_op(const Chunk& ch, int kb, int j, int c) { return ch.k[kb][j][c]; }
+  __device__ static u32x4 v_op(const Chunk& ch, int kb, int n) { return ch.v[kb][n]; }
+  // zero the V elements of tokens first_token(kb) + 2i (lo) and + 2i + 1 (hi) that are not kept
+  __device__ static void mask_v(Chunk& ch, int kb, int i, bool keep_lo, bool keep_hi) {
+    const uint32_t keep = (keep_lo ? 0x0000ffffu : 0u) | (keep_hi ? 0xffff0000u : 0u);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) ch.v[kb][n][i] &= keep;
+  }
+};
+
+// Two E4M3 codes (bytes 2*hi, 2*hi + 1 of x) -> two bf16 values in one dword, exactly.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t x) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, HI));
 }
+
+// 8-bit (E4M3) cache: K row r of S-tile (kb, j) is token 16(r/4) + 8kb + 4j + r%4; MFMA c takes
+// dims 32grp + 8c .. +7, so one lane's 32 dims of a token are two 16-byte loads; V fragment = 16
+// consecutive tokens (16 bytes) of dim 16n + r, the low 8 for k-block 0 and the high 8 for 1.
+struct KvFp8 {
+  static constexpr int kElem = 1;
+  struct Chunk {
+    u32x4 k[kKB][2][2];   // k-block, S-tile, half: dims 32grp + 16h .. +15
+    u32x4 v[8];           // dim tile n: dim 16n + r, tokens 16grp .. +15
+  };
+  __device__ static int first_token(int kb, const Lane& ln) { return 16 * ln.grp + 8 * kb; }
+  __device__ static int q_dim(int c, const Lane& ln) { return 32 * ln.grp + 8 * c; }
+  __device__ static void setup(Lane& ln, int page) {
+    const int tok0 = 16 * (ln.r >> 2) + (ln.r & 3);
+    ln.k_off = tok0 * kD + 32 * ln.grp;
+    ln.v_off = ln.r * page + 16 * ln.grp;
+  }
+  __device__ static void load(Chunk& ch, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int off, int page,
+                              const Lane& ln) {
+#pragma unroll
+    for (int kb = 0; kb < kKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) ch.k[kb][j][h] = buf_load(kr, ln.k_off + 16 * h, (off + 8 * kb + 4 * j) * kD);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) ch.v[n] = buf_load(vr, ln.v_off, 16 * n * page + off);
+  }
+  __device__ static u32x4 widen(uint32_t d0, uint32_t d1) {
+    return u32x4{e4m3x2_to_bf16x2<false>(d0), e4m3x2_to_bf16x2<true>(d0), e4m3x2_to_bf16x2<false>(d1),
+                 e4m3x2_to_bf16x2<true>(d1)};
+  }
+  __device__ static u32x4 k_op(const Chunk& ch, int kb, int j, int c) {
+    const u32x4 raw = ch.k[kb][j][c >> 1];
+    return widen(raw[2 * (c & 1)], raw[2 * (c & 1) + 1]);
+  }
+  __device__ static u32x4 v_op(const Chunk& ch, int kb, int n) { return widen(ch.v[n][2 * kb], ch.v[n][2 * kb + 1]); }
+  __device__ static void mask_v(Chunk& ch, int kb, int i, bool keep_lo, bool keep_hi) {
+    const int sh = 16 * (i & 1);
+    const uint32_t keep = (((keep_lo ? 0x00ffu : 0u) | (keep_hi ? 0xff00u : 0u)) << sh) | ~(0xffffu << sh);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) ch.v[n][2 * kb + (i >> 1)] &= keep;
+  }
+};
+
+// ---- online softmax and the PV product ------------------------------------------------------
 
 // Online-softmax state of one wave for its 8 query heads (lane: head r; o: dims 16n + 4grp + i).
 struct State {
@@ -119,45 +194,43 @@ struct State {
 
 constexpr float kRescaleSlack = 8.0f;
 
-__device__ __forceinline__ void compute_chunk(Chunk& ch, State& st, const u32x4 (&qf)[4], int c0, int kv_begin,
-                                              int kv_end, float scale_log2, const Lane& ln) {
-  // scores: sc[kb][4j + i] is token c0 + 32kb + 8grp + 4j + i of head r
+template <class KV>
+__device__ __forceinline__ void compute_chunk(typename KV::Chunk& ch, State& st, const u32x4 (&qf)[4], int c0,
+                                              int kv_begin, int kv_end, float scale_log2, const Lane& ln) {
+  // scores: sc[kb][4j + i] is token c0 + first_token(kb) + 4j + i of head r
   float sc[kKB][8];
 #pragma unroll
-  for (int kb_i = 0; kb_i < kKB; ++kb_i)
+  for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc = mfma16x16x32(ch.k[kb_i][j][c], qf[c], acc);
+      for (int c = 0; c < 4; ++c) acc = mfma16x16x32(KV::k_op(ch, kb, j, c), qf[c], acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[kb_i][4 * j + i] = acc[i] * scale_log2;
+      for (int i = 0; i < 4; ++i) sc[kb][4 * j + i] = acc[i] * scale_log2;
     }
 
   if (c0 < kv_begin || c0 + kChunk > kv_end) {
 #pragma unroll
-    for (int kb_i = 0; kb_i < kKB; ++kb_i) {
-      const int t0 = c0 + 32 * kb_i + 8 * ln.grp;
+    for (int kb = 0; kb < kKB; ++kb) {
+      const int t0 = c0 + KV::first_token(kb, ln);
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        sc[kb_i][e] = (t0 + e < kv_begin || t0 + e >= kv_end) ? -INFINITY : sc[kb_i][e];
+        sc[kb][e] = (t0 + e < kv_begin || t0 + e >= kv_end) ? -INFINITY : sc[kb][e];
       // masked tokens may hold any bits (NaN included), and p = 0 does not cancel a NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = t0 + 2 * i;
-        const uint32_t keep = ((t >= kv_begin && t < kv_end) ? 0x0000ffffu : 0u) |
-                              ((t + 1 >= kv_begin && t + 1 < kv_end) ? 0xffff0000u : 0u);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) ch.v[kb_i][n][i] &= keep;
+        KV::mask_v(ch, kb, i, t >= kv_begin && t < kv_end, t + 1 >= kv_begin && t + 1 < kv_end);
       }
     }
   }
 
   float mx = -INFINITY;
 #pragma unroll
-  for (int kb_i = 0; kb_i < kKB; ++kb_i)
+  for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[kb_i][e]);
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[kb][e]);
   mx = fmaxf(mx, xor_lane(mx, 16));
   mx = fmaxf(mx, xor_lane(mx, 32));
   st.m_true = fmaxf(st.m_true, mx);
@@ -176,11 +249,11 @@ __device__ __forceinline__ void compute_chunk(Chunk& ch, State& st, const u32x4 
   const float m_use = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
   float sum = 0.f;
 #pragma unroll
-  for (int kb_i = 0; kb_i < kKB; ++kb_i) {
+  for (int kb = 0; kb < kKB; ++kb) {
     float ps[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      ps[e] = fast_exp2(sc[kb_i][e] - m_use);
+      ps[e] = fast_exp2(sc[kb][e] - m_use);
       sum += ps[e];
     }
     // P split into bf16 hi + lo parts: two MFMAs keep ~16 significant bits of each probability
@@ -193,15 +266,19 @@ __device__ __forceinline__ void compute_chunk(Chunk& ch, State& st, const u32x4 
     }
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
-      st.o[n] = mfma16x16x32(ch.v[kb_i][n], phi, st.o[n]);
-      st.o[n] = mfma16x16x32(ch.v[kb_i][n], plo, st.o[n]);
+      const u32x4 vop = KV::v_op(ch, kb, n);
+      st.o[n] = mfma16x16x32(vop, phi, st.o[n]);
+      st.o[n] = mfma16x16x32(vop, plo, st.o[n]);
     }
   }
   st.l += sum;
 }
 
-template <int WAVES>
+// ---- the kernel -----------------------------------------------------------------------------
+
+template <class KV, int WAVES, int DEPTH>
 __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams p) {
+  using Chunk = typename KV::Chunk;
   const int lane = threadIdx.x & 63;
   // wave index is uniform across the wave; say so, so page addressing stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -211,11 +288,10 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
   Lane ln;
   ln.r = lane & 15;                                 // MFMA row / column index
   ln.grp = lane >> 4;                               // MFMA k group
-  // S-tile j row r is token 8*(r/4) + 4j + r%4, so C rows 4grp+i of tile j are tokens 8grp+4j+i
-  ln.tok0 = 8 * (ln.r >> 2) + (ln.r & 3);
-  ln.k_off = (ln.tok0 * kD + 8 * ln.grp) * 2;
-  ln.v_off = (ln.r * p.page + 8 * ln.grp) * 2;
-  const int block_bytes = p.page * kD * 2;
+  KV::setup(ln, p.page);
+  const int block_bytes = p.page * kD * KV::kElem;
+  const float s_log2 = p.k_scale ? p.scale_log2 * p.k_scale[h] : p.scale_log2;
+  const float o_scale = p.v_scale ? p.v_scale[h] : 1.f;
 
   uint64_t t_start = 0;
   if (p.timing && threadIdx.x == 0) t_start = realtime();
@@ -225,7 +301,7 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
   const int32_t* segs = p.map + 8 + (p.W + 1) + (U + 1) + 2 * U;
   const int s_begin = worker_ptr[w];
   const int s_end = min(worker_ptr[w + 1], p.S);
-  const size_t head_stride = (size_t)p.page * kD;   // elements per (page, KV head) block
+  const size_t head_bytes = (size_t)block_bytes;   // bytes per (page, KV head) block
 
   for (int s = s_begin; s < s_end; ++s) {
     const int b = segs[4 * s];
@@ -235,12 +311,12 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
     kv_end = min(kv_end, p.seq_lens[b]);
     kv_end = min(kv_end, p.bt_stride * p.page);
 
-    // Q^T fragments: column r = query head 8h + (r & 7), k = dims 32c + 8grp .. +7
+    // Q^T fragments: column r = query head 8h + (r & 7), k = dims q_dim(c) .. +7
     u32x4 qf[4];
     {
-      const uint16_t* qp = p.q + ((size_t)b * p.Hq + h * 8 + (ln.r & 7)) * kD + 8 * ln.grp;
+      const uint16_t* qp = p.q + ((size_t)b * p.Hq + h * 8 + (ln.r & 7)) * kD;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qf[c] = ld16(qp + 32 * c);
+      for (int c = 0; c < 4; ++c) qf[c] = ld16(qp + KV::q_dim(c, ln));
     }
 
     State st;
@@ -261,12 +337,19 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
       if (lp <= last_page) v = bt_row[lp];
       btv = min(max(v, 0), p.num_pages - 1);
     };
-    // descriptors of the (page, KV head) blocks holding chunk c, and c's offset in the page;
-    // chunks are visited in order, so the page index advances without a division
-    int pg_cur = (kv_begin & ~(kChunk - 1)) / p.page;
-    int off_cur = (kv_begin & ~(kChunk - 1)) - pg_cur * p.page;
-    auto chunk_rsrc = [&](int c, __amdgpu_buffer_rsrc_t& kr, __amdgpu_buffer_rsrc_t& vr) -> int {
-      (void)c;
+    // chunks are issued in order, so the page index advances without a division
+    int c = kv_begin & ~(kChunk - 1);
+    int next = c;   // first token of the next chunk to issue
+    int pg_cur = c / p.page;
+    int off_cur = c - pg_cur * p.page;
+    // Issue the loads of the next chunk into ch.  The buffer descriptors bound each load to its
+    // (page, KV head) block (a load outside it returns zeros, never faults).  A chunk past the
+    // segment's end is issued with an empty descriptor: its loads return zeros without touching
+    // memory, so the pipeline below issues one chunk per computed chunk with no branch, and the
+    // compiler's wait counts stay exact.
+    auto issue = [&](Chunk& ch) {
+      const bool live = next < kv_end;
+      next += kChunk;
       const int pg = pg_cur;
       const int off = off_cur;
       off_cur += kChunk;
@@ -279,54 +362,39 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
         load_window();
       }
       const int pid = __builtin_amdgcn_readlane(btv, pg - win);
-      const size_t blk = ((size_t)pid * p.Hkv + h) * head_stride;
-      kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k + blk), (short)0, block_bytes, 0x00020000);
-      vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + blk), (short)0, block_bytes, 0x00020000);
-      return off;
+      const size_t blk = ((size_t)pid * p.Hkv + h) * head_bytes;
+      const int nbytes = live ? block_bytes : 0;
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.k + blk), (short)0, nbytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.v + blk), (short)0, nbytes, 0x00020000);
+      KV::load(ch, kr, vr, off, p.page, ln);
     };
 
-    int c = kv_begin & ~(kChunk - 1);
     if (c < kv_end) {
       load_window();
-      __amdgpu_buffer_rsrc_t kr, vr;
-#if LBSA_DECODE_PIPE
-      Chunk A, B;
-      int off = chunk_rsrc(c, kr, vr);
-      load_chunk(A, kr, vr, off, p.page, ln);
-      while (true) {
-        int cn = c + kChunk;
-        bool more = cn < kv_end;
-        if (more) {
-          off = chunk_rsrc(cn, kr, vr);
-          load_chunk(B, kr, vr, off, p.page, ln);
-        }
-        compute_chunk(A, st, qf, c, kv_begin, kv_end, p.scale_log2, ln);
-        c = cn;
-        if (!more) break;
-        cn = c + kChunk;
-        more = cn < kv_end;
-        if (more) {
-          off = chunk_rsrc(cn, kr, vr);
-          load_chunk(A, kr, vr, off, p.page, ln);
-        }
-        compute_chunk(B, st, qf, c, kv_begin, kv_end, p.scale_log2, ln);
-        c = cn;
-        if (!more) break;
-      }
-#else
-      Chunk A;
-      for (; c < kv_end; c += kChunk) {
-        const int off = chunk_rsrc(c, kr, vr);
-        load_chunk(A, kr, vr, off, p.page, ln);
-        compute_chunk(A, st, qf, c, kv_begin, kv_end, p.scale_log2, ln);
-      }
-#endif
-    }
-
-    // express the partial against the true max: m = max score, l and o scaled to match
-    const float to_true = (st.m_true == -INFINITY) ? 0.f : fast_exp2(st.m_ref - st.m_true);
+      // ring of DEPTH chunk buffers: DEPTH - 1 chunks are in flight while one is computed
+      Chunk buf[DEPTH];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) st.o[n] *= to_true;
+      for (int i = 0; i < DEPTH - 1; ++i) issue(buf[i]);
+      while (true) {
+#pragma unroll
+        for (int i = 0; i < DEPTH; ++i) {
+          issue(buf[(i + DEPTH - 1) % DEPTH]);
+          compute_chunk<KV>(buf[i], st, qf, c, kv_begin, kv_end, s_log2, ln);
+          c += kChunk;
+          if (c >= kv_end) goto segment_done;
+        }
+      }
+    }
+  segment_done:
+
+    // express the partial against the true max: m = max score, l and o scaled to match; o also
+    // takes the V scale of an 8-bit cache
+    const float to_true = (st.m_true == -INFINITY) ? 0.f : fast_exp2(st.m_ref - st.m_true);
+    const float o_mul = to_true * o_scale;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[n] *= o_mul;
     float l = st.l * to_true;
     l += xor_lane(l, 16);
     l += xor_lane(l, 32);
@@ -342,6 +410,10 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
     }
   }
 
+  // the empty-descriptor loads issued past the last segment's end return zeros; drain them before
+  // the wave ends (gfx9 s_waitcnt encoding: vmcnt 0, expcnt and lgkmcnt at their maximum)
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+
   if (p.timing) {
     if constexpr (WAVES > 1) __syncthreads();
     if (threadIdx.x == 0) {
@@ -354,32 +426,40 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
   }
 }
 
-template <int WAVES>
+template <class KV>
+struct DecodeDepth;
+template <>
+struct DecodeDepth<KvBf16> {
+  static constexpr int value = LBSA_DECODE_DEPTH;
+};
+template <>
+struct DecodeDepth<KvFp8> {
+  static constexpr int value = LBSA_FP8_DEPTH;
+};
+
+template <class KV, int WAVES>
 hipError_t launch_decode(const DecodeParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(splitkv_decode_kernel<WAVES>, dim3(grid), dim3(64 * WAVES), 0, stream, p);
+  hipLaunchKernelGGL((splitkv_decode_kernel<KV, WAVES, DecodeDepth<KV>::value>), dim3(grid), dim3(64 * WAVES), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
-template <int WAVES>
+template <class KV, int WAVES>
 int decode_blocks_per_cu() {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, splitkv_decode_kernel<WAVES>, 64 * WAVES, 0) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, splitkv_decode_kernel<KV, WAVES, DecodeDepth<KV>::value>,
+                                                   64 * WAVES, 0) != hipSuccess)
     return 0;
   return nb;
 }
 
-}  // namespace lbsa
-
-using namespace lbsa;
-
-extern "C" int attn_splitkv(const void* q, const void* k_cache, const void* v_cache,
-                            const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
-                            const int32_t* seq_lens, const int32_t* map, int32_t num_workers,
-                            int32_t num_segments, int32_t head_groups, int32_t B, int32_t num_q_heads,
-                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
-                            float softmax_scale, float* part_m, float* part_l, float* part_o,
-                            uint64_t* timing, void* stream) {
+template <class KV>
+int splitkv_launch(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                   const float* v_scale, const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
+                   const int32_t* seq_lens, const int32_t* map, int32_t num_workers, int32_t num_segments,
+                   int32_t head_groups, int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t page_size, float softmax_scale, float* part_m, float* part_l, float* part_o,
+                   uint64_t* timing, void* stream) {
   if (num_workers < 1 || num_segments < 0 || B < 0 || head_groups < 1 || num_kv_heads < 1 ||
       num_pages < 1 || block_table_stride < 0 || page_size < 1)
     return LBSA_ERR_INVALID;
@@ -393,11 +473,15 @@ extern "C" int attn_splitkv(const void* q, const void* k_cache, const void* v_ca
   if (num_kv_heads % head_groups) return LBSA_ERR_INVALID;
   const int waves = num_kv_heads / head_groups;
   if (waves != 1 && waves != 2 && waves != 4 && waves != 8) return LBSA_ERR_UNSUPPORTED;
+  // one (page, KV head) block must stay addressable by a 32-bit buffer descriptor
+  if ((int64_t)page_size * kD * KV::kElem > INT32_MAX) return LBSA_ERR_UNSUPPORTED;
 
   DecodeParams p;
   p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k_cache);
-  p.v = static_cast<const uint16_t*>(v_cache);
+  p.k = static_cast<const uint8_t*>(k_cache);
+  p.v = static_cast<const uint8_t*>(v_cache);
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   p.block_table = block_table;
   p.seq_lens = seq_lens;
   p.map = map;
@@ -420,21 +504,63 @@ extern "C" int attn_splitkv(const void* q, const void* k_cache, const void* v_ca
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
   switch (waves) {
-    case 1: err = launch_decode<1>(p, (int)grid, st); break;
-    case 2: err = launch_decode<2>(p, (int)grid, st); break;
-    case 4: err = launch_decode<4>(p, (int)grid, st); break;
-    default: err = launch_decode<8>(p, (int)grid, st); break;
+    case 1: err = launch_decode<KV, 1>(p, (int)grid, st); break;
+    case 2: err = launch_decode<KV, 2>(p, (int)grid, st); break;
+    case 4: err = launch_decode<KV, 4>(p, (int)grid, st); break;
+    default: err = launch_decode<KV, 8>(p, (int)grid, st); break;
   }
   return err == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;
 }
 
-extern "C" int attn_query_workers(int device, int32_t head_groups, int32_t* num_workers_out) {
-  static int cached[64][9];
+template <class KV>
+int blocks_per_cu(int waves) {
+  switch (waves) {
+    case 1: return decode_blocks_per_cu<KV, 1>();
+    case 2: return decode_blocks_per_cu<KV, 2>();
+    case 4: return decode_blocks_per_cu<KV, 4>();
+    default: return decode_blocks_per_cu<KV, 8>();
+  }
+}
+
+}  // namespace lbsa
+
+using namespace lbsa;
+
+extern "C" int attn_splitkv(const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
+                            const int32_t* seq_lens, const int32_t* map, int32_t num_workers,
+                            int32_t num_segments, int32_t head_groups, int32_t B, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                            float softmax_scale, float* part_m, float* part_l, float* part_o,
+                            uint64_t* timing, void* stream) {
+  return splitkv_launch<KvBf16>(q, k_cache, v_cache, nullptr, nullptr, block_table, block_table_stride, num_pages,
+                                seq_lens, map, num_workers, num_segments, head_groups, B, num_q_heads,
+                                num_kv_heads, head_dim, page_size, softmax_scale, part_m, part_l, part_o, timing,
+                                stream);
+}
+
+extern "C" int attn_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                const float* v_scale, const int32_t* block_table, int32_t block_table_stride,
+                                int32_t num_pages, const int32_t* seq_lens, const int32_t* map,
+                                int32_t num_workers, int32_t num_segments, int32_t head_groups, int32_t B,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                float softmax_scale, float* part_m, float* part_l, float* part_o,
+                                uint64_t* timing, void* stream) {
+  if (!k_scale || !v_scale) return LBSA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3) return LBSA_ERR_INVALID;
+  return splitkv_launch<KvFp8>(q, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride, num_pages,
+                               seq_lens, map, num_workers, num_segments, head_groups, B, num_q_heads, num_kv_heads,
+                               head_dim, page_size, softmax_scale, part_m, part_l, part_o, timing, stream);
+}
+
+extern "C" int attn_query_workers(int device, int32_t head_groups, int32_t kv_dtype, int32_t* num_workers_out) {
+  static int cached[64][2][9];
   if (!num_workers_out || head_groups < 1 || head_groups > 8 || (8 % head_groups) || device < 0 ||
       device >= 64)
     return LBSA_ERR_INVALID;
-  if (cached[device][head_groups] > 0) {
-    *num_workers_out = cached[device][head_groups];
+  if (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3) return LBSA_ERR_INVALID;
+  if (cached[device][kv_dtype][head_groups] > 0) {
+    *num_workers_out = cached[device][kv_dtype][head_groups];
     return LBSA_OK;
   }
   int prev = 0;
@@ -444,18 +570,11 @@ extern "C" int attn_query_workers(int device, int32_t head_groups, int32_t* num_
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   const int waves = 8 / head_groups;
   int nb = 0;
-  if (e == hipSuccess) {
-    switch (waves) {
-      case 1: nb = decode_blocks_per_cu<1>(); break;
-      case 2: nb = decode_blocks_per_cu<2>(); break;
-      case 4: nb = decode_blocks_per_cu<4>(); break;
-      default: nb = decode_blocks_per_cu<8>(); break;
-    }
-  }
-  hipSetDevice(prev);
+  if (e == hipSuccess) nb = kv_dtype == LBSA_KV_BF16 ? blocks_per_cu<KvBf16>(waves) : blocks_per_cu<KvFp8>(waves);
+  if (hipSetDevice(prev) != hipSuccess) return LBSA_ERR_HIP;
   if (e != hipSuccess || nb < 1 || cus < 1) return LBSA_ERR_HIP;
   const int w = cus * nb / head_groups;
-  cached[device][head_groups] = w;
+  cached[device][kv_dtype][head_groups] = w;
   *num_workers_out = w;
   return LBSA_OK;
 }

@@ -13,26 +13,28 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import attn_combine, attn_plan, attn_plan_static, attn_query_workers, attn_splitkv, map_header, max_splits_of
+from . import (KV_BF16, KV_FP8_E4M3, attn_combine, attn_plan, attn_plan_static, attn_query_workers, attn_splitkv,
+               attn_splitkv_fp8, map_header, max_splits_of)
 
 
 class DecodeStep:
     def __init__(self, seq_lens: Sequence[int], device, num_workers: Optional[int] = None, tile: int = 512,
                  head_groups: int = 8, num_q_heads: int = 64, head_dim: int = 128,
-                 static_splits: Optional[int] = None):
+                 static_splits: Optional[int] = None, kv_dtype: int = KV_BF16):
         device = torch.device(device)
         self.seq_lens_host = [int(x) for x in seq_lens]
         if static_splits is not None:
             self.map_host = attn_plan_static(self.seq_lens_host, static_splits, tile)
         else:
             if num_workers is None:
-                num_workers = attn_query_workers(device.index or 0, head_groups)
+                num_workers = attn_query_workers(device.index or 0, head_groups, kv_dtype)
             self.map_host = attn_plan(self.seq_lens_host, num_workers, tile)
         hdr = map_header(self.map_host)
         self.W, self.S, self.U, self.T = hdr["W"], hdr["S"], hdr["U"], hdr["T"]
         self.max_splits = max_splits_of(self.map_host)
         self.tile = tile
         self.head_groups = head_groups
+        self.kv_dtype = kv_dtype
         self.device = device
         self.map = torch.from_numpy(self.map_host).to(device)
         self.seq_lens = torch.tensor(self.seq_lens_host, dtype=torch.int32, device=device)
@@ -41,9 +43,19 @@ class DecodeStep:
         self.part_l = torch.empty((S, num_q_heads), dtype=torch.float32, device=device)
         self.part_o = torch.empty((S, num_q_heads, head_dim), dtype=torch.float32, device=device)
 
-    def splitkv(self, q, k_cache, v_cache, block_table, scale: float, timing=None, stream=None) -> None:
-        attn_splitkv(q, k_cache, v_cache, block_table, self.seq_lens, self.map, self.W, self.S, self.head_groups,
-                     scale, self.part_m, self.part_l, self.part_o, timing=timing, stream=stream)
+    def splitkv(self, q, k_cache, v_cache, block_table, scale: float, timing=None, stream=None,
+                kv_scales=None) -> None:
+        """bf16 cache, or (kv_dtype KV_FP8_E4M3) uint8 codes with kv_scales = (k_scale, v_scale)."""
+        if self.kv_dtype == KV_FP8_E4M3:
+            if kv_scales is None:
+                raise ValueError("an 8-bit cache needs kv_scales=(k_scale, v_scale)")
+            attn_splitkv_fp8(q, k_cache, v_cache, kv_scales[0], kv_scales[1], block_table, self.seq_lens, self.map,
+                             self.W, self.S, self.head_groups, scale, self.part_m, self.part_l, self.part_o,
+                             timing=timing, stream=stream)
+        else:
+            attn_splitkv(q, k_cache, v_cache, block_table, self.seq_lens, self.map, self.W, self.S,
+                         self.head_groups, scale, self.part_m, self.part_l, self.part_o, timing=timing,
+                         stream=stream)
 
     def combine(self, out, stream=None) -> None:
         attn_combine(self.part_m, self.part_l, self.part_o, self.map, self.U, out, max_splits=self.max_splits,
@@ -51,11 +63,11 @@ class DecodeStep:
 
     def __call__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
                  scale: Optional[float] = None, out: Optional[torch.Tensor] = None, timing=None,
-                 stream=None) -> torch.Tensor:
+                 stream=None, kv_scales=None) -> torch.Tensor:
         if scale is None:
             scale = q.shape[-1] ** -0.5
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        self.splitkv(q, k_cache, v_cache, block_table, scale, timing=timing, stream=stream)
+        self.splitkv(q, k_cache, v_cache, block_table, scale, timing=timing, stream=stream, kv_scales=kv_scales)
         self.combine(out, stream=stream)
         return out

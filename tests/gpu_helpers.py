@@ -80,3 +80,23 @@ def oracle_prefill_rows(wl: WL.Workload, b: int, rows, causal=True, scale=SCALE)
         m, l, o = ref_partial(q[j:j + 1], kd, vd, scale, 0, kd.shape[0], causal, first_row=j, q_len=q.shape[0])
         out[j] = o[0] / l[0][:, None]
     return out
+
+
+def decode_inputs_fp8(wl: WL.Workload, device="cuda", page=64, pad_code=0):
+    """q (bf16), the 8-bit caches (uint8 E4M3 codes, paged), block table and per-head scales."""
+    q = wl.q().to(device)
+    k_cache, v_cache, bt = pack_paged(wl.kv_fp8, wl.kv_lens, page, wl.hkv, wl.head_dim, wl.page_permutation,
+                                      device, pad_value=pad_code, dtype=torch.uint8)
+    ks, vs = wl.kv_scales()
+    return q, k_cache, v_cache, bt, ks.to(device), vs.to(device)
+
+
+def oracle_decode_fp8(wl: WL.Workload, requests=None, scale=SCALE):
+    from oracle.fp8 import ref_decode_fp8
+    q = wl.q().to(torch.float64).numpy()
+    ks, vs = (s.to(torch.float64).numpy() for s in wl.kv_scales())
+    out = {}
+    for b in (range(wl.batch) if requests is None else requests):
+        k, v = wl.kv_fp8(b)
+        out[b] = ref_decode_fp8(q[b:b + 1], [k.numpy()], [v.numpy()], ks, vs, scale)[0]
+    return out

@@ -132,5 +132,13 @@ def test_errors_and_capacity(L):
     dummy = ctypes.c_void_p(16)
     assert lib.attn_splitkv(dummy, dummy, dummy, dummy, 1, 1, dummy, dummy, 4, 0, 8, 1, 64, 8, 96, 64, 1.0,
                             None, None, None, None, None) == -3
+    # the 8-bit cache entry point also needs both scale arrays
+    assert lib.attn_splitkv_fp8(dummy, dummy, dummy, None, dummy, dummy, 1, 1, dummy, dummy, 4, 0, 8, 1, 64, 8,
+                                128, 64, 1.0, None, None, None, None, None) == -1
+    assert lib.attn_splitkv_fp8(dummy, dummy, dummy, dummy, dummy, dummy, 1, 1, dummy, dummy, 4, 0, 8, 1, 64, 8,
+                                96, 64, 1.0, None, None, None, None, None) == -3
+    out = ctypes.c_int32(0)
+    assert lib.attn_query_workers(0, 8, 7, ctypes.byref(out)) == -1
+    assert lib.attn_query_workers(0, 3, 0, ctypes.byref(out)) == -1
     assert lib.attn_combine(None, None, None, dummy, 1, 1, None, None, 64, 128, None, 0, 0, None) == -1
     assert lib.attn_combine(dummy, dummy, dummy, dummy, 1, 1, None, None, 64, 128, dummy, 0, -1, None) == -1

@@ -46,3 +46,29 @@ def test_full_size(name):
     torch.cuda.synchronize()
     for b in range(wl.batch):
         assert errors(out2[b].cpu().numpy().astype(np.float64), got[b].astype(np.float64))[1] <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["mixed", "long_tail"])
+def test_full_size_fp8(name):
+    """The 8-bit cache path at full size, workers from the occupancy query of its own kernel."""
+    import load_balanced_split_attn_amd as lb
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    from gpu_helpers import decode_inputs_fp8, oracle_decode_fp8
+    wl = WL.BY_NAME[name]()
+    note(f"full-size fp8 {name}: B={wl.batch} tokens={sum(wl.kv_lens)}")
+    q, kc, vc, bt, ks, vs = decode_inputs_fp8(wl)
+    step = DecodeStep(wl.kv_lens, q.device, head_groups=8, kv_dtype=lb.KV_FP8_E4M3)
+    out = step(q, kc, vc, bt, scale=SCALE, kv_scales=(ks, vs))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    seen, sample = set(), [0]
+    for b, L in enumerate(wl.kv_lens):
+        if L not in seen:
+            seen.add(L)
+            sample.append(b)
+    sample = sorted(set(sample[:6] + [int(np.argmax(wl.kv_lens))]))
+    ref = oracle_decode_fp8(wl, sample)
+    for b, r in ref.items():
+        ma, rr = assert_close(got[b], r, f"fp8 {name} request {b} (L={wl.kv_lens[b]})")
+        note(f"  request {b} L={wl.kv_lens[b]}: max_abs={ma:.2e} rel_rms={rr:.2e}")
