@@ -443,7 +443,7 @@ def main() -> int:
         # the device's streaming-read ceiling, measured on the same run (the KV cache itself)
         sink = torch.zeros(8192 * 256, dtype=torch.int32, device=dev)
         best = None
-        for blocks in (2048, 4096, 8192):
+        for blocks in (1024, 2048, 4096):
             for _ in range(2):
                 lb.attn_probe_stream_read(kc, blocks, sink)
             torch.cuda.synchronize()

@@ -43,8 +43,15 @@
  *
  *   q        bf16 [rows, Hq, D]: decode rows = B (one query per request);
  *                                prefill rows = sum of q_len_b, request b from row q_start[b]
- *   k_cache  bf16 [num_pages, Hkv, page_size, D]     token-major inside a (page, head) block
- *   v_cache  bf16 [num_pages, Hkv, D, page_size]     dim-major ("V transposed") inside a block
+ *   k_cache, v_cache  [num_pages, Hkv] blocks, one contiguous block per (page, KV head),
+ *            stored in rows of 64 bytes (w = 64 / element bytes elements per row: 32 for
+ *            bf16, 64 for 8-bit codes):
+ *              k_cache block  [D / w][page_size][w]   dim tile, token, dim inside the tile
+ *              v_cache block  [page_size / w][D][w]   token tile, dim, token inside the tile
+ *            i.e. K is token-major and V dim-major ("V transposed") inside 64-byte tiles; the
+ *            kernels' load instructions then cover whole 128-byte lines.  Element (token t,
+ *            dim d) of a block: K at ((d / w) * page_size + t) * w + d % w, V at
+ *            ((t / w) * D + d) * w + t % w (in elements).
  *   block_table int32 [B, block_table_stride]: physical page of logical page p of request b
  *   part_m, part_l fp32 [S, R, Hq];  part_o fp32 [S, R, Hq, D]   (R = 1 decode, q_tile prefill)
  *   out      fp32 or bf16 [rows, Hq, D]
@@ -174,8 +181,7 @@ int attn_splitkv(const void* q, const void* k_cache, const void* v_cache,
  * Split-KV decode over an 8-bit KV cache (the 8-bit cache of the pages' production precision:
  * [P3] §1 and §14 "W8A8C8", §8 attention in FP8; [P4] §一: BF16 and FP8 formats).  Same work map,
  * launch shape, partial layout and errors as attn_splitkv; only the cache differs:
- *   k_cache  uint8 [num_pages, Hkv, page_size, D]   OCP E4M3 codes, token-major per block
- *   v_cache  uint8 [num_pages, Hkv, D, page_size]   dim-major per block
+ *   k_cache, v_cache  uint8 OCP E4M3 codes in the blocked layout above (w = 64)
  *   k_scale, v_scale  device fp32[Hkv] (4-byte aligned): element x of KV head g stands for
  *                 e4m3(x) * k_scale[g] (keys) or e4m3(x) * v_scale[g] (values)
  * The codes are widened exactly to bf16 before the matrix products; q stays bf16.  Partials are in

@@ -171,6 +171,19 @@ def max_splits_of(map_host: np.ndarray) -> int:
     return int(np.max(np.diff(ptr))) if hdr["U"] > 0 else 0
 
 
+def _cache_geometry(k_cache: torch.Tensor, v_cache: torch.Tensor, head_dim: int):
+    """(num_pages, Hkv, page_size) of caches in the blocked layout (rows of 64 bytes, w elements):
+    k_cache [P, Hkv, D/w, page, w], v_cache [P, Hkv, page/w, D, w]."""
+    w = 64 // k_cache.element_size()
+    if k_cache.dim() != 5 or v_cache.dim() != 5:
+        raise ValueError("k_cache/v_cache: need the blocked layout [P, Hkv, D/w, page, w] / [P, Hkv, page/w, D, w]")
+    P, Hkv, kt, page, wk = k_cache.shape
+    if wk != w or kt * w != head_dim or page % w or tuple(v_cache.shape) != (P, Hkv, page // w, head_dim, w):
+        raise ValueError(f"k_cache {tuple(k_cache.shape)} / v_cache {tuple(v_cache.shape)} do not match the blocked "
+                         f"layout [P, Hkv, D/w, page, w] / [P, Hkv, page/w, D, w] with w = {w}, D = {head_dim}")
+    return P, Hkv, page
+
+
 def _check_decode_args(q, k_cache, v_cache, block_table, seq_lens, map_dev, num_workers, num_segments, head_groups,
                        part_m, part_l, part_o, timing, cache_dtype):
     dev = q.device
@@ -183,9 +196,7 @@ def _check_decode_args(q, k_cache, v_cache, block_table, seq_lens, map_dev, num_
     for name, t in (("part_m", part_m), ("part_l", part_l), ("part_o", part_o)):
         _need(t, torch.float32, name, dev)
     B, Hq, D = q.shape
-    P, Hkv, page, Dk = k_cache.shape
-    if tuple(v_cache.shape) != (P, Hkv, D, page) or Dk != D:
-        raise ValueError("k_cache/v_cache shapes do not match [P, Hkv, page, D] / [P, Hkv, D, page]")
+    P, Hkv, page = _cache_geometry(k_cache, v_cache, D)
     if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.numel() != B:
         raise ValueError("block_table/seq_lens do not match the batch")
     if part_m.numel() < num_segments * Hq or part_l.numel() < num_segments * Hq or \
@@ -202,8 +213,9 @@ def attn_splitkv(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, 
                  seq_lens: torch.Tensor, map_dev: torch.Tensor, num_workers: int, num_segments: int,
                  head_groups: int, softmax_scale: float, part_m: torch.Tensor, part_l: torch.Tensor,
                  part_o: torch.Tensor, timing: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Launch the split-KV decode kernel.  Layouts: q [B, Hq, D]; k_cache [P, Hkv, page, D];
-    v_cache [P, Hkv, D, page]; block_table [B, stride]; part_m/l [S, Hq]; part_o [S, Hq, D]."""
+    """Launch the split-KV decode kernel.  Layouts: q [B, Hq, D]; k_cache [P, Hkv, D/32, page, 32] and
+    v_cache [P, Hkv, page/32, D, 32] bf16 (blocked, see ``paged``); block_table [B, stride];
+    part_m/l [S, Hq]; part_o [S, Hq, D]."""
     B, Hq, D, P, Hkv, page = _check_decode_args(q, k_cache, v_cache, block_table, seq_lens, map_dev, num_workers,
                                                 num_segments, head_groups, part_m, part_l, part_o, timing,
                                                 torch.bfloat16)
@@ -219,8 +231,9 @@ def attn_splitkv_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                      num_workers: int, num_segments: int, head_groups: int, softmax_scale: float,
                      part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor,
                      timing: Optional[torch.Tensor] = None, stream=None) -> None:
-    """Launch the split-KV decode kernel over an 8-bit E4M3 cache: k_cache/v_cache uint8 codes in the
-    layouts of attn_splitkv, k_scale/v_scale float32 [Hkv] (value = e4m3(code) * scale of the head)."""
+    """Launch the split-KV decode kernel over an 8-bit E4M3 cache: k_cache [P, Hkv, D/64, page, 64] and
+    v_cache [P, Hkv, page/64, D, 64] uint8 codes (blocked, see ``paged``), k_scale/v_scale float32 [Hkv]
+    (value = e4m3(code) * scale of the head)."""
     B, Hq, D, P, Hkv, page = _check_decode_args(q, k_cache, v_cache, block_table, seq_lens, map_dev, num_workers,
                                                 num_segments, head_groups, part_m, part_l, part_o, timing,
                                                 torch.uint8)
@@ -253,10 +266,8 @@ def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     for name, t in (("part_m", part_m), ("part_l", part_l), ("part_o", part_o)):
         _need(t, torch.float32, name, dev)
     rows, Hq, D = q.shape
-    P, Hkv, page, Dk = k_cache.shape
+    P, Hkv, page = _cache_geometry(k_cache, v_cache, D)
     B = q_lens.numel()
-    if tuple(v_cache.shape) != (P, Hkv, D, page) or Dk != D:
-        raise ValueError("k_cache/v_cache shapes do not match [P, Hkv, page, D] / [P, Hkv, D, page]")
     if block_table.dim() != 2 or block_table.shape[0] != B or q_start.numel() != B or kv_lens.numel() != B:
         raise ValueError("block_table/q_start/kv_lens do not match the batch")
     if part_m.numel() < num_segments * q_tile * Hq or part_o.numel() < num_segments * q_tile * Hq * D:

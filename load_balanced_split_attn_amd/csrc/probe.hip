@@ -1,7 +1,9 @@
 // Streaming-read probe: the device's practical HBM read ceiling, measured beside the kernels.
 //
-// Each wave reads UNROLL consecutive KiB (one 16-byte load per lane per KiB) per step, steps
-// spread over the grid; all loads of a step are issued before any is used.
+// Each wave reads UNROLL consecutive KiB (one 16-byte non-temporal load per lane per KiB) per step,
+// steps spread over the grid; all loads of a step are issued before any is used.  Non-temporal
+// loads of whole lines are the fastest plain read stream measured on gfx950 (~10% above default
+// loads), so this is the ceiling a streaming kernel is compared with.
 #include "common.h"
 #include "lbsa.h"
 #include "lbsa_probe.h"
@@ -24,7 +26,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   for (; base + step_elems <= n16; base += waves * step_elems) {
     u32x4 v[UNROLL];
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) v[u] = buf[base + 64 * u + lane];
+    for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(buf + base + 64 * u + lane);
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) acc ^= v[u];
   }

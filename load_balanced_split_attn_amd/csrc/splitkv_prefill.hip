@@ -8,8 +8,8 @@
 // position kv_len - q_len + j and sees keys [0, that position].
 //
 // gfx950 design.  Workgroup = (worker w, KV head g, query head h of the group), 4 waves; wave v
-// owns the 32 query rows 32v .. 32v+31 of the unit.  Each 64-key chunk of K (token-major) and V
-// (dim-major) goes from HBM straight into LDS with buffer->LDS loads (no registers), in XOR-swizzled
+// owns the 32 query rows 32v .. 32v+31 of the unit.  Each 64-key chunk of K and V (blocked cache
+// layout) goes from HBM straight into LDS with buffer->LDS loads (no registers), in XOR-swizzled
 // layouts that the MFMA fragment reads take without bank conflicts, and is read by all four waves:
 // 128 query rows per K/V load; the eight query heads of a KV head run as eight workgroups on one
 // XCD so K/V come from one L2.  Two 32 KiB LDS stages (the next chunk streams in while the current
@@ -30,8 +30,8 @@ namespace lbsa {
 
 struct PrefillParams {
   const uint16_t* q;            // [rows, Hq, 128]
-  const uint16_t* k;            // [pages, Hkv, page, 128]
-  const uint16_t* v;            // [pages, Hkv, 128, page]
+  const uint16_t* k;            // [pages, Hkv] blocks: [4][page][32] (dim tile, key, dim)
+  const uint16_t* v;            // [pages, Hkv] blocks: [page / 32][128][32] (key tile, dim, key)
   const int32_t* block_table;   // [B, bt_stride]
   const int32_t* q_lens;        // [B]
   const int32_t* q_start;       // [B]
@@ -45,6 +45,7 @@ struct PrefillParams {
 };
 
 constexpr int kPD = 128;          // head dim
+constexpr int kRow = 64;          // bytes per row of the blocked cache layout
 constexpr int kPChunk = 64;       // keys per staged chunk
 constexpr int kQTile = 128;       // query rows per unit
 constexpr int kColBlocks = 2;     // 16-row column blocks per wave (32 rows)
@@ -177,16 +178,21 @@ void splitkv_prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) v_base[kb] = v_slot(r, 4 * kb + grp);
 
-  // byte offsets inside a (page, KV head) block; the chunk's offset in the page goes in the scalar
-  // offset, so these registers stay unchanged while earlier loads that read them are in flight
+  // byte offsets inside a (page, KV head) block of the blocked cache layout (rows of 64 bytes: K
+  // [4 dim tiles][page keys][32 dims], V [page / 32 key tiles][128 dims][32 keys]); the chunk's
+  // offset in the page goes in the scalar offset, so these registers stay unchanged while earlier
+  // loads that read them are in flight.  LDS slot `slot` of the stage takes 16-byte piece kp of
+  // key row `key` (dims 8kp .. +7) and piece vp of dim row d (chunk keys 8vp .. +7).
   int k_src[4], v_src[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int slot = 64 * (4 * wave + t) + lane;
     const int key = slot >> 4;
-    k_src[t] = (key * kPD + 8 * ((slot & 15) ^ k_swz(key))) * 2;
+    const int kp = (slot & 15) ^ k_swz(key);
+    k_src[t] = ((kp >> 2) * p.page + key) * kRow + 16 * (kp & 3);
     const int d = slot >> 3;
-    v_src[t] = (d * p.page + 8 * ((slot & 7) ^ v_swz(d))) * 2;
+    const int vp = (slot & 7) ^ v_swz(d);
+    v_src[t] = ((vp >> 2) * kPD + d) * kRow + 16 * (vp & 3);
   }
 
   for (int s = s_begin; s < s_end; ++s) {
@@ -247,11 +253,11 @@ void splitkv_prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LBSA_LDS(st + 1024 * (4 * wave + t)), 16, k_src[t],
-                                                 off * kPD * 2, 0, 0);
+                                                 off * kRow, 0, 0);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LBSA_LDS(st + kKBytes + 1024 * (4 * wave + t)), 16, v_src[t],
-                                                 off * 2, 0, 0);
+                                                 (off / 32) * kPD * kRow, 0, 0);
     };
 
     auto compute = [&](int i, const uint8_t* st) {
