@@ -75,6 +75,11 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 #ifndef LBSA_PREFILL_STAGES
 #define LBSA_PREFILL_STAGES 2
 #endif
+//   LBSA_PREFILL_KV_POLICY  cache-policy bits of the K/V loads (0: default; the 16 query tiles of a
+//                           request re-read its K/V, which the default policy keeps in L2)
+#ifndef LBSA_PREFILL_KV_POLICY
+#define LBSA_PREFILL_KV_POLICY 0
+#endif
 
 
 constexpr int kPvExact = 0;
@@ -253,11 +258,11 @@ void splitkv_prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LBSA_LDS(st + 1024 * (4 * wave + t)), 16, k_src[t],
-                                                 off * kRow, 0, 0);
+                                                 off * kRow, 0, LBSA_PREFILL_KV_POLICY);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LBSA_LDS(st + kKBytes + 1024 * (4 * wave + t)), 16, v_src[t],
-                                                 (off / 32) * kPD * kRow, 0, 0);
+                                                 (off / 32) * kPD * kRow, 0, LBSA_PREFILL_KV_POLICY);
     };
 
     auto compute = [&](int i, const uint8_t* st) {
