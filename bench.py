@@ -294,6 +294,58 @@ def bench_fp8(dev, wl, args, bf16_us: float) -> dict:
             "per_cu_busy": per_cu_busy(timing)}
 
 
+def bench_mtp(dev, base: str, args, decode_us: float) -> dict:
+    """Multi-token decode (verify step of multi-token prediction) over the same KV lengths: every
+    request carries q_len = 2 or 4 query tokens, causal among themselves; bf16 and E4M3 caches."""
+    import numpy as np
+    import torch
+
+    import load_balanced_split_attn_amd as lb
+    import workloads as WL
+    from load_balanced_split_attn_amd.mtp import MtpDecodeStep
+    from load_balanced_split_attn_amd.paged import pack_paged
+    page = 64
+    scale = 1.0 / math.sqrt(128)
+    src = WL.BY_NAME[base]()
+    rows = []
+    for fp8 in (False, True):
+        if fp8:
+            kc, vc, bt = pack_paged(src.kv_fp8, src.kv_lens, page, src.hkv, src.head_dim, src.page_permutation, dev,
+                                    dtype=torch.uint8)
+            scales = tuple(s.to(dev) for s in src.kv_scales())
+        else:
+            kc, vc, bt = pack_paged(src.kv, src.kv_lens, page, src.hkv, src.head_dim, src.page_permutation, dev)
+            scales = None
+        for q_len in ((2, 4) if not fp8 else (4,)):
+            wl = WL.mtp(q_len, base)
+            q = torch.cat([wl.q(b) for b in range(wl.batch)]).to(dev)
+            kvd = lb.KV_FP8_E4M3 if fp8 else lb.KV_BF16
+            workers = args.workers or lb.attn_query_workers(0, args.head_groups, kvd)
+            st = MtpDecodeStep(wl.q_lens, wl.kv_lens, dev, num_workers=workers, tile=args.tile,
+                               head_groups=args.head_groups, kv_dtype=kvd)
+            out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+            r = time_steps(lambda i: st.splitkv(q, kc, vc, bt, scale, kv_scales=scales), lambda i: st.combine(out),
+                           args.steps, args.warmup)
+            ms = r["total_ms"] / args.steps
+            split_ms = float(np.mean(r["split_ms"]))
+            nb = algorithmic_bytes(src, page, kv_elem=1 if fp8 else 2)
+            n_rows = sum(wl.q_lens)
+            step_bytes = nb["kv"] + nb["block_table"] + n_rows * wl.hq * wl.head_dim * (2 + 4) + 3 * wl.batch * 4
+            rows.append({"kv": "e4m3" if fp8 else "bf16", "q_len": q_len, "query_tokens": n_rows,
+                         "us_per_step": round(ms * 1e3, 2), "splitkv_us": round(split_ms * 1e3, 2),
+                         "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 2),
+                         "TB_per_s": round(step_bytes / (ms * 1e-3) / 1e12, 4),
+                         "splitkv_frac_hbm": round((step_bytes - n_rows * wl.hq * wl.head_dim * 4) /
+                                                   (split_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+            log(f"mtp {rows[-1]['kv']} q_len={q_len}: step {ms * 1e3:.1f} us, splitkv {split_ms * 1e3:.1f} us")
+            del st, q, out
+        del kc, vc
+        torch.cuda.empty_cache()
+    return {"workload": f"multi-token decode over the {base} batch's KV lengths: q_len drafted tokens per "
+                        "request (the last q_len positions, causal among themselves)",
+            "decode_us_per_step": round(decode_us, 2), "sweep": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -316,6 +368,7 @@ def main() -> int:
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the chunked-prefill report (profiling runs); prints its JSON")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit KV cache report")
+    ap.add_argument("--no-mtp", action="store_true", help="skip the multi-token decode report")
     ap.add_argument("--only-fp8", action="store_true",
                     help="run only the 8-bit KV cache report on --workload (profiling runs); prints its JSON")
     args = ap.parse_args()
@@ -460,6 +513,9 @@ def main() -> int:
 
     if not args.no_fp8:
         result["fp8_kv"] = bench_fp8(dev, wl, args, ms_per_step * 1e3)
+
+    if not args.no_mtp and wl.name != "tiny":
+        result["mtp"] = bench_mtp(dev, wl.name, args, ms_per_step * 1e3)
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(dev, [int(x) for x in args.prefill_workers.split(",")],

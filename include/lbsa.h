@@ -199,6 +199,34 @@ int attn_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache,
                      uint64_t* timing, void* stream);
 
 /*
+ * Multi-token decode (the verify step of multi-token prediction, [P3] §7: a step checks several
+ * drafted tokens at once, so a request carries a few query tokens instead of one).  Request b has
+ * q_lens[b] <= rows_per_unit query rows stored from row q_start[b] of q [rows, Hq, D]; they are the
+ * last q_lens[b] positions of its kv_lens[b]-token context, and row j sees keys
+ * [0, kv_lens[b] - q_lens[b] + j] (causal among the drafted tokens).  The map is
+ * attn_plan_prefill(q_lens, kv_lens, W, q_tile = rows_per_unit, kv_tile, causal = 1), so every request
+ * is one unit whose tiles the greedy fill spreads over workers exactly as in decode.  Launch shape
+ * as attn_splitkv; each wave runs the rows x 8 query heads of its KV head as MFMA columns (up to 16
+ * columns in one block for 2 rows, two blocks for 3 or 4), streaming K and V once for all rows.
+ *   kv_dtype      LBSA_KV_BF16 (k_scale, v_scale NULL) or LBSA_KV_FP8_E4M3 (scales as attn_splitkv_fp8)
+ *   q_lens, q_start, kv_lens  device int32[B]
+ *   rows_per_unit R, 1..4 (the map's q_tile)
+ *   part_m, part_l [S, R, Hq]; part_o [S, R, Hq, D]; rows j >= q_lens[b] of a slot are not written
+ * Merge with attn_combine(..., rows_per_unit = R, q_lens, q_start, ...).
+ * Errors: as attn_splitkv; LBSA_ERR_UNSUPPORTED for R > 4; LBSA_ERR_INVALID for a NULL
+ * q_lens/q_start, an unknown kv_dtype or scales that do not match it.  Rows past R of a request
+ * with q_lens[b] > R are not computed (the caller keeps q_lens[b] <= R).
+ */
+int attn_splitkv_mtp(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                     const float* k_scale, const float* v_scale,
+                     const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
+                     const int32_t* q_lens, const int32_t* q_start, const int32_t* kv_lens,
+                     const int32_t* map, int32_t num_workers, int32_t num_segments, int32_t head_groups,
+                     int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t page_size, int32_t rows_per_unit, float softmax_scale,
+                     float* part_m, float* part_l, float* part_o, void* stream);
+
+/*
  * Split-KV chunked-prefill kernel over a cached prefix (the greedy map of attn_plan_prefill
  * applied to prefill units; prefix reuse as in [P3] §6: a request's new chunk attends to its
  * cached prefix and, causally, to itself).  Request b has q_lens[b] query rows stored from row

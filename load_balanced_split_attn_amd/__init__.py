@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill",
-    "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_prefill", "attn_combine",
+    "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
+    "attn_combine",
     "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
 ]
 
@@ -45,6 +46,9 @@ _SIGNATURES = {
     "attn_splitkv_fp8": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                         _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                         ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "attn_splitkv_mtp": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
+                                        _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                        _c_i32, _c_i32, _c_i32, ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp]),
     "attn_combine": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                     _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, _c_vp]),
     "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
@@ -246,6 +250,50 @@ def attn_splitkv_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                                 num_workers, num_segments, head_groups, B, Hq, Hkv, D, page, float(softmax_scale),
                                 _dptr(part_m), _dptr(part_l), _dptr(part_o), _dptr(timing), _stream(stream))
     _check(st, "attn_splitkv_fp8")
+
+
+def attn_splitkv_mtp(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                     q_lens: torch.Tensor, q_start: torch.Tensor, kv_lens: torch.Tensor, map_dev: torch.Tensor,
+                     num_workers: int, num_segments: int, head_groups: int, rows_per_unit: int, softmax_scale: float,
+                     part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor, kv_scales=None,
+                     stream=None) -> None:
+    """Multi-token decode: q [rows, Hq, D] with request b's q_lens[b] <= rows_per_unit rows from row
+    q_start[b]; caches bf16, or uint8 E4M3 codes with kv_scales = (k_scale, v_scale); map from
+    attn_plan_prefill(q_lens, kv_lens, W, q_tile=rows_per_unit); part_m/l [S, R, Hq], part_o [S, R, Hq, D]."""
+    fp8 = k_cache.dtype == torch.uint8
+    dev = q.device
+    _need(q, torch.bfloat16, "q", dev)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, torch.uint8 if fp8 else torch.bfloat16, name, dev)
+    _need(block_table, torch.int32, "block_table", dev)
+    for name, t in (("q_lens", q_lens), ("q_start", q_start), ("kv_lens", kv_lens), ("map", map_dev)):
+        _need(t, torch.int32, name, dev)
+    for name, t in (("part_m", part_m), ("part_l", part_l), ("part_o", part_o)):
+        _need(t, torch.float32, name, dev)
+    rows, Hq, D = q.shape
+    P, Hkv, page = _cache_geometry(k_cache, v_cache, D)
+    B = q_lens.numel()
+    if block_table.dim() != 2 or block_table.shape[0] != B or q_start.numel() != B or kv_lens.numel() != B:
+        raise ValueError("block_table/q_start/kv_lens do not match the batch")
+    R = int(rows_per_unit)
+    if part_m.numel() < num_segments * R * Hq or part_l.numel() < num_segments * R * Hq or \
+            part_o.numel() < num_segments * R * Hq * D:
+        raise ValueError("partial buffers smaller than num_segments x rows_per_unit")
+    ks = vs = None
+    if fp8:
+        if kv_scales is None:
+            raise ValueError("an 8-bit cache needs kv_scales=(k_scale, v_scale)")
+        ks, vs = kv_scales
+        for name, t in (("k_scale", ks), ("v_scale", vs)):
+            _need(t, torch.float32, name, dev)
+            if t.numel() != Hkv:
+                raise ValueError(f"{name}: need one scale per KV head ({Hkv})")
+    st = lib().attn_splitkv_mtp(_dptr(q), _dptr(k_cache), _dptr(v_cache), KV_FP8_E4M3 if fp8 else KV_BF16,
+                                _dptr(ks), _dptr(vs), _dptr(block_table), block_table.shape[1], P, _dptr(q_lens),
+                                _dptr(q_start), _dptr(kv_lens), _dptr(map_dev), num_workers, num_segments,
+                                head_groups, B, Hq, Hkv, D, page, R, float(softmax_scale), _dptr(part_m),
+                                _dptr(part_l), _dptr(part_o), _stream(stream))
+    _check(st, "attn_splitkv_mtp")
 
 
 def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

@@ -55,9 +55,12 @@ struct DecodeParams {
   const int32_t* map;
   float* part_m;                // [S, Hq]
   float* part_l;                // [S, Hq]
-  float* part_o;                // [S, Hq, 128]
+  float* part_o;                // [S, Hq, 128]; multi-token decode: [S, R, Hq(, 128)]
+  const int32_t* q_lens;        // multi-token decode: [B] query rows of request b (else null)
+  const int32_t* q_start;       // multi-token decode: [B] first row of request b in q (else null)
   uint64_t* timing;             // [grid, 4] or null
   int32_t bt_stride, num_pages, W, S, B, Hq, Hkv, page;
+  int32_t R;                    // partial rows per slot (1 for plain decode)
   float scale_log2;             // softmax scale * log2(e)
 };
 
@@ -84,6 +87,7 @@ struct Lane {
 #define LBSA_FP8_KV_POLICY 2
 #endif
 
+
 template <int POLICY>
 __device__ __forceinline__ u32x4 buf_load(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, POLICY));
@@ -109,8 +113,11 @@ __device__ __forceinline__ u32x4 buf_load(__amdgpu_buffer_rsrc_t rs, int voff, i
 // consecutive tokens (16 bytes) of dim 16n + r.
 struct KvBf16 {
   static constexpr int kElem = 2;
+  // loop shape: issue the next chunk only when one exists.  Issuing one per computed chunk (an
+  // empty one past the end) measured the same for one query row but needs more registers: the
+  // four-row kernel then spills
+  static constexpr bool kIssuePastEnd = false;
   static constexpr int kPolicy = LBSA_DECODE_KV_POLICY;
-  static constexpr bool kIssuePastEnd = false;   // loop shape measured faster for this type
   struct Chunk {
     u32x4 k[kKB][2][4];   // k-block, S-tile, MFMA c
     u32x4 v[kKB][8];      // k-block, dim tile n: dim 16n + r, tokens first_token(kb) .. +7
@@ -159,8 +166,10 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t x) {
 // (16 bytes) of dim 16n + r, the low 8 for k-block 0 and the high 8 for 1.
 struct KvFp8 {
   static constexpr int kElem = 1;
+  // loop shape: issue one chunk per computed chunk (an empty one past the end), so the compiler's
+  // wait counts stay exact; 1-4% faster than issuing only when a next chunk exists
+  static constexpr bool kIssuePastEnd = true;
   static constexpr int kPolicy = LBSA_FP8_KV_POLICY;
-  static constexpr bool kIssuePastEnd = true;    // loop shape measured faster for this type
   struct Chunk {
     u32x4 k[kKB][2][2];   // k-block, S-tile, dim tile h: dims 64h + 16grp .. +15
     u32x4 v[8];           // dim tile n: dim 16n + r, tokens 16grp .. +15
@@ -203,7 +212,9 @@ struct KvFp8 {
 
 // ---- online softmax and the PV product ------------------------------------------------------
 
-// Online-softmax state of one wave for its 8 query heads (lane: head r; o: dims 16n + 4grp + i).
+// Online-softmax state of one wave for one 16-column block (lane: column r; o: dims 16n + 4grp + i).
+// Column r of block cb is query head 8h + (r & 7) of query row 2cb + (r >> 3); plain decode has one
+// row, so its columns 8..15 repeat the heads and are not stored.
 struct State {
   float m_ref;    // reference max the probabilities are taken against, log2 units
   float m_true;   // true running max, log2 units
@@ -213,29 +224,44 @@ struct State {
 
 constexpr float kRescaleSlack = 8.0f;
 
-template <class KV>
-__device__ __forceinline__ void compute_chunk(typename KV::Chunk& ch, State& st, const u32x4 (&qf)[4], int c0,
-                                              int kv_begin, int kv_end, float scale_log2, const Lane& ln) {
-  // scores: sc[kb][4j + i] is token c0 + first_token(kb) + 4j + i of head r
-  float sc[kKB][8];
+// One 64-token chunk for NQB column blocks.  Keys outside [kv_begin, kv_end) are masked for every
+// column; a column also masks keys at or past vis_end[cb] (the causal end of its query row).
+// edge_end is the smallest visible end of any stored row: chunks that end before it and start at or
+// after kv_begin need no mask at all.
+template <class KV, int NQB>
+__device__ __forceinline__ void compute_chunk(typename KV::Chunk& ch, State (&st)[NQB], const u32x4 (&qf)[NQB][4],
+                                              int c0, int kv_begin, int kv_end, const int (&vis_end)[NQB],
+                                              int edge_end, float scale_log2, const Lane& ln) {
+  // scores: sc[cb][kb][4j + i] is token c0 + first_token(kb) + 4j + i of column r of block cb
+  float sc[NQB][kKB][8];
 #pragma unroll
   for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc[NQB];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc = mfma16x16x32(KV::k_op(ch, kb, j, c), qf[c], acc);
+      for (int cb = 0; cb < NQB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sc[kb][4 * j + i] = acc[i] * scale_log2;
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 kop = KV::k_op(ch, kb, j, c);
+#pragma unroll
+        for (int cb = 0; cb < NQB; ++cb) acc[cb] = mfma16x16x32(kop, qf[cb][c], acc[cb]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < NQB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[cb][kb][4 * j + i] = acc[cb][i] * scale_log2;
     }
 
-  if (c0 < kv_begin || c0 + kChunk > kv_end) {
+  if (c0 < kv_begin || c0 + kChunk > edge_end) {
 #pragma unroll
     for (int kb = 0; kb < kKB; ++kb) {
       const int t0 = c0 + KV::first_token(kb, ln);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sc[kb][e] = (t0 + e < kv_begin || t0 + e >= kv_end) ? -INFINITY : sc[kb][e];
+      for (int cb = 0; cb < NQB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sc[cb][kb][e] = (t0 + e < kv_begin || t0 + e >= vis_end[cb]) ? -INFINITY : sc[cb][kb][e];
       // masked tokens may hold any bits (NaN included), and p = 0 does not cancel a NaN
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -245,59 +271,77 @@ __device__ __forceinline__ void compute_chunk(typename KV::Chunk& ch, State& st,
     }
   }
 
-  float mx = -INFINITY;
+  float m_use[NQB];
 #pragma unroll
-  for (int kb = 0; kb < kKB; ++kb)
+  for (int cb = 0; cb < NQB; ++cb) {
+    float mx = -INFINITY;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[kb][e]);
-  mx = fmaxf(mx, xor_lane(mx, 16));
-  mx = fmaxf(mx, xor_lane(mx, 32));
-  st.m_true = fmaxf(st.m_true, mx);
-  // Lazy rescaling: probabilities are taken relative to a reference max that moves only when a
-  // score exceeds it by more than kRescaleSlack (log2 units), so p <= 2^kRescaleSlack and the
-  // O accumulators are rescaled in rare, wave-uniform steps instead of every chunk.
-  const bool need = mx > st.m_ref + kRescaleSlack;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    const float m_new = need ? mx : st.m_ref;
-    const float alpha = fast_exp2(st.m_ref - m_new);   // 1 where unchanged, 0 from -inf
-    st.m_ref = m_new;
-    st.l *= alpha;
+    for (int kb = 0; kb < kKB; ++kb)
 #pragma unroll
-    for (int n = 0; n < 8; ++n) st.o[n] *= alpha;
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[cb][kb][e]);
+    mx = fmaxf(mx, xor_lane(mx, 16));
+    mx = fmaxf(mx, xor_lane(mx, 32));
+    st[cb].m_true = fmaxf(st[cb].m_true, mx);
+    // Lazy rescaling: probabilities are taken relative to a reference max that moves only when a
+    // score exceeds it by more than kRescaleSlack (log2 units), so p <= 2^kRescaleSlack and the
+    // O accumulators are rescaled in rare, wave-uniform steps instead of every chunk.
+    const bool need = mx > st[cb].m_ref + kRescaleSlack;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      // only columns whose reference moves are rescaled (0 from -inf); the others keep theirs, which
+      // may still be -inf for a column with no visible key yet (-inf - -inf would be NaN)
+      const float m_new = need ? mx : st[cb].m_ref;
+      const float alpha = need ? fast_exp2(st[cb].m_ref - m_new) : 1.f;
+      st[cb].m_ref = m_new;
+      st[cb].l *= alpha;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) st[cb].o[n] *= alpha;
+    }
+    m_use[cb] = (st[cb].m_ref == -INFINITY) ? 0.f : st[cb].m_ref;
   }
-  const float m_use = (st.m_ref == -INFINITY) ? 0.f : st.m_ref;
-  float sum = 0.f;
 #pragma unroll
   for (int kb = 0; kb < kKB; ++kb) {
-    float ps[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ps[e] = fast_exp2(sc[kb][e] - m_use);
-      sum += ps[e];
-    }
     // P split into bf16 hi + lo parts: two MFMAs keep ~16 significant bits of each probability
-    u32x4 phi, plo;
+    u32x4 phi[NQB], plo[NQB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t hv = pack_bf16(ps[2 * i], ps[2 * i + 1]);
-      phi[i] = hv;
-      plo[i] = pack_bf16(ps[2 * i] - bf16_lo(hv), ps[2 * i + 1] - bf16_hi(hv));
+    for (int cb = 0; cb < NQB; ++cb) {
+      float ps[8];
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ps[e] = fast_exp2(sc[cb][kb][e] - m_use[cb]);
+        sum += ps[e];
+      }
+      st[cb].l += sum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t hv = pack_bf16(ps[2 * i], ps[2 * i + 1]);
+        phi[cb][i] = hv;
+        plo[cb][i] = pack_bf16(ps[2 * i] - bf16_lo(hv), ps[2 * i + 1] - bf16_hi(hv));
+      }
     }
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const u32x4 vop = KV::v_op(ch, kb, n);
-      st.o[n] = mfma16x16x32(vop, phi, st.o[n]);
-      st.o[n] = mfma16x16x32(vop, plo, st.o[n]);
+#pragma unroll
+      for (int cb = 0; cb < NQB; ++cb) {
+        st[cb].o[n] = mfma16x16x32(vop, phi[cb], st[cb].o[n]);
+        st[cb].o[n] = mfma16x16x32(vop, plo[cb], st[cb].o[n]);
+      }
     }
   }
-  st.l += sum;
 }
 
 // ---- the kernel -----------------------------------------------------------------------------
 
-template <class KV, int WAVES>
+// ROWS = 1: plain decode (one query row per request, row b of q, partial rows R = 1).  ROWS = 2 or 4:
+// up to ROWS query rows per request (multi-token decode): request b's q_lens[b] rows start at row
+// q_start[b] of q and are the last q_lens[b] positions of its context, row j seeing keys
+// [0, kv_len - q_len + j]; the map comes from attn_plan_prefill with q_tile = R >= q_lens[b], and
+// the partials have R rows per slot.
+template <class KV, int WAVES, int ROWS>
 __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams p) {
   using Chunk = typename KV::Chunk;
+  constexpr int NQB = ROWS <= 2 ? 1 : 2;   // 16-column blocks: 8 heads x 2 rows each
   const int lane = threadIdx.x & 63;
   // wave index is uniform across the wave; say so, so page addressing stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -327,23 +371,38 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
     const int kv_begin = segs[4 * s + 2];
     int kv_end = segs[4 * s + 3];
     if (b < 0 || b >= p.B) continue;
-    kv_end = min(kv_end, p.seq_lens[b]);
+    if (ROWS > 1 && segs[4 * s + 1] != 0) continue;   // every request is one unit of R rows
+    const int kv_len = p.seq_lens[b];
+    kv_end = min(kv_end, kv_len);
     kv_end = min(kv_end, p.bt_stride * p.page);
+    const int q_len = ROWS > 1 ? min(p.q_lens[b], p.R) : 1;
+    if (q_len <= 0) continue;
+    const int q_row0 = ROWS > 1 ? p.q_start[b] : b;
 
-    // Q^T fragments: column r = query head 8h + (r & 7), k = dims q_dim(c) .. +7
-    u32x4 qf[4];
-    {
-      const uint16_t* qp = p.q + ((size_t)b * p.Hq + h * 8 + (ln.r & 7)) * kD;
+    // Q^T fragments: column r of block cb = query head 8h + (r & 7) of row 2cb + (r >> 3) (zero for
+    // rows past q_len), k = dims q_dim(c) .. +7; vis_end = the column's causal key end
+    u32x4 qf[NQB][4];
+    int vis_end[NQB];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) qf[c] = ld16(qp + KV::q_dim(c, ln));
+    for (int cb = 0; cb < NQB; ++cb) {
+      const int row = ROWS > 1 ? 2 * cb + (ln.r >> 3) : 0;
+      const bool ok = row < q_len;
+      const uint16_t* qp = p.q + ((size_t)(q_row0 + (ok ? row : 0)) * p.Hq + h * 8 + (ln.r & 7)) * kD;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qf[cb][c] = ok ? ld16(qp + KV::q_dim(c, ln)) : u32x4{0u, 0u, 0u, 0u};
+      vis_end[cb] = ok ? min(kv_end, kv_len - q_len + row + 1) : kv_end;
     }
+    const int edge_end = ROWS > 1 ? min(kv_end, kv_len - q_len + 1) : kv_end;
 
-    State st;
-    st.m_ref = -INFINITY;
-    st.m_true = -INFINITY;
-    st.l = 0.f;
+    State st[NQB];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < NQB; ++cb) {
+      st[cb].m_ref = -INFINITY;
+      st[cb].m_true = -INFINITY;
+      st[cb].l = 0.f;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) st[cb].o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // block-table window: lane i holds the physical page of logical page win + i
     const int32_t* bt_row = p.block_table + (size_t)b * p.bt_stride;
@@ -396,11 +455,11 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
         // empty), so the compiler's wait counts stay exact through the loop
         while (true) {
           issue(B, c + kChunk < kv_end);
-          compute_chunk<KV>(A, st, qf, c, kv_begin, kv_end, s_log2, ln);
+          compute_chunk<KV, NQB>(A, st, qf, c, kv_begin, kv_end, vis_end, edge_end, s_log2, ln);
           c += kChunk;
           if (c >= kv_end) break;
           issue(A, c + kChunk < kv_end);
-          compute_chunk<KV>(B, st, qf, c, kv_begin, kv_end, s_log2, ln);
+          compute_chunk<KV, NQB>(B, st, qf, c, kv_begin, kv_end, vis_end, edge_end, s_log2, ln);
           c += kChunk;
           if (c >= kv_end) break;
         }
@@ -409,13 +468,13 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
           int cn = c + kChunk;
           bool more = cn < kv_end;
           if (more) issue(B, true);
-          compute_chunk<KV>(A, st, qf, c, kv_begin, kv_end, s_log2, ln);
+          compute_chunk<KV, NQB>(A, st, qf, c, kv_begin, kv_end, vis_end, edge_end, s_log2, ln);
           c = cn;
           if (!more) break;
           cn = c + kChunk;
           more = cn < kv_end;
           if (more) issue(A, true);
-          compute_chunk<KV>(B, st, qf, c, kv_begin, kv_end, s_log2, ln);
+          compute_chunk<KV, NQB>(B, st, qf, c, kv_begin, kv_end, vis_end, edge_end, s_log2, ln);
           c = cn;
           if (!more) break;
         }
@@ -424,22 +483,26 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
 
     // express the partial against the true max: m = max score, l and o scaled to match; o also
     // takes the V scale of an 8-bit cache
-    const float to_true = (st.m_true == -INFINITY) ? 0.f : fast_exp2(st.m_ref - st.m_true);
-    const float o_mul = to_true * o_scale;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) st.o[n] *= o_mul;
-    float l = st.l * to_true;
-    l += xor_lane(l, 16);
-    l += xor_lane(l, 32);
-    if (ln.r < 8) {
-      const size_t row = (size_t)s * p.Hq + h * 8 + ln.r;
-      if (ln.grp == 0) {
-        p.part_m[row] = (st.m_true == -INFINITY) ? -INFINITY : st.m_true * kLn2;
-        p.part_l[row] = l;
+    for (int cb = 0; cb < NQB; ++cb) {
+      const float to_true = (st[cb].m_true == -INFINITY) ? 0.f : fast_exp2(st[cb].m_ref - st[cb].m_true);
+      const float o_mul = to_true * o_scale;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) st[cb].o[n] *= o_mul;
+      float l = st[cb].l * to_true;
+      l += xor_lane(l, 16);
+      l += xor_lane(l, 32);
+      const int row = ROWS > 1 ? 2 * cb + (ln.r >> 3) : (ln.r >> 3);
+      if (row < q_len) {
+        const size_t slot = ((size_t)s * (ROWS > 1 ? p.R : 1) + row) * p.Hq + h * 8 + (ln.r & 7);
+        if (ln.grp == 0) {
+          p.part_m[slot] = (st[cb].m_true == -INFINITY) ? -INFINITY : st[cb].m_true * kLn2;
+          p.part_l[slot] = l;
+        }
+        float* dst = p.part_o + slot * kD + 4 * ln.grp;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) *reinterpret_cast<f32x4*>(dst + 16 * n) = st[cb].o[n];
       }
-      float* dst = p.part_o + row * kD + 4 * ln.grp;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) *reinterpret_cast<f32x4*>(dst + 16 * n) = st.o[n];
     }
   }
 
@@ -459,37 +522,52 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
   }
 }
 
-template <class KV, int WAVES>
+template <class KV, int WAVES, int ROWS>
 hipError_t launch_decode(const DecodeParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((splitkv_decode_kernel<KV, WAVES>), dim3(grid), dim3(64 * WAVES), 0, stream, p);
+  hipLaunchKernelGGL((splitkv_decode_kernel<KV, WAVES, ROWS>), dim3(grid), dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
+}
+
+template <class KV, int ROWS>
+hipError_t launch_waves(const DecodeParams& p, int waves, int grid, hipStream_t stream) {
+  switch (waves) {
+    case 1: return launch_decode<KV, 1, ROWS>(p, grid, stream);
+    case 2: return launch_decode<KV, 2, ROWS>(p, grid, stream);
+    case 4: return launch_decode<KV, 4, ROWS>(p, grid, stream);
+    default: return launch_decode<KV, 8, ROWS>(p, grid, stream);
+  }
 }
 
 template <class KV, int WAVES>
 int decode_blocks_per_cu() {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, splitkv_decode_kernel<KV, WAVES>, 64 * WAVES, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, splitkv_decode_kernel<KV, WAVES, 1>, 64 * WAVES, 0) !=
       hipSuccess)
     return 0;
   return nb;
 }
 
+// rows_per_unit = 1 with q_lens == null: plain decode; otherwise multi-token decode with up to
+// rows_per_unit (<= 4) query rows per request.
 template <class KV>
 int splitkv_launch(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
                    const float* v_scale, const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
-                   const int32_t* seq_lens, const int32_t* map, int32_t num_workers, int32_t num_segments,
-                   int32_t head_groups, int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                   int32_t page_size, float softmax_scale, float* part_m, float* part_l, float* part_o,
-                   uint64_t* timing, void* stream) {
+                   const int32_t* q_lens, const int32_t* q_start, const int32_t* seq_lens, const int32_t* map,
+                   int32_t num_workers, int32_t num_segments, int32_t head_groups, int32_t B, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t rows_per_unit,
+                   float softmax_scale, float* part_m, float* part_l, float* part_o, uint64_t* timing,
+                   void* stream) {
   if (num_workers < 1 || num_segments < 0 || B < 0 || head_groups < 1 || num_kv_heads < 1 ||
-      num_pages < 1 || block_table_stride < 0 || page_size < 1)
+      num_pages < 1 || block_table_stride < 0 || page_size < 1 || rows_per_unit < 1)
     return LBSA_ERR_INVALID;
   if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !map) return LBSA_ERR_INVALID;
+  if ((q_lens == nullptr) != (q_start == nullptr)) return LBSA_ERR_INVALID;
+  if (!q_lens && rows_per_unit != 1) return LBSA_ERR_INVALID;
   if (num_segments > 0 && (!part_m || !part_l || !part_o)) return LBSA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(part_o)) & 15)
     return LBSA_ERR_INVALID;
-  if (head_dim != kD || num_q_heads != 8 * num_kv_heads || page_size % kMinPage != 0)
+  if (head_dim != kD || num_q_heads != 8 * num_kv_heads || page_size % kMinPage != 0 || rows_per_unit > 4)
     return LBSA_ERR_UNSUPPORTED;
   if (num_kv_heads % head_groups) return LBSA_ERR_INVALID;
   const int waves = num_kv_heads / head_groups;
@@ -509,6 +587,8 @@ int splitkv_launch(const void* q, const void* k_cache, const void* v_cache, cons
   p.part_m = part_m;
   p.part_l = part_l;
   p.part_o = part_o;
+  p.q_lens = q_lens;
+  p.q_start = q_start;
   p.timing = timing;
   p.bt_stride = block_table_stride;
   p.num_pages = num_pages;
@@ -518,18 +598,19 @@ int splitkv_launch(const void* q, const void* k_cache, const void* v_cache, cons
   p.Hq = num_q_heads;
   p.Hkv = num_kv_heads;
   p.page = page_size;
+  p.R = rows_per_unit;
   p.scale_log2 = softmax_scale * kLog2e;
 
   const int64_t grid = (int64_t)num_workers * head_groups;
   if (grid > INT32_MAX) return LBSA_ERR_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
-  switch (waves) {
-    case 1: err = launch_decode<KV, 1>(p, (int)grid, st); break;
-    case 2: err = launch_decode<KV, 2>(p, (int)grid, st); break;
-    case 4: err = launch_decode<KV, 4>(p, (int)grid, st); break;
-    default: err = launch_decode<KV, 8>(p, (int)grid, st); break;
-  }
+  if (!q_lens)
+    err = launch_waves<KV, 1>(p, waves, (int)grid, st);
+  else if (rows_per_unit <= 2)
+    err = launch_waves<KV, 2>(p, waves, (int)grid, st);
+  else
+    err = launch_waves<KV, 4>(p, waves, (int)grid, st);
   return err == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;
 }
 
@@ -555,9 +636,9 @@ extern "C" int attn_splitkv(const void* q, const void* k_cache, const void* v_ca
                             float softmax_scale, float* part_m, float* part_l, float* part_o,
                             uint64_t* timing, void* stream) {
   return splitkv_launch<KvBf16>(q, k_cache, v_cache, nullptr, nullptr, block_table, block_table_stride, num_pages,
-                                seq_lens, map, num_workers, num_segments, head_groups, B, num_q_heads,
-                                num_kv_heads, head_dim, page_size, softmax_scale, part_m, part_l, part_o, timing,
-                                stream);
+                                nullptr, nullptr, seq_lens, map, num_workers, num_segments, head_groups, B,
+                                num_q_heads, num_kv_heads, head_dim, page_size, 1, softmax_scale, part_m, part_l,
+                                part_o, timing, stream);
 }
 
 extern "C" int attn_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
@@ -570,8 +651,34 @@ extern "C" int attn_splitkv_fp8(const void* q, const void* k_cache, const void* 
   if (!k_scale || !v_scale) return LBSA_ERR_INVALID;
   if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3) return LBSA_ERR_INVALID;
   return splitkv_launch<KvFp8>(q, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride, num_pages,
-                               seq_lens, map, num_workers, num_segments, head_groups, B, num_q_heads, num_kv_heads,
-                               head_dim, page_size, softmax_scale, part_m, part_l, part_o, timing, stream);
+                               nullptr, nullptr, seq_lens, map, num_workers, num_segments, head_groups, B,
+                               num_q_heads, num_kv_heads, head_dim, page_size, 1, softmax_scale, part_m, part_l,
+                               part_o, timing, stream);
+}
+
+extern "C" int attn_splitkv_mtp(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                                const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                int32_t block_table_stride, int32_t num_pages, const int32_t* q_lens,
+                                const int32_t* q_start, const int32_t* kv_lens, const int32_t* map,
+                                int32_t num_workers, int32_t num_segments, int32_t head_groups, int32_t B,
+                                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                int32_t rows_per_unit, float softmax_scale, float* part_m, float* part_l,
+                                float* part_o, void* stream) {
+  if (!q_lens || !q_start) return LBSA_ERR_INVALID;
+  if (kv_dtype == LBSA_KV_BF16) {
+    if (k_scale || v_scale) return LBSA_ERR_INVALID;
+    return splitkv_launch<KvBf16>(q, k_cache, v_cache, nullptr, nullptr, block_table, block_table_stride,
+                                  num_pages, q_lens, q_start, kv_lens, map, num_workers, num_segments, head_groups,
+                                  B, num_q_heads, num_kv_heads, head_dim, page_size, rows_per_unit, softmax_scale,
+                                  part_m, part_l, part_o, nullptr, stream);
+  }
+  if (kv_dtype != LBSA_KV_FP8_E4M3) return LBSA_ERR_INVALID;
+  if (!k_scale || !v_scale) return LBSA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3) return LBSA_ERR_INVALID;
+  return splitkv_launch<KvFp8>(q, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride, num_pages,
+                               q_lens, q_start, kv_lens, map, num_workers, num_segments, head_groups, B,
+                               num_q_heads, num_kv_heads, head_dim, page_size, rows_per_unit, softmax_scale, part_m,
+                               part_l, part_o, nullptr, stream);
 }
 
 extern "C" int attn_query_workers(int device, int32_t head_groups, int32_t kv_dtype, int32_t* num_workers_out) {

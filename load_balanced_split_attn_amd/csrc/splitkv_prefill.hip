@@ -325,8 +325,11 @@ void splitkv_prefill_kernel(PrefillParams p) {
       if (__builtin_amdgcn_ballot_w64(any_rescale)) {
 #pragma unroll
         for (int cb = 0; cb < kColBlocks; ++cb) {
-          const float m_new = (mxs[cb] > m_ref[cb] + slack_raw) ? mxs[cb] : m_ref[cb];
-          const float alpha = fast_exp2((m_ref[cb] - m_new) * c);   // 1 where unchanged, 0 from -inf
+          // only rows whose reference moves are rescaled (0 from -inf); the others keep theirs, which
+          // may still be -inf for a row with no visible key yet (-inf - -inf would be NaN)
+          const bool move = mxs[cb] > m_ref[cb] + slack_raw;
+          const float m_new = move ? mxs[cb] : m_ref[cb];
+          const float alpha = move ? fast_exp2((m_ref[cb] - m_new) * c) : 1.f;
           m_ref[cb] = m_new;
           lsum[cb] *= alpha;
 #pragma unroll

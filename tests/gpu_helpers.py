@@ -100,3 +100,39 @@ def oracle_decode_fp8(wl: WL.Workload, requests=None, scale=SCALE):
         k, v = wl.kv_fp8(b)
         out[b] = ref_decode_fp8(q[b:b + 1], [k.numpy()], [v.numpy()], ks, vs, scale)[0]
     return out
+
+
+def mtp_inputs(wl: WL.Workload, device="cuda", page=64, fp8=False, pad=0.0):
+    """Rows of every request concatenated (q_start order), the paged caches and the block table
+    (plus per-head scales for an 8-bit cache)."""
+    rows = [wl.q(b) for b in range(wl.batch)]
+    q = torch.cat(rows, dim=0).to(device) if sum(wl.q_lens) else torch.zeros((1, wl.hq, wl.head_dim),
+                                                                                dtype=torch.bfloat16, device=device)
+    if fp8:
+        kc, vc, bt = pack_paged(wl.kv_fp8, wl.kv_lens, page, wl.hkv, wl.head_dim, wl.page_permutation, device,
+                                pad_value=pad, dtype=torch.uint8)
+        ks, vs = wl.kv_scales()
+        return q, kc, vc, bt, (ks.to(device), vs.to(device))
+    kc, vc, bt = pack_paged(wl.kv, wl.kv_lens, page, wl.hkv, wl.head_dim, wl.page_permutation, device,
+                            pad_value=pad)
+    return q, kc, vc, bt, None
+
+
+def oracle_mtp(wl: WL.Workload, requests=None, fp8=False, scale=SCALE):
+    """fp64 oracle: request b's q_len rows as the last positions of its context, causal.  {b: [q_len, Hq, D]}"""
+    from oracle.fp8 import dequantize_kv
+    out = {}
+    if fp8:
+        ks, vs = (s.to(torch.float64).numpy() for s in wl.kv_scales())
+    for b in (range(wl.batch) if requests is None else requests):
+        if wl.q_lens[b] == 0:
+            continue
+        q = wl.q(b).to(torch.float64).numpy()
+        if fp8:
+            kc, vc = wl.kv_fp8(b)
+            k, v = dequantize_kv(kc.numpy(), ks), dequantize_kv(vc.numpy(), vs)
+        else:
+            kt, vt = wl.kv(b)
+            k, v = kt.to(torch.float64).numpy(), vt.to(torch.float64).numpy()
+        out[b] = ref_attention(q, k, v, scale, causal=True)
+    return out

@@ -66,6 +66,21 @@ def test_no_prefix_is_textbook_causal():
     _check_all(wl, got)
 
 
+@pytest.mark.parametrize("exact_pv", [False, True])
+def test_segment_boundary_inside_a_wave(exact_pv):
+    """Regression: a 128-row chunk after a 1000-token prefix sees keys up to 1000..1127, so the
+    worker boundary at key 1024 (three 512-key tiles, one per worker) falls inside the rows of the
+    first wave.  In the last segment rows 0..23 of that wave see no key while rows 24..31 do; the
+    rows without a key must keep an empty partial while the others rescale."""
+    wl = WL.Workload("boundary_in_wave", 250, [1128, 700], [128, 60], kind="prefill",
+                     meta={"prefix": [1000, 640]})
+    note(f"segment boundary inside a wave, exact_pv={exact_pv}")
+    got, step = _run(wl, 3, poison=True, exact_pv=exact_pv)
+    segs = step.map_host[-4 * step.S:].reshape(-1, 4)
+    assert any(s[0] == 0 and s[2] == 1024 for s in segs)
+    _check_all(wl, got)
+
+
 def test_exact_pv_agrees_with_fp16_pv():
     """Both P.V precisions give the same attention to well inside the tolerance."""
     wl = WL.random_prefill(10, 3, 2500, 300)

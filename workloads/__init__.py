@@ -70,7 +70,7 @@ class Workload:
     workload_id: int
     kv_lens: List[int]
     q_lens: List[int]                 # 1 per request for decode
-    kind: str = "decode"              # "decode" or "prefill"
+    kind: str = "decode"              # "decode" (one query row), "prefill" or "mtp" (q_lens rows each)
     workers: Optional[int] = None     # fixed worker count (None: from the device)
     paged: bool = True                # False: identity block table (contiguous pages)
     hq: int = HQ
@@ -83,7 +83,8 @@ class Workload:
         return len(self.kv_lens)
 
     def q(self, b: Optional[int] = None) -> torch.Tensor:
-        """Decode: all queries [B, Hq, D].  Prefill: request b's chunk [q_len_b, Hq, D]."""
+        """Decode: all queries [B, Hq, D].  Prefill and multi-token decode: request b's rows
+        [q_len_b, Hq, D]."""
         if self.kind == "decode":
             return randn_bf16((self.batch, self.hq, self.head_dim), seed_for(self.workload_id, STREAM_Q))
         return randn_bf16((self.q_lens[b], self.hq, self.head_dim), seed_for(self.workload_id, STREAM_Q, b))
@@ -187,6 +188,23 @@ def random_prefill(seed: int, batch: int, max_prefix: int, max_chunk: int) -> Wo
     chunk = torch.randint(1, max_chunk + 1, (batch,), generator=g).tolist()
     return Workload(f"random_prefill_{seed}", 200 + seed, [p + c for p, c in zip(prefix, chunk)], chunk,
                     kind="prefill", meta={"prefix": prefix})
+
+
+def mtp(q_len: int = 4, base: str = "mixed") -> Workload:
+    """Multi-token decode over the KV lengths of a decode batch: every request verifies q_len drafted
+    tokens (its last q_len positions), as in a multi-token-prediction step ([P3] §7)."""
+    src = BY_NAME[base]()
+    return Workload(f"mtp{q_len}_{base}", 300 + src.workload_id, list(src.kv_lens), [q_len] * src.batch, kind="mtp")
+
+
+def random_mtp(seed: int, batch: int, max_len: int, max_q: int = 4, min_len: int = 4) -> Workload:
+    """Small seeded multi-token decode batches: ragged KV lengths and 0..max_q query rows each."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed_for(400 + seed, STREAM_LENGTHS))
+    lens = torch.randint(min_len, max_len + 1, (batch,), generator=g).tolist()
+    qs = torch.randint(0, max_q + 1, (batch,), generator=g).tolist()
+    qs = [min(q, L) for q, L in zip(qs, lens)]
+    return Workload(f"random_mtp_{seed}", 400 + seed, lens, qs, kind="mtp")
 
 
 BY_NAME = {"tiny": tiny, "uniform": uniform, "mixed": mixed, "long_tail": long_tail, "prefill": prefill}
