@@ -137,6 +137,17 @@ def test_errors_and_capacity(L):
                                 128, 64, 1.0, None, None, None, None, None) == -1
     assert lib.attn_splitkv_fp8(dummy, dummy, dummy, dummy, dummy, dummy, 1, 1, dummy, dummy, 4, 0, 8, 1, 64, 8,
                                 96, 64, 1.0, None, None, None, None, None) == -3
+    # multi-token decode: q_lens/q_start required, kv_dtype and scales must agree, at most 4 rows
+    def mtp(kv_dtype, ks, vs, q_lens, rows, head_dim=128):
+        return lib.attn_splitkv_mtp(dummy, dummy, dummy, kv_dtype, ks, vs, dummy, 1, 1, q_lens, q_lens, dummy,
+                                    dummy, 4, 0, 8, 1, 64, 8, head_dim, 64, rows, 1.0, None, None, None, None)
+    assert mtp(0, None, None, None, 2) == -1
+    assert mtp(5, None, None, dummy, 2) == -1
+    assert mtp(0, dummy, dummy, dummy, 2) == -1
+    assert mtp(1, None, None, dummy, 2) == -1
+    assert mtp(0, None, None, dummy, 5) == -3
+    assert mtp(1, dummy, dummy, dummy, 0) == -1
+    assert mtp(0, None, None, dummy, 2, head_dim=64) == -3
     out = ctypes.c_int32(0)
     assert lib.attn_query_workers(0, 8, 7, ctypes.byref(out)) == -1
     assert lib.attn_query_workers(0, 3, 0, ctypes.byref(out)) == -1
