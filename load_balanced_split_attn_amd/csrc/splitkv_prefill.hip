@@ -425,31 +425,42 @@ void splitkv_prefill_kernel(PrefillParams p) {
       }
     }
 #else
+    // V^T of the chunk in stage st to fp16, in place: each thread converts the granules its own
+    // buffer->LDS loads wrote, so only its own loads need to have landed
+    auto to_f16 = [&](uint8_t* st) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        u32x4* gp = reinterpret_cast<u32x4*>(st + kKBytes + 1024 * (4 * wave + t) + 16 * lane);
+        u32x4 x = *gp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
+        *gp = x;
+      }
+    };
     // one pipeline step: start chunk i+1's DMA into the other stage (last read by chunk i-1,
-    // finished by every wave before the previous barrier), compute chunk i, wait, barrier
+    // finished by every wave before the previous barrier), compute chunk i, wait for the DMA,
+    // convert chunk i+1's V (fp16 path), barrier: one barrier per chunk makes chunk i+1 ready for
+    // every wave and releases chunk i's stage
     auto step = [&](int i, uint8_t* cur, uint8_t* ahead) {
       const bool more = i + 1 < n_chunks;
-      if constexpr (PV == kPvF16) {
-        // V^T of chunk i to fp16, in place: each thread converts the granules its own loads wrote
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          u32x4* gp = reinterpret_cast<u32x4*>(cur + kKBytes + 1024 * (4 * wave + t) + 16 * lane);
-          u32x4 x = *gp;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
-          *gp = x;
-        }
-        LBSA_WAIT_VM_LGKM(0, 0);
-        __builtin_amdgcn_s_barrier();
-      }
       if (more) dma(i + 1, ahead);
       compute(i, cur);
+      if constexpr (PV == kPvF16) {
+        if (more) {
+          LBSA_WAIT_VM_LGKM(0, 15);
+          to_f16(ahead);
+        }
+      }
       LBSA_WAIT_VM_LGKM(0, 0);
       __builtin_amdgcn_s_barrier();
     };
 
     if (n_chunks > 0) {
       dma(0, stage0);
+      if constexpr (PV == kPvF16) {
+        LBSA_WAIT_VM_LGKM(0, 15);
+        to_f16(stage0);
+      }
       LBSA_WAIT_VM_LGKM(0, 0);
       __builtin_amdgcn_s_barrier();
       for (int i = 0; i < n_chunks; i += 2) {
