@@ -267,6 +267,19 @@ def bench_fp8(dev, wl, args, bf16_us: float) -> dict:
     step = DecodeStep(wl.kv_lens, dev, num_workers=workers, tile=args.tile, head_groups=args.head_groups,
                       kv_dtype=lb.KV_FP8_E4M3)
     out = torch.empty((wl.batch, wl.hq, wl.head_dim), dtype=torch.float32, device=dev)
+    # the same map built on the device (attn_plan_device), timed with events on the stream
+    lens_d = torch.tensor(wl.kv_lens, dtype=torch.int32, device=dev)
+    map_d = torch.zeros(lb.device_map_words(wl.batch, workers), dtype=torch.int32, device=dev)
+    for _ in range(3):
+        lb.attn_plan_device(lens_d, workers, args.tile, map_d)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        lb.attn_plan_device(lens_d, workers, args.tile, map_d)
+    e1.record()
+    torch.cuda.synchronize()
+    plan_device_us = e0.elapsed_time(e1) / 20 * 1e3
+    plan_device_exact = bool(np.array_equal(map_d.cpu().numpy()[:len(step.map_host)], step.map_host))
 
     def split(i):
         k_, v_ = caches[i % copies]
@@ -421,6 +434,19 @@ def main() -> int:
         lb.attn_plan(wl.kv_lens, workers, args.tile)
     plan_us = (time.perf_counter() - t) / 100 * 1e6
     out = torch.empty((wl.batch, wl.hq, wl.head_dim), dtype=torch.float32, device=dev)
+    # the same map built on the device (attn_plan_device), timed with events on the stream
+    lens_d = torch.tensor(wl.kv_lens, dtype=torch.int32, device=dev)
+    map_d = torch.zeros(lb.device_map_words(wl.batch, workers), dtype=torch.int32, device=dev)
+    for _ in range(3):
+        lb.attn_plan_device(lens_d, workers, args.tile, map_d)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        lb.attn_plan_device(lens_d, workers, args.tile, map_d)
+    e1.record()
+    torch.cuda.synchronize()
+    plan_device_us = e0.elapsed_time(e1) / 20 * 1e3
+    plan_device_exact = bool(np.array_equal(map_d.cpu().numpy()[:len(step.map_host)], step.map_host))
 
     def split(i):
         k_, v_ = caches[i % copies]
@@ -455,7 +481,8 @@ def main() -> int:
                      "kernel_source_digest": kernel_source_digest()},
         "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 2),
         "plan": {"host_us": round(plan_us, 2), "map_words": int(len(step.map_host)),
-                 "first_plan_and_upload_s": round(plan_s, 4)},
+                 "first_plan_and_upload_s": round(plan_s, 4), "device_us": round(plan_device_us, 2),
+                 "device_map_equals_host": plan_device_exact},
     }
 
     # per-CU busy spread from the in-kernel timestamps (separate, instrumented run)

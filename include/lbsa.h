@@ -110,6 +110,24 @@ int attn_plan(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t t
               int32_t* map, int32_t map_capacity, int32_t* map_words_out);
 
 /*
+ * The attn_plan map built on the device, for serving loops whose lengths live on the GPU and for
+ * capture in a HIP graph together with the attention launches (the pages build the map once per
+ * step before every layer's attention, [P4] §二.1; [P3] §3.1 方案 steps 1-4).  One workgroup
+ * writes, on `stream`, exactly the buffer attn_plan writes for the same lengths.
+ *   seq_lens      device int32[B]
+ *   map           device int32[map_capacity]; attn_map_words(B, W, INT64_MAX) words always
+ *                 suffice (S <= W + B - 1)
+ * Host-side errors (returned): LBSA_ERR_INVALID (B < 0, W < 1, tile < 1, NULL pointers),
+ * LBSA_ERR_CAPACITY (capacity below the map's fixed part, 8 + W+1 + B+1 + 2B words), LBSA_ERR_HIP.
+ * Data errors are written to the device map instead, since the lengths are only known there:
+ * map[0] = LBSA_MAP_VERSION on success, LBSA_ERR_INVALID for a negative length or more than
+ * INT32_MAX tiles, LBSA_ERR_CAPACITY (with map[4] = the segment count needed) when the segments do
+ * not fit.  Split and combine kernels given a map whose map[0] is not LBSA_MAP_VERSION do nothing.
+ */
+int attn_plan_device(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile,
+                     int32_t* map, int32_t map_capacity, void* stream);
+
+/*
  * Static split-KV map, the imbalance baseline ([P3] §3.1 问题; [P4] §二.1: one
  * fixed split granularity for the whole batch).  Request b is cut into
  * k_b = min(num_splits, n_b) tile-aligned chunks whose tile counts differ by at

@@ -16,7 +16,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill",
+    "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill", "attn_plan_device",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
     "attn_combine",
     "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
@@ -40,6 +40,7 @@ _SIGNATURES = {
     "attn_plan_prefill": (ctypes.c_int, [_c_i32p, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                          _c_i32p, _c_i32, _c_i32p]),
     "attn_query_workers": (ctypes.c_int, [ctypes.c_int, _c_i32, _c_i32, _c_i32p]),
+    "attn_plan_device": (ctypes.c_int, [_c_vp, _c_i32, _c_i32, _c_i32, _c_vp, _c_i32, _c_vp]),
     "attn_splitkv": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                     ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
@@ -137,6 +138,22 @@ def attn_plan_prefill(q_lens: Sequence[int], kv_lens: Sequence[int], num_workers
         raise ValueError("q_lens and kv_lens differ in length")
     return _plan_call(lib().attn_plan_prefill, "attn_plan_prefill", _ptr_i32(ql), _ptr_i32(kl), len(ql),
                       num_workers, q_tile, kv_tile, int(bool(causal)))
+
+
+def attn_plan_device(seq_lens: torch.Tensor, num_workers: int, tile: int, map_dev: torch.Tensor,
+                     stream=None) -> None:
+    """Build the attn_plan map on the device (asynchronous, on the stream) from device lengths
+    seq_lens int32[B] into map_dev int32[capacity]; map_dev[0] reports data errors (see lbsa.h)."""
+    _need(seq_lens, torch.int32, "seq_lens", map_dev.device)
+    _need(map_dev, torch.int32, "map", map_dev.device)
+    st = lib().attn_plan_device(_dptr(seq_lens), seq_lens.numel(), num_workers, tile, _dptr(map_dev), map_dev.numel(),
+                                _stream(stream))
+    _check(st, "attn_plan_device")
+
+
+def device_map_words(num_units: int, num_workers: int) -> int:
+    """Map words that always suffice for a device-built decode map (S <= W + U - 1)."""
+    return attn_map_words(num_units, num_workers, 2**62)
 
 
 def attn_query_workers(device: int = 0, head_groups: int = 8, kv_dtype: int = KV_BF16) -> int:

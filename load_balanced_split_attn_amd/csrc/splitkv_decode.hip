@@ -359,6 +359,7 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
   uint64_t t_start = 0;
   if (p.timing && threadIdx.x == 0) t_start = realtime();
 
+  if (p.map[0] != LBSA_MAP_VERSION) return;   // a device-built map that reported an error
   const int U = p.map[7];
   const int32_t* worker_ptr = p.map + 8;
   const int32_t* segs = p.map + 8 + (p.W + 1) + (U + 1) + 2 * U;

@@ -71,3 +71,63 @@ class DecodeStep:
         self.splitkv(q, k_cache, v_cache, block_table, scale, timing=timing, stream=stream, kv_scales=kv_scales)
         self.combine(out, stream=stream)
         return out
+
+
+class DeviceDecodeStep:
+    """Decode with the work map built on the device.
+
+    The lengths stay on the GPU (``seq_lens``, int32[B]; update them in place), and ``plan``,
+    ``splitkv`` and ``combine`` are stream-ordered kernel launches with no host synchronisation,
+    so a whole step can be captured in one HIP graph and replayed with new lengths.  Buffers are
+    sized for the worst case: the map for S <= W + B - 1 segments, the partials likewise.
+    """
+
+    def __init__(self, batch: int, device, num_workers: Optional[int] = None, tile: int = 512,
+                 head_groups: int = 8, kv_dtype: int = KV_BF16, num_q_heads: int = 64, head_dim: int = 128):
+        from . import attn_plan_device, device_map_words
+        self._plan_device = attn_plan_device
+        device = torch.device(device)
+        if num_workers is None:
+            num_workers = attn_query_workers(device.index or 0, head_groups, kv_dtype)
+        self.B, self.W, self.tile = int(batch), int(num_workers), int(tile)
+        self.head_groups = head_groups
+        self.kv_dtype = kv_dtype
+        self.device = device
+        self.map = torch.zeros(device_map_words(self.B, self.W), dtype=torch.int32, device=device)
+        self.seq_lens = torch.zeros(self.B, dtype=torch.int32, device=device)
+        self.S_max = max(1, self.W + self.B - 1)
+        self.part_m = torch.empty((self.S_max, num_q_heads), dtype=torch.float32, device=device)
+        self.part_l = torch.empty((self.S_max, num_q_heads), dtype=torch.float32, device=device)
+        self.part_o = torch.empty((self.S_max, num_q_heads, head_dim), dtype=torch.float32, device=device)
+
+    def plan(self, stream=None) -> None:
+        self._plan_device(self.seq_lens, self.W, self.tile, self.map, stream=stream)
+
+    def splitkv(self, q, k_cache, v_cache, block_table, scale: float, timing=None, stream=None,
+                kv_scales=None) -> None:
+        if self.kv_dtype == KV_FP8_E4M3:
+            if kv_scales is None:
+                raise ValueError("an 8-bit cache needs kv_scales=(k_scale, v_scale)")
+            attn_splitkv_fp8(q, k_cache, v_cache, kv_scales[0], kv_scales[1], block_table, self.seq_lens, self.map,
+                             self.W, self.S_max, self.head_groups, scale, self.part_m, self.part_l, self.part_o,
+                             timing=timing, stream=stream)
+        else:
+            attn_splitkv(q, k_cache, v_cache, block_table, self.seq_lens, self.map, self.W, self.S_max,
+                         self.head_groups, scale, self.part_m, self.part_l, self.part_o, timing=timing,
+                         stream=stream)
+
+    def combine(self, out, stream=None) -> None:
+        # the split count per request is only known on the device: pass the worker count as the bound
+        attn_combine(self.part_m, self.part_l, self.part_o, self.map, self.B, out, max_splits=self.W, stream=stream)
+
+    def __call__(self, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                 scale: Optional[float] = None, out: Optional[torch.Tensor] = None, stream=None,
+                 kv_scales=None) -> torch.Tensor:
+        if scale is None:
+            scale = q.shape[-1] ** -0.5
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        self.plan(stream=stream)
+        self.splitkv(q, k_cache, v_cache, block_table, scale, stream=stream, kv_scales=kv_scales)
+        self.combine(out, stream=stream)
+        return out

@@ -148,6 +148,13 @@ def test_errors_and_capacity(L):
     assert mtp(0, None, None, dummy, 5) == -3
     assert mtp(1, dummy, dummy, dummy, 0) == -1
     assert mtp(0, None, None, dummy, 2, head_dim=64) == -3
+    # device planner: host-side argument checks (no launch)
+    assert lib.attn_plan_device(dummy, -1, 4, 512, dummy, 100, None) == -1
+    assert lib.attn_plan_device(dummy, 3, 0, 512, dummy, 100, None) == -1
+    assert lib.attn_plan_device(dummy, 3, 4, 0, dummy, 100, None) == -1
+    assert lib.attn_plan_device(dummy, 3, 4, 512, None, 100, None) == -1
+    assert lib.attn_plan_device(None, 3, 4, 512, dummy, 100, None) == -1
+    assert lib.attn_plan_device(dummy, 3, 4, 512, dummy, 8 + 5 + 4 + 6 - 1, None) == -2
     out = ctypes.c_int32(0)
     assert lib.attn_query_workers(0, 8, 7, ctypes.byref(out)) == -1
     assert lib.attn_query_workers(0, 3, 0, ctypes.byref(out)) == -1
