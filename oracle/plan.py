@@ -42,6 +42,11 @@ exactly these words)::
 
 A decode unit is one request (q_tile_index 0).  A prefill unit is one
 q_tile-row block of one request's query chunk.
+
+Version 2 (the LPT comparison planner below): a worker's segments need not be
+contiguous in unit-major order, so the segments stay unit-major (segment i owns
+partial slot i) and an extra ``order[S]`` follows ``seg``: worker w runs the
+segments ``order[worker_ptr[w] .. worker_ptr[w+1])``.
 """
 
 from __future__ import annotations
@@ -52,6 +57,7 @@ from typing import List, Sequence, Tuple
 import numpy as np
 
 MAP_VERSION = 1
+MAP_VERSION_ORDERED = 2   # version 1 plus order[S]: the segments each worker runs, by slot index
 HEADER_WORDS = 8
 
 
@@ -232,6 +238,69 @@ def ref_plan_prefill(q_lens: Sequence[int], kv_lens: Sequence[int], num_workers:
     return _serialise(len(q_lens), units, lists, kv_tile, q_tile, total)
 
 
+def ref_plan_lpt(seq_lens: Sequence[int], num_workers: int, tile: int) -> np.ndarray:
+    """LPT bucket packing, the assignment of [P5] "大模型推理性能优化揭秘" §五(一): every request is
+    cut into tiles, the tiles are taken in decreasing size, and each goes to the worker with the
+    smallest load so far; a tile's size (and a worker's load) is counted in KV tokens.
+
+    Readings: equal sizes keep stream order (batch order, ascending tile); equal loads go to the
+    lowest worker index; inside a worker the tiles are run in stream order and consecutive tiles of
+    one request merge into one segment.  Serialised as a version-2 map (see the module header).
+    """
+    _check_common(num_workers, tile)
+    units = decode_units(seq_lens)
+    pieces = []                                   # (size, unit index, tile index)
+    for ui, u in enumerate(units):
+        for t in range(tiles_of(u.extent, tile)):
+            pieces.append((min(tile, u.extent - t * tile), ui, t))
+    total = len(pieces)
+    pieces.sort(key=lambda x: (-x[0], x[1], x[2]))
+    load = [0] * num_workers
+    mine: List[List[Tuple[int, int]]] = [[] for _ in range(num_workers)]
+    for size, ui, t in pieces:
+        w = min(range(num_workers), key=lambda i: (load[i], i))
+        load[w] += size
+        mine[w].append((ui, t))
+    # per worker: runs of consecutive tiles of one unit, in stream order
+    runs: List[List[Tuple[int, int, int]]] = []   # (unit index, first tile, last tile)
+    for w in range(num_workers):
+        got = sorted(mine[w])
+        lst: List[Tuple[int, int, int]] = []
+        for ui, t in got:
+            if lst and lst[-1][0] == ui and lst[-1][2] == t - 1:
+                lst[-1] = (ui, lst[-1][1], t)
+            else:
+                lst.append((ui, t, t))
+        runs.append(lst)
+    # slots: all segments in unit-major order (by unit, then KV start)
+    all_runs = sorted({r for lst in runs for r in lst})
+    slot = {r: i for i, r in enumerate(all_runs)}
+    segs = []
+    for ui, t0, t1 in all_runs:
+        u = units[ui]
+        segs.append(Segment(u.b, u.qt, t0 * tile, min(u.extent, (t1 + 1) * tile)))
+    counts = [0] * len(units)
+    for ui, _, _ in all_runs:
+        counts[ui] += 1
+    unit_ptr = [0]
+    for c in counts:
+        unit_ptr.append(unit_ptr[-1] + c)
+    worker_ptr = [0]
+    order = []
+    for lst in runs:
+        order += [slot[r] for r in lst]
+        worker_ptr.append(len(order))
+    S = len(segs)
+    words = [MAP_VERSION_ORDERED, len(seq_lens), num_workers, tile, S, total, 1, len(units)]
+    words += worker_ptr + unit_ptr
+    for u in units:
+        words += [u.b, u.qt]
+    for sg in segs:
+        words += [sg.b, sg.qt, sg.kv_begin, sg.kv_end]
+    words += order
+    return np.asarray(words, dtype=np.int32)
+
+
 # ----------------------------------------------------------------------------------------------
 # Reading a map back (used by tests and by the attention oracle's split helpers)
 
@@ -249,9 +318,14 @@ class WorkMap:
     unit_ptr: np.ndarray
     units: np.ndarray      # [U, 2]
     segs: np.ndarray       # [S, 4]
+    order: np.ndarray = None   # version 2: slot indices, worker-major
+
+    def worker_slots(self, w: int) -> np.ndarray:
+        idx = np.arange(self.worker_ptr[w], self.worker_ptr[w + 1])
+        return idx if self.order is None else self.order[idx]
 
     def worker_segments(self, w: int) -> np.ndarray:
-        return self.segs[self.worker_ptr[w]:self.worker_ptr[w + 1]]
+        return self.segs[self.worker_slots(w)]
 
     def unit_segments(self, u: int) -> np.ndarray:
         return self.segs[self.unit_ptr[u]:self.unit_ptr[u + 1]]
@@ -265,9 +339,14 @@ def parse_map(words: np.ndarray) -> WorkMap:
     unit_ptr = words[o:o + U + 1]; o += U + 1
     units = words[o:o + 2 * U].reshape(U, 2); o += 2 * U
     segs = words[o:o + 4 * S].reshape(S, 4); o += 4 * S
+    order = None
+    if version == MAP_VERSION_ORDERED:
+        order = words[o:o + S]; o += S
+    elif version != MAP_VERSION:
+        raise ValueError(f"unknown map version {version}")
     if o != len(words):
         raise ValueError(f"map has {len(words)} words, layout implies {o}")
-    return WorkMap(version, B, W, kv_tile, S, T, q_tile, U, worker_ptr, unit_ptr, units, segs)
+    return WorkMap(version, B, W, kv_tile, S, T, q_tile, U, worker_ptr, unit_ptr, units, segs, order)
 
 
 def map_words(num_units: int, num_workers: int, num_segments: int) -> int:

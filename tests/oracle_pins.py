@@ -350,3 +350,66 @@ def pin_fp8_scale_laws(ref_decode_fp8):
     one = ref_decode_fp8(q, [kc[0][:1]], [vc[0][:1]], ks, vs, 0.2)[0]
     exp = _torch_e4m3_values()[vc[0][0]] * vs[:, None]            # [Hkv, D]
     assert np.array_equal(one, np.repeat(exp, Hq // Hkv, axis=0))
+
+
+# ------------------------------------------------------------------------------------------------
+# LPT comparison planner.
+
+def _lpt_worker_tiles(ref_plan_lpt, parse_map, lens, W, tile):
+    mp = parse_map(ref_plan_lpt(lens, W, tile))
+    assert mp.version == 2 and sorted(mp.order.tolist()) == list(range(mp.S))
+    per = []
+    for w in range(W):
+        tiles = []
+        for b, qt, a, e in mp.worker_segments(w).tolist():
+            assert qt == 0 and 0 <= a < e <= lens[b] and a % tile == 0
+            tiles += [(b, t) for t in range(a // tile, -(-e // tile))]
+        per.append(tiles)
+    # slots are unit-major and each unit's slots are contiguous
+    for u in range(mp.U):
+        assert all(s[0] == u for s in mp.unit_segments(u).tolist())
+    return mp, per
+
+
+def pin_lpt_coverage_and_balance(ref_plan_lpt, parse_map, trials=120, seed=9):
+    """Every tile on exactly one worker; max load - min load <= the largest tile (the greedy
+    least-loaded rule guarantees it); loads counted in tokens."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        B = int(rng.integers(0, 9))
+        W = int(rng.integers(1, 9))
+        tile = int(rng.choice([16, 64, 512]))
+        lens = [int(x) for x in rng.integers(0, 3000, size=B)]
+        mp, per = _lpt_worker_tiles(ref_plan_lpt, parse_map, lens, W, tile)
+        seen = sorted(t for tiles in per for t in tiles)
+        expect = sorted((b, t) for b, L in enumerate(lens) for t in range(-(-L // tile) if L > 0 else 0))
+        assert seen == expect
+        size = lambda bt: min(tile, lens[bt[0]] - bt[1] * tile)
+        loads = [sum(size(bt) for bt in tiles) for tiles in per]
+        if expect:
+            assert max(loads) - min(loads) <= max(size(bt) for bt in expect)
+
+
+def pin_lpt_equal_sizes_round_robin(ref_plan_lpt, parse_map):
+    """With every tile full-size, decreasing size keeps stream order and each tile goes to the least
+    loaded (lowest-index) worker: stream tile j lands on worker j mod W."""
+    for lens, W in (([1024, 5120, 2048], 4), ([512 * 7, 512 * 3], 3), ([2048] * 5, 7)):
+        _, per = _lpt_worker_tiles(ref_plan_lpt, parse_map, lens, W, 512)
+        stream = [(b, t) for b, L in enumerate(lens) for t in range(L // 512)]
+        for j, bt in enumerate(stream):
+            assert bt in per[j % W], (lens, W, j)
+    # one worker: every request's tiles are consecutive there and merge into one segment
+    mp, _ = _lpt_worker_tiles(ref_plan_lpt, parse_map, [1024, 5120, 0, 2048], 1, 512)
+    assert mp.S == 3 and mp.segs.tolist() == [[0, 0, 0, 1024], [1, 0, 0, 5120], [3, 0, 0, 2048]]
+
+
+def pin_lpt_hand_example(ref_plan_lpt, parse_map):
+    """Lengths 700, 1500, 0, 300 with 512-token tiles on 3 workers, worked by hand: tile sizes
+    512 (0:0), 188 (0:1), 512 (1:0), 512 (1:1), 476 (1:2), 300 (3:0); in decreasing size
+    0:0 -> w0, 1:0 -> w1, 1:1 -> w2, 1:2 -> w0 (988), 3:0 -> w1 (812), 0:1 -> w2 (700)."""
+    _, per = _lpt_worker_tiles(ref_plan_lpt, parse_map, [700, 1500, 0, 300], 3, 512)
+    assert [sorted(p) for p in per] == [[(0, 0), (1, 2)], [(1, 0), (3, 0)], [(0, 1), (1, 1)]]
+    # loads are tokens, not tiles: lengths 512, 100, 100, 100 on 2 workers put the 512-token tile
+    # alone on w0 (512) and the three 100-token tiles on w1 (100, 200, 300 < 512)
+    _, per = _lpt_worker_tiles(ref_plan_lpt, parse_map, [512, 100, 100, 100], 2, 512)
+    assert [sorted(p) for p in per] == [[(0, 0)], [(1, 0), (2, 0), (3, 0)]]

@@ -48,6 +48,14 @@ def _plan_pins(m):
     ]
 
 
+def _lpt_pins(m):
+    return [
+        lambda: P.pin_lpt_hand_example(m.ref_plan_lpt, m.parse_map),
+        lambda: P.pin_lpt_equal_sizes_round_robin(m.ref_plan_lpt, m.parse_map),
+        lambda: P.pin_lpt_coverage_and_balance(m.ref_plan_lpt, m.parse_map, trials=60),
+    ]
+
+
 def _fp8_pins(m):
     return [
         lambda: P.pin_e4m3_library(m.e4m3_table),
@@ -91,6 +99,15 @@ FP8_MUTANTS = {
     "scale of the first head for all": ("vals * scale[None, :, None]", "vals * scale[0]"),
 }
 
+LPT_MUTANTS = {
+    "ties to the highest worker": ("key=lambda i: (load[i], i))", "key=lambda i: (load[i], -i))"),
+    "smallest tiles first": ("pieces.sort(key=lambda x: (-x[0], x[1], x[2]))", "pieces.sort(key=lambda x: (x[0], x[1], x[2]))"),
+    "loads counted in tiles": ("load[w] += size", "load[w] += 1"),
+    "most loaded worker": ("w = min(range(num_workers), key=lambda i: (load[i], i))",
+                           "w = max(range(num_workers), key=lambda i: (load[i], -i))"),
+    "runs not merged": ("if lst and lst[-1][0] == ui and lst[-1][2] == t - 1:", "if False:"),
+}
+
 PLAN_MUTANTS = {
     "floor tile count": ("return ceil_div(extent, tile) if extent > 0 else 0", "return extent // tile"),
     "extra tiles to the last workers": ("base + (1 if w < rem else 0)", "base + (1 if w >= workers - rem else 0)"),
@@ -114,6 +131,13 @@ def test_plan_mutant_is_caught(name):
     assert _caught(_plan_pins(m)), f"no pin catches: {name}"
 
 
+@pytest.mark.parametrize("name", sorted(LPT_MUTANTS))
+def test_lpt_mutant_is_caught(name):
+    old, new = LPT_MUTANTS[name]
+    m = _load_mutant("plan", old, new, count=1)
+    assert _caught(_lpt_pins(m)), f"no pin catches: {name}"
+
+
 @pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
 def test_fp8_mutant_is_caught(name):
     old, new = FP8_MUTANTS[name]
@@ -125,5 +149,5 @@ def test_unmutated_oracle_passes_all_pins():
     import oracle.attention as A
     import oracle.fp8 as F
     import oracle.plan as Pl
-    for pin in _attention_pins(A) + _plan_pins(Pl) + _fp8_pins(F):
+    for pin in _attention_pins(A) + _plan_pins(Pl) + _fp8_pins(F) + _lpt_pins(Pl):
         pin()

@@ -143,3 +143,18 @@ def test_prefill_extents():
     for b, i, a, e in mp.segs.tolist():
         ends[(b, i)] = max(ends.get((b, i), 0), e)
     assert ends == {(0, 0): 828, (0, 1): 956, (0, 2): 1000, (1, 0): 128}
+
+
+def test_lpt_coverage_and_balance():
+    from oracle.plan import parse_map, ref_plan_lpt
+    P.pin_lpt_coverage_and_balance(ref_plan_lpt, parse_map)
+
+
+def test_lpt_equal_sizes_round_robin():
+    from oracle.plan import parse_map, ref_plan_lpt
+    P.pin_lpt_equal_sizes_round_robin(ref_plan_lpt, parse_map)
+
+
+def test_lpt_hand_example():
+    from oracle.plan import parse_map, ref_plan_lpt
+    P.pin_lpt_hand_example(ref_plan_lpt, parse_map)
