@@ -519,6 +519,33 @@ def main() -> int:
             "speedup_vs_plain": round(plain_row["us_per_step"] / (ms_per_step * 1e3), 3),
             "speedup_vs_best": round(best["us_per_step"] / (ms_per_step * 1e3), 3), "sweep": rows}
 
+    if not args.no_static and wl.name != "tiny":
+        # the LPT assignment of the fifth page (largest tile first onto the least-loaded worker)
+        st = DecodeStep(wl.kv_lens, dev, num_workers=workers, tile=args.tile, head_groups=args.head_groups,
+                        planner="lpt")
+
+        def l_split(i, st=st):
+            k_, v_ = caches[i % copies]
+            st.splitkv(q, k_, v_, bt, scale)
+
+        rl = time_steps(l_split, lambda i, st=st: st.combine(out), args.static_steps, 2)
+        timing_l = torch.zeros((st.W * args.head_groups, 4), dtype=torch.int64, device=dev)
+        st.splitkv(q, kc, vc, bt, scale, timing=timing_l)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            lb.attn_plan_lpt(wl.kv_lens, workers, args.tile)
+        lpt_host_us = (time.perf_counter() - t0) / 5 * 1e6
+        result["lpt_baseline"] = {
+            "segments": st.S, "us_per_step": round(rl["total_ms"] / args.static_steps * 1e3, 2),
+            "splitkv_us": round(float(np.mean(rl["split_ms"])) * 1e3, 2),
+            "combine_us": round(float(np.mean(rl["combine_ms"])) * 1e3, 2),
+            "per_cu_max_over_mean": round(per_cu_busy(timing_l)["max_over_mean"], 3),
+            "host_plan_us": round(lpt_host_us, 1),
+            "dynamic_speedup": round(rl["total_ms"] / args.static_steps / ms_per_step, 3)}
+        log(f"lpt map: S={st.S}, step {result['lpt_baseline']['us_per_step']} us")
+        del st
+
     if not args.no_probe:
         # the device's streaming-read ceiling, measured on the same run (the KV cache itself)
         sink = torch.zeros(8192 * 256, dtype=torch.int32, device=dev)

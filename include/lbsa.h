@@ -122,10 +122,27 @@ int attn_plan(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t t
  * Data errors are written to the device map instead, since the lengths are only known there:
  * map[0] = LBSA_MAP_VERSION on success, LBSA_ERR_INVALID for a negative length or more than
  * INT32_MAX tiles, LBSA_ERR_CAPACITY (with map[4] = the segment count needed) when the segments do
- * not fit.  Split and combine kernels given a map whose map[0] is not LBSA_MAP_VERSION do nothing.
+ * not fit.  Split and combine kernels given a map whose map[0] is not a map version (1, or 2 where
+ * accepted) do nothing.
  */
 int attn_plan_device(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile,
                      int32_t* map, int32_t map_capacity, void* stream);
+
+/*
+ * LPT comparison map ([P5] "大模型推理性能优化揭秘：从算子到系统的全链路技术解析" §五(一): tiles
+ * sorted by decreasing size, each put on the least-loaded worker).  A tile's size and a worker's
+ * load are counted in KV tokens; equal sizes keep stream order, equal loads go to the lowest worker
+ * index; inside a worker the tiles run in stream order and consecutive tiles of one request merge
+ * into one segment.  A request's tiles end up scattered over workers, so the map is written in
+ * version 2 (LBSA_MAP_VERSION_ORDERED): segments unit-major (segment i = partial slot i), plus
+ * order[S] after seg[S][4], and worker w runs segments order[worker_ptr[w] .. worker_ptr[w+1]).
+ * attn_splitkv, attn_splitkv_fp8 and attn_combine accept it; the prefill and multi-token kernels take
+ * version 1 only.  Uses O(T) host memory (not a per-step hot-path routine).  Arguments and errors as
+ * attn_plan.
+ */
+#define LBSA_MAP_VERSION_ORDERED 2
+int attn_plan_lpt(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile,
+                  int32_t* map, int32_t map_capacity, int32_t* map_words_out);
 
 /*
  * Static split-KV map, the imbalance baseline ([P3] §3.1 问题; [P4] §二.1: one

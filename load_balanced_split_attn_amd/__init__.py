@@ -17,6 +17,7 @@ import torch
 
 __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill", "attn_plan_device",
+    "attn_plan_lpt",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
     "attn_combine",
     "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
@@ -37,6 +38,7 @@ _SIGNATURES = {
     "attn_map_words": (ctypes.c_int32, [_c_i32, _c_i32, ctypes.c_int64]),
     "attn_plan": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
     "attn_plan_static": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
+    "attn_plan_lpt": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
     "attn_plan_prefill": (ctypes.c_int, [_c_i32p, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                          _c_i32p, _c_i32, _c_i32p]),
     "attn_query_workers": (ctypes.c_int, [ctypes.c_int, _c_i32, _c_i32, _c_i32p]),
@@ -129,6 +131,12 @@ def attn_plan_static(seq_lens: Sequence[int], num_splits: int, tile: int = 512) 
     """Static split-KV map: min(num_splits, tiles) chunks per request, one worker each."""
     lens = _i32_host(seq_lens)
     return _plan_call(lib().attn_plan_static, "attn_plan_static", _ptr_i32(lens), len(lens), num_splits, tile)
+
+
+def attn_plan_lpt(seq_lens: Sequence[int], num_workers: int, tile: int = 512) -> np.ndarray:
+    """LPT comparison map (version 2, with a per-worker order list)."""
+    lens = _i32_host(seq_lens)
+    return _plan_call(lib().attn_plan_lpt, "attn_plan_lpt", _ptr_i32(lens), len(lens), num_workers, tile)
 
 
 def attn_plan_prefill(q_lens: Sequence[int], kv_lens: Sequence[int], num_workers: int, q_tile: int = 128,

@@ -11,9 +11,14 @@
 // Budgets follow [P2] "大模型推理性能优化新范式" §二.1: base = T / W, plus one for the first
 // T % W workers.
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <functional>
+#include <queue>
+#include <utility>
+#include <vector>
 
 #include "lbsa.h"
 
@@ -245,6 +250,122 @@ int attn_plan_static(const int32_t* seq_lens, int32_t B, int32_t num_splits, int
     }
   }
   wr.unit_ptr()[B] = (int32_t)s;
+  return LBSA_OK;
+}
+
+// LPT bucket packing ([P5] "大模型推理性能优化揭秘：从算子到系统的全链路技术解析" §五(一)), the
+// comparison planner: tiles in decreasing token size (ties in stream order), each onto the worker
+// with the smallest token load (ties to the lowest index).  Unlike the contiguous fill it needs
+// O(T) host memory (the tile list and a heap), so it is not meant for the per-step hot path.
+int attn_plan_lpt(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile,
+                  int32_t* map, int32_t map_capacity, int32_t* map_words_out) {
+  if (B < 0 || num_workers < 1 || tile < 1 || !map || map_capacity < 0) return LBSA_ERR_INVALID;
+  if (B > 0 && !seq_lens) return LBSA_ERR_INVALID;
+  int64_t T = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (seq_lens[b] < 0) return LBSA_ERR_INVALID;
+    T += tiles_for(seq_lens[b], tile);
+  }
+  if (T > INT32_MAX) return LBSA_ERR_INVALID;
+  struct Piece {
+    int32_t size, b, t;
+  };
+  std::vector<Piece> pieces;
+  pieces.reserve((size_t)T);
+  for (int32_t b = 0; b < B; ++b) {
+    const int64_t n = tiles_for(seq_lens[b], tile);
+    for (int64_t t = 0; t < n; ++t) {
+      const int64_t left = (int64_t)seq_lens[b] - t * tile;
+      pieces.push_back({(int32_t)(left < tile ? left : tile), b, (int32_t)t});
+    }
+  }
+  std::stable_sort(pieces.begin(), pieces.end(), [](const Piece& x, const Piece& y) { return x.size > y.size; });
+  // least-loaded worker: min-heap on (load, worker index)
+  using Slot = std::pair<int64_t, int32_t>;
+  std::priority_queue<Slot, std::vector<Slot>, std::greater<Slot>> heap;
+  for (int32_t w = 0; w < num_workers; ++w) heap.push({0, w});
+  std::vector<int32_t> owner(pieces.size());
+  for (size_t i = 0; i < pieces.size(); ++i) {
+    Slot s = heap.top();
+    heap.pop();
+    owner[i] = s.second;
+    s.first += pieces[i].size;
+    heap.push(s);
+  }
+  // per worker, its tiles in stream order; consecutive tiles of one request form one segment
+  struct Run {
+    int32_t w, b, t0, t1;
+  };
+  std::vector<int32_t> idx(pieces.size());
+  for (size_t i = 0; i < idx.size(); ++i) idx[i] = (int32_t)i;
+  std::sort(idx.begin(), idx.end(), [&](int32_t x, int32_t y) {
+    if (owner[x] != owner[y]) return owner[x] < owner[y];
+    if (pieces[x].b != pieces[y].b) return pieces[x].b < pieces[y].b;
+    return pieces[x].t < pieces[y].t;
+  });
+  std::vector<Run> runs;
+  for (int32_t i : idx) {
+    const Piece& p = pieces[i];
+    if (!runs.empty() && runs.back().w == owner[i] && runs.back().b == p.b && runs.back().t1 == p.t - 1)
+      runs.back().t1 = p.t;
+    else
+      runs.push_back({owner[i], p.b, p.t, p.t});
+  }
+  const int64_t S = (int64_t)runs.size();
+  const int64_t words = LBSA_MAP_HEADER_WORDS + (int64_t)num_workers + 1 + (int64_t)B + 1 + 2 * (int64_t)B +
+                        4 * S + S;
+  if (words > INT32_MAX) return LBSA_ERR_INVALID;
+  if (map_words_out) *map_words_out = (int32_t)words;
+  if (words > map_capacity) return LBSA_ERR_CAPACITY;
+  // slots: segments in unit-major order (request, then first tile)
+  std::vector<int32_t> by_unit(runs.size());
+  for (size_t i = 0; i < by_unit.size(); ++i) by_unit[i] = (int32_t)i;
+  std::sort(by_unit.begin(), by_unit.end(), [&](int32_t x, int32_t y) {
+    if (runs[x].b != runs[y].b) return runs[x].b < runs[y].b;
+    return runs[x].t0 < runs[y].t0;
+  });
+  std::vector<int32_t> slot_of(runs.size());
+  for (size_t k = 0; k < by_unit.size(); ++k) slot_of[by_unit[k]] = (int32_t)k;
+  Writer wr{map, num_workers, B};
+  map[0] = LBSA_MAP_VERSION_ORDERED;
+  map[1] = B;
+  map[2] = num_workers;
+  map[3] = tile;
+  map[4] = (int32_t)S;
+  map[5] = (int32_t)T;
+  map[6] = 1;
+  map[7] = B;
+  // unit table and unit_ptr
+  {
+    int64_t k = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      wr.unit_ptr()[b] = (int32_t)k;
+      wr.units()[2 * b] = b;
+      wr.units()[2 * b + 1] = 0;
+      while (k < S && runs[by_unit[k]].b == b) ++k;
+    }
+    wr.unit_ptr()[B] = (int32_t)S;
+  }
+  for (int64_t k = 0; k < S; ++k) {
+    const Run& r = runs[by_unit[k]];
+    int32_t* sg = wr.seg(k);
+    const int64_t end = ((int64_t)r.t1 + 1) * tile;
+    sg[0] = r.b;
+    sg[1] = 0;
+    sg[2] = (int32_t)((int64_t)r.t0 * tile);
+    sg[3] = (int32_t)(end < seq_lens[r.b] ? end : seq_lens[r.b]);
+  }
+  // worker_ptr and the order list (runs are already worker-major, stream order inside a worker)
+  int32_t* order = wr.seg(S);
+  int64_t k = 0;
+  for (int32_t w = 0; w < num_workers; ++w) {
+    wr.worker_ptr()[w] = (int32_t)k;
+    while (k < S && runs[k].w == w) {
+      order[k] = slot_of[k];
+      ++k;
+    }
+  }
+  wr.worker_ptr()[num_workers] = (int32_t)S;
   return LBSA_OK;
 }
 

@@ -359,15 +359,21 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
   uint64_t t_start = 0;
   if (p.timing && threadIdx.x == 0) t_start = realtime();
 
-  if (p.map[0] != LBSA_MAP_VERSION) return;   // a device-built map that reported an error
+  const int version = p.map[0];
+  // a device-built map that reported an error, or an unknown layout
+  if (version != LBSA_MAP_VERSION && version != LBSA_MAP_VERSION_ORDERED) return;
   const int U = p.map[7];
   const int32_t* worker_ptr = p.map + 8;
   const int32_t* segs = p.map + 8 + (p.W + 1) + (U + 1) + 2 * U;
+  // version 2: worker w runs the segments order[worker_ptr[w] ..), by slot index
+  const int32_t* order = version == LBSA_MAP_VERSION_ORDERED ? segs + 4 * p.map[4] : nullptr;
   const int s_begin = worker_ptr[w];
   const int s_end = min(worker_ptr[w + 1], p.S);
   const size_t head_bytes = (size_t)block_bytes;   // bytes per (page, KV head) block
 
-  for (int s = s_begin; s < s_end; ++s) {
+  for (int j = s_begin; j < s_end; ++j) {
+    const int s = order ? order[j] : j;
+    if (s < 0 || s >= p.S) continue;
     const int b = segs[4 * s];
     const int kv_begin = segs[4 * s + 2];
     int kv_end = segs[4 * s + 3];

@@ -13,14 +13,14 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (KV_BF16, KV_FP8_E4M3, attn_combine, attn_plan, attn_plan_static, attn_query_workers, attn_splitkv,
-               attn_splitkv_fp8, map_header, max_splits_of)
+from . import (KV_BF16, KV_FP8_E4M3, attn_combine, attn_plan, attn_plan_lpt, attn_plan_static, attn_query_workers,
+               attn_splitkv, attn_splitkv_fp8, map_header, max_splits_of)
 
 
 class DecodeStep:
     def __init__(self, seq_lens: Sequence[int], device, num_workers: Optional[int] = None, tile: int = 512,
                  head_groups: int = 8, num_q_heads: int = 64, head_dim: int = 128,
-                 static_splits: Optional[int] = None, kv_dtype: int = KV_BF16):
+                 static_splits: Optional[int] = None, kv_dtype: int = KV_BF16, planner: str = "greedy"):
         device = torch.device(device)
         self.seq_lens_host = [int(x) for x in seq_lens]
         if static_splits is not None:
@@ -28,7 +28,12 @@ class DecodeStep:
         else:
             if num_workers is None:
                 num_workers = attn_query_workers(device.index or 0, head_groups, kv_dtype)
-            self.map_host = attn_plan(self.seq_lens_host, num_workers, tile)
+            if planner == "greedy":
+                self.map_host = attn_plan(self.seq_lens_host, num_workers, tile)
+            elif planner == "lpt":
+                self.map_host = attn_plan_lpt(self.seq_lens_host, num_workers, tile)
+            else:
+                raise ValueError(f"unknown planner {planner!r} (greedy or lpt)")
         hdr = map_header(self.map_host)
         self.W, self.S, self.U, self.T = hdr["W"], hdr["S"], hdr["U"], hdr["T"]
         self.max_splits = max_splits_of(self.map_host)

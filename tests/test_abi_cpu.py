@@ -160,3 +160,21 @@ def test_errors_and_capacity(L):
     assert lib.attn_query_workers(0, 3, 0, ctypes.byref(out)) == -1
     assert lib.attn_combine(None, None, None, dummy, 1, 1, None, None, 64, 128, None, 0, 0, None) == -1
     assert lib.attn_combine(dummy, dummy, dummy, dummy, 1, 1, None, None, 64, 128, dummy, 0, -1, None) == -1
+
+
+def test_lpt_plan_bit_exact():
+    """attn_plan_lpt (C++) reproduces the oracle's version-2 LPT map word for word."""
+    import load_balanced_split_attn_amd as lb
+    from oracle.plan import ref_plan_lpt
+    rng = np.random.default_rng(21)
+    for _ in range(400):
+        B = int(rng.integers(0, 12))
+        W = int(rng.integers(1, 20))
+        tile = int(rng.choice([16, 64, 512]))
+        lens = [int(x) for x in rng.integers(0, 4000, size=B)]
+        assert np.array_equal(lb.attn_plan_lpt(lens, W, tile), ref_plan_lpt(lens, W, tile)), (lens, W, tile)
+    import workloads as WL
+    for name in ("tiny", "uniform", "mixed", "long_tail"):
+        wl = WL.BY_NAME[name]()
+        W = wl.workers or 128
+        assert np.array_equal(lb.attn_plan_lpt(wl.kv_lens, W, 512), ref_plan_lpt(wl.kv_lens, W, 512)), name

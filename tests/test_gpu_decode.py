@@ -90,7 +90,8 @@ def test_maps_agree_and_paging_invariance(lb):
     outs = []
     for words in (lb.attn_plan(wl.kv_lens, 37, 512), lb.attn_plan(wl.kv_lens, 1, 512),
                   lb.attn_plan_static(wl.kv_lens, 1, 512), lb.attn_plan_static(wl.kv_lens, 3, 512),
-                  lb.attn_plan(wl.kv_lens, 37, 64)):
+                  lb.attn_plan(wl.kv_lens, 37, 64), lb.attn_plan_lpt(wl.kv_lens, 37, 512),
+                  lb.attn_plan_lpt(wl.kv_lens, 5, 64)):
         out, _ = _run(lb, wl, words, inputs=inputs)
         outs.append(out.cpu().numpy().astype(np.float64))
     for o in outs[1:]:
@@ -156,3 +157,25 @@ def test_timing_records(lb):
     ref = oracle_decode(wl)
     for b in range(wl.batch):
         assert_close(out[b].cpu().numpy(), ref[b], f"timed run request {b}")
+
+
+def test_lpt_map_partials(lb):
+    """A version-2 (LPT) map: every slot's partial matches the oracle's partial of that segment, and
+    the combined output matches the oracle."""
+    wl = WL.random_decode(16, 5, 3000, min_len=300)
+    words = lb.attn_plan_lpt(wl.kv_lens, 9, 512)
+    from oracle.plan import ref_plan_lpt
+    assert np.array_equal(words, ref_plan_lpt(wl.kv_lens, 9, 512))
+    out, parts = _run(lb, wl, words, poison=True)
+    ref = oracle_decode(wl)
+    got = out.cpu().numpy()
+    for b in range(wl.batch):
+        assert_close(got[b], ref[b], f"lpt request {b}")
+    q = wl.q().double().numpy()
+    kvs = [wl.kv(b) for b in range(wl.batch)]
+    rparts = ref_split_partials(words, [q[b:b + 1] for b in range(wl.batch)],
+                                [k.double().numpy() for k, _ in kvs], [v.double().numpy() for _, v in kvs], SCALE)
+    pm, pl, po = (t.cpu().numpy() for t in parts)
+    for s_, (m, l, o) in enumerate(rparts):
+        assert np.max(np.abs(pm[s_] - m[0])) <= 1e-3, f"slot {s_} m"
+        assert_close(po[s_] / pl[s_][:, None], o[0] / l[0][:, None], f"slot {s_} o/l")
