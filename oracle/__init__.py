@@ -16,6 +16,8 @@ Two parts:
 * ``oracle.fp8``       - the value of an element of an 8-bit (OCP E4M3) KV
   cache with per-KV-head scales, and decode attention over such a cache
   (dequantise, then ``oracle.attention``).
+* ``oracle.store_kv``  - the producer step of a decode step: RMSNorm, RoPE and
+  Hadamard rotation of the new q/k, bf16 or E4M3 rounding, the values stored.
 
 Sources (the web pages this method is described on):
 
@@ -36,4 +38,4 @@ text); its pins are the worked example's tile and budget counts plus
 invariants that any contiguous equal-budget fill must satisfy.
 """
 
-from . import attention, fp8, plan  # noqa: F401
+from . import attention, fp8, plan, store_kv  # noqa: F401

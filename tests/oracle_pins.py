@@ -413,3 +413,92 @@ def pin_lpt_hand_example(ref_plan_lpt, parse_map):
     # alone on w0 (512) and the three 100-token tiles on w1 (100, 200, 300 < 512)
     _, per = _lpt_worker_tiles(ref_plan_lpt, parse_map, [512, 100, 100, 100], 2, 512)
     assert [sorted(p) for p in per] == [[(0, 0)], [(1, 0), (2, 0), (3, 0)]]
+
+
+# ------------------------------------------------------------------------------------------------
+# Producer step (normalise, rotate, quantise, store).
+
+def pin_round_bf16_library(round_bf16):
+    """bf16 rounding of float32 inputs equals torch's float32 -> bfloat16 conversion (RNE)."""
+    rng = np.random.default_rng(31)
+    x = np.concatenate([rng.standard_normal(50000) * 3, rng.standard_normal(2000) * 1e-30,
+                        [0.0, -0.0, 1.0, -1.5, 1.00390625, 1.005859375]]).astype(np.float32)
+    # exact ties: a bf16 value plus half of its step (8 significant bits)
+    t = torch.randn(3000, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16).to(torch.float32).numpy()
+    m, e = np.frexp(t.astype(np.float64))
+    x = np.concatenate([x, (t + np.ldexp(1.0, e - 9)).astype(np.float32)])
+    got = round_bf16(x.astype(np.float64))
+    exp = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(got, exp)
+
+
+def pin_e4m3_round_library(e4m3_round, e4m3_table):
+    """E4M3 rounding of float32 inputs in [-448, 448] equals torch's float8_e4m3fn conversion, exact
+    ties (midpoints of neighbouring codes) included."""
+    rng = np.random.default_rng(32)
+    x = np.concatenate([rng.standard_normal(40000) * 60, rng.uniform(-448, 448, 20000),
+                        rng.standard_normal(5000) * 1e-3, [0.0, 448.0, -448.0, 1e-9, -1e-9]])
+    vals = e4m3_table()[np.arange(0x00, 0x7F)]
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([x, mids, -mids]).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    got = e4m3_round(x.astype(np.float64))
+    exp = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, exp), int((got != exp).sum())
+
+
+def pin_hadamard(hadamard):
+    """Against scipy's Hadamard matrix; an involution (H / sqrt(n) is symmetric and orthogonal)."""
+    import scipy.linalg
+    for n in (1, 2, 8, 128):
+        assert np.allclose(hadamard(np.eye(n)), scipy.linalg.hadamard(n) / math.sqrt(n), atol=1e-15)
+    x = np.random.default_rng(33).standard_normal((5, 128))
+    assert np.allclose(hadamard(hadamard(x)), x, atol=1e-12)
+
+
+def pin_rope(rope):
+    """Closed forms: position 0 is the identity; (1, 0, 0, 0) at position 1 with theta 10000 and D 4
+    turns into (cos 1, 0, sin 1, 0) (pair (0, 2) at frequency 1) and (0, 1, 0, 0) at position 100
+    into (0, cos 1, 0, sin 1) (pair (1, 3) at frequency 0.01); each pair keeps its length; and
+    <rope(q, p), rope(k, r)> depends on p - r only (the relative-position property)."""
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((3, 2, 16))
+    assert np.allclose(rope(x, np.zeros(3), 10000.0), x, atol=1e-15)
+    one = rope(np.array([[[1.0, 0.0, 0.0, 0.0]]]), np.array([1.0]), 10000.0)[0, 0]
+    assert np.allclose(one, [math.cos(1.0), 0.0, math.sin(1.0), 0.0], atol=1e-15)
+    # pair (1, 3) turns at 10000^(-2/4) = 0.01 per position: position 100 -> angle 1
+    two = rope(np.array([[[0.0, 1.0, 0.0, 0.0]]]), np.array([100.0]), 10000.0)[0, 0]
+    assert np.allclose(two, [0.0, math.cos(1.0), 0.0, math.sin(1.0)], atol=1e-12)
+    y = rope(x, np.array([5.0, 77.0, 123456.0]), 10000.0)
+    assert np.allclose(x[..., :8] ** 2 + x[..., 8:] ** 2, y[..., :8] ** 2 + y[..., 8:] ** 2, atol=1e-12)
+    q = rng.standard_normal((1, 1, 16))
+    k = rng.standard_normal((1, 1, 16))
+    d1 = np.sum(rope(q, np.array([10.0]), 500.0) * rope(k, np.array([3.0]), 500.0))
+    d2 = np.sum(rope(q, np.array([1010.0]), 500.0) * rope(k, np.array([1003.0]), 500.0))
+    assert abs(d1 - d2) < 1e-9
+
+
+def pin_rms_norm_library(rms_norm):
+    """Against torch.nn.functional.rms_norm in float64."""
+    rng = np.random.default_rng(35)
+    x = rng.standard_normal((4, 3, 128)) * 5
+    w = rng.standard_normal(128)
+    exp = torch.nn.functional.rms_norm(torch.from_numpy(x), (128,), torch.from_numpy(w), eps=1e-6).numpy()
+    assert np.allclose(rms_norm(x, w, 1e-6), exp, rtol=1e-12, atol=1e-12)
+
+
+def pin_store_kv_scores_invariant(ref_store_kv):
+    """The Hadamard step rotates q and k alike, so every q.k is unchanged (before rounding)."""
+    from oracle import store_kv as SK
+    rng = np.random.default_rng(36)
+    q = rng.standard_normal((2, 16, 128))
+    k = rng.standard_normal((2, 2, 128))
+    pos = np.array([7.0, 300.0])
+    a = SK.rope(q, pos, 10000.0), SK.rope(k, pos, 10000.0)
+    s1 = np.einsum("nhd,ngd->nhg", a[0], a[1])
+    s2 = np.einsum("nhd,ngd->nhg", SK.hadamard(a[0]), SK.hadamard(a[1]))
+    assert np.allclose(s1, s2, atol=1e-10)
+    # and the full step with Hadamard on matches the library pieces composed by hand
+    qo, ko, vo = ref_store_kv(q, k, k, pos, None, None, 1e-6, 10000.0, True)
+    assert np.array_equal(qo, SK.round_bf16(SK.hadamard(a[0])))
+    assert np.array_equal(ko, SK.round_bf16(SK.hadamard(a[1])))

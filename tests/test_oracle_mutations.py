@@ -56,6 +56,17 @@ def _lpt_pins(m):
     ]
 
 
+def _store_pins(m):
+    from oracle import fp8
+    return [
+        lambda: P.pin_round_bf16_library(m.round_bf16),
+        lambda: P.pin_e4m3_round_library(m.e4m3_round, fp8.e4m3_table),
+        lambda: P.pin_hadamard(m.hadamard),
+        lambda: P.pin_rope(m.rope),
+        lambda: P.pin_rms_norm_library(m.rms_norm),
+    ]
+
+
 def _fp8_pins(m):
     return [
         lambda: P.pin_e4m3_library(m.e4m3_table),
@@ -108,6 +119,17 @@ LPT_MUTANTS = {
     "runs not merged": ("if lst and lst[-1][0] == ui and lst[-1][2] == t - 1:", "if False:"),
 }
 
+STORE_MUTANTS = {
+    "rope sign flipped": ("[x1 * c - x2 * s, x2 * c + x1 * s]", "[x1 * c + x2 * s, x2 * c - x1 * s]"),
+    "rope frequency exponent": ("freq = theta ** (-2.0 * i / D)", "freq = theta ** (-1.0 * i / D)"),
+    "rms norm without the gain": ("keepdims=True) + eps) * np.asarray(w, dtype=np.float64)", "keepdims=True) + eps)"),
+    "rms norm over the sum": ("np.mean(x * x, axis=-1, keepdims=True)", "np.sum(x * x, axis=-1, keepdims=True)"),
+    "hadamard without normalisation": ("hadamard_matrix(D).T / math.sqrt(D)", "hadamard_matrix(D).T"),
+    "bf16 truncates": ("return np.round(np.ldexp(x, -step_exp))", "return np.trunc(np.ldexp(x, -step_exp))"),
+    "e4m3 ties away": ("((hi - a == a - lo) & ((pos_codes[j] & 1) == 0))", "(hi - a == a - lo)"),
+    "e4m3 drops the sign": ("return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)", "return code.astype(np.uint8)"),
+}
+
 PLAN_MUTANTS = {
     "floor tile count": ("return ceil_div(extent, tile) if extent > 0 else 0", "return extent // tile"),
     "extra tiles to the last workers": ("base + (1 if w < rem else 0)", "base + (1 if w >= workers - rem else 0)"),
@@ -138,6 +160,13 @@ def test_lpt_mutant_is_caught(name):
     assert _caught(_lpt_pins(m)), f"no pin catches: {name}"
 
 
+@pytest.mark.parametrize("name", sorted(STORE_MUTANTS))
+def test_store_mutant_is_caught(name):
+    old, new = STORE_MUTANTS[name]
+    m = _load_mutant("store_kv", old, new, count=1)
+    assert _caught(_store_pins(m)), f"no pin catches: {name}"
+
+
 @pytest.mark.parametrize("name", sorted(FP8_MUTANTS))
 def test_fp8_mutant_is_caught(name):
     old, new = FP8_MUTANTS[name]
@@ -149,5 +178,6 @@ def test_unmutated_oracle_passes_all_pins():
     import oracle.attention as A
     import oracle.fp8 as F
     import oracle.plan as Pl
-    for pin in _attention_pins(A) + _plan_pins(Pl) + _fp8_pins(F) + _lpt_pins(Pl):
+    import oracle.store_kv as SK
+    for pin in _attention_pins(A) + _plan_pins(Pl) + _fp8_pins(F) + _lpt_pins(Pl) + _store_pins(SK):
         pin()
