@@ -359,6 +359,59 @@ def bench_mtp(dev, base: str, args, decode_us: float) -> dict:
             "decode_us_per_step": round(decode_us, 2), "sweep": rows}
 
 
+def bench_store_kv(dev, wl, args) -> dict:
+    """The fused producer step (RMSNorm + RoPE + Hadamard on q and k, K/V stored into the blocked
+    paged cache) for one decode step of the batch, and for a 4096-token step; bf16 and E4M3."""
+    import numpy as np
+    import torch
+
+    import load_balanced_split_attn_amd as lb
+    from load_balanced_split_attn_amd.paged import cache_shapes, pages_for
+    rows = []
+    for B, lens in ((wl.batch, list(wl.kv_lens)), (4096, [int(x) for x in np.random.default_rng(3).integers(
+            0, 131072, size=4096)])):
+        g = torch.Generator().manual_seed(B)
+        q = torch.randn(B, wl.hq, wl.head_dim, generator=g).to(torch.bfloat16).to(dev)
+        k = torch.randn(B, wl.hkv, wl.head_dim, generator=g).to(torch.bfloat16).to(dev)
+        v = torch.randn(B, wl.hkv, wl.head_dim, generator=g).to(torch.bfloat16).to(dev)
+        qw = torch.ones(wl.head_dim, device=dev)
+        kw = torch.ones(wl.head_dim, device=dev)
+        pos = torch.tensor(lens, dtype=torch.int32, device=dev)
+        # one page per request around its new token is enough to receive the writes
+        stride = max(pages_for(L + 1, 64) for L in lens)
+        bt = torch.zeros((B, stride), dtype=torch.int32)
+        for b, L in enumerate(lens):
+            bt[b, L // 64] = b
+        bt = bt.to(dev)
+        q_out = torch.empty_like(q)
+        for fp8 in (False, True):
+            dtype = torch.uint8 if fp8 else torch.bfloat16
+            ksh, vsh = cache_shapes(B, wl.hkv, 64, wl.head_dim, dtype)
+            kc = torch.zeros(ksh, dtype=dtype, device=dev)
+            vc = torch.zeros(vsh, dtype=dtype, device=dev)
+            sc = (torch.full((wl.hkv,), 0.02, device=dev), torch.full((wl.hkv,), 0.02, device=dev)) if fp8 else None
+            f = lambda: lb.attn_store_kv(q, k, v, pos, q_out, kc, vc, bt, q_norm_w=qw, k_norm_w=kw,
+                                         rope_theta=10000.0, hadamard=True, kv_scales=sc)
+            for _ in range(3):
+                f()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(50):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / 50 * 1e3
+            nbytes = B * (wl.hq + 2 * wl.hkv) * wl.head_dim * 2 + B * wl.hq * wl.head_dim * 2 + \
+                B * 2 * wl.hkv * wl.head_dim * (1 if fp8 else 2) + B * 8
+            rows.append({"tokens": B, "kv": "e4m3" if fp8 else "bf16", "us": round(us, 2),
+                         "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1)})
+            log(f"store_kv B={B} {'e4m3' if fp8 else 'bf16'}: {us:.1f} us")
+            del kc, vc
+    return {"workload": "producer step: RMSNorm + RoPE + Hadamard on q and k, K/V stored in the blocked paged "
+                        "cache, for the batch's new tokens and for a 4096-token step",
+            "bound": "latency at the batch's size (one wave per head vector); HBM at 4096 tokens", "sweep": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,6 +435,7 @@ def main() -> int:
                     help="run only the chunked-prefill report (profiling runs); prints its JSON")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit KV cache report")
     ap.add_argument("--no-mtp", action="store_true", help="skip the multi-token decode report")
+    ap.add_argument("--no-store", action="store_true", help="skip the producer-step report")
     ap.add_argument("--only-fp8", action="store_true",
                     help="run only the 8-bit KV cache report on --workload (profiling runs); prints its JSON")
     args = ap.parse_args()
@@ -570,6 +624,9 @@ def main() -> int:
 
     if not args.no_mtp and wl.name != "tiny":
         result["mtp"] = bench_mtp(dev, wl.name, args, ms_per_step * 1e3)
+
+    if not args.no_store and wl.name != "tiny":
+        result["store_kv"] = bench_store_kv(dev, wl, args)
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(dev, [int(x) for x in args.prefill_workers.split(",")],

@@ -262,6 +262,34 @@ int attn_splitkv_mtp(const void* q, const void* k_cache, const void* v_cache, in
                      float* part_m, float* part_l, float* part_o, void* stream);
 
 /*
+ * Producer step of a decode step, fused ([P3] §4.1: RoPE, RMSNorm, Hadamard, quantisation and the
+ * KV-cache write in one kernel; §8: q and k Hadamard-rotated before quantisation).  For each new
+ * token b and head vector x (128 dims) of the projection output:
+ *   1. RMSNorm if the gain is given: x / sqrt(mean(x^2) + norm_eps) * w (q_norm_w for q heads,
+ *      k_norm_w for k heads; fp32[128] each, or NULL to skip)
+ *   2. RoPE if rope_theta > 0, rotate-half: pairs (i, i + 64) turned by positions[b] * theta^(-i/64)
+ *   3. Hadamard if hadamard = 1: x -> H x / sqrt(128), H the Sylvester-ordered Walsh-Hadamard matrix
+ * q takes 1-3 and is written to q_out (bf16, round to nearest even; q_out may be q_in); k takes 1-3
+ * and v none, and both are written at token positions[b] of request b's pages (block_table, the
+ * blocked cache layout above), as bf16 (kv_dtype LBSA_KV_BF16) or as E4M3 codes of x / scale[head]
+ * clamped to +-448, round to nearest even (LBSA_KV_FP8_E4M3, k_scale / v_scale fp32[Hkv]).
+ *   q_in bf16 [B, Hq, 128]; k_in, v_in bf16 [B, Hkv, 128]; positions device int32[B]
+ * A token whose position lies outside its block-table row, or whose page id is outside
+ * [0, num_pages), is not stored (q_out is still written).  The caller advances seq_lens afterwards.
+ * Errors: LBSA_ERR_INVALID (NULL pointers, negative sizes, eps or theta negative or NaN, hadamard
+ * not 0/1, unknown kv_dtype, missing scales for E4M3), LBSA_ERR_UNSUPPORTED (head_dim != 128,
+ * page_size not a multiple of 64), LBSA_ERR_HIP.
+ */
+int attn_store_kv(const void* q_in, const void* k_in, const void* v_in,
+                  const float* q_norm_w, const float* k_norm_w, float norm_eps,
+                  const int32_t* positions, float rope_theta, int32_t hadamard,
+                  void* q_out, void* k_cache, void* v_cache, int32_t kv_dtype,
+                  const float* k_scale, const float* v_scale,
+                  const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
+                  int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t page_size, void* stream);
+
+/*
  * Split-KV chunked-prefill kernel over a cached prefix (the greedy map of attn_plan_prefill
  * applied to prefill units; prefix reuse as in [P3] §6: a request's new chunk attends to its
  * cached prefix and, causally, to itself).  Request b has q_lens[b] query rows stored from row

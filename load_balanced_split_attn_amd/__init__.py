@@ -19,7 +19,7 @@ __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill", "attn_plan_device",
     "attn_plan_lpt",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
-    "attn_combine",
+    "attn_combine", "attn_store_kv",
     "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
 ]
 
@@ -52,6 +52,9 @@ _SIGNATURES = {
     "attn_splitkv_mtp": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
                                         _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                         _c_i32, _c_i32, _c_i32, ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "attn_store_kv": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_float,
+                                     _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
+                                     _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp]),
     "attn_combine": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                     _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, _c_vp]),
     "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
@@ -351,6 +354,46 @@ def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                                     int(bool(causal)), float(softmax_scale), _dptr(part_m), _dptr(part_l),
                                     _dptr(part_o), 1 if exact_pv else 0, _stream(stream))
     _check(st, "attn_splitkv_prefill")
+
+
+def attn_store_kv(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tensor, positions: torch.Tensor,
+                  q_out: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                  q_norm_w: Optional[torch.Tensor] = None, k_norm_w: Optional[torch.Tensor] = None,
+                  eps: float = 1e-6, rope_theta: float = 0.0, hadamard: bool = False, kv_scales=None,
+                  stream=None) -> None:
+    """Producer step: RMSNorm / RoPE / Hadamard on the new q and k, q to q_out (bf16), k and v stored
+    at positions[b] of each request's pages (bf16 cache, or uint8 E4M3 with kv_scales)."""
+    dev = q_in.device
+    for name, t in (("q_in", q_in), ("k_in", k_in), ("v_in", v_in), ("q_out", q_out)):
+        _need(t, torch.bfloat16, name, dev)
+    fp8 = k_cache.dtype == torch.uint8
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, torch.uint8 if fp8 else torch.bfloat16, name, dev)
+    _need(positions, torch.int32, "positions", dev)
+    _need(block_table, torch.int32, "block_table", dev)
+    B, Hq, D = q_in.shape
+    P, Hkv, page = _cache_geometry(k_cache, v_cache, D)
+    if tuple(k_in.shape) != (B, Hkv, D) or tuple(v_in.shape) != (B, Hkv, D) or tuple(q_out.shape) != (B, Hq, D):
+        raise ValueError("q_in/k_in/v_in/q_out shapes do not match [B, Hq, D] / [B, Hkv, D]")
+    if positions.numel() != B or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("positions/block_table do not match the batch")
+    for name, t in (("q_norm_w", q_norm_w), ("k_norm_w", k_norm_w)):
+        if t is not None:
+            _need(t, torch.float32, name, dev)
+            if t.numel() != D:
+                raise ValueError(f"{name}: need {D} gains")
+    ks = vs = None
+    if fp8:
+        if kv_scales is None:
+            raise ValueError("an 8-bit cache needs kv_scales=(k_scale, v_scale)")
+        ks, vs = kv_scales
+        for name, t in (("k_scale", ks), ("v_scale", vs)):
+            _need(t, torch.float32, name, dev)
+    st = lib().attn_store_kv(_dptr(q_in), _dptr(k_in), _dptr(v_in), _dptr(q_norm_w), _dptr(k_norm_w), float(eps),
+                             _dptr(positions), float(rope_theta), 1 if hadamard else 0, _dptr(q_out), _dptr(k_cache),
+                             _dptr(v_cache), KV_FP8_E4M3 if fp8 else KV_BF16, _dptr(ks), _dptr(vs),
+                             _dptr(block_table), block_table.shape[1], P, B, Hq, Hkv, D, page, _stream(stream))
+    _check(st, "attn_store_kv")
 
 
 def attn_combine(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor, map_dev: torch.Tensor,

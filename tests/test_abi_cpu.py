@@ -155,6 +155,24 @@ def test_errors_and_capacity(L):
     assert lib.attn_plan_device(dummy, 3, 4, 512, None, 100, None) == -1
     assert lib.attn_plan_device(None, 3, 4, 512, dummy, 100, None) == -1
     assert lib.attn_plan_device(dummy, 3, 4, 512, dummy, 8 + 5 + 4 + 6 - 1, None) == -2
+    # producer step: argument checks before any launch
+    def store(**kw):
+        a = dict(q=dummy, k=dummy, v=dummy, qw=None, kw=None, eps=1e-6, pos=dummy, theta=0.0, had=0, qo=dummy,
+                 kc=dummy, vc=dummy, dt=0, ks=None, vs=None, bt=dummy, bts=1, np_=1, B=1, Hq=64, Hkv=8, D=128,
+                 page=64)
+        a.update(kw)
+        return lib.attn_store_kv(a["q"], a["k"], a["v"], a["qw"], a["kw"], a["eps"], a["pos"], a["theta"], a["had"],
+                                 a["qo"], a["kc"], a["vc"], a["dt"], a["ks"], a["vs"], a["bt"], a["bts"], a["np_"],
+                                 a["B"], a["Hq"], a["Hkv"], a["D"], a["page"], None)
+    assert store(q=None) == -1
+    assert store(had=2) == -1
+    assert store(eps=-1.0) == -1
+    assert store(theta=float("nan")) == -1
+    assert store(dt=1) == -1                 # E4M3 without scales
+    assert store(dt=3, ks=dummy, vs=dummy) == -1
+    assert store(D=64) == -3
+    assert store(page=48) == -3
+    assert store(B=0, q=None) == 0           # nothing to do
     out = ctypes.c_int32(0)
     assert lib.attn_query_workers(0, 8, 7, ctypes.byref(out)) == -1
     assert lib.attn_query_workers(0, 3, 0, ctypes.byref(out)) == -1

@@ -1,0 +1,212 @@
+"""GPU parity of the fused producer step (attn_store_kv) against the fp64 oracle: the rotated q,
+the stored K/V (bf16 values or E4M3 codes) read back from the blocked paged cache, exact hardware
+rounding where the input fixes it, and a decode step over the appended tokens end to end."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as WL
+from gpu_helpers import SCALE, assert_close, note
+from oracle import store_kv as SK
+from oracle.attention import ref_attention
+from oracle.fp8 import dequantize_kv, e4m3_table
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lb():
+    import load_balanced_split_attn_amd as m
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    m.lib()
+    return m
+
+
+def _bf16_step(x):
+    """Spacing of bf16 values at |x| (8 significant bits)."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def _tol(ref):
+    """One bf16 step at the value, plus the fp32 arithmetic's absolute error on a head vector (a
+    128-term Hadamard sum): 1e-5 of the vector's largest magnitude.  Near-zero outputs have bf16
+    steps far below that error, so their rounding may land one or more steps away."""
+    ref = np.asarray(ref, dtype=np.float64)
+    return _bf16_step(ref) + 1e-5 * np.max(np.abs(ref), axis=-1, keepdims=True)
+
+
+def _inputs(seed, B, Hq=64, Hkv=8, D=128):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    k = (torch.randn(B, Hkv, D, generator=g) * 2).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, D, generator=g).to(torch.bfloat16)
+    qw = (1 + 0.3 * torch.randn(D, generator=g)).float()
+    kw = (1 + 0.3 * torch.randn(D, generator=g)).float()
+    return q, k, v, qw, kw
+
+
+def _empty_cache(lens, page, fp8, dev, Hkv=8, D=128):
+    """A paged cache holding len_b tokens per request plus room for one more; contents zero."""
+    from load_balanced_split_attn_amd.paged import cache_shapes, pages_for
+    need = [pages_for(L + 1, page) for L in lens]
+    P = sum(need)
+    dtype = torch.uint8 if fp8 else torch.bfloat16
+    ks, vs = cache_shapes(P, Hkv, page, D, dtype)
+    kc = torch.zeros(ks, dtype=dtype, device=dev)
+    vc = torch.zeros(vs, dtype=dtype, device=dev)
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(3))
+    bt = torch.zeros((len(lens), max(need)), dtype=torch.int32)
+    first = 0
+    for b, n in enumerate(need):
+        bt[b, :n] = perm[first:first + n].to(torch.int32)
+        first += n
+    return kc, vc, bt.to(dev)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("norm,theta,had", [(True, 10000.0, True), (False, 1e6, False), (True, 0.0, True),
+                                            (False, 0.0, False)])
+def test_store_matches_oracle(lb, fp8, norm, theta, had):
+    from load_balanced_split_attn_amd.paged import unpack_request
+    dev = torch.device("cuda")
+    B = 37
+    q, k, v, qw, kw = _inputs(40 + int(fp8), B)
+    lens = [int(x) for x in np.random.default_rng(7).integers(0, 200000, size=B)]
+    lens[0], lens[1] = 0, 63                      # first token of a page, last token of a page
+    kc, vc, bt = _empty_cache(lens, 64, fp8, dev)
+    pos = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ks = vs = None
+    if fp8:
+        ks = torch.exp2(torch.rand(8, generator=torch.Generator().manual_seed(9)) * 2 - 5).float()
+        vs = torch.exp2(torch.rand(8, generator=torch.Generator().manual_seed(10)) * 2 - 6).float()
+    q_out = torch.empty_like(q, device=dev)
+    lb.attn_store_kv(q.to(dev), k.to(dev), v.to(dev), pos, q_out, kc, vc, bt,
+                     q_norm_w=qw.to(dev) if norm else None, k_norm_w=kw.to(dev) if norm else None, eps=1e-6,
+                     rope_theta=theta, hadamard=had, kv_scales=(ks.to(dev), vs.to(dev)) if fp8 else None)
+    torch.cuda.synchronize()
+    rq, rk, rv = SK.ref_store_kv(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                 np.array(lens, dtype=np.float64), qw.double().numpy() if norm else None,
+                                 kw.double().numpy() if norm else None, 1e-6, theta, had,
+                                 ks.double().numpy() if fp8 else None, vs.double().numpy() if fp8 else None)
+    got_q = q_out.float().cpu().numpy().astype(np.float64)
+    dq = np.abs(got_q - rq)
+    assert np.all(dq <= _tol(rq)), f"q: {int((dq > _tol(rq)).sum())} beyond tolerance"
+    assert np.mean(dq == 0) > 0.99
+    table = e4m3_table()
+    for b, L in enumerate(lens):
+        kb, vb = unpack_request(kc, vc, bt, b, L + 1)
+        got_k, got_v = kb[L].cpu(), vb[L].cpu()
+        if fp8:
+            gk, gv = got_k.numpy(), got_v.numpy()
+            for got, ref, sc in ((gk, rk[b], ks), (gv, rv[b], vs)):
+                # codes equal, or one step apart where fp32 and fp64 land on different sides of a tie
+                dv = np.abs(table[got] - table[ref])
+                step = np.abs(table[np.minimum(ref.astype(np.int32) & 0x7F, 0x7D) + 1] - table[ref.astype(np.int32) & 0x7F])
+                assert np.all((got == ref) | (dv <= step + 1e-12)), f"request {b}"
+                assert np.mean(got == ref) > 0.98
+        else:
+            for got, ref in ((got_k.double().numpy(), rk[b]), (got_v.double().numpy(), rv[b])):
+                assert np.all(np.abs(got - ref) <= _tol(ref)), f"request {b}"
+    note(f"fp8={fp8} norm={norm} theta={theta} hadamard={had}: q exact {np.mean(dq == 0):.4f}")
+
+
+def test_hardware_rounding_exact(lb):
+    """With no norm, RoPE or Hadamard the stored V is the input itself: the bf16 path stores it
+    unchanged and the E4M3 path rounds x / scale with scale 1 exactly as the oracle does, exact
+    midpoints between neighbouring codes included (ties to even)."""
+    from load_balanced_split_attn_amd.paged import unpack_request
+    dev = torch.device("cuda")
+    table = e4m3_table()
+    vals = table[np.arange(0, 0x7F)]
+    mids = (vals[:-1] + vals[1:]) / 2
+    cand = np.concatenate([mids, -mids, vals, -vals, [500.0, -1000.0, 1e-4, -1e-4]])
+    cand = torch.from_numpy(cand).to(torch.bfloat16)
+    keep = cand.double().numpy()
+    B = -(-len(keep) // (8 * 128))
+    v = torch.zeros(B * 8 * 128, dtype=torch.bfloat16)
+    v[:len(keep)] = cand
+    v = v.view(B, 8, 128)
+    q, k, _, _, _ = _inputs(50, B)
+    lens = [5] * B
+    pos = torch.tensor(lens, dtype=torch.int32, device=dev)
+    for fp8 in (False, True):
+        kc, vc, bt = _empty_cache(lens, 64, fp8, dev)
+        ones = torch.ones(8, dtype=torch.float32, device=dev)
+        q_out = torch.empty_like(q, device=dev)
+        lb.attn_store_kv(q.to(dev), k.to(dev), v.to(dev), pos, q_out, kc, vc, bt,
+                         kv_scales=(ones, ones) if fp8 else None)
+        torch.cuda.synchronize()
+        got = torch.cat([unpack_request(kc, vc, bt, b, 6)[1][5].reshape(-1).cpu() for b in range(B)])
+        ref = v.reshape(-1).double().numpy()
+        if fp8:
+            assert np.array_equal(got.numpy(), SK.e4m3_round(np.clip(ref, -448, 448)))
+        else:
+            assert np.array_equal(got.double().numpy(), ref)
+        assert torch.equal(q_out.cpu(), q)                # q unchanged when every step is off
+
+
+def test_out_of_table_positions_not_stored(lb):
+    dev = torch.device("cuda")
+    q, k, v, _, _ = _inputs(60, 3)
+    kc, vc, bt = _empty_cache([10, 20, 30], 64, False, dev)
+    pos = torch.tensor([10, 5000, -1], dtype=torch.int32, device=dev)
+    q_out = torch.empty_like(q, device=dev)
+    lb.attn_store_kv(q.to(dev), k.to(dev), v.to(dev), pos, q_out, kc, vc, bt)
+    torch.cuda.synchronize()
+    from load_balanced_split_attn_amd.paged import unpack_request
+    kb, _ = unpack_request(kc, vc, bt, 0, 11)
+    assert torch.equal(kb[10].cpu(), k[0])
+    nz = int(torch.count_nonzero(kc).item())
+    assert nz == int(torch.count_nonzero(k[0]).item())    # nothing else was written
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_append_then_decode(lb, fp8):
+    """A decode step end to end: each request's cache holds L_b tokens; the producer step appends the
+    new token (RMSNorm + RoPE + Hadamard on q and k), then decode attention runs over L_b + 1 keys
+    with the produced q.  Reference: the oracle's stored values and rotated q, plain attention."""
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    from load_balanced_split_attn_amd.paged import pack_paged
+    dev = torch.device("cuda")
+    wl = WL.random_decode(70 + int(fp8), 6, 3000, min_len=1)
+    B = wl.batch
+    q, k, v, qw, kw = _inputs(80, B)
+    # caches with room for the new token: pack L_b + 1 tokens whose last one is a placeholder
+    ks = vs = None
+    if fp8:
+        ks, vs = wl.kv_scales()
+        old = [wl.kv_fp8(b) for b in range(B)]
+        kv_of = lambda b: (torch.cat([old[b][0], torch.zeros(1, 8, 128, dtype=torch.uint8)]),
+                           torch.cat([old[b][1], torch.zeros(1, 8, 128, dtype=torch.uint8)]))
+    else:
+        old = [wl.kv(b) for b in range(B)]
+        kv_of = lambda b: (torch.cat([old[b][0], torch.zeros(1, 8, 128, dtype=torch.bfloat16)]),
+                           torch.cat([old[b][1], torch.zeros(1, 8, 128, dtype=torch.bfloat16)]))
+    new_lens = [L + 1 for L in wl.kv_lens]
+    kc, vc, bt = pack_paged(kv_of, new_lens, 64, 8, 128, wl.page_permutation, dev,
+                            dtype=torch.uint8 if fp8 else torch.bfloat16)
+    pos = torch.tensor(wl.kv_lens, dtype=torch.int32, device=dev)
+    q_out = torch.empty_like(q, device=dev)
+    scales = (ks.to(dev), vs.to(dev)) if fp8 else None
+    lb.attn_store_kv(q.to(dev), k.to(dev), v.to(dev), pos, q_out, kc, vc, bt, q_norm_w=qw.to(dev),
+                     k_norm_w=kw.to(dev), rope_theta=10000.0, hadamard=True, kv_scales=scales)
+    step = DecodeStep(new_lens, dev, num_workers=11, kv_dtype=lb.KV_FP8_E4M3 if fp8 else lb.KV_BF16)
+    out = step(q_out, kc, vc, bt, scale=SCALE, kv_scales=scales)
+    torch.cuda.synchronize()
+    rq, rk, rv = SK.ref_store_kv(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                 np.array(wl.kv_lens, dtype=np.float64), qw.double().numpy(), kw.double().numpy(),
+                                 1e-6, 10000.0, True, ks.double().numpy() if fp8 else None,
+                                 vs.double().numpy() if fp8 else None)
+    got = out.cpu().numpy()
+    qg = q_out.float().cpu().numpy().astype(np.float64)   # attention parity against the produced q
+    for b in range(B):
+        if fp8:
+            kk = dequantize_kv(np.concatenate([old[b][0].numpy(), rk[b:b + 1]]), ks.double().numpy())
+            vv = dequantize_kv(np.concatenate([old[b][1].numpy(), rv[b:b + 1]]), vs.double().numpy())
+        else:
+            kk = np.concatenate([old[b][0].double().numpy(), rk[b:b + 1]])
+            vv = np.concatenate([old[b][1].double().numpy(), rv[b:b + 1]])
+        ref = ref_attention(qg[b:b + 1], kk, vv, SCALE)[0]
+        assert_close(got[b], ref, f"append+decode fp8={fp8} request {b}")
