@@ -15,11 +15,12 @@
 // 8 v heads of a token), lane l holding dims l and l + 64 — exactly one RoPE pair — so RoPE is
 // in-lane, the Hadamard's first stage (stride 64) is in-lane and its five other stages are lane
 // exchanges, and the RMSNorm sum is one wave reduction.  The RoPE angle is formed in fp64 (a
-// position of 2^17 times a frequency near 1 would lose ~0.01 rad in fp32) and reduced mod 2 pi
-// before the fp32-accurate sine and cosine.  The work is a few hundred bytes per vector: the kernel
-// is launch- and latency-bound.
+// position of 2^17 times a frequency near 1 would lose ~0.01 rad in fp32) from frequencies the host
+// computes once per call, and reduced mod 2 pi (one rint and one fma) before the fp32-accurate sine
+// and cosine.  The work is a few hundred bytes per vector: the kernel is launch- and latency-bound.
 
 #include <climits>
+#include <cmath>
 
 #include "common.h"
 #include "lbsa.h"
@@ -43,6 +44,7 @@ struct StoreParams {
   const int32_t* block_table;
   int32_t bt_stride, num_pages, B, Hq, Hkv, page, fp8, hadamard;
   float eps, theta;
+  double freq[kSD / 2];   // RoPE frequencies theta^(-2i/128), fp64, filled on the host
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
@@ -87,10 +89,10 @@ __global__ __launch_bounds__(256) void store_kv_kernel(StoreParams p) {
       x1 = x1 * r * w[lane + 64];
     }
     if (p.theta > 0.f) {
-      // angle = pos * theta^(-2 lane / 128), in fp64, reduced to [-pi, pi]
-      const double freq = exp2(-(2.0 * lane / kSD) * log2((double)p.theta));
-      double a = (double)pos * freq;
-      a = remainder(a, 6.283185307179586476925286766559);
+      // angle = pos * theta^(-2 lane / 128) in fp64, reduced to [-pi, pi]
+      constexpr double kTwoPi = 6.283185307179586476925286766559;
+      double a = (double)pos * p.freq[lane];
+      a = fma(-kTwoPi, rint(a * (1.0 / kTwoPi)), a);
       float s, c;
       sincosf((float)a, &s, &c);
       const float y0 = x0 * c - x1 * s;
@@ -167,7 +169,9 @@ extern "C" int attn_store_kv(const void* q_in, const void* k_in, const void* v_i
                       static_cast<const uint16_t*>(v_in), q_norm_w, k_norm_w, positions,
                       static_cast<uint16_t*>(q_out), static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
                       k_scale, v_scale, block_table, block_table_stride, num_pages, B, num_q_heads, num_kv_heads,
-                      page_size, kv_dtype == LBSA_KV_FP8_E4M3 ? 1 : 0, hadamard, norm_eps, rope_theta};
+                      page_size, kv_dtype == LBSA_KV_FP8_E4M3 ? 1 : 0, hadamard, norm_eps, rope_theta, {}};
+  for (int i = 0; i < lbsa::kSD / 2; ++i)
+    p.freq[i] = rope_theta > 0.f ? std::pow((double)rope_theta, -2.0 * i / lbsa::kSD) : 0.0;
   const int vecs = num_q_heads + 2 * num_kv_heads;
   hipLaunchKernelGGL(lbsa::store_kv_kernel, dim3(B, (vecs + 3) / 4), dim3(256), 0, static_cast<hipStream_t>(stream),
                      p);
