@@ -361,13 +361,16 @@ def bench_mtp(dev, base: str, args, decode_us: float) -> dict:
 
 def bench_store_kv(dev, wl, args) -> dict:
     """The fused producer step (RMSNorm + RoPE + Hadamard on q and k, K/V stored into the blocked
-    paged cache) for one decode step of the batch, and for a 4096-token step; bf16 and E4M3."""
+    paged cache) for one decode step of the batch, and for a 4096-token step; bf16 and E4M3.  Each
+    point is a HIP graph of 20 launches replayed back to back (the kernel, not the Python binding's
+    per-call cost), timed with events on the replay stream."""
     import numpy as np
     import torch
 
     import load_balanced_split_attn_amd as lb
     from load_balanced_split_attn_amd.paged import cache_shapes, pages_for
     rows = []
+    reps, replays = 20, 10
     for B, lens in ((wl.batch, list(wl.kv_lens)), (4096, [int(x) for x in np.random.default_rng(3).integers(
             0, 131072, size=4096)])):
         g = torch.Generator().manual_seed(B)
@@ -392,24 +395,40 @@ def bench_store_kv(dev, wl, args) -> dict:
             sc = (torch.full((wl.hkv,), 0.02, device=dev), torch.full((wl.hkv,), 0.02, device=dev)) if fp8 else None
             f = lambda: lb.attn_store_kv(q, k, v, pos, q_out, kc, vc, bt, q_norm_w=qw, k_norm_w=kw,
                                          rope_theta=10000.0, hadamard=True, kv_scales=sc)
-            for _ in range(3):
-                f()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                for _ in range(3):
+                    f()
+            torch.cuda.current_stream().wait_stream(side)
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(reps):
+                    f()
+            graph.replay()
+            torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(50):
-                f()
+            for _ in range(replays):
+                graph.replay()
             e1.record()
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / 50 * 1e3
+            us = e0.elapsed_time(e1) / (reps * replays) * 1e3
+            e = 1 if fp8 else 2
             nbytes = B * (wl.hq + 2 * wl.hkv) * wl.head_dim * 2 + B * wl.hq * wl.head_dim * 2 + \
-                B * 2 * wl.hkv * wl.head_dim * (1 if fp8 else 2) + B * 8
+                B * 2 * wl.hkv * wl.head_dim * e + B * 8 + 2 * wl.head_dim * 4
+            # appending one token to the dim-major V tiles touches one 64-byte row per (dim, head)
+            v_rows = B * wl.hkv * wl.head_dim * 64
             rows.append({"tokens": B, "kv": "e4m3" if fp8 else "bf16", "us": round(us, 2),
-                         "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1)})
+                         "algorithmic_bytes": nbytes, "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                         "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 8e12, 4), "v_rows_touched_bytes": v_rows})
             log(f"store_kv B={B} {'e4m3' if fp8 else 'bf16'}: {us:.1f} us")
-            del kc, vc
+            del graph, kc, vc
     return {"workload": "producer step: RMSNorm + RoPE + Hadamard on q and k, K/V stored in the blocked paged "
-                        "cache, for the batch's new tokens and for a 4096-token step",
-            "bound": "latency at the batch's size (one wave per head vector); HBM at 4096 tokens", "sweep": rows}
+                        "cache, for the batch's new tokens and for a 4096-token step (each token its own page)",
+            "timing": f"HIP graph of {reps} launches, {replays} replays, events on the replay stream",
+            "bound": "latency at the batch's size; at 4096 tokens the one-token V append, which touches one "
+                     "64-byte row per (dim, head)", "sweep": rows}
 
 
 def main() -> int:
@@ -436,6 +455,8 @@ def main() -> int:
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit KV cache report")
     ap.add_argument("--no-mtp", action="store_true", help="skip the multi-token decode report")
     ap.add_argument("--no-store", action="store_true", help="skip the producer-step report")
+    ap.add_argument("--only-store", action="store_true",
+                    help="run only the producer-step report on --workload (profiling runs); prints its JSON")
     ap.add_argument("--only-fp8", action="store_true",
                     help="run only the 8-bit KV cache report on --workload (profiling runs); prints its JSON")
     args = ap.parse_args()
@@ -464,6 +485,9 @@ def main() -> int:
     wl = WL.BY_NAME[args.workload]()
     if args.only_fp8:
         print(json.dumps(bench_fp8(dev, wl, args, float("nan"))), flush=True)
+        return 0
+    if args.only_store:
+        print(json.dumps(bench_store_kv(dev, wl, args)), flush=True)
         return 0
     scale = 1.0 / math.sqrt(wl.head_dim)
     page = 64

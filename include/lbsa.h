@@ -276,8 +276,10 @@ int attn_splitkv_mtp(const void* q, const void* k_cache, const void* v_cache, in
  *   q_in bf16 [B, Hq, 128]; k_in, v_in bf16 [B, Hkv, 128]; positions device int32[B]
  * A token whose position lies outside its block-table row, or whose page id is outside
  * [0, num_pages), is not stored (q_out is still written).  The caller advances seq_lens afterwards.
+ * q_in, k_in, v_in, q_out and the caches must be 8-byte aligned, the gains 16-byte aligned.
+ * Launches B x ceil((ceil(Hq/4) + 2 ceil(Hkv/4)) / 4) workgroups of 256 threads.
  * Errors: LBSA_ERR_INVALID (NULL pointers, negative sizes, eps or theta negative or NaN, hadamard
- * not 0/1, unknown kv_dtype, missing scales for E4M3), LBSA_ERR_UNSUPPORTED (head_dim != 128,
+ * not 0/1, unknown kv_dtype, missing scales for E4M3, misaligned pointers), LBSA_ERR_UNSUPPORTED (head_dim != 128,
  * page_size not a multiple of 64), LBSA_ERR_HIP.
  */
 int attn_store_kv(const void* q_in, const void* k_in, const void* v_in,

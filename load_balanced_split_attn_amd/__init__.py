@@ -389,6 +389,8 @@ def attn_store_kv(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tensor, po
         ks, vs = kv_scales
         for name, t in (("k_scale", ks), ("v_scale", vs)):
             _need(t, torch.float32, name, dev)
+            if t.numel() != Hkv:
+                raise ValueError(f"{name}: need {Hkv} scales (one per KV head)")
     st = lib().attn_store_kv(_dptr(q_in), _dptr(k_in), _dptr(v_in), _dptr(q_norm_w), _dptr(k_norm_w), float(eps),
                              _dptr(positions), float(rope_theta), 1 if hadamard else 0, _dptr(q_out), _dptr(k_cache),
                              _dptr(v_cache), KV_FP8_E4M3 if fp8 else KV_BF16, _dptr(ks), _dptr(vs),

@@ -11,13 +11,16 @@
 // position in its request's paged cache (blocked layout of the attention kernels), as bf16 or as
 // E4M3 codes of x / scale[head] (clamped to +-448, round to nearest even).
 //
-// gfx950 design: one wave per head vector (grid: B x 20 workgroups of 4 waves = the 64 q, 8 k and
-// 8 v heads of a token), lane l holding dims l and l + 64 — exactly one RoPE pair — so RoPE is
-// in-lane, the Hadamard's first stage (stride 64) is in-lane and its five other stages are lane
-// exchanges, and the RMSNorm sum is one wave reduction.  The RoPE angle is formed in fp64 (a
-// position of 2^17 times a frequency near 1 would lose ~0.01 rad in fp32) from frequencies the host
-// computes once per call, and reduced mod 2 pi (one rint and one fma) before the fp32-accurate sine
-// and cosine.  The work is a few hundred bytes per vector: the kernel is launch- and latency-bound.
+// gfx950 design: a head vector is held by one row of 16 lanes, lane r keeping dims 4r..4r+3 and
+// 64+4r..64+4r+3 — its four RoPE pairs — so RoPE is in-lane, loads and stores are 8-byte pieces
+// (4-byte for E4M3 K), and of the Hadamard's seven stages three (strides 1, 2, 64) are in-lane and
+// four (strides 4..32, lane bits 0..3) are DPP exchanges inside the 16-lane row; the RMSNorm sum is
+// four more.  No LDS.  A wave holds four head vectors of one kind of one token (grid: B x ceil(20/4)
+// workgroups of 4 waves for 64 q, 8 k and 8 v heads), which share the token's RoPE angles: lane l
+// forms angle l in fp64 (a position of 2^17 times a frequency near 1 would lose ~0.01 rad in fp32)
+// from frequencies the host computes once per call, reduces it mod 2 pi (one rint and one fma),
+// takes the fp32-accurate sine and cosine, and the rows fetch theirs with lane permutes.  Every
+// load of a wave is issued before the first wait.
 
 #include <climits>
 #include <cmath>
@@ -47,103 +50,180 @@ struct StoreParams {
   double freq[kSD / 2];   // RoPE frequencies theta^(-2i/128), fp64, filled on the host
 };
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-
-__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
   const __bf16 b = (__bf16)x;   // round to nearest even
   return __builtin_bit_cast(uint16_t, b);
 }
 
-__device__ __forceinline__ float wave_sum_f32(float v) {
+// DPP moves inside a row of 16 lanes (all source lanes valid)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+// value of lane (lane ^ M) of the same 16-lane row
+template <int M>
+__device__ __forceinline__ float row_xor(float x) {
+  if constexpr (M == 1) return dpp<0xB1>(x);                 // quad_perm [1, 0, 3, 2]
+  else if constexpr (M == 2) return dpp<0x4E>(x);            // quad_perm [2, 3, 0, 1]
+  else if constexpr (M == 4) return dpp<0x141>(dpp<0x1B>(x));   // quad_perm [3, 2, 1, 0] then half-row mirror (^7)
+  else return dpp<0x128>(x);                                 // row rotate by 8
+}
+
+// one Hadamard stage across lanes: (u, v) -> (u + v, u - v), u on the lane whose bit M is clear
+template <int M>
+__device__ __forceinline__ void lane_stage(float (&x)[8], int r) {
+  const float sgn = (r & M) ? -1.f : 1.f;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += xor_lane(v, m);
-  return v;
+  for (int j = 0; j < 8; ++j) x[j] = fmaf(sgn, x[j], row_xor<M>(x[j]));
 }
 
 // E4M3 code of x (already clamped to +-448), round to nearest even (OCP E4M3 on gfx950)
-__device__ __forceinline__ uint8_t f32_to_e4m3(float x) {
-  const int packed = __builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false);
-  return (uint8_t)(packed & 0xff);
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+__device__ __forceinline__ uint8_t e4m3_one(float x) {
+  return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.f, 0, false) & 0xff);
 }
 
 __global__ __launch_bounds__(256) void store_kv_kernel(StoreParams p) {
   const int lane = threadIdx.x & 63;
+  const int r = lane & 15;   // lane within the vector's row: dims 4r..4r+3 and 64+4r..64+4r+3
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int b = blockIdx.x;
-  const int vec = blockIdx.y * 4 + wave;   // 0..Hq-1: q heads, then Hkv k heads, then Hkv v heads
-  if (vec >= p.Hq + 2 * p.Hkv) return;
-  const int kind = vec < p.Hq ? 0 : (vec < p.Hq + p.Hkv ? 1 : 2);
-  const int head = kind == 0 ? vec : (kind == 1 ? vec - p.Hq : vec - p.Hq - p.Hkv);
+  const int nq = (p.Hq + 3) >> 2, nk = (p.Hkv + 3) >> 2;
+  const int task = blockIdx.y * 4 + wave;   // 4 heads of one kind: q blocks, then k blocks, then v blocks
+  if (task >= nq + 2 * nk) return;
+  const int kind = task < nq ? 0 : (task < nq + nk ? 1 : 2);
+  const int hb = kind == 0 ? task : (kind == 1 ? task - nq : task - nq - nk);
   const int H = kind == 0 ? p.Hq : p.Hkv;
-  const uint16_t* src = (kind == 0 ? p.q_in : (kind == 1 ? p.k_in : p.v_in)) + ((size_t)b * H + head) * kSD;
-  float x0 = bf16_to_f32(src[lane]);
-  float x1 = bf16_to_f32(src[lane + 64]);
+  const int head_raw = hb * 4 + (lane >> 4);
+  const bool live = head_raw < H;
+  const int head = live ? head_raw : H - 1;   // rows past the last head load a valid vector, store nothing
+
+  // every load first
   const int pos = p.positions[b];
+  const uint16_t* src = (kind == 0 ? p.q_in : (kind == 1 ? p.k_in : p.v_in)) + ((size_t)b * H + head) * kSD;
+  const uint2 raw_lo = *reinterpret_cast<const uint2*>(src + 4 * r);
+  const uint2 raw_hi = *reinterpret_cast<const uint2*>(src + 64 + 4 * r);
+  const float* w = kind == 0 ? p.q_norm_w : (kind == 1 ? p.k_norm_w : nullptr);
+  float4 w_lo = {}, w_hi = {};
+  if (w) {
+    w_lo = *reinterpret_cast<const float4*>(w + 4 * r);
+    w_hi = *reinterpret_cast<const float4*>(w + 64 + 4 * r);
+  }
+  const bool rope = kind < 2 && p.theta > 0.f;
+  const double freq = rope ? p.freq[lane] : 0.0;
+  int pid = -1, t = 0;
+  if (kind > 0 && pos >= 0 && pos < p.bt_stride * p.page) {
+    pid = p.block_table[(size_t)b * p.bt_stride + pos / p.page];
+    t = pos % p.page;
+  }
+  const float scale = kind > 0 && p.fp8 ? (kind == 1 ? p.k_scale : p.v_scale)[head] : 1.f;
+
+  float x[8] = {bf16_lo(raw_lo.x), bf16_hi(raw_lo.x), bf16_lo(raw_lo.y), bf16_hi(raw_lo.y),
+                bf16_lo(raw_hi.x), bf16_hi(raw_hi.x), bf16_lo(raw_hi.y), bf16_hi(raw_hi.y)};
 
   if (kind < 2) {
-    const float* w = kind == 0 ? p.q_norm_w : p.k_norm_w;
     if (w) {
-      const float ss = wave_sum_f32(x0 * x0 + x1 * x1);
-      const float r = 1.0f / sqrtf(ss * (1.0f / kSD) + p.eps);
-      x0 = x0 * r * w[lane];
-      x1 = x1 * r * w[lane + 64];
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fmaf(x[j], x[j], ss);
+      ss += row_xor<1>(ss);
+      ss += row_xor<2>(ss);
+      ss += row_xor<4>(ss);
+      ss += row_xor<8>(ss);
+      const float rn = 1.0f / sqrtf(ss * (1.0f / kSD) + p.eps);
+      const float wv[8] = {w_lo.x, w_lo.y, w_lo.z, w_lo.w, w_hi.x, w_hi.y, w_hi.z, w_hi.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = x[j] * rn * wv[j];
     }
-    if (p.theta > 0.f) {
-      // angle = pos * theta^(-2 lane / 128) in fp64, reduced to [-pi, pi]
+    if (rope) {
+      // angle of pair `lane` = pos * theta^(-2 lane / 128) in fp64, reduced to [-pi, pi]
       constexpr double kTwoPi = 6.283185307179586476925286766559;
-      double a = (double)pos * p.freq[lane];
+      double a = (double)pos * freq;
       a = fma(-kTwoPi, rint(a * (1.0 / kTwoPi)), a);
-      float s, c;
-      sincosf((float)a, &s, &c);
-      const float y0 = x0 * c - x1 * s;
-      const float y1 = x1 * c + x0 * s;
-      x0 = y0;
-      x1 = y1;
+      float sn, cs;
+      sincosf((float)a, &sn, &cs);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int from = (4 * r + j) << 2;   // pair 4r + j: dims (4r + j, 64 + 4r + j) = (x[j], x[4 + j])
+        const float c = __int_as_float(__builtin_amdgcn_ds_bpermute(from, __float_as_int(cs)));
+        const float s = __int_as_float(__builtin_amdgcn_ds_bpermute(from, __float_as_int(sn)));
+        const float y0 = x[j] * c - x[4 + j] * s;
+        const float y1 = x[4 + j] * c + x[j] * s;
+        x[j] = y0;
+        x[4 + j] = y1;
+      }
     }
     if (p.hadamard) {
-      // stride 64 in-lane, then strides 32 .. 1 across lanes: (u, v) -> (u + v, u - v)
-      float y0 = x0 + x1, y1 = x0 - x1;
+      // in-lane strides 1, 2 (dim bits 0, 1) and 64 (bit 6), then strides 4..32 over the row's lanes
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float o0 = xor_lane(y0, m), o1 = xor_lane(y1, m);
-        const bool low = (lane & m) == 0;
-        y0 = low ? y0 + o0 : o0 - y0;
-        y1 = low ? y1 + o1 : o1 - y1;
+      for (int h = 0; h < 8; h += 4) {
+        float a0 = x[h] + x[h + 1], a1 = x[h] - x[h + 1], a2 = x[h + 2] + x[h + 3], a3 = x[h + 2] - x[h + 3];
+        x[h] = a0 + a2;
+        x[h + 1] = a1 + a3;
+        x[h + 2] = a0 - a2;
+        x[h + 3] = a1 - a3;
       }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float u = x[j], v = x[4 + j];
+        x[j] = u + v;
+        x[4 + j] = u - v;
+      }
+      lane_stage<1>(x, r);
+      lane_stage<2>(x, r);
+      lane_stage<4>(x, r);
+      lane_stage<8>(x, r);
       const float norm = 0.08838834764831845f;   // 1 / sqrt(128)
-      x0 = y0 * norm;
-      x1 = y1 * norm;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] *= norm;
     }
   }
 
+  if (!live) return;
   if (kind == 0) {
     uint16_t* dst = p.q_out + ((size_t)b * p.Hq + head) * kSD;
-    dst[lane] = f32_to_bf16(x0);
-    dst[lane + 64] = f32_to_bf16(x1);
+    *reinterpret_cast<uint2*>(dst + 4 * r) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+    *reinterpret_cast<uint2*>(dst + 64 + 4 * r) = make_uint2(pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7]));
     return;
   }
 
   // the cache slot of this token: page block_table[b][pos / page], offset pos % page; a position
   // or page id outside the table / cache is not stored
-  if (pos < 0 || pos >= p.bt_stride * p.page) return;
-  const int pid = p.block_table[(size_t)b * p.bt_stride + pos / p.page];
   if (pid < 0 || pid >= p.num_pages) return;
-  const int t = pos % p.page;
-  const int e = p.fp8 ? 1 : 2;
-  const int w = 64 / e;   // elements per 64-byte row
-  const size_t blk = ((size_t)pid * p.Hkv + head) * (size_t)p.page * kSD * e;
-  const int d0 = lane, d1 = lane + 64;
-  // K: [128 / w dim tiles][page][w]; V: [page / w token tiles][128][w]
-  const size_t o0 = kind == 1 ? (size_t)((d0 / w) * p.page + t) * w + d0 % w : (size_t)((t / w) * kSD + d0) * w + t % w;
-  const size_t o1 = kind == 1 ? (size_t)((d1 / w) * p.page + t) * w + d1 % w : (size_t)((t / w) * kSD + d1) * w + t % w;
-  uint8_t* base = (kind == 1 ? p.k_cache : p.v_cache) + blk;
+  const size_t blk = ((size_t)pid * p.Hkv + head) * (size_t)p.page * kSD;   // elements of one (page, head) block
   if (p.fp8) {
-    const float inv = 1.0f / (kind == 1 ? p.k_scale[head] : p.v_scale[head]);
-    base[o0] = f32_to_e4m3(fminf(fmaxf(x0 * inv, -448.f), 448.f));
-    base[o1] = f32_to_e4m3(fminf(fmaxf(x1 * inv, -448.f), 448.f));
+    const float inv = 1.0f / scale;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = fminf(fmaxf(x[j] * inv, -448.f), 448.f);
+    constexpr int wr = 64;   // codes per 64-byte row
+    if (kind == 1) {
+      // K: [2 dim tiles][page][64]; dims 4r..4r+3 in tile 0, 64+4r.. in tile 1
+      uint8_t* k = p.k_cache + blk + (size_t)t * wr + 4 * r;
+      *reinterpret_cast<uint32_t*>(k) = e4m3_pack4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<uint32_t*>(k + (size_t)p.page * wr) = e4m3_pack4(x[4], x[5], x[6], x[7]);
+    } else {
+      // V: [page / 64 token tiles][128][64]; each dim is its own 64-byte row
+      uint8_t* v = p.v_cache + blk + (size_t)(t / wr) * kSD * wr + t % wr;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[(size_t)((j < 4 ? 4 * r : 60 + 4 * r) + j) * wr] = e4m3_one(x[j]);
+    }
   } else {
-    reinterpret_cast<uint16_t*>(base)[o0] = f32_to_bf16(x0);
-    reinterpret_cast<uint16_t*>(base)[o1] = f32_to_bf16(x1);
+    constexpr int wr = 32;   // bf16 elements per 64-byte row
+    if (kind == 1) {
+      // K: [4 dim tiles][page][32]; dims 4r..4r+3 in tile r / 8, 64+4r.. in tile 2 + r / 8
+      uint16_t* k = reinterpret_cast<uint16_t*>(p.k_cache) + blk + (size_t)((r >> 3) * p.page + t) * wr + (4 * r) % wr;
+      *reinterpret_cast<uint2*>(k) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
+      *reinterpret_cast<uint2*>(k + (size_t)2 * p.page * wr) = make_uint2(pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7]));
+    } else {
+      // V: [page / 32 token tiles][128][32]
+      uint16_t* v = reinterpret_cast<uint16_t*>(p.v_cache) + blk + (size_t)(t / wr) * kSD * wr + t % wr;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[(size_t)((j < 4 ? 4 * r : 60 + 4 * r) + j) * wr] = (uint16_t)f32_to_bf16(x[j]);
+    }
   }
 }
 
@@ -164,6 +244,11 @@ extern "C" int attn_store_kv(const void* q_in, const void* k_in, const void* v_i
   if (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3) return LBSA_ERR_INVALID;
   if (kv_dtype == LBSA_KV_FP8_E4M3 && (!k_scale || !v_scale)) return LBSA_ERR_INVALID;
   if (head_dim != lbsa::kSD || page_size % 64 != 0) return LBSA_ERR_UNSUPPORTED;
+  // 8-byte pieces of the vectors and caches, 16-byte pieces of the gains
+  auto aligned = [](const void* ptr, uintptr_t a) { return ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % a == 0; };
+  if (!aligned(q_in, 8) || !aligned(k_in, 8) || !aligned(v_in, 8) || !aligned(q_out, 8) || !aligned(k_cache, 8) ||
+      !aligned(v_cache, 8) || !aligned(q_norm_w, 16) || !aligned(k_norm_w, 16))
+    return LBSA_ERR_INVALID;
   if ((int64_t)page_size * block_table_stride > INT32_MAX) return LBSA_ERR_INVALID;
   lbsa::StoreParams p{static_cast<const uint16_t*>(q_in), static_cast<const uint16_t*>(k_in),
                       static_cast<const uint16_t*>(v_in), q_norm_w, k_norm_w, positions,
@@ -172,8 +257,8 @@ extern "C" int attn_store_kv(const void* q_in, const void* k_in, const void* v_i
                       page_size, kv_dtype == LBSA_KV_FP8_E4M3 ? 1 : 0, hadamard, norm_eps, rope_theta, {}};
   for (int i = 0; i < lbsa::kSD / 2; ++i)
     p.freq[i] = rope_theta > 0.f ? std::pow((double)rope_theta, -2.0 * i / lbsa::kSD) : 0.0;
-  const int vecs = num_q_heads + 2 * num_kv_heads;
-  hipLaunchKernelGGL(lbsa::store_kv_kernel, dim3(B, (vecs + 3) / 4), dim3(256), 0, static_cast<hipStream_t>(stream),
+  const int tasks = (num_q_heads + 3) / 4 + 2 * ((num_kv_heads + 3) / 4);   // 4 heads of one kind per wave
+  hipLaunchKernelGGL(lbsa::store_kv_kernel, dim3(B, (tasks + 3) / 4), dim3(256), 0, static_cast<hipStream_t>(stream),
                      p);
   return hipGetLastError() == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;
 }

@@ -112,6 +112,51 @@ def test_store_matches_oracle(lb, fp8, norm, theta, had):
     note(f"fp8={fp8} norm={norm} theta={theta} hadamard={had}: q exact {np.mean(dq == 0):.4f}")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(6, 3), (5, 1), (12, 4)])
+def test_store_head_counts(lb, fp8, hq, hkv):
+    """Head counts that leave rows of a wave without a head (a wave holds four head vectors of one
+    kind): every stored value still matches the oracle and nothing past the heads is written."""
+    from load_balanced_split_attn_amd.paged import unpack_request
+    dev = torch.device("cuda")
+    B = 9
+    q, k, v, qw, kw = _inputs(90 + hq, B, Hq=hq, Hkv=hkv)
+    lens = [int(x) for x in np.random.default_rng(hq).integers(0, 3000, size=B)]
+    kc, vc, bt = _empty_cache(lens, 64, fp8, dev, Hkv=hkv)
+    pos = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ks = vs = None
+    if fp8:
+        ks = torch.exp2(torch.rand(hkv, generator=torch.Generator().manual_seed(11)) * 2 - 5).float()
+        vs = torch.exp2(torch.rand(hkv, generator=torch.Generator().manual_seed(12)) * 2 - 6).float()
+    q_dev = q.to(dev)
+    q_out = torch.full((B + 1, hq, 128), 7.0, dtype=torch.bfloat16, device=dev)   # one row of guard
+    lb.attn_store_kv(q_dev, k.to(dev), v.to(dev), pos, q_out[:B], kc, vc, bt, q_norm_w=qw.to(dev),
+                     k_norm_w=kw.to(dev), rope_theta=10000.0, hadamard=True,
+                     kv_scales=(ks.to(dev), vs.to(dev)) if fp8 else None)
+    torch.cuda.synchronize()
+    assert torch.all(q_out[B] == 7.0)
+    rq, rk, rv = SK.ref_store_kv(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                 np.array(lens, dtype=np.float64), qw.double().numpy(), kw.double().numpy(),
+                                 1e-6, 10000.0, True, ks.double().numpy() if fp8 else None,
+                                 vs.double().numpy() if fp8 else None)
+    dq = np.abs(q_out[:B].float().cpu().numpy().astype(np.float64) - rq)
+    assert np.all(dq <= _tol(rq))
+    table = e4m3_table()
+    for b, L in enumerate(lens):
+        kb, vb = unpack_request(kc, vc, bt, b, L + 1)
+        for got, ref in ((kb[L].cpu(), rk[b]), (vb[L].cpu(), rv[b])):
+            if fp8:
+                g = got.numpy()
+                dv = np.abs(table[g] - table[ref])
+                step = np.abs(table[np.minimum(ref.astype(np.int32) & 0x7F, 0x7D) + 1] - table[ref.astype(np.int32) & 0x7F])
+                assert np.all((g == ref) | (dv <= step + 1e-12)), f"request {b}"
+            else:
+                assert np.all(np.abs(got.double().numpy() - ref) <= _tol(ref)), f"request {b}"
+    # exactly the B new tokens were written: nonzero elements only at the stored positions
+    stored = sum(int(torch.count_nonzero(unpack_request(kc, vc, bt, b, L + 1)[0][L]).item()) for b, L in enumerate(lens))
+    assert int(torch.count_nonzero(kc).item()) == stored
+
+
 def test_hardware_rounding_exact(lb):
     """With no norm, RoPE or Hadamard the stored V is the input itself: the bf16 path stores it
     unchanged and the E4M3 path rounds x / scale with scale 1 exactly as the oracle does, exact
