@@ -463,7 +463,7 @@ def main() -> int:
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (decode attention shards by "
-              "request or KV head with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr)
+              "request or KV head with no exchange). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import numpy as np

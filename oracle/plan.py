@@ -17,7 +17,7 @@ The budget arithmetic is the one in [P2] §二.1 ``dynamic_tile_scheduler``:
 extra tile.  [P3]'s worked example: lengths 1024, 5120 and 2048 with 512-token
 tiles give 2, 10 and 4 tiles, and 4 workers receive 4 tiles each.
 
-Readings where the pages are silent (each one is also listed in the design doc):
+Readings where the pages are silent:
 
 * tile count is a ceiling (a partial last tile is still a tile; a floor, as in
   [P2]'s pseudocode, would drop tokens and make attention wrong);
@@ -114,18 +114,24 @@ def _greedy_fill(units: Sequence[Unit], num_workers: int, tile: int) -> Tuple[Li
     for w in range(num_workers):
         taken = stream[cursor:cursor + budget[w]]
         cursor += budget[w]
-        segs: List[Segment] = []
-        run_start = 0
-        for i in range(1, len(taken) + 1):
-            if i == len(taken) or taken[i][0] != taken[run_start][0]:
-                ui, t_first = taken[run_start]
-                t_last = taken[i - 1][1]
-                u = units[ui]
-                segs.append(Segment(u.b, u.qt, t_first * tile, min(u.extent, (t_last + 1) * tile)))
-                run_start = i
-        lists.append(segs)
+        lists.append(_runs(units, taken, tile))
     assert cursor == total
     return lists, total
+
+
+def _runs(units: Sequence[Unit], taken: Sequence[Tuple[int, int]], tile: int) -> List[Segment]:
+    """A worker's consecutive stretch of the stream, (unit, tile) pairs in stream order, as segments:
+    each maximal run of one unit's tiles is one segment."""
+    segs: List[Segment] = []
+    run_start = 0
+    for i in range(1, len(taken) + 1):
+        if i == len(taken) or taken[i][0] != taken[run_start][0]:
+            ui, t_first = taken[run_start]
+            t_last = taken[i - 1][1]
+            u = units[ui]
+            segs.append(Segment(u.b, u.qt, t_first * tile, min(u.extent, (t_last + 1) * tile)))
+            run_start = i
+    return segs
 
 
 def _serialise(B: int, units: Sequence[Unit], lists: Sequence[Sequence[Segment]],
@@ -299,6 +305,40 @@ def ref_plan_lpt(seq_lens: Sequence[int], num_workers: int, tile: int) -> np.nda
         words += [sg.b, sg.qt, sg.kv_begin, sg.kv_end]
     words += order
     return np.asarray(words, dtype=np.int32)
+
+
+def ref_plan_weighted(seq_lens: Sequence[int], num_workers: int, tile: int, split_cost: int) -> np.ndarray:
+    """Cost-weighted contiguous fill: steps 1, 2 and 4 as in ``ref_plan``, with step 3's equal
+    budgets counted in cost instead of tiles.  A variant of the pages' scheduler ([P3] §3.1 方案
+    steps 3-4 count uniform tiles; [P5] §五(一) counts a tile's size in tokens) for comparison.
+
+    Readings: a tile costs its KV tokens (a partial last tile costs less than a full one), and the
+    first tile of a request costs ``split_cost`` more — every request opens at least one split
+    (query load, pipeline start, a partial to write and combine); the splits a worker boundary adds
+    fall one per boundary whatever the placement, so they are not charged.  With C the total cost and
+    P_i the cost of the stream before tile i, tile i goes to worker
+        floor(W (2 P_i + c_i) / (2 C))
+    — the worker whose equal share [w C / W, (w + 1) C / W) of the cost holds the tile's midpoint —
+    which keeps every worker's stretch of the stream contiguous and its cost within one tile's cost
+    of C / W.  Serialised as a version-1 map, so the decode and combine kernels take it unchanged.
+    """
+    _check_common(num_workers, tile)
+    if split_cost < 0:
+        raise ValueError("split_cost must be >= 0")
+    units = decode_units(seq_lens)
+    stream = []                                   # (unit index, tile index, cost)
+    for ui, u in enumerate(units):
+        for t in range(tiles_of(u.extent, tile)):
+            stream.append((ui, t, min(tile, u.extent - t * tile) + (split_cost if t == 0 else 0)))
+    total_cost = sum(c for _, _, c in stream)
+    mine: List[List[Tuple[int, int]]] = [[] for _ in range(num_workers)]
+    before = 0
+    for ui, t, c in stream:
+        w = (num_workers * (2 * before + c)) // (2 * total_cost)
+        mine[w].append((ui, t))
+        before += c
+    lists = [_runs(units, taken, tile) for taken in mine]
+    return _serialise(len(seq_lens), units, lists, tile, 1, len(stream))
 
 
 # ----------------------------------------------------------------------------------------------

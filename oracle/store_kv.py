@@ -5,7 +5,7 @@ infrastructure only).
 projection — RoPE, RMSNorm, Hadamard, quantisation and the KV-cache write — into one kernel, so
 intermediates stay in registers and the cache is written directly in its low-bit format; §8 adds
 that the query/key are Hadamard-rotated before quantisation to spread outliers.  The pages list the
-steps but not their order or formulas.  Readings (each also stated in the design notes):
+steps but not their order or formulas.  Readings:
 
 * per head vector x of length D (D even):
   1. RMSNorm (optional):  x <- x / sqrt(mean(x^2) + eps) * w,  w a per-dim gain shared by all heads

@@ -416,6 +416,81 @@ def pin_lpt_hand_example(ref_plan_lpt, parse_map):
 
 
 # ------------------------------------------------------------------------------------------------
+# Cost-weighted comparison planner.
+
+def _weighted_worker_tiles(ref_plan_weighted, parse_map, lens, W, tile, split_cost):
+    mp = parse_map(ref_plan_weighted(lens, W, tile, split_cost))
+    assert mp.version == 1
+    per = []
+    for w in range(W):
+        tiles = []
+        for b, qt, a, e in mp.worker_segments(w).tolist():
+            assert qt == 0 and 0 <= a < e <= lens[b] and a % tile == 0 and (e % tile == 0 or e == lens[b])
+            tiles += [(b, t) for t in range(a // tile, -(-e // tile))]
+        per.append(tiles)
+    return mp, per
+
+
+def pin_weighted_contiguous_and_balanced(ref_plan_weighted, parse_map, trials=150, seed=11):
+    """The workers' tiles read in worker order are the task stream itself (a contiguous fill: no tile
+    lost, repeated or reordered); each worker holds one segment per request it touches; and every
+    worker's cost is within the largest tile cost of C / W.  The bound follows from the midpoint
+    rule: worker w's share [wC/W, (w+1)C/W) of the cost line is covered by its own tiles plus at most
+    half a tile at each end, and its own tiles reach at most half a tile beyond it on each side."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        B = int(rng.integers(0, 10))
+        W = int(rng.integers(1, 10))
+        tile = int(rng.choice([64, 128, 512]))
+        sc = int(rng.choice([0, 1, 64, 300, 2000]))
+        lens = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 4000, size=B)]
+        mp, per = _weighted_worker_tiles(ref_plan_weighted, parse_map, lens, W, tile, sc)
+        stream = [(b, t) for b, L in enumerate(lens) for t in range(-(-L // tile))]
+        assert [x for tiles in per for x in tiles] == stream
+        assert mp.T == len(stream)
+        assert mp.S == sum(len({b for b, _ in tiles}) for tiles in per)
+        if not stream:
+            continue
+        cost = lambda bt: min(tile, lens[bt[0]] - bt[1] * tile) + (sc if bt[1] == 0 else 0)
+        C = sum(cost(x) for x in stream)
+        cmax = max(cost(x) for x in stream)
+        for tiles in per:
+            cw = sum(cost(x) for x in tiles)
+            assert C - W * cmax <= W * cw <= C + W * cmax, (lens, W, tile, sc)
+
+
+def pin_weighted_worked_example(ref_plan_weighted, parse_map):
+    """With no split cost and whole tiles every tile costs the same, and the pages' worked example
+    (lengths 1024, 5120, 2048; 512-token tiles; 4 workers) again gives 4 tiles per worker with the
+    long request spread over workers — the same map as the pages' fill."""
+    ex = load_worked_example()
+    _, per = _weighted_worker_tiles(ref_plan_weighted, parse_map, ex["seq_lens"], ex["num_workers"], ex["tile"], 0)
+    assert [len(t) for t in per] == ex["tiles_per_worker"]
+    assert len({w for w, tiles in enumerate(per) for b, _ in tiles if b == 1}) > 1
+
+
+def pin_weighted_hand_examples(ref_plan_weighted, parse_map):
+    """Worked by hand (c = tile cost, mid = cost before the tile + c / 2, worker = floor(W mid / C)):
+    (a) 512, 100, 100, 100 on 2 workers: c = 512, 100, 100, 100, C = 812, mids 256, 562, 662, 762
+        -> workers 0, 1, 1, 1 (a tile count would pair the 512-token tile with a 100-token one);
+    (b) 512, 512, 10, 10 on 2 workers: split cost 0 -> C = 1044, mids 256, 768, 1029, 1039 -> 0, 1, 1, 1;
+        split cost 500 -> c = 1012, 1012, 510, 510, C = 3044, mids 506, 1518, 2279, 2789 -> 0, 0, 1, 1;
+    (c) 700, 1500, 0, 300 on 3 workers, 512-token tiles: c = 512, 188 | 512, 512, 476 | 300, C = 2500,
+        mids 256, 606, 956, 1468, 1962, 2350 -> 0, 0, 1, 1, 2, 2: worker loads 700, 1024, 776;
+    (d) 4096 then eight 64-token requests on 2 workers, split cost 512: the long request costs
+        4096 + 512 = 4608 and the eight short ones 8 x 576 = 4608, C = 9216; its last tile's mid is
+        4352 < 4608 and the first short one's 4896 -> the long request alone on worker 0."""
+    f = lambda lens, W, sc: [sorted(t) for t in _weighted_worker_tiles(ref_plan_weighted, parse_map, lens, W, 512, sc)[1]]
+    assert f([512, 100, 100, 100], 2, 0) == [[(0, 0)], [(1, 0), (2, 0), (3, 0)]]
+    assert f([512, 512, 10, 10], 2, 0) == [[(0, 0)], [(1, 0), (2, 0), (3, 0)]]
+    assert f([512, 512, 10, 10], 2, 500) == [[(0, 0), (1, 0)], [(2, 0), (3, 0)]]
+    assert f([700, 1500, 0, 300], 3, 0) == [[(0, 0), (0, 1)], [(1, 0), (1, 1)], [(1, 2), (3, 0)]]
+    mp, _ = _weighted_worker_tiles(ref_plan_weighted, parse_map, [700, 1500, 0, 300], 3, 512, 0)
+    assert mp.segs.tolist() == [[0, 0, 0, 700], [1, 0, 0, 1024], [1, 0, 1024, 1500], [3, 0, 0, 300]]
+    assert f([4096] + [64] * 8, 2, 512) == [[(0, t) for t in range(8)], [(b, 0) for b in range(1, 9)]]
+
+
+# ------------------------------------------------------------------------------------------------
 # Producer step (normalise, rotate, quantise, store).
 
 def pin_round_bf16_library(round_bf16):

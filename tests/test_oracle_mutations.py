@@ -56,6 +56,14 @@ def _lpt_pins(m):
     ]
 
 
+def _weighted_pins(m):
+    return [
+        lambda: P.pin_weighted_hand_examples(m.ref_plan_weighted, m.parse_map),
+        lambda: P.pin_weighted_worked_example(m.ref_plan_weighted, m.parse_map),
+        lambda: P.pin_weighted_contiguous_and_balanced(m.ref_plan_weighted, m.parse_map, trials=60),
+    ]
+
+
 def _store_pins(m):
     from oracle import fp8
     return [
@@ -119,6 +127,17 @@ LPT_MUTANTS = {
     "runs not merged": ("if lst and lst[-1][0] == ui and lst[-1][2] == t - 1:", "if False:"),
 }
 
+WEIGHTED_MUTANTS = {
+    "tile start instead of its midpoint": ("w = (num_workers * (2 * before + c)) // (2 * total_cost)",
+                                           "w = (num_workers * (2 * before)) // (2 * total_cost)"),
+    "split cost ignored": ("+ (split_cost if t == 0 else 0)))", "+ 0))"),
+    "split cost on every tile": ("+ (split_cost if t == 0 else 0)))", "+ split_cost))"),
+    "tiles counted, not tokens": ("stream.append((ui, t, min(tile, u.extent - t * tile) +",
+                                  "stream.append((ui, t, tile +"),
+    "worker index rounded up": ("w = (num_workers * (2 * before + c)) // (2 * total_cost)",
+                                "w = min(num_workers - 1, -(-(num_workers * (2 * before + c)) // (2 * total_cost)))"),
+}
+
 STORE_MUTANTS = {
     "rope sign flipped": ("[x1 * c - x2 * s, x2 * c + x1 * s]", "[x1 * c + x2 * s, x2 * c - x1 * s]"),
     "rope frequency exponent": ("freq = theta ** (-2.0 * i / D)", "freq = theta ** (-1.0 * i / D)"),
@@ -160,6 +179,13 @@ def test_lpt_mutant_is_caught(name):
     assert _caught(_lpt_pins(m)), f"no pin catches: {name}"
 
 
+@pytest.mark.parametrize("name", sorted(WEIGHTED_MUTANTS))
+def test_weighted_mutant_is_caught(name):
+    old, new = WEIGHTED_MUTANTS[name]
+    m = _load_mutant("plan", old, new, count=1)
+    assert _caught(_weighted_pins(m)), f"no pin catches: {name}"
+
+
 @pytest.mark.parametrize("name", sorted(STORE_MUTANTS))
 def test_store_mutant_is_caught(name):
     old, new = STORE_MUTANTS[name]
@@ -179,5 +205,5 @@ def test_unmutated_oracle_passes_all_pins():
     import oracle.fp8 as F
     import oracle.plan as Pl
     import oracle.store_kv as SK
-    for pin in _attention_pins(A) + _plan_pins(Pl) + _fp8_pins(F) + _lpt_pins(Pl) + _store_pins(SK):
+    for pin in _attention_pins(A) + _plan_pins(Pl) + _fp8_pins(F) + _lpt_pins(Pl) + _weighted_pins(Pl) + _store_pins(SK):
         pin()

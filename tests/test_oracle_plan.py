@@ -158,3 +158,25 @@ def test_lpt_equal_sizes_round_robin():
 def test_lpt_hand_example():
     from oracle.plan import parse_map, ref_plan_lpt
     P.pin_lpt_hand_example(ref_plan_lpt, parse_map)
+
+
+def test_weighted_contiguous_and_balanced():
+    from oracle.plan import parse_map, ref_plan_weighted
+    P.pin_weighted_contiguous_and_balanced(ref_plan_weighted, parse_map)
+
+
+def test_weighted_worked_example():
+    from oracle.plan import parse_map, ref_plan_weighted
+    P.pin_weighted_worked_example(ref_plan_weighted, parse_map)
+
+
+def test_weighted_hand_examples():
+    from oracle.plan import parse_map, ref_plan_weighted
+    P.pin_weighted_hand_examples(ref_plan_weighted, parse_map)
+
+
+def test_weighted_rejects_negative_split_cost():
+    import pytest
+    from oracle.plan import ref_plan_weighted
+    with pytest.raises(ValueError):
+        ref_plan_weighted([100], 2, 64, -1)
