@@ -462,7 +462,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (decode attention shards by "
+        print("bench.py measures one GPU: the library has no multi-GPU path (decode attention shards by "
               "request or KV head with no exchange). Run with --gpus 1.", file=sys.stderr)
         return 2
 
@@ -623,6 +623,38 @@ def main() -> int:
             "dynamic_speedup": round(rl["total_ms"] / args.static_steps / ms_per_step, 3)}
         log(f"lpt map: S={st.S}, step {result['lpt_baseline']['us_per_step']} us")
         del st
+
+    if not args.no_static and wl.name != "tiny":
+        # the cost-weighted contiguous fill (tile cost in tokens plus a per-request split cost) at a
+        # few tile sizes and split costs
+        rows = []
+        for planner, tile_w, sc in (("greedy", 128, 0), ("greedy", 64, 0), ("weighted", 512, 0), ("weighted", 512, 128),
+                                    ("weighted", 128, 0), ("weighted", 128, 128), ("weighted", 64, 256)):
+            st = DecodeStep(wl.kv_lens, dev, num_workers=workers, tile=tile_w, head_groups=args.head_groups,
+                            planner=planner, split_cost=sc)
+
+            def w_split(i, st=st):
+                k_, v_ = caches[i % copies]
+                st.splitkv(q, k_, v_, bt, scale)
+
+            rw = time_steps(w_split, lambda i, st=st: st.combine(out), args.static_steps, 2)
+            timing_w = torch.zeros((st.W * args.head_groups, 4), dtype=torch.int64, device=dev)
+            st.splitkv(q, kc, vc, bt, scale, timing=timing_w)
+            torch.cuda.synchronize()
+            us = rw["total_ms"] / args.static_steps * 1e3
+            rows.append({"planner": planner, "tile": tile_w, "split_cost": sc, "segments": st.S,
+                         "us_per_step": round(us, 2),
+                         "splitkv_us": round(float(np.mean(rw["split_ms"])) * 1e3, 2),
+                         "combine_us": round(float(np.mean(rw["combine_ms"])) * 1e3, 2),
+                         "per_cu_max_over_mean": round(per_cu_busy(timing_w)["max_over_mean"], 3),
+                         "greedy_speedup": round(us / (ms_per_step * 1e3), 3)})
+            log(f"{planner} map tile={tile_w} split_cost={sc}: S={st.S}, step {us:.1f} us")
+            del st
+        result["weighted_baseline"] = {
+            "what": "cost-weighted contiguous fill: tile cost = KV tokens + split_cost on a request's first "
+                    "tile, tile to the worker whose equal cost share holds its midpoint; beside it the greedy "
+                    "fill at smaller tiles; greedy_speedup = this step / the 512-token greedy-fill step",
+            "sweep": rows}
 
     if not args.no_probe:
         # the device's streaming-read ceiling, measured on the same run (the KV cache itself)

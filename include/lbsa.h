@@ -129,6 +129,22 @@ int attn_plan_device(const int32_t* seq_lens, int32_t B, int32_t num_workers, in
                      int32_t* map, int32_t map_capacity, void* stream);
 
 /*
+ * Cost-weighted contiguous fill, a comparison planner: the tile cut and task stream of attn_plan
+ * ([P3] §3.1 方案 steps 1-2), with the equal budgets of steps 3-4 counted in cost instead of
+ * tiles — a tile costs its KV tokens (the tile sizes of [P5] §五(一)) and a request's first tile
+ * costs split_cost more (the fixed work of a split: query load, pipeline start, partial and
+ * combine).  With P_i the cost of the stream before tile i, c_i its cost and C the total, tile i
+ * goes to worker floor(W (2 P_i + c_i) / (2 C)): every worker takes one contiguous stretch of the
+ * stream whose cost is within the largest tile cost of C / W.  Writes a version-1 map (the layout
+ * of attn_plan, read by the same kernels), S <= W + B - 1.
+ *   split_cost   >= 0, in KV tokens
+ * O(B + T) time, no allocation.  Errors and capacity reporting as attn_plan (LBSA_ERR_INVALID also
+ * for a negative split_cost).
+ */
+int attn_plan_weighted(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile,
+                       int32_t split_cost, int32_t* map, int32_t map_capacity, int32_t* map_words_out);
+
+/*
  * LPT comparison map ([P5] "大模型推理性能优化揭秘：从算子到系统的全链路技术解析" §五(一): tiles
  * sorted by decreasing size, each put on the least-loaded worker).  A tile's size and a worker's
  * load are counted in KV tokens; equal sizes keep stream order, equal loads go to the lowest worker

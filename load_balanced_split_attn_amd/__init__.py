@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill", "attn_plan_device",
-    "attn_plan_lpt",
+    "attn_plan_lpt", "attn_plan_weighted",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
     "attn_combine", "attn_store_kv",
     "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
@@ -39,6 +39,7 @@ _SIGNATURES = {
     "attn_plan": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
     "attn_plan_static": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
     "attn_plan_lpt": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
+    "attn_plan_weighted": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
     "attn_plan_prefill": (ctypes.c_int, [_c_i32p, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                          _c_i32p, _c_i32, _c_i32p]),
     "attn_query_workers": (ctypes.c_int, [ctypes.c_int, _c_i32, _c_i32, _c_i32p]),
@@ -140,6 +141,14 @@ def attn_plan_lpt(seq_lens: Sequence[int], num_workers: int, tile: int = 512) ->
     """LPT comparison map (version 2, with a per-worker order list)."""
     lens = _i32_host(seq_lens)
     return _plan_call(lib().attn_plan_lpt, "attn_plan_lpt", _ptr_i32(lens), len(lens), num_workers, tile)
+
+
+def attn_plan_weighted(seq_lens: Sequence[int], num_workers: int, tile: int = 512, split_cost: int = 0) -> np.ndarray:
+    """Cost-weighted contiguous fill (version-1 map): tile cost = KV tokens, plus split_cost on each
+    request's first tile; tile i to worker floor(W (2 P_i + c_i) / (2 C))."""
+    lens = _i32_host(seq_lens)
+    return _plan_call(lib().attn_plan_weighted, "attn_plan_weighted", _ptr_i32(lens), len(lens), num_workers, tile,
+                      split_cost)
 
 
 def attn_plan_prefill(q_lens: Sequence[int], kv_lens: Sequence[int], num_workers: int, q_tile: int = 128,

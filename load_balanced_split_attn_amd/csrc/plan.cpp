@@ -155,6 +155,65 @@ int plan_units(const Units& units, int32_t B, int32_t W, int32_t kv_tile, int32_
   return S2 == S ? LBSA_OK : LBSA_ERR_INVALID;
 }
 
+// Cost-weighted contiguous fill (a comparison planner): the stream of attn_plan, with tile costs in
+// KV tokens (as [P5] "大模型推理性能优化揭秘" §五(一) sizes its tiles) plus split_cost on each
+// request's first tile.  Tile i goes to worker floor(W (2 P_i + c_i) / (2 C)) — P_i the cost before
+// it, C the total — so workers take contiguous stretches whose costs are within one tile's cost of
+// C / W.  One walk over the tiles per pass, no allocation; the map is version 1.
+int64_t weighted_fill(const int32_t* lens, int32_t B, int32_t W, int64_t tile, int64_t split_cost, int64_t C,
+                      const Writer* wr) {
+  int64_t segs = 0, before = 0;
+  int32_t w_open = 0;   // workers <= w_open have their worker_ptr set
+  bool have = false;
+  int32_t run_b = 0, run_w = 0;
+  int64_t run_t0 = 0, run_t1 = 0;
+  auto close = [&]() {
+    if (!have) return;
+    if (wr) {
+      int32_t* sg = wr->seg(segs);
+      const int64_t end = (run_t1 + 1) * tile;
+      sg[0] = run_b;
+      sg[1] = 0;
+      sg[2] = (int32_t)(run_t0 * tile);
+      sg[3] = (int32_t)(end < lens[run_b] ? end : lens[run_b]);
+    }
+    ++segs;
+    have = false;
+  };
+  if (wr) wr->worker_ptr()[0] = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    close();
+    if (wr) {
+      wr->unit_ptr()[b] = (int32_t)segs;
+      wr->units()[2 * b] = b;
+      wr->units()[2 * b + 1] = 0;
+    }
+    const int64_t L = lens[b];
+    const int64_t n = tiles_for(L, tile);
+    for (int64_t t = 0; t < n; ++t) {
+      const int64_t c = (L - t * tile < tile ? L - t * tile : tile) + (t == 0 ? split_cost : 0);
+      const int32_t w = (int32_t)((__int128)W * (2 * before + c) / (2 * (__int128)C));
+      before += c;
+      if (have && w != run_w) close();
+      if (have) {
+        run_t1 = t;
+        continue;
+      }
+      for (; w_open < w; ++w_open)
+        if (wr) wr->worker_ptr()[w_open + 1] = (int32_t)segs;
+      have = true;
+      run_b = b;
+      run_w = w;
+      run_t0 = run_t1 = t;
+    }
+  }
+  close();
+  if (wr) {
+    wr->unit_ptr()[B] = (int32_t)segs;
+    for (; w_open < W; ++w_open) wr->worker_ptr()[w_open + 1] = (int32_t)segs;
+  }
+  return segs;
+}
 }  // namespace
 
 extern "C" {
@@ -251,6 +310,35 @@ int attn_plan_static(const int32_t* seq_lens, int32_t B, int32_t num_splits, int
   }
   wr.unit_ptr()[B] = (int32_t)s;
   return LBSA_OK;
+}
+
+int attn_plan_weighted(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile, int32_t split_cost,
+                       int32_t* map, int32_t map_capacity, int32_t* map_words_out) {
+  if (B < 0 || num_workers < 1 || tile < 1 || split_cost < 0 || !map || map_capacity < 0) return LBSA_ERR_INVALID;
+  if (B > 0 && !seq_lens) return LBSA_ERR_INVALID;
+  int64_t T = 0, C = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (seq_lens[b] < 0) return LBSA_ERR_INVALID;
+    T += tiles_for(seq_lens[b], tile);
+    C += seq_lens[b] + (seq_lens[b] > 0 ? split_cost : 0);
+  }
+  if (T > INT32_MAX) return LBSA_ERR_INVALID;
+  Writer probe{nullptr, num_workers, B};
+  const int64_t S = weighted_fill(seq_lens, B, num_workers, tile, split_cost, C, nullptr);
+  const int64_t words = probe.seg_base() + 4 * S;
+  if (words > INT32_MAX) return LBSA_ERR_INVALID;
+  if (map_words_out) *map_words_out = (int32_t)words;
+  if (words > map_capacity) return LBSA_ERR_CAPACITY;
+  Writer wr{map, num_workers, B};
+  map[0] = LBSA_MAP_VERSION;
+  map[1] = B;
+  map[2] = num_workers;
+  map[3] = tile;
+  map[4] = (int32_t)S;
+  map[5] = (int32_t)T;
+  map[6] = 1;
+  map[7] = B;
+  return weighted_fill(seq_lens, B, num_workers, tile, split_cost, C, &wr) == S ? LBSA_OK : LBSA_ERR_INVALID;
 }
 
 // LPT bucket packing ([P5] "大模型推理性能优化揭秘：从算子到系统的全链路技术解析" §五(一)), the

@@ -13,14 +13,16 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (KV_BF16, KV_FP8_E4M3, attn_combine, attn_plan, attn_plan_lpt, attn_plan_static, attn_query_workers,
+from . import (KV_BF16, KV_FP8_E4M3, attn_combine, attn_plan, attn_plan_lpt, attn_plan_static, attn_plan_weighted,
+               attn_query_workers,
                attn_splitkv, attn_splitkv_fp8, map_header, max_splits_of)
 
 
 class DecodeStep:
     def __init__(self, seq_lens: Sequence[int], device, num_workers: Optional[int] = None, tile: int = 512,
                  head_groups: int = 8, num_q_heads: int = 64, head_dim: int = 128,
-                 static_splits: Optional[int] = None, kv_dtype: int = KV_BF16, planner: str = "greedy"):
+                 static_splits: Optional[int] = None, kv_dtype: int = KV_BF16, planner: str = "greedy",
+                 split_cost: int = 0):
         device = torch.device(device)
         self.seq_lens_host = [int(x) for x in seq_lens]
         if static_splits is not None:
@@ -32,8 +34,10 @@ class DecodeStep:
                 self.map_host = attn_plan(self.seq_lens_host, num_workers, tile)
             elif planner == "lpt":
                 self.map_host = attn_plan_lpt(self.seq_lens_host, num_workers, tile)
+            elif planner == "weighted":
+                self.map_host = attn_plan_weighted(self.seq_lens_host, num_workers, tile, split_cost)
             else:
-                raise ValueError(f"unknown planner {planner!r} (greedy or lpt)")
+                raise ValueError(f"unknown planner {planner!r} (greedy, lpt or weighted)")
         hdr = map_header(self.map_host)
         self.W, self.S, self.U, self.T = hdr["W"], hdr["S"], hdr["U"], hdr["T"]
         self.max_splits = max_splits_of(self.map_host)

@@ -180,6 +180,40 @@ def test_errors_and_capacity(L):
     assert lib.attn_combine(dummy, dummy, dummy, dummy, 1, 1, None, None, 64, 128, dummy, 0, -1, None) == -1
 
 
+def test_weighted_plan_bit_exact():
+    """attn_plan_weighted (C++) reproduces the oracle's cost-weighted map word for word: random
+    batches with empty requests and partial tiles, several split costs, and the bench workloads at
+    the tile sizes and split costs the bench compares."""
+    import load_balanced_split_attn_amd as lb
+    from oracle.plan import ref_plan_weighted
+    rng = np.random.default_rng(23)
+    for _ in range(600):
+        B = int(rng.integers(0, 14))
+        W = int(rng.integers(1, 24))
+        tile = int(rng.choice([16, 64, 128, 512]))
+        sc = int(rng.choice([0, 1, 64, 256, 5000]))
+        lens = [int(x) if rng.random() > 0.2 else 0 for x in rng.integers(1, 5000, size=B)]
+        got = lb.attn_plan_weighted(lens, W, tile, sc)
+        assert np.array_equal(got, ref_plan_weighted(lens, W, tile, sc)), (lens, W, tile, sc)
+    import workloads as WL
+    for name in ("tiny", "uniform", "mixed", "long_tail"):
+        wl = WL.BY_NAME[name]()
+        W = wl.workers or 128
+        for tile, sc in ((512, 0), (512, 128), (128, 128), (64, 256)):
+            assert np.array_equal(lb.attn_plan_weighted(wl.kv_lens, W, tile, sc),
+                                  ref_plan_weighted(wl.kv_lens, W, tile, sc)), (name, tile, sc)
+    # lengths at the int32 limit: the cost products need more than 64 bits of headroom
+    big = [2**31 - 1, 2**31 - 1, 5]
+    assert np.array_equal(lb.attn_plan_weighted(big, 7, 2**20, 2**30), ref_plan_weighted(big, 7, 2**20, 2**30))
+
+
+def test_weighted_plan_errors():
+    import load_balanced_split_attn_amd as lb
+    for args in (([10], 2, 64, -1), ([10], 0, 64, 0), ([10], 2, 0, 0), ([-1], 2, 64, 0)):
+        with pytest.raises(lb.LbsaError):
+            lb.attn_plan_weighted(*args)
+
+
 def test_lpt_plan_bit_exact():
     """attn_plan_lpt (C++) reproduces the oracle's version-2 LPT map word for word."""
     import load_balanced_split_attn_amd as lb

@@ -159,6 +159,29 @@ def test_timing_records(lb):
         assert_close(out[b].cpu().numpy(), ref[b], f"timed run request {b}")
 
 
+@pytest.mark.parametrize("tile,split_cost", [(512, 0), (128, 128), (64, 300)])
+def test_weighted_map_partials(lb, tile, split_cost):
+    """A cost-weighted map (segments cut at any tile boundary, partial tiles weighted by their
+    tokens): every slot's partial and the combined output match the oracle's."""
+    wl = WL.random_decode(17 + tile, 7, 3000, min_len=1)
+    words = lb.attn_plan_weighted(wl.kv_lens, 10, tile, split_cost)
+    from oracle.plan import ref_plan_weighted
+    assert np.array_equal(words, ref_plan_weighted(wl.kv_lens, 10, tile, split_cost))
+    out, parts = _run(lb, wl, words, poison=True)
+    ref = oracle_decode(wl)
+    got = out.cpu().numpy()
+    for b in range(wl.batch):
+        assert_close(got[b], ref[b], f"weighted request {b}")
+    q = wl.q().double().numpy()
+    kvs = [wl.kv(b) for b in range(wl.batch)]
+    rparts = ref_split_partials(words, [q[b:b + 1] for b in range(wl.batch)],
+                                [k.double().numpy() for k, _ in kvs], [v.double().numpy() for _, v in kvs], SCALE)
+    pm, pl, po = (t.cpu().numpy() for t in parts)
+    for s_, (m, l, o) in enumerate(rparts):
+        assert np.max(np.abs(pm[s_] - m[0])) <= 1e-3, f"slot {s_} m"
+        assert_close(po[s_] / pl[s_][:, None], o[0] / l[0][:, None], f"slot {s_} o/l")
+
+
 def test_lpt_map_partials(lb):
     """A version-2 (LPT) map: every slot's partial matches the oracle's partial of that segment, and
     the combined output matches the oracle."""
