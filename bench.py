@@ -34,6 +34,8 @@ DESCRIPTIONS = {
                "(shuffled block table), tile 512",
     "long_tail": "single long request plus short tail: KV 192K + 15 x U[1K,2K], 1 query token, GQA 64q/8kv, "
                  "d=128, bf16, paged 64-token KV (shuffled block table), tile 512",
+    "control": "even control for the mixed batch: B=40 x KV 43622 (the mixed batch's tokens), 1 query token, "
+               "GQA 64q/8kv, d=128, bf16, paged 64-token KV (shuffled block table), tile 512",
     "tiny": "worked example: KV 1024/5120/2048, 1 query token, GQA 64q/8kv, d=128, bf16, contiguous pages, "
             "tile 512, 4 workers",
 }
@@ -152,10 +154,11 @@ def calibration_copy(dev) -> None:
     del src, dst
 
 
-def cpu_oracle_baseline(wl, budget_s: float, scale: float) -> dict:
+def cpu_oracle_baseline(wl, budget_s: float, scale: float, workers: int, tile: int) -> dict:
     import numpy as np
     import torch
     from oracle.attention import ref_attention
+    from oracle.plan import ref_plan
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
@@ -176,7 +179,13 @@ def cpu_oracle_baseline(wl, budget_s: float, scale: float) -> dict:
         if spent >= budget_s:
             break
     kv_bytes = tokens * wl.hkv * wl.head_dim * 2 * 2
+    # the oracle's planner (pure Python) on the same batch, beside the library's host planner
+    t = time.perf_counter()
+    for _ in range(5):
+        ref_plan(wl.kv_lens, workers, tile)
+    ref_plan_us = (time.perf_counter() - t) / 5 * 1e6
     return {"value": kv_bytes / spent / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
+            "ref_plan_us": round(ref_plan_us, 1),
             "sample": f"fp64 oracle (numpy) on the first {len(done)} of {wl.batch} requests of the same batch "
                       f"({tokens} KV tokens), {spent:.1f} s of CPU time; bf16 KV bytes / time",
             "seconds": spent, "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count()}
@@ -690,7 +699,7 @@ def main() -> int:
 
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a CPU sample")
-        result["cpu_baseline"] = cpu_oracle_baseline(wl, args.cpu_seconds, scale)
+        result["cpu_baseline"] = cpu_oracle_baseline(wl, args.cpu_seconds, scale, workers, args.tile)
     print(json.dumps(result), flush=True)
     return 0
 

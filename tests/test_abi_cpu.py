@@ -82,7 +82,7 @@ def test_plan_prefill_bit_exact_random(L):
         assert np.array_equal(got, exp), (q_lens, kv_lens, W, q_tile, kv_tile, causal)
 
 
-@pytest.mark.parametrize("name", ["tiny", "uniform", "mixed", "long_tail"])
+@pytest.mark.parametrize("name", ["tiny", "uniform", "mixed", "long_tail", "control"])
 @pytest.mark.parametrize("W", [4, 256, 384, 512, 1024])
 def test_plan_bit_exact_workloads(L, name, W):
     wl = WL.BY_NAME[name]()

@@ -13,7 +13,7 @@ from gpu_helpers import SCALE, assert_close, decode_inputs, errors, note, oracle
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["uniform", "mixed", "long_tail"])
+@pytest.mark.parametrize("name", ["uniform", "mixed", "long_tail", "control"])
 def test_full_size(name):
     import load_balanced_split_attn_amd as lb
     from load_balanced_split_attn_amd.decode import DecodeStep

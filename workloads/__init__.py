@@ -159,6 +159,12 @@ def long_tail() -> Workload:
     return Workload("long_tail", 4, lens, [1] * len(lens))
 
 
+def control() -> Workload:
+    """The mixed batch's token count spread evenly: 40 requests of 43,622 tokens (control for the
+    length mix: same KV bytes, no imbalance to remove)."""
+    return Workload("control", 6, [43622] * 40, [1] * 40)
+
+
 def prefill(chunk: int = 2048, requests: int = 8) -> Workload:
     """Chunked causal prefill: per request a ``chunk``-row query chunk after a cached prefix whose
     length is log-uniform in [8K, 128K] tokens."""
@@ -207,4 +213,5 @@ def random_mtp(seed: int, batch: int, max_len: int, max_q: int = 4, min_len: int
     return Workload(f"random_mtp_{seed}", 400 + seed, lens, qs, kind="mtp")
 
 
-BY_NAME = {"tiny": tiny, "uniform": uniform, "mixed": mixed, "long_tail": long_tail, "prefill": prefill}
+BY_NAME = {"tiny": tiny, "uniform": uniform, "mixed": mixed, "long_tail": long_tail, "control": control,
+           "prefill": prefill}
