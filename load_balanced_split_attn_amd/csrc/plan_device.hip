@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_device_kernel(const int32_t
   const int tid = threadIdx.x;
   int32_t* worker_ptr = map + LBSA_MAP_HEADER_WORDS;
   int32_t* unit_ptr = worker_ptr + W + 1;
-  int32_t* units = unit_ptr + B + 1;   // [B][2]; during the build: (nonempty-before count, pre)
+  int32_t* units = unit_ptr + B + 1;   // [B][2]; while the map is built: (nonempty-before count, pre)
   int32_t* segs = units + 2 * (int64_t)B;
   if (tid == 0) bad_lds = 0;
   __syncthreads();
