@@ -165,33 +165,29 @@ def cpu_oracle_baseline(wl, budget_s: float, scale: float, workers: int, tile: i
     except Exception:
         threads = os.cpu_count() or 1
     q = wl.q().to(torch.float64).numpy()
-    # one pass over the batch's requests, each request's oracle call repeated `reps` times so the
-    # pass takes about the time budget (reps from the first request's warm rate); input generation and
-    # the bf16 -> fp64 widening are done once per request and not timed
-    total_tokens = max(sum(wl.kv_lens), 1)
-    spent, tokens, runs, reps = 0.0, 0, 0, None
+    # one pass over the batch's requests, each request's oracle call repeated so that the pass takes
+    # about the time budget: before each request the repeat count is set from the rate measured so
+    # far and the budget and tokens left; input generation and the bf16 -> fp64 widening are done
+    # once per request and not timed
+    left_tokens = sum(wl.kv_lens)
+    spent, tokens, runs, reps_used = 0.0, 0, 0, []
     for b in range(wl.batch):
         k, v = wl.kv(b)
         kd, vd = k.to(torch.float64).numpy(), v.to(torch.float64).numpy()
-        if reps is None:
+        if b == 0:
             ref_attention(q[b:b + 1], kd, vd, scale)   # untimed warm-up (library and page faults)
-        n = 1 if reps is None else reps
-        for _ in range(n):
+        reps = 1
+        if tokens > 0 and left_tokens > 0:
+            rate = spent / tokens
+            reps = max(1, int(round((budget_s - spent) / max(rate * left_tokens, 1e-9))))
+        for _ in range(reps):
             t = time.perf_counter()
             ref_attention(q[b:b + 1], kd, vd, scale)
-            dt = time.perf_counter() - t
-            spent += dt
+            spent += time.perf_counter() - t
             tokens += wl.kv_lens[b]
             runs += 1
-        if reps is None:
-            est_pass = dt / max(wl.kv_lens[b], 1) * total_tokens
-            reps = max(1, int(round(budget_s / max(est_pass, 1e-9))))
-            for _ in range(reps - 1):
-                t = time.perf_counter()
-                ref_attention(q[b:b + 1], kd, vd, scale)
-                spent += time.perf_counter() - t
-                tokens += wl.kv_lens[b]
-                runs += 1
+        reps_used.append(reps)
+        left_tokens -= wl.kv_lens[b]
         del kd, vd
     kv_bytes = tokens * wl.hkv * wl.head_dim * 2 * 2
     # the oracle's planner (pure Python) on the same batch, beside the library's host planner
@@ -201,8 +197,9 @@ def cpu_oracle_baseline(wl, budget_s: float, scale: float, workers: int, tile: i
     ref_plan_us = (time.perf_counter() - t) / 5 * 1e6
     return {"value": kv_bytes / spent / 1e12, "unit": "TB/s", "cores": int(threads), "kind": "oracle",
             "ref_plan_us": round(ref_plan_us, 1),
-            "sample": f"fp64 oracle (numpy) over all {wl.batch} requests of the same batch, each run {reps} times "
-                      f"({runs} runs, {tokens} KV tokens), {spent:.1f} s of CPU time; bf16 KV bytes / time",
+            "sample": f"fp64 oracle (numpy) over all {wl.batch} requests of the same batch, each run "
+                      f"{min(reps_used)}-{max(reps_used)} times ({runs} runs, {tokens} KV tokens), {spent:.1f} s of "
+                      f"CPU time; bf16 KV bytes / time",
             "seconds": spent, "cpu_model": _cpu_model(), "os_cpu_count": os.cpu_count()}
 
 
