@@ -61,6 +61,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int u = (int)(rest / p.R);
   const int b = units[2 * u];
   const int qt = units[2 * u + 1];
+  // the map's own header bounds its requests and slots (the sizes the caller allocated from)
+  if (b < 0 || b >= p.map[1]) return;
   int64_t orow;
   if (p.q_lens) {
     const int row_in_req = qt * p.R + r;
@@ -71,6 +73,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   }
   const int s0 = unit_ptr[u];
   const int n = unit_ptr[u + 1] - s0;
+  if (s0 < 0 || n < 0 || s0 + n > p.map[4]) return;
   auto slot = [&](int i) -> int64_t { return ((int64_t)(s0 + i) * p.R + r) * p.Hq + h; };
 
   float M = -INFINITY;

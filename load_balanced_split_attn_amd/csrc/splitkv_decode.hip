@@ -375,7 +375,7 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
     const int s = order ? order[j] : j;
     if (s < 0 || s >= p.S) continue;
     const int b = segs[4 * s];
-    const int kv_begin = segs[4 * s + 2];
+    const int kv_begin = max(segs[4 * s + 2], 0);
     int kv_end = segs[4 * s + 3];
     if (b < 0 || b >= p.B) continue;
     if (ROWS > 1 && segs[4 * s + 1] != 0) continue;   // every request is one unit of R rows

@@ -204,7 +204,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
   for (int s = s_begin; s < s_end; ++s) {
     const int b = segs[4 * s];
     const int qt = segs[4 * s + 1];
-    const int kv_begin = segs[4 * s + 2];
+    const int kv_begin = max(segs[4 * s + 2], 0);
     int kv_end = segs[4 * s + 3];
     if (b < 0 || b >= p.B) continue;
     const int q_len = q_lens[b];
