@@ -532,6 +532,24 @@ def main() -> int:
     for _ in range(100):
         lb.attn_plan(wl.kv_lens, workers, args.tile)
     plan_us = (time.perf_counter() - t) / 100 * 1e6
+    # the C planner alone (one ctypes call into a buffer of the right size), and the map's upload
+    import ctypes
+    lens_h = np.ascontiguousarray(np.asarray(wl.kv_lens, dtype=np.int32))
+    buf = np.zeros(len(step.map_host), dtype=np.int32)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    words = ctypes.c_int32(0)
+    t = time.perf_counter()
+    for _ in range(1000):
+        lb.lib().attn_plan(lens_h.ctypes.data_as(i32p), len(lens_h), workers, args.tile, buf.ctypes.data_as(i32p),
+                           len(buf), ctypes.byref(words))
+    plan_c_us = (time.perf_counter() - t) / 1000 * 1e6
+    assert np.array_equal(buf, step.map_host)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(100):
+        torch.from_numpy(buf).to(dev)
+    torch.cuda.synchronize()
+    upload_us = (time.perf_counter() - t) / 100 * 1e6
     out = torch.empty((wl.batch, wl.hq, wl.head_dim), dtype=torch.float32, device=dev)
     # the same map built on the device (attn_plan_device), timed with events on the stream
     lens_d = torch.tensor(wl.kv_lens, dtype=torch.int32, device=dev)
@@ -579,7 +597,9 @@ def main() -> int:
                      "bytes_per_launch": nbytes["splitkv"], "avg_launch_us": round(split_ms * 1e3, 2),
                      "kernel_source_digest": kernel_source_digest()},
         "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 2),
-        "plan": {"host_us": round(plan_us, 2), "map_words": int(len(step.map_host)),
+        "plan": {"host_us": round(plan_us, 2), "host_c_us": round(plan_c_us, 2), "upload_us": round(upload_us, 2),
+                 "per_layer_amortised_us": round((plan_c_us + upload_us) / 80, 3),
+                 "map_words": int(len(step.map_host)),
                  "first_plan_and_upload_s": round(plan_s, 4), "device_us": round(plan_device_us, 2),
                  "device_map_equals_host": plan_device_exact},
     }
