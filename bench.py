@@ -538,10 +538,12 @@ def main() -> int:
     buf = np.zeros(len(step.map_host), dtype=np.int32)
     i32p = ctypes.POINTER(ctypes.c_int32)
     words = ctypes.c_int32(0)
+    fn, lens_p, buf_p, words_p = lb.lib().attn_plan, lens_h.ctypes.data_as(i32p), buf.ctypes.data_as(i32p), \
+        ctypes.byref(words)
+    n_lens, n_buf = len(lens_h), len(buf)
     t = time.perf_counter()
     for _ in range(1000):
-        lb.lib().attn_plan(lens_h.ctypes.data_as(i32p), len(lens_h), workers, args.tile, buf.ctypes.data_as(i32p),
-                           len(buf), ctypes.byref(words))
+        fn(lens_p, n_lens, workers, args.tile, buf_p, n_buf, words_p)
     plan_c_us = (time.perf_counter() - t) / 1000 * 1e6
     assert np.array_equal(buf, step.map_host)
     torch.cuda.synchronize()
