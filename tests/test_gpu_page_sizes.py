@@ -1,7 +1,7 @@
-"""GPU parity at cache page sizes other than 64 tokens (any multiple of 64 is accepted): the decode
-kernels (bf16 and E4M3), multi-token decode, chunked prefill and the producer step walk pages of
-128, 256 and 1024 tokens — several 64-token chunks per page, segment starts inside a page — against
-the fp64 oracle, with NaN-poisoned pads."""
+"""GPU parity against the fp64 oracle, with NaN-poisoned pads, at cache page sizes other than 64
+tokens (any multiple of 64 is accepted) and on a batch of many small requests.  With pages of 128,
+256 and 1024 tokens the decode kernels (bf16 and E4M3), multi-token decode, chunked prefill and the
+producer step walk several 64-token chunks per page and start segments inside a page."""
 
 import numpy as np
 import pytest
@@ -157,3 +157,22 @@ def test_store_kv_page_sizes(lb, page, fp8):
     # nothing but the B new tokens was written
     stored = sum(int(torch.count_nonzero(unpack_request(kc, vc, bt, b, L + 1)[0][L]).item()) for b, L in enumerate(lens))
     assert int(torch.count_nonzero(kc).item()) == stored
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_many_small_requests(lb, fp8):
+    """777 requests of 0-130 tokens on the device's own worker count: most workers hold several
+    requests, many requests hold no tile, and the combine covers 777 units."""
+    wl = WL.random_decode(60 + int(fp8), 777, 130)
+    W = lb.attn_query_workers(0, 8, lb.KV_FP8_E4M3 if fp8 else lb.KV_BF16)
+    note(f"many small requests fp8={fp8}: B={wl.batch} tokens={sum(wl.kv_lens)} zeros={wl.kv_lens.count(0)} W={W}")
+    words = lb.attn_plan(wl.kv_lens, W, 512)
+    assert np.array_equal(words, ref_plan(wl.kv_lens, W, 512))
+    if fp8:
+        got = _decode(lb, wl, words, decode_inputs_fp8(wl, pad_code=NAN_CODE), 8, True)
+        ref = oracle_decode_fp8(wl)
+    else:
+        got = _decode(lb, wl, words, decode_inputs(wl, pad_value=float("nan")), 8, False)
+        ref = oracle_decode(wl)
+    for b in range(wl.batch):
+        assert_close(got[b], ref[b], f"request {b} (L={wl.kv_lens[b]})")
