@@ -380,6 +380,108 @@ def bench_mtp(dev, base: str, args, decode_us: float) -> dict:
             "decode_us_per_step": round(decode_us, 2), "sweep": rows}
 
 
+def unfused_store_step(dev, hq: int, hkv: int, page: int, theta: float, eps: float):
+    """The producer step as separate GPU tensor ops, the unfused form the fused kernel replaces:
+    RMSNorm, RoPE (fp64 angles), Hadamard as a matrix product, rounding / E4M3 quantisation, and an
+    index scatter into the blocked paged cache.  A measurement baseline only."""
+    import math
+    import torch
+    import torch.nn.functional as F
+    D = 128
+    h = torch.ones((1, 1), dtype=torch.float32)
+    while h.shape[0] < D:
+        h = torch.cat([torch.cat([h, h], 1), torch.cat([h, -h], 1)], 0)
+    hmat = (h / math.sqrt(D)).to(dev)                       # symmetric: x @ H = H x
+    freq = torch.tensor([theta ** (-2.0 * i / D) for i in range(D // 2)], dtype=torch.float64, device=dev)
+    d = torch.arange(D, device=dev)
+    heads = torch.arange(hkv, device=dev)
+
+    def rope(x, cos, sin):
+        x1, x2 = x[..., :D // 2], x[..., D // 2:]
+        return torch.cat([x1 * cos - x2 * sin, x2 * cos + x1 * sin], -1)
+
+    def step(q, k, v, pos, q_out, kc, vc, bt, qw, kw, scales):
+        fp8 = kc.dtype == torch.uint8
+        w = 64 if fp8 else 32
+        qf = F.rms_norm(q.float(), (D,), qw, eps)
+        kf = F.rms_norm(k.float(), (D,), kw, eps)
+        ang = torch.remainder(pos.double()[:, None] * freq[None, :], 2 * math.pi)
+        cos, sin = torch.cos(ang).float()[:, None, :], torch.sin(ang).float()[:, None, :]
+        qf = rope(qf, cos, sin) @ hmat
+        kf = rope(kf, cos, sin) @ hmat
+        q_out.copy_(qf.to(torch.bfloat16))
+        if fp8:
+            ks, vs = scales
+            kq = (kf / ks[None, :, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+            vq = (v.float() / vs[None, :, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+        else:
+            kq, vq = kf.to(torch.bfloat16), v
+        p64 = pos.long()
+        pid = bt.gather(1, (p64 // page)[:, None])[:, 0].long()
+        t = p64 % page
+        blk = ((pid[:, None] * hkv + heads[None, :]) * (page * D))[:, :, None]
+        k_idx = blk + (((d // w) * page)[None, None, :] + t[:, None, None]) * w + (d % w)[None, None, :]
+        v_idx = blk + ((t // w)[:, None, None] * D + d[None, None, :]) * w + (t % w)[:, None, None]
+        kc.view(-1).index_copy_(0, k_idx.reshape(-1), kq.reshape(-1))
+        vc.view(-1).index_copy_(0, v_idx.reshape(-1), vq.reshape(-1))
+
+    return step
+
+
+def bench_unfused_store(dev, wl, q, k, v, pos, bt, qw, kw, scales, q_ref, kc_ref, vc_ref, reps: int) -> dict:
+    """Time the unfused producer step on the same inputs after checking it stores what the fused
+    kernel stored (q within one bf16 step, cache bytes equal but for rounding ties); timed eagerly
+    (launch by launch, as an unfused framework runs it) and as one HIP graph of `reps` calls, whose
+    replays are checked against the eager result."""
+    import torch
+    step = unfused_store_step(dev, wl.hq, wl.hkv, 64, 10000.0, 1e-6)
+    kc, vc, q_out = torch.zeros_like(kc_ref), torch.zeros_like(vc_ref), torch.empty_like(q_ref)
+    f = lambda: step(q, k, v, pos, q_out, kc, vc, bt, qw, kw, scales)
+    f()
+    torch.cuda.synchronize()
+    dq = (q_out.float() - q_ref.float()).abs()
+    step_q = torch.ldexp(torch.ones_like(dq), torch.frexp(q_ref.float())[1] - 8)
+    same = {"q_within_one_bf16_step": bool((dq <= step_q + 1e-6).all().item()),
+            "k_bytes_equal": round(float((kc.view(torch.uint8) == kc_ref.view(torch.uint8)).float().mean().item()), 5),
+            "v_bytes_equal": round(float((vc.view(torch.uint8) == vc_ref.view(torch.uint8)).float().mean().item()), 5)}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) / reps * 1e3
+    # the same calls captured once and replayed; kept only if every replay reproduces the eager result
+    graph_us = None
+    kc_eager, vc_eager, q_eager = kc.clone(), vc.clone(), q_out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        f()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            f()
+    ok = True
+    for _ in range(3):
+        kc.zero_()
+        vc.zero_()
+        q_out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        ok &= bool(torch.equal(kc, kc_eager) and torch.equal(vc, vc_eager) and torch.equal(q_out, q_eager))
+    if ok:
+        e0.record()
+        for _ in range(10):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = round(e0.elapsed_time(e1) / (10 * reps) * 1e3, 2)
+    del graph
+    return {"eager_us": round(eager_us, 2), "graph_us": graph_us, "graph_replays_match": ok, "matches_fused": same}
+
+
 def bench_store_kv(dev, wl, args) -> dict:
     """The fused producer step (RMSNorm + RoPE + Hadamard on q and k, K/V stored into the blocked
     paged cache) for one decode step of the batch, and for a 4096-token step; bf16 and E4M3.  Each
@@ -435,6 +537,7 @@ def bench_store_kv(dev, wl, args) -> dict:
             e1.record()
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) / (reps * replays) * 1e3
+            unfused = bench_unfused_store(dev, wl, q, k, v, pos, bt, qw, kw, sc, q_out, kc, vc, reps)
             e = 1 if fp8 else 2
             nbytes = B * (wl.hq + 2 * wl.hkv) * wl.head_dim * 2 + B * wl.hq * wl.head_dim * 2 + \
                 B * 2 * wl.hkv * wl.head_dim * e + B * 8 + 2 * wl.head_dim * 4
@@ -442,8 +545,11 @@ def bench_store_kv(dev, wl, args) -> dict:
             v_rows = B * wl.hkv * wl.head_dim * 64
             rows.append({"tokens": B, "kv": "e4m3" if fp8 else "bf16", "us": round(us, 2),
                          "algorithmic_bytes": nbytes, "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
-                         "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 8e12, 4), "v_rows_touched_bytes": v_rows})
-            log(f"store_kv B={B} {'e4m3' if fp8 else 'bf16'}: {us:.1f} us")
+                         "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 8e12, 4), "v_rows_touched_bytes": v_rows,
+                         "unfused": unfused,
+                         "fused_speedup_graph": (round(unfused["graph_us"] / us, 2) if unfused["graph_us"] else None)})
+            log(f"store_kv B={B} {'e4m3' if fp8 else 'bf16'}: {us:.1f} us; unfused ops: graph "
+                f"{unfused['graph_us']} us, eager {unfused['eager_us']} us")
             del graph, kc, vc
     return {"workload": "producer step: RMSNorm + RoPE + Hadamard on q and k, K/V stored in the blocked paged "
                         "cache, for the batch's new tokens and for a 4096-token step (each token its own page)",
