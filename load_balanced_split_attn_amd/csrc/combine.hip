@@ -23,27 +23,16 @@ struct CombineParams {
   int32_t U, R, Hq, out_bf16;
 };
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, xor_lane(v, m));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += xor_lane(v, m);
-  return v;
-}
-
-// WPI waves per (unit, row, query head) item.  Pass 1 spreads the unit's slots over the lanes for
-// the maximum and the weighted sum of l (every wave of the item does it); pass 2 gives each lane two
-// output dims and walks the slots s = wave, wave + WPI, ... with independent loads (unrolled), so
-// the short, latency-bound loop keeps several in flight; with WPI > 1 the waves' sums meet in LDS.
-// WPI = 1 serves units with a few slots (4 items per workgroup), WPI = 4 units split over many
-// workers (one item per workgroup).
+// WPI waves per (unit, row, query head) item.  Each lane owns two output dims and a wave walks the
+// slots s = wave, wave + WPI, ... once, reading m, l and o together and keeping a running maximum
+// (the online form of the definition above: the same sums, rescaled as the maximum grows), with
+// four slots' loads in flight; with WPI > 1 the waves' states meet in LDS.  WPI = 1 serves units
+// with a few slots (4 items per workgroup), WPI = 4 units split over many workers (one item per
+// workgroup).
 template <int WPI>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   __shared__ float2 red[WPI > 1 ? WPI * 64 : 1];
+  __shared__ float2 red_ml[WPI > 1 ? WPI : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t item = (int64_t)blockIdx.x * (4 / WPI) + (WPI == 1 ? wave : 0);
@@ -76,60 +65,70 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   if (s0 < 0 || n < 0 || s0 + n > p.map[4]) return;
   auto slot = [&](int i) -> int64_t { return ((int64_t)(s0 + i) * p.R + r) * p.Hq + h; };
 
-  float M = -INFINITY;
-  for (int i = lane; i < n; i += 64) M = fmaxf(M, p.part_m[slot(i)]);
-  M = wave_max(M);
-  float L = 0.f;
-  if (M != -INFINITY) {
-    for (int i = lane; i < n; i += 64) {
-      const float m = p.part_m[slot(i)];
-      if (m != -INFINITY) L += fast_exp2((m - M) * kLog2e) * p.part_l[slot(i)];
+  // one pass over the wave's slots s = sub, sub + WPI, ... with a running maximum M: the slot's
+  // (m, l) are the same for every lane (each lane owns two output dims), so M, the rescaling and L
+  // stay wave-uniform and need no lane reduction; four slots' loads are in flight at a time
+  float M = -INFINITY, L = 0.f, a0 = 0.f, a1 = 0.f;
+  // branch-free, so the loads of the next slots stay in flight: a slot with no visible key
+  // (m = -inf) gets weight 0, and the running sums are rescaled by 0 when the first finite maximum
+  // replaces -inf (they are still 0 then) and by 1 while the maximum is unchanged
+  auto absorb = [&](float m, float l, float2 o) {
+    const float Mn = fmaxf(M, m);
+    const float sc = Mn == -INFINITY ? 1.f : fast_exp2((M - Mn) * kLog2e);
+    const float w = m == -INFINITY ? 0.f : fast_exp2((m - Mn) * kLog2e);
+    a0 = fmaf(w, o.x, a0 * sc);
+    a1 = fmaf(w, o.y, a1 * sc);
+    L = fmaf(w, l, L * sc);
+    M = Mn;
+  };
+  int i = sub;
+  for (; i + 3 * WPI < n; i += 4 * WPI) {
+    float m[4], l[4];
+    float2 o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m[j] = p.part_m[slot(i + j * WPI)];
+      l[j] = p.part_l[slot(i + j * WPI)];
+      o[j] = *reinterpret_cast<const float2*>(p.part_o + slot(i + j * WPI) * 128 + 2 * lane);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) absorb(m[j], l[j], o[j]);
   }
-  L = wave_sum(L);
+  for (; i < n; i += WPI)
+    absorb(p.part_m[slot(i)], p.part_l[slot(i)],
+           *reinterpret_cast<const float2*>(p.part_o + slot(i) * 128 + 2 * lane));
 
-  float a0 = 0.f, a1 = 0.f;
-  if (L > 0.f) {
-    int i = sub;
-    for (; i + 3 * WPI < n; i += 4 * WPI) {
-      float m[4];
-      float2 o[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        m[j] = p.part_m[slot(i + j * WPI)];
-        o[j] = *reinterpret_cast<const float2*>(p.part_o + slot(i + j * WPI) * 128 + 2 * lane);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float w = (m[j] == -INFINITY) ? 0.f : fast_exp2((m[j] - M) * kLog2e);
-        a0 += w * o[j].x;
-        a1 += w * o[j].y;
-      }
-    }
-    for (; i < n; i += WPI) {
-      const float m = p.part_m[slot(i)];
-      const float2 o = *reinterpret_cast<const float2*>(p.part_o + slot(i) * 128 + 2 * lane);
-      const float w = (m == -INFINITY) ? 0.f : fast_exp2((m - M) * kLog2e);
-      a0 += w * o.x;
-      a1 += w * o.y;
-    }
-  }
   if constexpr (WPI > 1) {
+    // merge the waves' running states: rescale each to the largest maximum
     red[wave * 64 + lane] = make_float2(a0, a1);
+    if (lane == 0) red_ml[wave] = make_float2(M, L);
     __syncthreads();
     if (wave != 0) return;
+    float Mx = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < WPI; ++w) Mx = fmaxf(Mx, red_ml[w].x);
     a0 = 0.f;
     a1 = 0.f;
+    L = 0.f;
+    if (Mx != -INFINITY) {
 #pragma unroll
-    for (int w = 0; w < WPI; ++w) {
-      a0 += red[w * 64 + lane].x;
-      a1 += red[w * 64 + lane].y;
+      for (int w = 0; w < WPI; ++w) {
+        const float2 ml = red_ml[w];
+        if (ml.x == -INFINITY) continue;
+        const float sc = fast_exp2((ml.x - Mx) * kLog2e);
+        a0 += sc * red[w * 64 + lane].x;
+        a1 += sc * red[w * 64 + lane].y;
+        L += sc * ml.y;
+      }
     }
   }
   if (L > 0.f) {
     const float inv = 1.f / L;
     a0 *= inv;
     a1 *= inv;
+  } else {
+    a0 = 0.f;   // a unit with no visible key
+    a1 = 0.f;
   }
   const int64_t obase = (orow * p.Hq + h) * 128 + 2 * lane;
   if (p.out_bf16) {
