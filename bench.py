@@ -225,9 +225,9 @@ def prefill_flops(wl) -> int:
     return 4 * wl.head_dim * wl.hq * total
 
 
-def bench_prefill(dev, workers_list, steps: int, warmup: int) -> dict:
+def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tile: int = 256) -> dict:
     """Chunked prefill over cached prefixes: 8 requests x 2048-row causal chunks after prefixes drawn
-    log-uniform in [8K, 128K]; q tiles of 128 rows x KV tiles of 512 on the same greedy planner."""
+    log-uniform in [8K, 128K]; q tiles of `q_tile` rows x KV tiles of 512 on the same greedy planner."""
     import numpy as np
     import torch
 
@@ -242,11 +242,12 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int) -> dict:
     flops = prefill_flops(wl)
     rows = []
     for W in workers_list:
-        st = PrefillStep(wl.q_lens, wl.kv_lens, dev, num_workers=W)
+        st = PrefillStep(wl.q_lens, wl.kv_lens, dev, num_workers=W, q_tile=q_tile)
         r = time_steps(lambda i, st=st: st.splitkv(q, kc, vc, bt, scale), lambda i, st=st: st.combine(out),
                        steps, warmup)
         split_ms = float(np.mean(r["split_ms"]))
-        rows.append({"workers": W, "segments": st.S, "us_per_step": round(r["total_ms"] / steps * 1e3, 1),
+        rows.append({"workers": W, "q_tile": q_tile, "segments": st.S,
+                     "us_per_step": round(r["total_ms"] / steps * 1e3, 1),
                      "splitkv_us": round(split_ms * 1e3, 1),
                      "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 1),
                      "splitkv_tflops": round(flops / (split_ms * 1e-3) / 1e12, 1)})
@@ -256,7 +257,7 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int) -> dict:
     prefix = wl.meta["prefix"]
     cached = sum(prefix) / sum(wl.kv_lens)
     return {"workload": "chunked prefill: 8 x 2048-row causal chunks after prefixes log-uniform in [8K, 128K] "
-                        f"({prefix}), GQA 64q/8kv, d=128, bf16, q tile 128 x KV tile 512",
+                        f"({prefix}), GQA 64q/8kv, d=128, bf16, q tile {q_tile} x KV tile 512",
             "cached_fraction": round(cached, 4), "flops_per_step": flops,
             "us_per_step": best["us_per_step"], "tflops_per_step": round(flops / (best["us_per_step"] * 1e-6) / 1e12, 1),
             "roofline": {"bound": "mfma", "kernel": "splitkv_prefill_kernel",
@@ -576,6 +577,7 @@ def main() -> int:
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill report")
     ap.add_argument("--prefill-workers", default="64,128")
+    ap.add_argument("--prefill-q-tile", type=int, default=256, choices=(128, 256))
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the chunked-prefill report (profiling runs); prints its JSON")
@@ -607,7 +609,7 @@ def main() -> int:
         calibration_copy(dev)
     if args.only_prefill:
         print(json.dumps(bench_prefill(dev, [int(x) for x in args.prefill_workers.split(",")],
-                                       args.prefill_steps, 1)), flush=True)
+                                       args.prefill_steps, 1, q_tile=args.prefill_q_tile)), flush=True)
         return 0
     wl = WL.BY_NAME[args.workload]()
     if args.only_fp8:
@@ -835,7 +837,7 @@ def main() -> int:
 
     if not args.no_prefill:
         result["prefill"] = bench_prefill(dev, [int(x) for x in args.prefill_workers.split(",")],
-                                          args.prefill_steps, 1)
+                                          args.prefill_steps, 1, q_tile=args.prefill_q_tile)
 
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a CPU sample")

@@ -312,8 +312,8 @@ int attn_store_kv(const void* q_in, const void* k_in, const void* v_in,
  * applied to prefill units; prefix reuse as in [P3] §6: a request's new chunk attends to its
  * cached prefix and, causally, to itself).  Request b has q_lens[b] query rows stored from row
  * q_start[b] of q [rows, Hq, D]; they are the last q_lens[b] positions of a kv_lens[b]-token
- * context held in the paged caches.  Launches 8 x ceil(W x Hkv / 8) x 8 workgroups of 256
- * threads: workgroup (w, g, h) walks worker w's segments for query head h of KV head g, 32 rows per
+ * context held in the paged caches.  Launches 8 x ceil(W x Hkv / 8) x 8 workgroups of q_tile / 32
+ * waves: workgroup (w, g, h) walks worker w's segments for query head h of KV head g, 32 rows per
  * wave.  Writes, for every segment s and row i < q_tile of its unit that lies inside the chunk,
  * part_m/part_l [S, q_tile, Hq] and part_o [S, q_tile, Hq, D] (rows past the chunk are not
  * written).  With causal != 0 row j sees keys [0, kv_lens[b] - q_lens[b] + j]; otherwise all keys.
@@ -322,7 +322,9 @@ int attn_store_kv(const void* q_in, const void* k_in, const void* v_in,
  *   flags         0: P.V in fp16 (V converted exactly from bf16 while staged, P rounded to 11
  *                 significant bits; |v| above 65504 saturates); LBSA_PREFILL_EXACT_PV: bf16 V with
  *                 P as bf16 hi + lo parts (~16 bits, no range limit, ~15% slower)
- * Supported: head_dim 128, Hq/Hkv = 8, bf16, q_tile 128, page_size a multiple of 64.
+ * Supported: head_dim 128, Hq/Hkv = 8, bf16, q_tile 128 (four waves of 32 rows per workgroup,
+ * 256 threads) or 256 (eight waves, 512 threads), page_size a multiple of 64.  The map must come
+ * from attn_plan_prefill with the same q_tile (a map of another unit height is skipped).
  * Errors: LBSA_ERR_INVALID (also unknown flag bits), LBSA_ERR_UNSUPPORTED, LBSA_ERR_HIP.
  */
 #define LBSA_PREFILL_EXACT_PV 1

@@ -47,7 +47,7 @@ struct PrefillParams {
 constexpr int kPD = 128;          // head dim
 constexpr int kRow = 64;          // bytes per row of the blocked cache layout
 constexpr int kPChunk = 64;       // keys per staged chunk
-constexpr int kQTile = 128;       // query rows per unit
+constexpr int kMaxQTile = 256;    // query rows per unit: 32 per wave, 4 or 8 waves
 constexpr int kColBlocks = 2;     // 16-row column blocks per wave (32 rows)
 constexpr int kKRow = kPD * 2;             // LDS bytes per key row of K (16 granules, XOR-swizzled)
 constexpr int kVRow = kPChunk * 2;         // LDS bytes per dim row of V^T (8 granules, XOR-swizzled)
@@ -129,9 +129,18 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;
 #define LBSA_WAIT_VM_LGKM(vm, lgkm) \
   __builtin_amdgcn_s_waitcnt(((vm) & 0xF) | (((vm) >> 4) << 14) | (0x7 << 4) | (((lgkm) & 0xF) << 8))
 
-template <int PV>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(LBSA_PREFILL_WPE, LBSA_PREFILL_WPE)))
+// Unit height and DMA share of a workgroup of WAVES waves (a struct, not function-local constants:
+// the host pass of the kernel template needs them as constant expressions in array bounds).
+template <int WAVES>
+struct PrefillShape {
+  static constexpr int kQTile = 32 * WAVES;   // query rows per unit
+  static constexpr int kTpw = 16 / WAVES;     // 1 KiB DMA slots per wave in each half of a stage
+};
+
+template <int PV, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(LBSA_PREFILL_WPE, LBSA_PREFILL_WPE)))
 void splitkv_prefill_kernel(PrefillParams p) {
+  using Shape = PrefillShape<WAVES>;
   // three pipeline stages, separate objects so the compiler can tell their DMA writes apart
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
@@ -160,6 +169,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
 
   const_i32* map = (const_i32*)p.map;
   if (map[0] != LBSA_MAP_VERSION) return;   // a device-built map that reported an error
+  if (map[6] != Shape::kQTile) return;              // a map planned for another unit height
   const int U = map[7];
   const_i32* worker_ptr = map + 8;
   const_i32* segs = map + 8 + (p.W + 1) + (U + 1) + 2 * U;
@@ -189,10 +199,10 @@ void splitkv_prefill_kernel(PrefillParams p) {
   // offset in the page goes in the scalar offset, so these registers stay unchanged while earlier
   // loads that read them are in flight.  LDS slot `slot` of the stage takes 16-byte piece kp of
   // key row `key` (dims 8kp .. +7) and piece vp of dim row d (chunk keys 8vp .. +7).
-  int k_src[4], v_src[4];
+  int k_src[4], v_src[4];   // the first Shape::kTpw are used (a fixed size keeps the lambdas host-compilable)
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int slot = 64 * (4 * wave + t) + lane;
+  for (int t = 0; t < Shape::kTpw; ++t) {
+    const int slot = 64 * (Shape::kTpw * wave + t) + lane;
     const int key = slot >> 4;
     const int kp = (slot & 15) ^ k_swz(key);
     k_src[t] = ((kp >> 2) * p.page + key) * kRow + 16 * (kp & 3);
@@ -212,7 +222,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
     const int prefix = kv_len - q_len;
     kv_end = min(kv_end, kv_len);
     kv_end = min(kv_end, p.bt_stride * p.page);
-    const int unit_row0 = qt * kQTile;                 // first row of the unit inside the chunk
+    const int unit_row0 = qt * Shape::kQTile;                 // first row of the unit inside the chunk
     const int wave_row0 = unit_row0 + rbase;           // first row of this wave
     // last key any row of this wave may see (-1: the wave has no row inside the chunk)
     const int wave_last_key = wave_row0 >= q_len ? -1
@@ -257,12 +267,12 @@ void splitkv_prefill_kernel(PrefillParams p) {
       __amdgpu_buffer_rsrc_t vr =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + blk), (short)0, block_bytes, 0x00020000);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LBSA_LDS(st + 1024 * (4 * wave + t)), 16, k_src[t],
+      for (int t = 0; t < Shape::kTpw; ++t)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LBSA_LDS(st + 1024 * (Shape::kTpw * wave + t)), 16, k_src[t],
                                                  off * kRow, 0, LBSA_PREFILL_KV_POLICY);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LBSA_LDS(st + kKBytes + 1024 * (4 * wave + t)), 16, v_src[t],
+      for (int t = 0; t < Shape::kTpw; ++t)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LBSA_LDS(st + kKBytes + 1024 * (Shape::kTpw * wave + t)), 16, v_src[t],
                                                  (off / 32) * kPD * kRow, 0, LBSA_PREFILL_KV_POLICY);
     };
 
@@ -430,8 +440,8 @@ void splitkv_prefill_kernel(PrefillParams p) {
     // buffer->LDS loads wrote, so only its own loads need to have landed
     auto to_f16 = [&](uint8_t* st) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        u32x4* gp = reinterpret_cast<u32x4*>(st + kKBytes + 1024 * (4 * wave + t) + 16 * lane);
+      for (int t = 0; t < Shape::kTpw; ++t) {
+        u32x4* gp = reinterpret_cast<u32x4*>(st + kKBytes + 1024 * (Shape::kTpw * wave + t) + 16 * lane);
         u32x4 x = *gp;
 #pragma unroll
         for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
@@ -481,7 +491,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
       l += xor_lane(l, 32);
       const int row_in_unit = rbase + 16 * cb + r;
       if (unit_row0 + row_in_unit < q_len) {
-        const size_t slot = ((size_t)s * kQTile + row_in_unit) * p.Hq + h;
+        const size_t slot = ((size_t)s * Shape::kQTile + row_in_unit) * p.Hq + h;
         if (grp == 0) {
           p.part_m[slot] = (m_true[cb] == -INFINITY) ? -INFINITY : m_true[cb] * c * kLn2;
           p.part_l[slot] = l;
@@ -492,6 +502,11 @@ void splitkv_prefill_kernel(PrefillParams p) {
       }
     }
   }
+}
+
+template <int PV, int WAVES>
+void launch_prefill(unsigned grid, hipStream_t stream, const PrefillParams& p) {
+  hipLaunchKernelGGL((splitkv_prefill_kernel<PV, WAVES>), dim3(grid), dim3(64 * WAVES), 0, stream, p);
 }
 
 }  // namespace lbsa
@@ -514,7 +529,8 @@ extern "C" int attn_splitkv_prefill(const void* q, const void* k_cache, const vo
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(part_o)) & 15)
     return LBSA_ERR_INVALID;
-  if (head_dim != kPD || num_q_heads != 8 * num_kv_heads || page_size % kPChunk != 0 || q_tile != kQTile)
+  if (head_dim != kPD || num_q_heads != 8 * num_kv_heads || page_size % kPChunk != 0 ||
+      (q_tile != 128 && q_tile != kMaxQTile))
     return LBSA_ERR_UNSUPPORTED;
   if (flags & ~LBSA_PREFILL_EXACT_PV) return LBSA_ERR_INVALID;
   PrefillParams p;
@@ -543,11 +559,15 @@ extern "C" int attn_splitkv_prefill(const void* q, const void* k_cache, const vo
   const int64_t pairs = (int64_t)num_workers * num_kv_heads;
   const int64_t grid = ((pairs + 7) / 8) * 8 * 8;
   if (grid > INT32_MAX) return LBSA_ERR_INVALID;
-  if (flags & LBSA_PREFILL_EXACT_PV)
-    hipLaunchKernelGGL(splitkv_prefill_kernel<kPvExact>, dim3((unsigned)grid), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), p);
-  else
-    hipLaunchKernelGGL(splitkv_prefill_kernel<kPvF16>, dim3((unsigned)grid), dim3(256), 0,
-                       static_cast<hipStream_t>(stream), p);
+  const bool exact = flags & LBSA_PREFILL_EXACT_PV;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned g = (unsigned)grid;
+  if (q_tile == 128) {
+    if (exact) launch_prefill<kPvExact, 4>(g, st, p);
+    else launch_prefill<kPvF16, 4>(g, st, p);
+  } else {
+    if (exact) launch_prefill<kPvExact, 8>(g, st, p);
+    else launch_prefill<kPvF16, 8>(g, st, p);
+  }
   return hipGetLastError() == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;
 }

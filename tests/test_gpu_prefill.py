@@ -13,12 +13,12 @@ from oracle.plan import ref_plan_prefill
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, W, causal=True, inputs=None, poison=False, kv_tile=512, exact_pv=False):
+def _run(wl, W, causal=True, inputs=None, poison=False, kv_tile=512, exact_pv=False, q_tile=256):
     from load_balanced_split_attn_amd.prefill import PrefillStep
     q, kc, vc, bt = inputs if inputs is not None else prefill_inputs(wl, pad_value=float("nan"))
     step = PrefillStep(wl.q_lens, wl.kv_lens, q.device, num_workers=W, causal=causal, kv_tile=kv_tile,
-                       exact_pv=exact_pv)
-    assert np.array_equal(step.map_host, ref_plan_prefill(wl.q_lens, wl.kv_lens, W, 128, kv_tile, causal))
+                       exact_pv=exact_pv, q_tile=q_tile)
+    assert np.array_equal(step.map_host, ref_plan_prefill(wl.q_lens, wl.kv_lens, W, q_tile, kv_tile, causal))
     if poison:
         for t in (step.part_m, step.part_l, step.part_o):
             t.fill_(float("nan"))
@@ -37,14 +37,15 @@ def _check_all(wl, got, causal=True):
                      f"{wl.name} request {b} (q_len={wl.q_lens[b]}, kv_len={wl.kv_lens[b]}, causal={causal})")
 
 
+@pytest.mark.parametrize("q_tile", [256, 128])
 @pytest.mark.parametrize("exact_pv", [False, True])
 @pytest.mark.parametrize("seed,batch,max_prefix,max_chunk,W", [
     (0, 3, 1500, 300, 3), (1, 4, 700, 200, 1), (2, 2, 3000, 260, 8), (3, 5, 100, 140, 16),
 ])
-def test_random_prefill(seed, batch, max_prefix, max_chunk, W, exact_pv):
+def test_random_prefill(seed, batch, max_prefix, max_chunk, W, exact_pv, q_tile):
     wl = WL.random_prefill(seed, batch, max_prefix, max_chunk)
-    note(f"prefill seed={seed} q_lens={wl.q_lens} kv_lens={wl.kv_lens} W={W} exact_pv={exact_pv}")
-    got, _ = _run(wl, W, causal=True, poison=True, exact_pv=exact_pv)
+    note(f"prefill seed={seed} q_lens={wl.q_lens} kv_lens={wl.kv_lens} W={W} exact_pv={exact_pv} q_tile={q_tile}")
+    got, _ = _run(wl, W, causal=True, poison=True, exact_pv=exact_pv, q_tile=q_tile)
     _check_all(wl, got, causal=True)
 
 
@@ -137,3 +138,20 @@ def test_full_size_prefill_sampled():
         for j in rows:
             ma, rr = assert_close(got[starts[b] + j], ref[j], f"prefill request {b} row {j}")
         note(f"  request {b} kv_len={wl.kv_lens[b]}: rows {rows} ok (last rel_rms {rr:.2e})")
+
+
+def test_unit_height_mismatch_writes_nothing():
+    """A map planned for 128-row units given to the 256-row kernel is skipped, not misread."""
+    import load_balanced_split_attn_amd as lb
+    from load_balanced_split_attn_amd.prefill import PrefillStep
+    wl = WL.random_prefill(12, 2, 300, 200)
+    q, kc, vc, bt = prefill_inputs(wl)
+    st = PrefillStep(wl.q_lens, wl.kv_lens, q.device, num_workers=2, q_tile=128)   # 128-row map
+    S = max(st.S, 1)
+    pm = torch.full((S, 256, 64), 7.0, device=q.device)
+    pl = torch.full((S, 256, 64), 7.0, device=q.device)
+    po = torch.full((S, 256, 64, 128), 7.0, device=q.device)
+    lb.attn_splitkv_prefill(q, kc, vc, bt, st.q_lens, st.q_start, st.kv_lens, st.map, st.W, st.S, SCALE,
+                            pm, pl, po, q_tile=256)
+    torch.cuda.synchronize()
+    assert bool((pm == 7.0).all()) and bool((pl == 7.0).all()) and bool((po == 7.0).all())
