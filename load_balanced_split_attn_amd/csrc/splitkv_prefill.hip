@@ -2,19 +2,20 @@
 //
 // The pages' load-balanced scheduler ([P3] "Hy3 Preview AI Infra 推理优化精读笔记" §3.1 方案;
 // [P4] "腾讯混元AI Infra进化：HPC-Ops推理核心算子全面升级" §二.1) applied to prefill units: a unit
-// is a 128-row block of one request's query chunk, cut into 512-token KV tiles that the planner
-// packs onto workers exactly as in decode.  Prefix-cache reuse ([P3] §6) means each chunk attends
-// to a long cached prefix plus itself under a causal mask: row j of a q_len-row chunk sits at
+// is a 256-row (or 128-row) block of one request's query chunk, cut into 512-token KV tiles that the
+// planner packs onto workers exactly as in decode.  Prefix-cache reuse ([P3] §6) means each chunk
+// attends to a long cached prefix plus itself under a causal mask: row j of a q_len-row chunk sits at
 // position kv_len - q_len + j and sees keys [0, that position].
 //
-// gfx950 design.  Workgroup = (worker w, KV head g, query head h of the group), 4 waves; wave v
-// owns the 32 query rows 32v .. 32v+31 of the unit.  Each 64-key chunk of K and V (blocked cache
-// layout) goes from HBM straight into LDS with buffer->LDS loads (no registers), in XOR-swizzled
-// layouts that the MFMA fragment reads take without bank conflicts, and is read by all four waves:
-// 128 query rows per K/V load; the eight query heads of a KV head run as eight workgroups on one
-// XCD so K/V come from one L2.  Two 32 KiB LDS stages (the next chunk streams in while the current
-// one is computed) and a register budget of 256 let two workgroups share a CU, so one wave's
-// softmax VALU work overlaps another wave's MFMAs.
+// gfx950 design.  Workgroup = (worker w, KV head g, query head h of the group), WAVES = 8 (or 4)
+// waves; wave v owns the 32 query rows 32v .. 32v+31 of the unit.  Each 64-key chunk of K and V
+// (blocked cache layout) goes from HBM straight into LDS with buffer->LDS loads (no registers), in
+// XOR-swizzled layouts that the MFMA fragment reads take without bank conflicts, and is read by
+// every wave: 256 (128) query rows per K/V load, so the staging and the fp16 conversion of V are
+// shared by all of them; the eight query heads of a KV head run as eight workgroups on one XCD so
+// K/V come from one L2.  Two 32 KiB LDS stages (the next chunk streams in while the current one is
+// computed) and a register budget of 256 give two waves per SIMD (one 8-wave workgroup or two
+// 4-wave ones per CU), so one wave's softmax VALU work can overlap another wave's MFMAs.
 // Per wave, with the query rows as the MFMA columns:
 //   S^T (keys x rows) = K . Q^T       v_mfma_f32_16x16x32_bf16, Q^T fragments held in VGPRs
 //   O^T (dims x rows) += V^T . P^T    fp16 operands (V converted in LDS), or bf16 with P as
@@ -141,7 +142,7 @@ template <int PV, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(LBSA_PREFILL_WPE, LBSA_PREFILL_WPE)))
 void splitkv_prefill_kernel(PrefillParams p) {
   using Shape = PrefillShape<WAVES>;
-  // three pipeline stages, separate objects so the compiler can tell their DMA writes apart
+  // the pipeline stages, separate objects so the compiler can tell their DMA writes apart
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
 #if LBSA_PREFILL_STAGES == 3
