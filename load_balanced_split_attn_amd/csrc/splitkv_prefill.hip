@@ -71,10 +71,10 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 #ifndef LBSA_PREFILL_WPE
 #define LBSA_PREFILL_WPE 2
 #endif
-//   LBSA_PREFILL_STAGES  LDS pipeline stages of 32 KiB (3: two chunks in flight, one workgroup per
-//                        CU; 2: one chunk in flight, two workgroups per CU)
-#ifndef LBSA_PREFILL_STAGES
-#define LBSA_PREFILL_STAGES 2
+//   LBSA_PREFILL_STAGES_8  LDS pipeline stages of 32 KiB of the 8-wave kernel (2: one chunk in
+//                          flight; 3: two, measured ~3% slower)
+#ifndef LBSA_PREFILL_STAGES_8
+#define LBSA_PREFILL_STAGES_8 2
 #endif
 //   LBSA_PREFILL_KV_POLICY  cache-policy bits of the K/V loads (0: default; the 16 query tiles of a
 //                           request re-read its K/V, which the default policy keeps in L2)
@@ -136,6 +136,9 @@ template <int WAVES>
 struct PrefillShape {
   static constexpr int kQTile = 32 * WAVES;   // query rows per unit
   static constexpr int kTpw = 16 / WAVES;     // 1 KiB DMA slots per wave in each half of a stage
+  // LDS stages of 32 KiB: two (one chunk in flight); an 8-wave workgroup, which has the CU to
+  // itself, may take three (two chunks in flight) at compile time
+  static constexpr int kStages = WAVES == 8 ? LBSA_PREFILL_STAGES_8 : 2;
 };
 
 template <int PV, int WAVES>
@@ -145,9 +148,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
   // the pipeline stages, separate objects so the compiler can tell their DMA writes apart
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
-#if LBSA_PREFILL_STAGES == 3
-  __shared__ __attribute__((aligned(16))) uint8_t stage2[kStage];
-#endif
+  __shared__ __attribute__((aligned(16))) uint8_t stage2[Shape::kStages == 3 ? kStage : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -402,43 +403,10 @@ void splitkv_prefill_kernel(PrefillParams p) {
       }
     };
 
-#if LBSA_PREFILL_STAGES == 3
-    static_assert(PV == kPvExact || LBSA_PREFILL_STAGES == 2, "in-LDS V conversion needs the two-stage pipeline");
-    // one pipeline step: start chunk i+2's DMA, compute chunk i, then make chunk i+1 visible to
-    // every wave (own DMA complete -> barrier).  Stage i+2 was last read by chunk i-1, which every
-    // wave finished before the previous step's barrier.
-    auto step = [&](int i, uint8_t* cur, uint8_t* ahead) {
-      const bool more = i + 2 < n_chunks;
-      if (more) dma(i + 2, ahead);
-      compute(i, cur);
-      if (more) {
-        LBSA_WAIT_VM_LGKM(8, 0);
-      } else {
-        LBSA_WAIT_VM_LGKM(0, 0);
-      }
-      __builtin_amdgcn_s_barrier();
-    };
-
-    if (n_chunks > 0) {
-      dma(0, stage0);
-      if (n_chunks > 1) {
-        dma(1, stage1);
-        LBSA_WAIT_VM_LGKM(8, 0);
-      } else {
-        LBSA_WAIT_VM_LGKM(0, 0);
-      }
-      __builtin_amdgcn_s_barrier();
-      for (int i = 0; i < n_chunks; i += 3) {
-        step(i, stage0, stage2);
-        if (i + 1 >= n_chunks) break;
-        step(i + 1, stage1, stage0);
-        if (i + 2 >= n_chunks) break;
-        step(i + 2, stage2, stage1);
-      }
-    }
-#else
-    // V^T of the chunk in stage st to fp16, in place: each thread converts the granules its own
-    // buffer->LDS loads wrote, so only its own loads need to have landed
+    // V^T of the chunk in stage st: keys outside [kv_begin, kv_end) stay as loaded (the P.V
+    // fragments mask them); on the fp16 path the values are converted to fp16 in place.  Each
+    // thread converts the granules its own buffer->LDS loads wrote, so only its own loads need to
+    // have landed.
     auto to_f16 = [&](uint8_t* st) {
 #pragma unroll
       for (int t = 0; t < Shape::kTpw; ++t) {
@@ -449,39 +417,88 @@ void splitkv_prefill_kernel(PrefillParams p) {
         *gp = x;
       }
     };
-    // one pipeline step: start chunk i+1's DMA into the other stage (last read by chunk i-1,
-    // finished by every wave before the previous barrier), compute chunk i, wait for the DMA,
-    // convert chunk i+1's V (fp16 path), barrier: one barrier per chunk makes chunk i+1 ready for
-    // every wave and releases chunk i's stage
-    auto step = [&](int i, uint8_t* cur, uint8_t* ahead) {
-      const bool more = i + 1 < n_chunks;
-      if (more) dma(i + 1, ahead);
-      compute(i, cur);
-      if constexpr (PV == kPvF16) {
-        if (more) {
+    constexpr int kLoads = 2 * Shape::kTpw;   // buffer->LDS loads per thread per chunk
+
+    if constexpr (Shape::kStages == 3) {
+      // one pipeline step: start chunk i+2's DMA into the stage chunk i-1 used (every wave finished
+      // it before the previous barrier), compute chunk i, wait for the own loads of chunk i+1 (chunk
+      // i+2's may stay in flight), convert its V, barrier
+      auto step = [&](int i, uint8_t* cur, uint8_t* nxt, uint8_t* ahead) {
+        const bool more2 = i + 2 < n_chunks;
+        if (more2) dma(i + 2, ahead);
+        compute(i, cur);
+        if (i + 1 < n_chunks) {
+          if (more2) {
+            LBSA_WAIT_VM_LGKM(kLoads, 15);
+          } else {
+            LBSA_WAIT_VM_LGKM(0, 15);
+          }
+          if constexpr (PV == kPvF16) to_f16(nxt);
+        }
+        if (more2) {
+          LBSA_WAIT_VM_LGKM(kLoads, 0);
+        } else {
+          LBSA_WAIT_VM_LGKM(0, 0);
+        }
+        __builtin_amdgcn_s_barrier();
+      };
+      if (n_chunks > 0) {
+        dma(0, stage0);
+        if (n_chunks > 1) dma(1, stage1);
+        if (n_chunks > 1) {
+          LBSA_WAIT_VM_LGKM(kLoads, 15);
+        } else {
           LBSA_WAIT_VM_LGKM(0, 15);
-          to_f16(ahead);
+        }
+        if constexpr (PV == kPvF16) to_f16(stage0);
+        if (n_chunks > 1) {
+          LBSA_WAIT_VM_LGKM(kLoads, 0);
+        } else {
+          LBSA_WAIT_VM_LGKM(0, 0);
+        }
+        __builtin_amdgcn_s_barrier();
+        for (int i = 0; i < n_chunks; i += 3) {
+          step(i, stage0, stage1, stage2);
+          if (i + 1 >= n_chunks) break;
+          step(i + 1, stage1, stage2, stage0);
+          if (i + 2 >= n_chunks) break;
+          step(i + 2, stage2, stage0, stage1);
         }
       }
-      LBSA_WAIT_VM_LGKM(0, 0);
-      __builtin_amdgcn_s_barrier();
-    };
+    } else {
+      // one pipeline step: start chunk i+1's DMA into the other stage (last read by chunk i-1,
+      // finished by every wave before the previous barrier), compute chunk i, wait for the DMA,
+      // convert chunk i+1's V (fp16 path), barrier: one barrier per chunk makes chunk i+1 ready for
+      // every wave and releases chunk i's stage
+      auto step = [&](int i, uint8_t* cur, uint8_t* ahead) {
+        const bool more = i + 1 < n_chunks;
+        if (more) dma(i + 1, ahead);
+        compute(i, cur);
+        if constexpr (PV == kPvF16) {
+          if (more) {
+            LBSA_WAIT_VM_LGKM(0, 15);
+            to_f16(ahead);
+          }
+        }
+        LBSA_WAIT_VM_LGKM(0, 0);
+        __builtin_amdgcn_s_barrier();
+      };
 
-    if (n_chunks > 0) {
-      dma(0, stage0);
-      if constexpr (PV == kPvF16) {
-        LBSA_WAIT_VM_LGKM(0, 15);
-        to_f16(stage0);
-      }
-      LBSA_WAIT_VM_LGKM(0, 0);
-      __builtin_amdgcn_s_barrier();
-      for (int i = 0; i < n_chunks; i += 2) {
-        step(i, stage0, stage1);
-        if (i + 1 >= n_chunks) break;
-        step(i + 1, stage1, stage0);
+      if (n_chunks > 0) {
+        dma(0, stage0);
+        if constexpr (PV == kPvF16) {
+          LBSA_WAIT_VM_LGKM(0, 15);
+          to_f16(stage0);
+        }
+        LBSA_WAIT_VM_LGKM(0, 0);
+        __builtin_amdgcn_s_barrier();
+        for (int i = 0; i < n_chunks; i += 2) {
+          step(i, stage0, stage1);
+          if (i + 1 >= n_chunks) break;
+          step(i + 1, stage1, stage0);
+        }
       }
     }
-#endif
 
     // write the partials of this wave's rows (rows past the chunk's end are not stored)
 #pragma unroll
