@@ -71,11 +71,6 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 #ifndef LBSA_PREFILL_WPE
 #define LBSA_PREFILL_WPE 2
 #endif
-//   LBSA_PREFILL_STAGES_8  LDS pipeline stages of 32 KiB of the 8-wave kernel (2: one chunk in
-//                          flight; 3: two, measured ~3% slower)
-#ifndef LBSA_PREFILL_STAGES_8
-#define LBSA_PREFILL_STAGES_8 2
-#endif
 //   LBSA_PREFILL_KV_POLICY  cache-policy bits of the K/V loads (0: default; the 16 query tiles of a
 //                           request re-read its K/V, which the default policy keeps in L2)
 #ifndef LBSA_PREFILL_KV_POLICY
@@ -105,6 +100,17 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// maximum of v over lanes l, l ^ 16, l ^ 32 and l ^ 48 (one value from each 16-lane row): gfx950's
+// row-swap permutes exchange the two halves of the wave, then rows 0/1 and 2/3, as VALU operations
+__device__ __forceinline__ float max_over_rows(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t w = __float_as_uint(m);
+  const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ u32x4 lds_ld16(const uint8_t* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
 }
@@ -122,6 +128,26 @@ __device__ __forceinline__ int v_slot(int d, int granule) { return kKBytes + d *
 
 #define LBSA_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
 
+// Buffer resource of `bytes` bytes at p (stride 0, raw buffer): base, num_records, flags.
+__device__ __forceinline__ u32x4 raw_rsrc(const void* p, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)bytes, 0x00020000u};
+}
+
+// Copy of 16 bytes per lane from a buffer straight into LDS (the 64 lanes fill 1 KiB at LDS address
+// lds), written as inline assembly on purpose: with copies still in flight across the loop, the
+// compiler's wait-count pass no longer tells the LDS stages apart and would make every LDS read wait
+// for all outstanding copies.  The kernel waits for its own copies (vmcnt) and publishes them with
+// a barrier before any wave reads them; the memory clobber keeps LDS accesses in program order
+// around the copy.
+__device__ __forceinline__ void lds_dma16(u32x4 rsrc, const uint8_t* lds, int voff, int soff) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LBSA_LDS(lds)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+
 // Read-only kernel inputs read at wave-uniform addresses (block table): the constant address
 // space makes them scalar loads, counted apart from the vector-memory queue the LDS DMA uses.
 typedef const __attribute__((address_space(4))) int32_t const_i32;
@@ -131,14 +157,11 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;
   __builtin_amdgcn_s_waitcnt(((vm) & 0xF) | (((vm) >> 4) << 14) | (0x7 << 4) | (((lgkm) & 0xF) << 8))
 
 // Unit height and DMA share of a workgroup of WAVES waves (a struct, not function-local constants:
-// the host pass of the kernel template needs them as constant expressions in array bounds).
+// the host pass of the kernel template needs them as constant expressions).
 template <int WAVES>
 struct PrefillShape {
   static constexpr int kQTile = 32 * WAVES;   // query rows per unit
   static constexpr int kTpw = 16 / WAVES;     // 1 KiB DMA slots per wave in each half of a stage
-  // LDS stages of 32 KiB: two (one chunk in flight); an 8-wave workgroup, which has the CU to
-  // itself, may take three (two chunks in flight) at compile time
-  static constexpr int kStages = WAVES == 8 ? LBSA_PREFILL_STAGES_8 : 2;
 };
 
 template <int PV, int WAVES>
@@ -148,7 +171,6 @@ void splitkv_prefill_kernel(PrefillParams p) {
   // the pipeline stages, separate objects so the compiler can tell their DMA writes apart
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t stage2[Shape::kStages == 3 ? kStage : 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -240,6 +262,9 @@ void splitkv_prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qf[cb][ks] = ok ? ld16(qp + 32 * ks) : u32x4{0u, 0u, 0u, 0u};
     }
+    // Q has landed before any K/V copy is issued: the copies are invisible to the compiler, whose own
+    // wait for Q would otherwise wait for every copy in flight too
+    LBSA_WAIT_VM_LGKM(0, 15);
 
     float m_ref[kColBlocks], m_true[kColBlocks], lsum[kColBlocks];
     f32x4 o[kColBlocks][8];
@@ -257,71 +282,61 @@ void splitkv_prefill_kernel(PrefillParams p) {
     const int n_chunks = kv_end > c_first ? (kv_end - c_first + kPChunk - 1) / kPChunk : 0;
 
     // chunk i -> stage: each wave issues 8 buffer->LDS loads of 1 KiB (4 of K, 4 of V^T)
-    auto dma = [&](int i, uint8_t* st) {
+    auto dma = [&](int i, uint8_t* st) __attribute__((always_inline)) {
       const int c0 = c_first + kPChunk * i;
       const int pg = c0 / p.page;
       const int off = c0 - pg * p.page;
       int pid = bt_row[pg];
       pid = min(max(pid, 0), p.num_pages - 1);
       const size_t blk = ((size_t)pid * p.Hkv + g) * (size_t)p.page * kPD;
-      __amdgpu_buffer_rsrc_t kr =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.k + blk), (short)0, block_bytes, 0x00020000);
-      __amdgpu_buffer_rsrc_t vr =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.v + blk), (short)0, block_bytes, 0x00020000);
+      const u32x4 kr = raw_rsrc(p.k + blk, block_bytes);
+      const u32x4 vr = raw_rsrc(p.v + blk, block_bytes);
+#pragma unroll
+      for (int t = 0; t < Shape::kTpw; ++t) lds_dma16(kr, st + 1024 * (Shape::kTpw * wave + t), k_src[t], off * kRow);
 #pragma unroll
       for (int t = 0; t < Shape::kTpw; ++t)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, LBSA_LDS(st + 1024 * (Shape::kTpw * wave + t)), 16, k_src[t],
-                                                 off * kRow, 0, LBSA_PREFILL_KV_POLICY);
-#pragma unroll
-      for (int t = 0; t < Shape::kTpw; ++t)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, LBSA_LDS(st + kKBytes + 1024 * (Shape::kTpw * wave + t)), 16, v_src[t],
-                                                 (off / 32) * kPD * kRow, 0, LBSA_PREFILL_KV_POLICY);
+        lds_dma16(vr, st + kKBytes + 1024 * (Shape::kTpw * wave + t), v_src[t], (off / 32) * kPD * kRow);
     };
 
-    auto compute = [&](int i, const uint8_t* st) {
-      const int c0 = c_first + kPChunk * i;
-      if (c0 > wave_last_key) return;   // chunk entirely past this wave's rows (causal) or no rows
-      // mask needed: keys outside [kv_begin, kv_end), or (causal) keys after some row's position
-      const bool edge = (c0 < kv_begin) || (c0 + kPChunk > kv_end) ||
-                        (p.causal && c0 + kPChunk - 1 > prefix + wave_row0);
-      // sc[kb][cb][4j+i] = key c0 + 32kb + 8grp + 4j + i, column (row) r of block cb
-      auto qk = [&](int kb, float (&scb)[kColBlocks][8]) {
+    // a chunk needs masking if it holds keys outside [kv_begin, kv_end) or (causal) keys after the
+    // position of some row of this wave
+    auto chunk_edge = [&](int c0) __attribute__((always_inline)) {
+      return (c0 < kv_begin) || (c0 + kPChunk > kv_end) || (p.causal && c0 + kPChunk - 1 > prefix + wave_row0);
+    };
+    // S^T of one 32-key block of the chunk in stage st: scb[cb][4j+i] = raw q.k of key
+    // c0 + 32kb + 8grp + 4j + i and column (row) r of block cb; masked keys get -inf
+    auto scores = [&](int c0, bool edge, const uint8_t* st, int kb, float (&scb)[kColBlocks][8]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          u32x4 kf[4];
+      for (int j = 0; j < 2; ++j) {
+        u32x4 kf[4];
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) kf[ks] = lds_ld16(st, k_base[ks] + (32 * kb + 4 * j) * kKRow);
+        for (int ks = 0; ks < 4; ++ks) kf[ks] = lds_ld16(st, k_base[ks] + (32 * kb + 4 * j) * kKRow);
 #pragma unroll
-          for (int cb = 0; cb < kColBlocks; ++cb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int cb = 0; cb < kColBlocks; ++cb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(kf[ks], qf[cb][ks], acc);
+          for (int ks = 0; ks < 4; ++ks) acc = mfma16x16x32(kf[ks], qf[cb][ks], acc);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) scb[cb][4 * j + e] = acc[e];   // raw q.k; scaled inside exp2
+          for (int e = 0; e < 4; ++e) scb[cb][4 * j + e] = acc[e];   // raw q.k; scaled inside exp2
+        }
+      }
+      if (edge) {
+#pragma unroll
+        for (int cb = 0; cb < kColBlocks; ++cb) {
+          const int row = wave_row0 + 16 * cb + r;
+          const int last = p.causal ? prefix + row : kv_len - 1;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int t = c0 + 32 * kb + 8 * grp + e;
+            scb[cb][e] = (t < kv_begin || t >= kv_end || t > last) ? -INFINITY : scb[cb][e];
           }
         }
-        if (edge) {
-#pragma unroll
-          for (int cb = 0; cb < kColBlocks; ++cb) {
-            const int row = wave_row0 + 16 * cb + r;
-            const int last = p.causal ? prefix + row : kv_len - 1;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int t = c0 + 32 * kb + 8 * grp + e;
-              scb[cb][e] = (t < kv_begin || t >= kv_end || t > last) ? -INFINITY : scb[cb][e];
-            }
-          }
-        }
-      };
-      // S^T of both 32-key blocks, then one softmax update for the whole chunk, then P.V for both
-      // blocks: the exp / split work of one tile and the P.V MFMAs of another sit in one straight
-      // line of code the scheduler can interleave
-      float sc[2][kColBlocks][8];
-      qk(0, sc[0]);
-      qk(1, sc[1]);
-      float neg_mc[kColBlocks];
+      }
+    };
+    // maximum of a chunk's 64 scores per row (column): mxs, the running true maximum, and whether
+    // this lane's rows pass their reference maximum by more than the slack
+    auto chunk_max = [&](const float (&sc)[2][kColBlocks][8], float (&mxs)[kColBlocks]) __attribute__((always_inline)) {
       bool any_rescale = false;
-      float mxs[kColBlocks];
 #pragma unroll
       for (int cb = 0; cb < kColBlocks; ++cb) {
         float mx = sc[0][cb][0];
@@ -329,47 +344,36 @@ void splitkv_prefill_kernel(PrefillParams p) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[kb][cb][e]);
-        mx = fmaxf(mx, xor_lane(mx, 16));
-        mx = fmaxf(mx, xor_lane(mx, 32));
+        mx = max_over_rows(mx);
         m_true[cb] = fmaxf(m_true[cb], mx);
         mxs[cb] = mx;
         any_rescale |= mx > m_ref[cb] + slack_raw;
       }
-      if (__builtin_amdgcn_ballot_w64(any_rescale)) {
+      return any_rescale;
+    };
+    // move the reference maximum of the rows whose chunk maximum passed it (0 from -inf), rescaling
+    // their accumulators and row sums; the others keep theirs, which may still be -inf for a row
+    // with no visible key yet (-inf - -inf would be NaN)
+    auto rescale_to = [&](const float (&mxs)[kColBlocks]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int cb = 0; cb < kColBlocks; ++cb) {
-          // only rows whose reference moves are rescaled (0 from -inf); the others keep theirs, which
-          // may still be -inf for a row with no visible key yet (-inf - -inf would be NaN)
-          const bool move = mxs[cb] > m_ref[cb] + slack_raw;
-          const float m_new = move ? mxs[cb] : m_ref[cb];
-          const float alpha = move ? fast_exp2((m_ref[cb] - m_new) * c) : 1.f;
-          m_ref[cb] = m_new;
-          lsum[cb] *= alpha;
+      for (int cb = 0; cb < kColBlocks; ++cb) {
+        const bool move = mxs[cb] > m_ref[cb] + slack_raw;
+        const float m_new = move ? mxs[cb] : m_ref[cb];
+        const float alpha = move ? fast_exp2((m_ref[cb] - m_new) * c) : 1.f;
+        m_ref[cb] = m_new;
+        lsum[cb] *= alpha;
 #pragma unroll
-          for (int n = 0; n < 8; ++n) o[cb][n] *= alpha;
-        }
+        for (int n = 0; n < 8; ++n) o[cb][n] *= alpha;
       }
+    };
+    // probabilities of a chunk against the reference maximum, their row sums, and P packed as the B
+    // operand of the P.V products (fp16; or bf16 hi + lo parts)
+    auto exp_pack = [&](const float (&sc)[2][kColBlocks][8], u32x4 (&pf)[2][kColBlocks][2]) __attribute__((always_inline)) {
+      float neg_mc[kColBlocks];
 #pragma unroll
       for (int cb = 0; cb < kColBlocks; ++cb) neg_mc[cb] = (m_ref[cb] == -INFINITY) ? 0.f : -m_ref[cb] * c;
-
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int kbase = c0 + 32 * kb;
-        // V^T fragments of this 32-key block: dim 16n + r, keys kbase + 8grp .. +7
-        u32x4 vf[8];
-#pragma unroll
-        for (int n = 0; n < 8; ++n) vf[n] = lds_ld16(st, v_base[kb] + 16 * n * kVRow);
-        if (edge) {
-          // keys outside [kv_begin, kv_end) may hold any bits; p = 0 does not cancel a NaN
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int t = kbase + 8 * grp + 2 * e;
-            const uint32_t keep = ((t >= kv_begin && t < kv_end) ? 0x0000ffffu : 0u) |
-                                  ((t + 1 >= kv_begin && t + 1 < kv_end) ? 0xffff0000u : 0u);
-#pragma unroll
-            for (int n = 0; n < 8; ++n) vf[n][e] &= keep;
-          }
-        }
 #pragma unroll
         for (int cb = 0; cb < kColBlocks; ++cb) {
           float ps[8];
@@ -379,35 +383,85 @@ void splitkv_prefill_kernel(PrefillParams p) {
             lsum[cb] += ps[e];
           }
           if constexpr (PV == kPvF16) {
-          u32x4 pf;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) pf[e] = pack_f16(ps[2 * e], ps[2 * e + 1]);
-#pragma unroll
-          for (int n = 0; n < 8; ++n) o[cb][n] = mfma16x16x32_f16(vf[n], pf, o[cb][n]);
+            for (int e = 0; e < 4; ++e) pf[kb][cb][0][e] = pack_f16(ps[2 * e], ps[2 * e + 1]);
           } else {
-          // P split into bf16 hi + lo parts: two MFMAs keep ~16 significant bits of each probability
-          u32x4 phi, plo;
+            // P split into bf16 hi + lo parts: two MFMAs keep ~16 significant bits of each probability
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t hv = pack_bf16(ps[2 * e], ps[2 * e + 1]);
-            phi[e] = hv;
-            plo[e] = pack_bf16(ps[2 * e] - bf16_lo(hv), ps[2 * e + 1] - bf16_hi(hv));
-          }
-#pragma unroll
-          for (int n = 0; n < 8; ++n) {
-            o[cb][n] = mfma16x16x32(vf[n], phi, o[cb][n]);
-            o[cb][n] = mfma16x16x32(vf[n], plo, o[cb][n]);
-          }
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t hv = pack_bf16(ps[2 * e], ps[2 * e + 1]);
+              pf[kb][cb][0][e] = hv;
+              pf[kb][cb][1][e] = pack_bf16(ps[2 * e] - bf16_lo(hv), ps[2 * e + 1] - bf16_hi(hv));
+            }
           }
         }
       }
     };
+    // one online-softmax update over the 64 scores of a chunk
+    auto softmax_chunk = [&](const float (&sc)[2][kColBlocks][8], u32x4 (&pf)[2][kColBlocks][2]) __attribute__((always_inline)) {
+      float mxs[kColBlocks];
+      if (__builtin_amdgcn_ballot_w64(chunk_max(sc, mxs))) rescale_to(mxs);
+      exp_pack(sc, pf);
+    };
+    // O^T += V^T . P^T for the chunk in stage st
+    // (vedge: the chunk holds keys outside [kv_begin, kv_end), whose V must be masked)
+    auto v_edge = [&](int c0) __attribute__((always_inline)) { return (c0 < kv_begin) || (c0 + kPChunk > kv_end); };
+    // O^T += V^T . P^T for 32-key block kb of the chunk in stage st
+    auto pv_block = [&](int c0, bool vedge, const uint8_t* st, int kb, const u32x4 (&pb)[kColBlocks][2]) __attribute__((always_inline)) {
+      const int kbase = c0 + 32 * kb;
+      // V^T fragments of this 32-key block: dim 16n + r, keys kbase + 8grp .. +7
+      u32x4 vf[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) vf[n] = lds_ld16(st, v_base[kb] + 16 * n * kVRow);
+      if (vedge) {
+        // keys outside [kv_begin, kv_end) may hold any bits; p = 0 does not cancel a NaN
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = kbase + 8 * grp + 2 * e;
+          const uint32_t keep = ((t >= kv_begin && t < kv_end) ? 0x0000ffffu : 0u) |
+                                ((t + 1 >= kv_begin && t + 1 < kv_end) ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int n = 0; n < 8; ++n) vf[n][e] &= keep;
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < kColBlocks; ++cb) {
+        if constexpr (PV == kPvF16) {
+#pragma unroll
+          for (int n = 0; n < 8; ++n) o[cb][n] = mfma16x16x32_f16(vf[n], pb[cb][0], o[cb][n]);
+        } else {
+#pragma unroll
+          for (int n = 0; n < 8; ++n) {
+            o[cb][n] = mfma16x16x32(vf[n], pb[cb][0], o[cb][n]);
+            o[cb][n] = mfma16x16x32(vf[n], pb[cb][1], o[cb][n]);
+          }
+        }
+      }
+    };
+    // O^T += V^T . P^T for the chunk in stage st
+    auto pv_chunk = [&](int c0, bool vedge, const uint8_t* st, const u32x4 (&pf)[2][kColBlocks][2]) __attribute__((always_inline)) {
+      pv_block(c0, vedge, st, 0, pf[0]);
+      pv_block(c0, vedge, st, 1, pf[1]);
+    };
+    // the whole chunk i in one wave: S^T, softmax, P.V
+    auto compute = [&](int i, const uint8_t* st) __attribute__((always_inline)) {
+      const int c0 = c_first + kPChunk * i;
+      if (c0 > wave_last_key) return;   // chunk entirely past this wave's rows (causal) or no rows
+      const bool edge = chunk_edge(c0);
+      float sc[2][kColBlocks][8];
+      scores(c0, edge, st, 0, sc[0]);
+      scores(c0, edge, st, 1, sc[1]);
+      u32x4 pf[2][kColBlocks][2];
+      softmax_chunk(sc, pf);
+      pv_chunk(c0, v_edge(c0), st, pf);
+    };
+
 
     // V^T of the chunk in stage st: keys outside [kv_begin, kv_end) stay as loaded (the P.V
     // fragments mask them); on the fp16 path the values are converted to fp16 in place.  Each
     // thread converts the granules its own buffer->LDS loads wrote, so only its own loads need to
     // have landed.
-    auto to_f16 = [&](uint8_t* st) {
+    auto to_f16 = [&](uint8_t* st) __attribute__((always_inline)) {
 #pragma unroll
       for (int t = 0; t < Shape::kTpw; ++t) {
         u32x4* gp = reinterpret_cast<u32x4*>(st + kKBytes + 1024 * (Shape::kTpw * wave + t) + 16 * lane);
@@ -417,86 +471,36 @@ void splitkv_prefill_kernel(PrefillParams p) {
         *gp = x;
       }
     };
-    constexpr int kLoads = 2 * Shape::kTpw;   // buffer->LDS loads per thread per chunk
-
-    if constexpr (Shape::kStages == 3) {
-      // one pipeline step: start chunk i+2's DMA into the stage chunk i-1 used (every wave finished
-      // it before the previous barrier), compute chunk i, wait for the own loads of chunk i+1 (chunk
-      // i+2's may stay in flight), convert its V, barrier
-      auto step = [&](int i, uint8_t* cur, uint8_t* nxt, uint8_t* ahead) {
-        const bool more2 = i + 2 < n_chunks;
-        if (more2) dma(i + 2, ahead);
-        compute(i, cur);
-        if (i + 1 < n_chunks) {
-          if (more2) {
-            LBSA_WAIT_VM_LGKM(kLoads, 15);
-          } else {
-            LBSA_WAIT_VM_LGKM(0, 15);
-          }
-          if constexpr (PV == kPvF16) to_f16(nxt);
-        }
-        if (more2) {
-          LBSA_WAIT_VM_LGKM(kLoads, 0);
-        } else {
-          LBSA_WAIT_VM_LGKM(0, 0);
-        }
-        __builtin_amdgcn_s_barrier();
-      };
-      if (n_chunks > 0) {
-        dma(0, stage0);
-        if (n_chunks > 1) dma(1, stage1);
-        if (n_chunks > 1) {
-          LBSA_WAIT_VM_LGKM(kLoads, 15);
-        } else {
+    // one pipeline step: start chunk i+1's DMA into the other stage (last read by chunk i-1,
+    // finished by every wave before the previous barrier), compute chunk i, wait for the DMA,
+    // convert chunk i+1's V (fp16 path), barrier: one barrier per chunk makes chunk i+1 ready for
+    // every wave and releases chunk i's stage
+    auto step = [&](int i, uint8_t* cur, uint8_t* ahead) __attribute__((always_inline)) {
+      const bool more = i + 1 < n_chunks;
+      if (more) dma(i + 1, ahead);
+      compute(i, cur);
+      if constexpr (PV == kPvF16) {
+        if (more) {
           LBSA_WAIT_VM_LGKM(0, 15);
-        }
-        if constexpr (PV == kPvF16) to_f16(stage0);
-        if (n_chunks > 1) {
-          LBSA_WAIT_VM_LGKM(kLoads, 0);
-        } else {
-          LBSA_WAIT_VM_LGKM(0, 0);
-        }
-        __builtin_amdgcn_s_barrier();
-        for (int i = 0; i < n_chunks; i += 3) {
-          step(i, stage0, stage1, stage2);
-          if (i + 1 >= n_chunks) break;
-          step(i + 1, stage1, stage2, stage0);
-          if (i + 2 >= n_chunks) break;
-          step(i + 2, stage2, stage0, stage1);
+          to_f16(ahead);
         }
       }
-    } else {
-      // one pipeline step: start chunk i+1's DMA into the other stage (last read by chunk i-1,
-      // finished by every wave before the previous barrier), compute chunk i, wait for the DMA,
-      // convert chunk i+1's V (fp16 path), barrier: one barrier per chunk makes chunk i+1 ready for
-      // every wave and releases chunk i's stage
-      auto step = [&](int i, uint8_t* cur, uint8_t* ahead) {
-        const bool more = i + 1 < n_chunks;
-        if (more) dma(i + 1, ahead);
-        compute(i, cur);
-        if constexpr (PV == kPvF16) {
-          if (more) {
-            LBSA_WAIT_VM_LGKM(0, 15);
-            to_f16(ahead);
-          }
-        }
-        LBSA_WAIT_VM_LGKM(0, 0);
-        __builtin_amdgcn_s_barrier();
-      };
+      LBSA_WAIT_VM_LGKM(0, 0);
+      __builtin_amdgcn_s_barrier();
+    };
 
-      if (n_chunks > 0) {
-        dma(0, stage0);
-        if constexpr (PV == kPvF16) {
-          LBSA_WAIT_VM_LGKM(0, 15);
-          to_f16(stage0);
-        }
-        LBSA_WAIT_VM_LGKM(0, 0);
-        __builtin_amdgcn_s_barrier();
-        for (int i = 0; i < n_chunks; i += 2) {
-          step(i, stage0, stage1);
-          if (i + 1 >= n_chunks) break;
-          step(i + 1, stage1, stage0);
-        }
+    if (n_chunks > 0) {
+      dma(0, stage0);
+      if constexpr (PV == kPvF16) {
+        LBSA_WAIT_VM_LGKM(0, 15);
+        to_f16(stage0);
+      }
+      LBSA_WAIT_VM_LGKM(0, 0);
+      __builtin_amdgcn_s_barrier();
+      for (int i = 0; i < n_chunks; i += 2) {
+        step(i, stage0, stage1);
+        if (i + 1 >= n_chunks) break;
+        step(i + 1, stage1, stage0);
       }
     }
 
