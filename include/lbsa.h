@@ -349,7 +349,12 @@ int attn_splitkv_prefill(const void* q, const void* k_cache, const void* v_cache
  *   max_splits    largest slot count of any unit (from the host map), or 0 if unknown; above 16 a
  *                 unit's slots are spread over four waves (a launch-shape hint, any value >= 0 is
  *                 correct)
- * Errors: LBSA_ERR_INVALID, LBSA_ERR_UNSUPPORTED (head_dim != 128), LBSA_ERR_HIP.
+ * Launch shapes: prefill with rows_per_unit >= 64 and 64 query heads takes one 256-thread
+ * workgroup per (unit, row), each thread a quarter of one head (part_o and out then 16-byte
+ * aligned, 8 for a bf16 out); otherwise one wave per (unit, row, query head) (part_o and out
+ * 8-byte aligned, 4 for a bf16 out).
+ * Errors: LBSA_ERR_INVALID (also a misaligned part_o or out), LBSA_ERR_UNSUPPORTED
+ * (head_dim != 128), LBSA_ERR_HIP.
  */
 int attn_combine(const float* part_m, const float* part_l, const float* part_o,
                  const int32_t* map, int32_t num_units, int32_t rows_per_unit,

@@ -138,6 +138,87 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   }
 }
 
+// Row-wide form for units of many rows with 64 query heads (prefill): one workgroup per
+// (unit, row), thread t owns query head t / 4 and output dims 32 (t % 4) .. +31, so a slot's
+// partial row (64 heads x 128 dims, 32 KiB) and the output row are read and written as whole
+// contiguous rows, and the four threads of a head keep the same running maximum.  Two slots' loads
+// are in flight at a time.
+__global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
+  const int64_t ur = blockIdx.x;   // u * R + r
+  const int t = threadIdx.x;
+  const int h = t >> 2;
+  const int d0 = 32 * (t & 3);
+  if (ur >= (int64_t)p.U * p.R) return;
+  if (p.map[0] != LBSA_MAP_VERSION && p.map[0] != LBSA_MAP_VERSION_ORDERED) return;
+  const int W = p.map[2];
+  const int32_t* unit_ptr = p.map + 8 + (W + 1);
+  const int32_t* units = unit_ptr + (p.U + 1);
+  const int r = (int)(ur % p.R);
+  const int u = (int)(ur / p.R);
+  const int b = units[2 * u];
+  const int qt = units[2 * u + 1];
+  if (b < 0 || b >= p.map[1]) return;
+  const int row_in_req = qt * p.R + r;
+  if (row_in_req >= p.q_lens[b]) return;
+  const int64_t orow = (int64_t)p.q_start[b] + row_in_req;
+  const int s0 = unit_ptr[u];
+  const int n = unit_ptr[u + 1] - s0;
+  if (s0 < 0 || n < 0 || s0 + n > p.map[4]) return;
+  auto ml_index = [&](int i) -> int64_t { return ((int64_t)(s0 + i) * p.R + r) * 64 + h; };
+
+  float M = -INFINITY, L = 0.f;
+  f32x4 a[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the same branch-free online update as the per-head form, on eight float4 per slot
+  auto absorb = [&](float m, float l, const f32x4 (&o)[8]) {
+    const float Mn = fmaxf(M, m);
+    const float sc = Mn == -INFINITY ? 1.f : fast_exp2((M - Mn) * kLog2e);
+    const float w = m == -INFINITY ? 0.f : fast_exp2((m - Mn) * kLog2e);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a[k] = w * o[k] + a[k] * sc;
+    L = fmaf(w, l, L * sc);
+    M = Mn;
+  };
+  auto load = [&](int i, float& m, float& l, f32x4 (&o)[8]) {
+    const int64_t mi = ml_index(i);
+    m = p.part_m[mi];
+    l = p.part_l[mi];
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + mi * 128 + d0);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o[k] = src[k];
+  };
+  int i = 0;
+  for (; i + 1 < n; i += 2) {
+    float m0, l0, m1, l1;
+    f32x4 o0[8], o1[8];
+    load(i, m0, l0, o0);
+    load(i + 1, m1, l1, o1);
+    absorb(m0, l0, o0);
+    absorb(m1, l1, o1);
+  }
+  if (i < n) {
+    float m0, l0;
+    f32x4 o0[8];
+    load(i, m0, l0, o0);
+    absorb(m0, l0, o0);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;   // a row with no visible key gets 0
+  const int64_t obase = (orow * 64 + h) * 128 + d0;
+  if (p.out_bf16) {
+    uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + obase);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const f32x4 v = a[k] * inv;
+      *reinterpret_cast<uint2*>(dst + 2 * k) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+    }
+  } else {
+    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) dst[k] = a[k] * inv;
+  }
+}
+
 }  // namespace lbsa
 
 using namespace lbsa;
@@ -160,7 +241,14 @@ extern "C" int attn_combine(const float* part_m, const float* part_l, const floa
                   num_q_heads, out_dtype};
   const int64_t items = (int64_t)num_units * rows_per_unit * num_q_heads;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (max_splits > 16) {
+  if (q_lens && rows_per_unit >= 64 && num_q_heads == 64) {
+    // units of many rows (prefill): one workgroup per (unit, row)
+    const int64_t rows = (int64_t)num_units * rows_per_unit;
+    if (rows > INT32_MAX) return LBSA_ERR_INVALID;
+    if (reinterpret_cast<uintptr_t>(part_o) & 15 || reinterpret_cast<uintptr_t>(out) & (out_dtype ? 7 : 15))
+      return LBSA_ERR_INVALID;
+    hipLaunchKernelGGL(combine_rows_kernel, dim3((unsigned)rows), dim3(256), 0, st, p);
+  } else if (max_splits > 16) {
     if (items > INT32_MAX) return LBSA_ERR_INVALID;
     hipLaunchKernelGGL(combine_kernel<4>, dim3((unsigned)items), dim3(256), 0, st, p);
   } else {

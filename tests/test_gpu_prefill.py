@@ -155,3 +155,23 @@ def test_unit_height_mismatch_writes_nothing():
                             pm, pl, po, q_tile=256)
     torch.cuda.synchronize()
     assert bool((pm == 7.0).all()) and bool((pl == 7.0).all()) and bool((po == 7.0).all())
+
+
+@pytest.mark.parametrize("q_tile", [256, 128])
+def test_bf16_output_is_rounded_fp32_output(q_tile):
+    """The combine run twice on the same partials: its bf16 output is its fp32 output rounded to
+    nearest even, bit for bit, on every row of a ragged batch (the combine's store path for bf16)."""
+    from load_balanced_split_attn_amd.prefill import PrefillStep
+    wl = WL.random_prefill(7, 4, 1200, 300)
+    note(f"bf16 out q_tile={q_tile} q_lens={wl.q_lens} kv_lens={wl.kv_lens}")
+    q, kc, vc, bt = prefill_inputs(wl, pad_value=float("nan"))
+    step = PrefillStep(wl.q_lens, wl.kv_lens, q.device, num_workers=5, q_tile=q_tile)
+    step.splitkv(q, kc, vc, bt, SCALE)
+    o32 = torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device)
+    o16 = torch.full(q.shape, float("nan"), dtype=torch.bfloat16, device=q.device)
+    step.combine(o32)
+    step.combine(o16)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o32).any()
+    assert torch.equal(o16.view(torch.int16).cpu(), o32.to(torch.bfloat16).view(torch.int16).cpu())
+    _check_all(wl, o32.cpu().numpy())
