@@ -187,13 +187,14 @@ def random_decode(seed: int, batch: int, max_len: int, min_len: int = 0, hq: int
                     head_dim=head_dim, paged=paged)
 
 
-def random_prefill(seed: int, batch: int, max_prefix: int, max_chunk: int) -> Workload:
+def random_prefill(seed: int, batch: int, max_prefix: int, max_chunk: int, hq: int = HQ,
+                   hkv: int = HKV) -> Workload:
     g = torch.Generator(device="cpu")
     g.manual_seed(seed_for(200 + seed, STREAM_LENGTHS))
     prefix = torch.randint(0, max_prefix + 1, (batch,), generator=g).tolist()
     chunk = torch.randint(1, max_chunk + 1, (batch,), generator=g).tolist()
     return Workload(f"random_prefill_{seed}", 200 + seed, [p + c for p, c in zip(prefix, chunk)], chunk,
-                    kind="prefill", meta={"prefix": prefix})
+                    kind="prefill", meta={"prefix": prefix}, hq=hq, hkv=hkv)
 
 
 def mtp(q_len: int = 4, base: str = "mixed") -> Workload:
