@@ -60,9 +60,9 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 // Tuning knobs (compile-time):
 //
 // P.V precision (runtime, template parameter PV):
-//   kPvF16   (default) each chunk's V^T is converted to fp16 once, in LDS, by the workgroup (one
-//            extra barrier per chunk) and P is rounded to fp16 (11 significant bits); the products
-//            run on v_mfma_f32_16x16x32_f16.  The bf16 -> fp16 conversion is exact for |v| in the
+//   kPvF16   (default) each chunk's V^T is converted to fp16 once, in LDS, by the workgroup (each
+//            thread its own copied granules, before the chunk's barrier) and P is rounded to fp16
+//            (11 significant bits); the products run on v_mfma_f32_16x16x32_f16.  The bf16 -> fp16 conversion is exact for |v| in the
 //            fp16 normal range; larger magnitudes saturate at 65504.
 //   kPvExact bf16 V with P split into bf16 hi + lo parts (two MFMAs, ~16 significant bits), no
 //            range limit.
@@ -71,12 +71,6 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 #ifndef LBSA_PREFILL_WPE
 #define LBSA_PREFILL_WPE 2
 #endif
-//   LBSA_PREFILL_KV_POLICY  cache-policy bits of the K/V loads (0: default; the 16 query tiles of a
-//                           request re-read its K/V, which the default policy keeps in L2)
-#ifndef LBSA_PREFILL_KV_POLICY
-#define LBSA_PREFILL_KV_POLICY 0
-#endif
-
 
 constexpr int kPvExact = 0;
 constexpr int kPvF16 = 2;
