@@ -260,13 +260,16 @@ void splitkv_prefill_kernel(PrefillParams p) {
     // wait for Q would otherwise wait for every copy in flight too
     LBSA_WAIT_VM_LGKM(0, 15);
 
-    float m_ref[kColBlocks], m_true[kColBlocks], lsum[kColBlocks];
+    // reference maximum (raw score units), true maximum, row sum, and -m_ref in log2 units (0 while
+    // m_ref is -inf) per column block
+    float m_ref[kColBlocks], m_true[kColBlocks], lsum[kColBlocks], neg_mc[kColBlocks];
     f32x4 o[kColBlocks][8];
 #pragma unroll
     for (int cb = 0; cb < kColBlocks; ++cb) {
       m_ref[cb] = -INFINITY;
       m_true[cb] = -INFINITY;
       lsum[cb] = 0.f;
+      neg_mc[cb] = 0.f;
 #pragma unroll
       for (int n = 0; n < 8; ++n) o[cb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -355,6 +358,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
         const float m_new = move ? mxs[cb] : m_ref[cb];
         const float alpha = move ? fast_exp2((m_ref[cb] - m_new) * c) : 1.f;
         m_ref[cb] = m_new;
+        neg_mc[cb] = move ? -m_new * c : neg_mc[cb];
         lsum[cb] *= alpha;
 #pragma unroll
         for (int n = 0; n < 8; ++n) o[cb][n] *= alpha;
@@ -362,27 +366,31 @@ void splitkv_prefill_kernel(PrefillParams p) {
     };
     // probabilities of a chunk against the reference maximum, their row sums, and P packed as the B
     // operand of the P.V products (fp16; or bf16 hi + lo parts)
+    // (fp16 path: the row sums add the fp16-rounded probabilities, the very values the P.V products
+    // take, two per v_dot2_f32_f16 against (1, 1) with fp32 accumulation)
     auto exp_pack = [&](const float (&sc)[2][kColBlocks][8], u32x4 (&pf)[2][kColBlocks][2]) __attribute__((always_inline)) {
-      float neg_mc[kColBlocks];
-#pragma unroll
-      for (int cb = 0; cb < kColBlocks; ++cb) neg_mc[cb] = (m_ref[cb] == -INFINITY) ? 0.f : -m_ref[cb] * c;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int cb = 0; cb < kColBlocks; ++cb) {
           float ps[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            ps[e] = fast_exp2(fmaf(sc[kb][cb][e], c, neg_mc[cb]));
-            lsum[cb] += ps[e];
-          }
+          for (int e = 0; e < 8; ++e) ps[e] = fast_exp2(fmaf(sc[kb][cb][e], c, neg_mc[cb]));
           if constexpr (PV == kPvF16) {
+            const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pf[kb][cb][0][e] = pack_f16(ps[2 * e], ps[2 * e + 1]);
+            for (int e = 0; e < 4; ++e) {
+              // (the sum reads the packed pair itself: reading the element back through pf was
+              // compiled to the first element's register for every e)
+              const f16x2 ph = {(_Float16)ps[2 * e], (_Float16)ps[2 * e + 1]};
+              pf[kb][cb][0][e] = __builtin_bit_cast(uint32_t, ph);
+              lsum[cb] = __builtin_amdgcn_fdot2(ph, ones, lsum[cb], false);
+            }
           } else {
             // P split into bf16 hi + lo parts: two MFMAs keep ~16 significant bits of each probability
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+              lsum[cb] += ps[2 * e] + ps[2 * e + 1];
               const uint32_t hv = pack_bf16(ps[2 * e], ps[2 * e + 1]);
               pf[kb][cb][0][e] = hv;
               pf[kb][cb][1][e] = pack_bf16(ps[2 * e] - bf16_lo(hv), ps[2 * e + 1] - bf16_hi(hv));
