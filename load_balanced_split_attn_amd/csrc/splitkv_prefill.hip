@@ -94,15 +94,20 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Maximum of two scores.  Scores are finite or -inf (masked keys are selected to -inf, never
+// computed from padding), so the NaN-propagating maximum gives the same result as fmaxf; unlike
+// fmaxf it needs no quieting of its inputs and maps to gfx950's v_maximum3_f32.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // maximum of v over lanes l, l ^ 16, l ^ 32 and l ^ 48 (one value from each 16-lane row): gfx950's
 // row-swap permutes exchange the two halves of the wave, then rows 0/1 and 2/3, as VALU operations
 __device__ __forceinline__ float max_over_rows(float v) {
   const uint32_t u = __float_as_uint(v);
   const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const float m = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const uint32_t w = __float_as_uint(m);
   const auto b = __builtin_amdgcn_permlane16_swap(w, w, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ u32x4 lds_ld16(const uint8_t* base, int off) {
@@ -340,9 +345,9 @@ void splitkv_prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sc[kb][cb][e]);
+          for (int e = 0; e < 8; ++e) mx = vmax(mx, sc[kb][cb][e]);
         mx = max_over_rows(mx);
-        m_true[cb] = fmaxf(m_true[cb], mx);
+        m_true[cb] = vmax(m_true[cb], mx);
         mxs[cb] = mx;
         any_rescale |= mx > m_ref[cb] + slack_raw;
       }
