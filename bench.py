@@ -84,6 +84,9 @@ def per_cu_busy(timing) -> dict:
             "mean_busy_over_span": float(vals.mean() / span), "workgroups": int(t.shape[0])}
 
 
+WARM_SECONDS = 0.05
+
+
 def time_steps(fn_split, fn_combine, steps: int, warmup: int):
     """Two timed passes on the launch stream: (1) `steps` back-to-back steps bracketed by one event
     pair (the step rate); (2) the same steps with an event pair around every split-KV launch and
@@ -93,6 +96,16 @@ def time_steps(fn_split, fn_combine, steps: int, warmup: int):
         fn_split(i)
         fn_combine(i)
     torch.cuda.synchronize()
+    # untimed warmup also lasts at least WARM_SECONDS of device work: after a pause (cache packing
+    # between sections) a few steps leave the clocks low for the start of the timed pass
+    t_warm = time.perf_counter() + WARM_SECONDS
+    i = warmup
+    while time.perf_counter() < t_warm:
+        for _ in range(4):
+            fn_split(i)
+            fn_combine(i)
+            i += 1
+        torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
