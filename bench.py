@@ -132,13 +132,8 @@ def time_steps(fn_split, fn_combine, steps: int, warmup: int):
 
 
 def kernel_source_digest() -> str:
-    import hashlib
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "load_balanced_split_attn_amd", "csrc")
-    for name in ("common.h", "splitkv_decode.hip"):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    from load_balanced_split_attn_amd.record_traffic import kernel_source_digest as digest
+    return digest()
 
 
 def recorded_traffic(kernel: str, workload: str):

@@ -210,7 +210,8 @@ int attn_query_workers(int device, int32_t head_groups, int32_t kv_dtype, int32_
  *   num_pages     pages in the caches (physical page ids are clamped into range)
  *   seq_lens      device int32[B]; a segment's KV end is clamped to seq_lens[b]
  *   map           device copy of an attn_plan / attn_plan_static map for this batch
- *   num_workers, num_segments   W and S of that map
+ *   num_workers, num_segments   W and S of that map (a map whose word 2 is not num_workers is
+ *                 skipped on the device: nothing is written)
  *   head_groups   G, a divisor of Hkv
  *   part_m, part_l, part_o       device fp32 outputs sized by S (see layouts)
  *   timing        optional device uint64[W*G*4] (start, end, HW_ID, XCC_ID per
@@ -324,7 +325,8 @@ int attn_store_kv(const void* q_in, const void* k_in, const void* v_in,
  *                 P as bf16 hi + lo parts (~16 bits, no range limit, ~15% slower)
  * Supported: head_dim 128, Hq/Hkv = 8, bf16, q_tile 128 (four waves of 32 rows per workgroup,
  * 256 threads) or 256 (eight waves, 512 threads), page_size a multiple of 64.  The map must come
- * from attn_plan_prefill with the same q_tile (a map of another unit height is skipped).
+ * from attn_plan_prefill with the same q_tile and num_workers (a map of another unit height or
+ * worker count is skipped: nothing is written).
  * Errors: LBSA_ERR_INVALID (also unknown flag bits), LBSA_ERR_UNSUPPORTED, LBSA_ERR_HIP.
  */
 #define LBSA_PREFILL_EXACT_PV 1

@@ -362,6 +362,8 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
   const int version = p.map[0];
   // a device-built map that reported an error, or an unknown layout
   if (version != LBSA_MAP_VERSION && version != LBSA_MAP_VERSION_ORDERED) return;
+  // a map planned for another worker count (its lists would be read past their end)
+  if (p.map[2] != p.W) return;
   const int U = p.map[7];
   const int32_t* worker_ptr = p.map + 8;
   const int32_t* segs = p.map + 8 + (p.W + 1) + (U + 1) + 2 * U;

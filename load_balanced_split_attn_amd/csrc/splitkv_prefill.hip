@@ -193,6 +193,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
   const_i32* map = (const_i32*)p.map;
   if (map[0] != LBSA_MAP_VERSION) return;   // a device-built map that reported an error
   if (map[6] != Shape::kQTile) return;              // a map planned for another unit height
+  if (map[2] != p.W) return;                        // a map planned for another worker count
   const int U = map[7];
   const_i32* worker_ptr = map + 8;
   const_i32* segs = map + 8 + (p.W + 1) + (U + 1) + 2 * U;

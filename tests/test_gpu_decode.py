@@ -202,3 +202,29 @@ def test_lpt_map_partials(lb):
     for s_, (m, l, o) in enumerate(rparts):
         assert np.max(np.abs(pm[s_] - m[0])) <= 1e-3, f"slot {s_} m"
         assert_close(po[s_] / pl[s_][:, None], o[0] / l[0][:, None], f"slot {s_} o/l")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("launch_workers", [6, 4])
+def test_worker_count_mismatch_writes_nothing(lb, launch_workers, fp8):
+    """A map planned for five workers launched with another worker count is skipped on the device
+    (its lists are never read past their end), for a larger and a smaller grid, both caches."""
+    from gpu_helpers import decode_inputs_fp8
+    wl = WL.random_decode(14, 6, 2000)
+    words = lb.attn_plan(wl.kv_lens, 5, 512)
+    inputs = decode_inputs_fp8(wl) if fp8 else decode_inputs(wl)
+    q, kc, vc, bt = inputs[:4]
+    dev = q.device
+    mp = torch.from_numpy(np.asarray(words, dtype=np.int32)).to(dev)
+    lens = torch.tensor(wl.kv_lens, dtype=torch.int32, device=dev)
+    S = max(int(words[4]), 1)
+    pm = torch.full((S, wl.hq), 7.0, device=dev)
+    pl = torch.full((S, wl.hq), 7.0, device=dev)
+    po = torch.full((S, wl.hq, wl.head_dim), 7.0, device=dev)
+    if fp8:
+        lb.attn_splitkv_fp8(q, kc, vc, inputs[4], inputs[5], bt, lens, mp, launch_workers, int(words[4]), 8, SCALE,
+                            pm, pl, po)
+    else:
+        lb.attn_splitkv(q, kc, vc, bt, lens, mp, launch_workers, int(words[4]), 8, SCALE, pm, pl, po)
+    torch.cuda.synchronize()
+    assert bool((pm == 7.0).all()) and bool((pl == 7.0).all()) and bool((po == 7.0).all())

@@ -175,3 +175,22 @@ def test_bf16_output_is_rounded_fp32_output(q_tile):
     assert not torch.isnan(o32).any()
     assert torch.equal(o16.view(torch.int16).cpu(), o32.to(torch.bfloat16).view(torch.int16).cpu())
     _check_all(wl, o32.cpu().numpy())
+
+
+@pytest.mark.parametrize("launch_workers", [3, 1])
+def test_worker_count_mismatch_writes_nothing(launch_workers):
+    """A map planned for two workers launched with another worker count is skipped on the device
+    (its lists are never read past their end), for a larger and a smaller grid."""
+    import load_balanced_split_attn_amd as lb
+    from load_balanced_split_attn_amd.prefill import PrefillStep
+    wl = WL.random_prefill(13, 2, 300, 200)
+    q, kc, vc, bt = prefill_inputs(wl)
+    st = PrefillStep(wl.q_lens, wl.kv_lens, q.device, num_workers=2)
+    S = max(st.S, 1)
+    pm = torch.full((S, 256, 64), 7.0, device=q.device)
+    pl = torch.full((S, 256, 64), 7.0, device=q.device)
+    po = torch.full((S, 256, 64, 128), 7.0, device=q.device)
+    lb.attn_splitkv_prefill(q, kc, vc, bt, st.q_lens, st.q_start, st.kv_lens, st.map, launch_workers, st.S, SCALE,
+                            pm, pl, po)
+    torch.cuda.synchronize()
+    assert bool((pm == 7.0).all()) and bool((pl == 7.0).all()) and bool((po == 7.0).all())
