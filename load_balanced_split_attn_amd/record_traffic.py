@@ -67,11 +67,11 @@ def kernel_mean(rows: list[tuple[str, int, float]], name: str) -> float:
     return sum(vals) / len(vals)
 
 
-def record(fetch_dir: str, write_dir: str, workload: str = "mixed") -> dict:
+def record(fetch_dir: str, write_dir: str, workload: str = "mixed", json_path: str = TRAFFIC_JSON) -> dict:
     fetch = read_counter(fetch_dir, "FETCH_SIZE")
     write = read_counter(write_dir, "WRITE_SIZE")
     f_fac, w_fac = calibration_factor(fetch), calibration_factor(write)
-    with open(TRAFFIC_JSON) as f:
+    with open(json_path) as f:
         old = json.load(f)
     digest = kernel_source_digest()
     out = {}
@@ -92,7 +92,7 @@ def record(fetch_dir: str, write_dir: str, workload: str = "mixed") -> dict:
             "profile": "profiles/splitkv_decode_mixed_hbm_traffic.md",
         }
         out[key] = {workload: entry}
-    with open(TRAFFIC_JSON, "w") as f:
+    with open(json_path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     return out
