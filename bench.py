@@ -38,6 +38,9 @@ DESCRIPTIONS = {
                "GQA 64q/8kv, d=128, bf16, paged 64-token KV (shuffled block table), tile 512",
     "tiny": "worked example: KV 1024/5120/2048, 1 query token, GQA 64q/8kv, d=128, bf16, contiguous pages, "
             "tile 512, 4 workers",
+    "mixed_tp8": "one GPU's share of the mixed batch under 8-way KV-head sharding: B=40, 8 each of KV "
+                 "1K/4K/16K/64K/128K (shuffled), 1 query token, 8q/1kv, d=128, bf16, paged 64-token KV "
+                 "(shuffled block table), tile 512",
 }
 
 
@@ -294,7 +297,8 @@ def bench_fp8(dev, wl, args, bf16_us: float) -> dict:
     caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(copies - 1)]
     workers = args.workers or (wl.workers if wl.workers else
                                lb.attn_query_workers(0, args.head_groups, lb.KV_FP8_E4M3))
-    step = DecodeStep(wl.kv_lens, dev, num_workers=workers, tile=args.tile, head_groups=args.head_groups,
+    step = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=workers, tile=args.tile,
+                      head_groups=args.head_groups,
                       kv_dtype=lb.KV_FP8_E4M3)
     out = torch.empty((wl.batch, wl.hq, wl.head_dim), dtype=torch.float32, device=dev)
     # the same map built on the device (attn_plan_device), timed with events on the stream
@@ -642,7 +646,8 @@ def main() -> int:
 
     workers = args.workers or (wl.workers if wl.workers else lb.attn_query_workers(0, args.head_groups))
     plan_t = time.perf_counter()
-    step = DecodeStep(wl.kv_lens, dev, num_workers=workers, tile=args.tile, head_groups=args.head_groups)
+    step = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=workers, tile=args.tile,
+                      head_groups=args.head_groups)
     plan_s = time.perf_counter() - plan_t
     t = time.perf_counter()
     for _ in range(100):
@@ -734,7 +739,8 @@ def main() -> int:
         splits = sorted(set([plain] + [s for s in (1, 2, 4, 8, 16, 32, 64) if s <= max_tiles]))
         rows = []
         for S in splits:
-            st = DecodeStep(wl.kv_lens, dev, tile=args.tile, head_groups=args.head_groups, static_splits=S)
+            st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, tile=args.tile, head_groups=args.head_groups,
+                            static_splits=S)
 
             def s_split(i, st=st):
                 k_, v_ = caches[i % copies]
@@ -758,7 +764,8 @@ def main() -> int:
 
     if not args.no_static and wl.name != "tiny":
         # the LPT assignment of the fifth page (largest tile first onto the least-loaded worker)
-        st = DecodeStep(wl.kv_lens, dev, num_workers=workers, tile=args.tile, head_groups=args.head_groups,
+        st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=workers, tile=args.tile,
+                        head_groups=args.head_groups,
                         planner="lpt")
 
         def l_split(i, st=st):
@@ -789,7 +796,8 @@ def main() -> int:
         rows = []
         for planner, tile_w, sc in (("greedy", 128, 0), ("greedy", 64, 0), ("weighted", 512, 0), ("weighted", 512, 128),
                                     ("weighted", 128, 0), ("weighted", 128, 128), ("weighted", 64, 256)):
-            st = DecodeStep(wl.kv_lens, dev, num_workers=workers, tile=tile_w, head_groups=args.head_groups,
+            st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=workers, tile=tile_w,
+                            head_groups=args.head_groups,
                             planner=planner, split_cost=sc)
 
             def w_split(i, st=st):

@@ -150,6 +150,14 @@ def mixed() -> Workload:
     return Workload("mixed", 3, lens, [1] * len(lens))
 
 
+def mixed_tp8() -> Workload:
+    """One GPU's share of the mixed batch under 8-way KV-head sharding: the same lengths, 8 query
+    heads over 1 KV head (its own seeds)."""
+    lens = [n * 1024 for n in (1, 4, 16, 64, 128) for _ in range(8)]
+    lens = _shuffled(lens, seed_for(3, STREAM_LENGTHS))
+    return Workload("mixed_tp8", 7, lens, [1] * len(lens), hq=8, hkv=1)
+
+
 def long_tail() -> Workload:
     """One 192K-token request followed by 15 requests of uniform length in [1024, 2048]."""
     g = torch.Generator(device="cpu")
@@ -215,4 +223,4 @@ def random_mtp(seed: int, batch: int, max_len: int, max_q: int = 4, min_len: int
 
 
 BY_NAME = {"tiny": tiny, "uniform": uniform, "mixed": mixed, "long_tail": long_tail, "control": control,
-           "prefill": prefill}
+           "prefill": prefill, "mixed_tp8": mixed_tp8}
