@@ -72,3 +72,46 @@ def test_full_size_fp8(name):
     for b, r in ref.items():
         ma, rr = assert_close(got[b], r, f"fp8 {name} request {b} (L={wl.kv_lens[b]})")
         note(f"  request {b} L={wl.kv_lens[b]}: max_abs={ma:.2e} rel_rms={rr:.2e}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_full_size_kv_head_share(fp8):
+    """One GPU's share of the mixed batch under 8-way KV-head sharding (8 query heads over one KV
+    head) in the launch bench.py times: 1,024 workers, one wave per (worker, KV head); sampled
+    requests against the fp64 oracle, every request against the plain static split map."""
+    import load_balanced_split_attn_amd as lb
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    from gpu_helpers import decode_inputs_fp8, oracle_decode_fp8
+    from oracle.plan import ref_plan
+    wl = WL.BY_NAME["mixed_tp8"]()
+    assert (wl.hq, wl.hkv) == (8, 1)
+    note(f"full-size KV-head share ({'E4M3' if fp8 else 'bf16'}): B={wl.batch} tokens={sum(wl.kv_lens)}")
+    kw = dict(num_q_heads=wl.hq, head_groups=1)
+    if fp8:
+        q, kc, vc, bt, ks, vs = decode_inputs_fp8(wl)
+        kw["kv_dtype"] = lb.KV_FP8_E4M3
+        call = dict(kv_scales=(ks, vs))
+    else:
+        q, kc, vc, bt = decode_inputs(wl)
+        call = {}
+    step = DecodeStep(wl.kv_lens, q.device, num_workers=1024, **kw)
+    assert np.array_equal(step.map_host, ref_plan(wl.kv_lens, 1024, 512))
+    out = step(q, kc, vc, bt, scale=SCALE, **call)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    seen, sample = set(), [0]
+    for b, L in enumerate(wl.kv_lens):
+        if L not in seen:
+            seen.add(L)
+            sample.append(b)
+    sample = sorted(set(sample + [int(np.argmax(wl.kv_lens))]))
+    ref = (oracle_decode_fp8 if fp8 else oracle_decode)(wl, sample)
+    for b, r in ref.items():
+        ma, rr = assert_close(got[b], r, f"share request {b} (L={wl.kv_lens[b]})")
+        note(f"  request {b} L={wl.kv_lens[b]}: max_abs={ma:.2e} rel_rms={rr:.2e}")
+    st = DecodeStep(wl.kv_lens, q.device, static_splits=26, **kw)
+    out2 = st(q, kc, vc, bt, scale=SCALE, **call)
+    torch.cuda.synchronize()
+    for b in range(wl.batch):
+        assert errors(out2[b].cpu().numpy().astype(np.float64), got[b].astype(np.float64))[1] <= 1e-5
