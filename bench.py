@@ -761,6 +761,17 @@ def main() -> int:
             "best_us": best["us_per_step"],
             "speedup_vs_plain": round(plain_row["us_per_step"] / (ms_per_step * 1e3), 3),
             "speedup_vs_best": round(best["us_per_step"] / (ms_per_step * 1e3), 3), "sweep": rows}
+        # the pages' own single-operator figures for dynamic over static split-KV, on Hopper-class GPUs
+        # with batches they do not specify: context beside this run's figures, not a target
+        result["pages_context"] = {
+            "source": "\"Hy3 Preview AI Infra 推理优化精读笔记\" §3.1 收益; "
+                      "\"腾讯混元AI Infra进化：HPC-Ops推理核心算子全面升级\" §三 Attention",
+            "hardware": "Hopper-class (not this machine)",
+            "speedup_vs_static_mixed_lengths": [1.59, 1.76],
+            "speedup_vs_static_single_long_request": 2.95,
+            "this_run": {"workload": wl.name,
+                         "speedup_vs_plain_static": result["static_baseline"]["speedup_vs_plain"],
+                         "speedup_vs_best_static": result["static_baseline"]["speedup_vs_best"]}}
 
     if not args.no_static and wl.name != "tiny":
         # the LPT assignment of the fifth page (largest tile first onto the least-loaded worker)
