@@ -248,9 +248,10 @@ void splitkv_prefill_kernel(PrefillParams p) {
     kv_end = min(kv_end, p.bt_stride * p.page);
     const int unit_row0 = qt * Shape::kQTile;                 // first row of the unit inside the chunk
     const int wave_row0 = unit_row0 + rbase;           // first row of this wave
-    // last key any row of this wave may see (-1: the wave has no row inside the chunk)
+    // last key any row of this wave may see (-1: the wave has no row inside the chunk); the wave's
+    // rows are wave_row0 .. wave_row0 + 16 * kColBlocks - 1
     const int wave_last_key = wave_row0 >= q_len ? -1
-                              : (p.causal ? prefix + min(wave_row0 + 32 * kColBlocks - 1, q_len - 1) : kv_len - 1);
+                              : (p.causal ? prefix + min(wave_row0 + 16 * kColBlocks - 1, q_len - 1) : kv_len - 1);
 
     // Q^T fragments: column r of block cb = row wave_row0 + 16cb + r, k = dims 32ks + 8grp .. +7
     u32x4 qf[kColBlocks][4];
