@@ -115,3 +115,31 @@ def test_full_size_kv_head_share(fp8):
     torch.cuda.synchronize()
     for b in range(wl.batch):
         assert errors(out2[b].cpu().numpy().astype(np.float64), got[b].astype(np.float64))[1] <= 1e-5
+
+
+def test_full_size_million_token_request():
+    """Maximum-size case: one request of 2^20 tokens (16,384 pages, so cache offsets pass 2^31
+    bytes) beside three short ones, in the launch bench.py times (workers from the occupancy query,
+    512-token tiles, one wave per KV head).  The long request is cut over every worker and its
+    ~128 splits take the many-split combine; every request is checked against the fp64 oracle."""
+    import load_balanced_split_attn_amd as lb
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    from oracle.plan import ref_plan
+    wl = WL.random_decode(21, 4, 3000, min_len=1)
+    wl.kv_lens[1] = 1 << 20
+    note(f"million-token request: lengths {wl.kv_lens}")
+    q, kc, vc, bt = decode_inputs(wl)
+    assert kc.numel() * kc.element_size() > 2 ** 31
+    W = lb.attn_query_workers(0, 8)
+    step = DecodeStep(wl.kv_lens, q.device, num_workers=W, head_groups=8)
+    assert np.array_equal(step.map_host, ref_plan(wl.kv_lens, W, 512))
+    assert step.max_splits > 16
+    out = step(q, kc, vc, bt, scale=SCALE)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    del kc, vc
+    torch.cuda.empty_cache()
+    for b in range(wl.batch):
+        ref = oracle_decode(wl, [b])[b]
+        ma, rr = assert_close(got[b], ref, f"request {b} (L={wl.kv_lens[b]})")
+        note(f"  request {b} L={wl.kv_lens[b]}: max_abs={ma:.2e} rel_rms={rr:.2e}")
