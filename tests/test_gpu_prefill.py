@@ -140,6 +140,29 @@ def test_full_size_prefill_sampled():
         note(f"  request {b} kv_len={wl.kv_lens[b]}: rows {rows} ok (last rel_rms {rr:.2e})")
 
 
+def test_million_token_prefix_sampled():
+    """Maximum-size prefill: a 2048-row causal chunk after a prefix of 2^20 - 2048 tokens (16,384
+    pages, cache offsets past 2^31 bytes) beside a short request, in the bench launch (256-row
+    units, 64 workers); sampled rows of the long request and every row of the short one against the
+    fp64 oracle."""
+    wl = WL.random_prefill(30, 2, 1000, 300)
+    wl.q_lens[0] = 2048
+    wl.kv_lens[0] = 1 << 20
+    note(f"million-token prefill: q_lens={wl.q_lens} kv_lens={wl.kv_lens}")
+    got, step = _run(wl, 64, poison=True)
+    assert np.all(np.isfinite(got))
+    starts = q_starts(wl)
+    rows = [0, 1, 255, 256, 1023, 2047]
+    ref = oracle_prefill_rows(wl, 0, rows)
+    for j in rows:
+        ma, rr = assert_close(got[starts[0] + j], ref[j], f"long request row {j}")
+    note(f"  long request rows {rows} ok (last rel_rms {rr:.2e})")
+    short = list(range(wl.q_lens[1]))
+    ref = oracle_prefill_rows(wl, 1, short)
+    for j in short:
+        assert_close(got[starts[1] + j], ref[j], f"short request row {j}")
+
+
 def test_unit_height_mismatch_writes_nothing():
     """A map planned for 128-row units given to the 256-row kernel is skipped, not misread."""
     import load_balanced_split_attn_amd as lb
