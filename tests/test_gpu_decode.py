@@ -228,3 +228,31 @@ def test_worker_count_mismatch_writes_nothing(lb, launch_workers, fp8):
         lb.attn_splitkv(q, kc, vc, bt, lens, mp, launch_workers, int(words[4]), 8, SCALE, pm, pl, po)
     torch.cuda.synchronize()
     assert bool((pm == 7.0).all()) and bool((pl == 7.0).all()) and bool((po == 7.0).all())
+
+
+def test_two_streams_concurrently(lb):
+    """The library keeps no per-call global state: two different decode batches launched on two
+    streams at once (split-KV and combine interleaved on the device) give bitwise the results of
+    running them one after the other."""
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    wls = [WL.random_decode(31, 9, 9000, min_len=1), WL.random_decode(32, 5, 30000, min_len=500)]
+    inputs = [decode_inputs(w) for w in wls]
+    steps = [DecodeStep(w.kv_lens, inp[0].device, num_workers=W) for w, inp, W in zip(wls, inputs, (37, 64))]
+    seq = []
+    for st, (q, kc, vc, bt) in zip(steps, inputs):
+        seq.append(st(q, kc, vc, bt, scale=SCALE).clone())
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    outs = [torch.full(inp[0].shape, float("nan"), dtype=torch.float32, device=inp[0].device) for inp in inputs]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for st, (q, kc, vc, bt), s, o in zip(steps, inputs, streams, outs):
+            st.splitkv(q, kc, vc, bt, SCALE, stream=s)
+        for st, s, o in zip(steps, streams, outs):
+            st.combine(o, stream=s)
+        torch.cuda.synchronize()
+        for a, b in zip(seq, outs):
+            assert torch.equal(a, b)
+    ref = oracle_decode(wls[1], [0, 4])
+    for b, r in ref.items():
+        assert_close(outs[1][b].cpu().numpy(), r, f"stream request {b}")
