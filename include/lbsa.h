@@ -195,7 +195,8 @@ int attn_plan_prefill(const int32_t* q_lens, const int32_t* kv_lens, int32_t B,
 /*
  * Workers that fill the device with one resident wave of decode workgroups:
  * CUs x (resident split-KV workgroups per CU) / head_groups, for the decode kernel of cache type
- * kv_dtype (LBSA_KV_*) launched with head_groups workgroups per worker.  Cached per device and type.
+ * kv_dtype (LBSA_KV_*) launched with head_groups workgroups per worker.  Cached per device and type;
+ * safe to call from several host threads at once.
  * Errors: LBSA_ERR_INVALID (head_groups not a divisor of 8, unknown kv_dtype, device out of range),
  * LBSA_ERR_HIP.
  */

@@ -39,6 +39,8 @@
 // exhausted (about 2,300 VALU lane operations per token and KV head for QK, PV and softmax, against
 // ~2,500 available at the bf16 byte rate and half that at the 8-bit rate).
 
+#include <atomic>
+
 #include "common.h"
 #include "lbsa.h"
 
@@ -691,13 +693,16 @@ extern "C" int attn_splitkv_mtp(const void* q, const void* k_cache, const void* 
 }
 
 extern "C" int attn_query_workers(int device, int32_t head_groups, int32_t kv_dtype, int32_t* num_workers_out) {
-  static int cached[64][2][9];
+  // per (device, cache type, head groups); atomics so that host threads may query at once (each
+  // computes the same value)
+  static std::atomic<int> cached[64][2][9];
   if (!num_workers_out || head_groups < 1 || head_groups > 8 || (8 % head_groups) || device < 0 ||
       device >= 64)
     return LBSA_ERR_INVALID;
   if (kv_dtype != LBSA_KV_BF16 && kv_dtype != LBSA_KV_FP8_E4M3) return LBSA_ERR_INVALID;
-  if (cached[device][kv_dtype][head_groups] > 0) {
-    *num_workers_out = cached[device][kv_dtype][head_groups];
+  const int known = cached[device][kv_dtype][head_groups].load(std::memory_order_relaxed);
+  if (known > 0) {
+    *num_workers_out = known;
     return LBSA_OK;
   }
   int prev = 0;
@@ -711,7 +716,7 @@ extern "C" int attn_query_workers(int device, int32_t head_groups, int32_t kv_dt
   if (hipSetDevice(prev) != hipSuccess) return LBSA_ERR_HIP;
   if (e != hipSuccess || nb < 1 || cus < 1) return LBSA_ERR_HIP;
   const int w = cus * nb / head_groups;
-  cached[device][kv_dtype][head_groups] = w;
+  cached[device][kv_dtype][head_groups].store(w, std::memory_order_relaxed);
   *num_workers_out = w;
   return LBSA_OK;
 }
