@@ -1,7 +1,8 @@
 """Full-size decode workloads in the launch configuration bench.py times (workers from the device
-occupancy query, 512-token tiles, one workgroup per KV head): sampled requests against the fp64
-oracle, and all requests against the static split-KV map (an exact re-association, so the two must
-agree to fp32 rounding)."""
+occupancy query, 512-token tiles, one workgroup per KV head): every request of the bf16 batches
+against the fp64 oracle (sampled requests for the 8-bit cache and the KV-head share), and all
+requests against the static split-KV map (an exact re-association, so the two must agree to fp32
+rounding)."""
 
 import numpy as np
 import pytest
@@ -28,17 +29,12 @@ def test_full_size(name):
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
-    # sampled requests: one of each distinct length (the longest included) and the first two
-    seen, sample = set(), [0, 1]
-    for b, L in enumerate(wl.kv_lens):
-        if L not in seen:
-            seen.add(L)
-            sample.append(b)
-    sample = sorted(set(sample))[:8] + [int(np.argmax(wl.kv_lens))]
-    ref = oracle_decode(wl, sorted(set(sample)))
-    for b, r in ref.items():
-        ma, rr = assert_close(got[b], r, f"{name} request {b} (L={wl.kv_lens[b]})")
-        note(f"  request {b} L={wl.kv_lens[b]}: max_abs={ma:.2e} rel_rms={rr:.2e}")
+    # every request against the fp64 oracle, one request at a time
+    worst = (0.0, 0.0)
+    for b in range(wl.batch):
+        ma, rr = assert_close(got[b], oracle_decode(wl, [b])[b], f"{name} request {b} (L={wl.kv_lens[b]})")
+        worst = (max(worst[0], ma), max(worst[1], rr))
+    note(f"  all {wl.batch} requests: worst max_abs={worst[0]:.2e} rel_rms={worst[1]:.2e}")
     # every request: static split-KV map gives the same attention
     plain = min(max(1, -(-W // wl.batch)), max(-(-L // 512) for L in wl.kv_lens))
     st = DecodeStep(wl.kv_lens, q.device, head_groups=8, static_splits=plain)
