@@ -86,20 +86,17 @@ def test_single_row_equals_plain_decode(lb):
 
 @pytest.mark.parametrize("fp8", [False, True])
 def test_full_size_mtp4_mixed(lb, fp8):
-    """The mixed batch with 4 drafted tokens per request in the bench launch configuration; sampled
-    requests (one per length, the longest included) against the oracle."""
+    """The mixed batch with 4 drafted tokens per request in the bench launch configuration; every
+    request against the oracle."""
     wl = WL.mtp(4)
     note(f"full-size mtp4 mixed fp8={fp8}")
     W = lb.attn_query_workers(0, 8, lb.KV_FP8_E4M3 if fp8 else lb.KV_BF16)
     got, _ = _run(lb, wl, W, 8, fp8, poison=False)
     assert np.all(np.isfinite(got))
-    seen, sample = set(), []
-    for b, L in enumerate(wl.kv_lens):
-        if L not in seen:
-            seen.add(L)
-            sample.append(b)
-    ref = oracle_mtp(wl, sample, fp8=fp8)
     starts = q_starts(wl)
-    for b, r in ref.items():
+    worst = (0.0, 0.0)
+    for b in range(wl.batch):
+        r = oracle_mtp(wl, [b], fp8=fp8)[b]
         ma, rr = assert_close(got[starts[b]:starts[b] + 4], r, f"mtp4 request {b} (L={wl.kv_lens[b]})")
-        note(f"  request {b} L={wl.kv_lens[b]}: max_abs={ma:.2e} rel_rms={rr:.2e}")
+        worst = (max(worst[0], ma), max(worst[1], rr))
+    note(f"  all {wl.batch} requests: worst max_abs={worst[0]:.2e} rel_rms={worst[1]:.2e}")
