@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 product path (the HIP library and its Python binding) never imports it and
 shares no code with it: no kernels, headers, helpers, tables or constants.
 
-Two parts:
+Four parts:
 
 * ``oracle.plan``      - the tile cut, the equal budgets and the greedy fill
   that build the work map, written out step by step.  Integer-only; the GPU
