@@ -35,7 +35,7 @@ def _device_map(lb, lens, W, tile, words=None):
 def test_bit_exact_random_batches(lb):
     rng = np.random.default_rng(17)
     cases = 0
-    for trial in range(120):
+    for trial in range(1200):
         B = int(rng.choice([0, 1, 2, 3, 7, 40, 333, 1500, 3000]))
         W = int(rng.choice([1, 2, 3, 5, 64, 128, 256, 1000, 2048]))
         tile = int(rng.choice([16, 64, 512, 4096]))
