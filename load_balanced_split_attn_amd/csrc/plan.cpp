@@ -320,7 +320,7 @@ int attn_plan_weighted(const int32_t* seq_lens, int32_t B, int32_t num_workers, 
   for (int32_t b = 0; b < B; ++b) {
     if (seq_lens[b] < 0) return LBSA_ERR_INVALID;
     T += tiles_for(seq_lens[b], tile);
-    C += seq_lens[b] + (seq_lens[b] > 0 ? split_cost : 0);
+    C += (int64_t)seq_lens[b] + (seq_lens[b] > 0 ? split_cost : 0);   // widened before the sum
   }
   if (T > INT32_MAX) return LBSA_ERR_INVALID;
   Writer probe{nullptr, num_workers, B};
