@@ -255,3 +255,59 @@ def test_append_then_decode(lb, fp8):
             vv = np.concatenate([old[b][1].double().numpy(), rv[b:b + 1]])
         ref = ref_attention(qg[b:b + 1], kk, vv, SCALE)[0]
         assert_close(got[b], ref, f"append+decode fp8={fp8} request {b}")
+
+
+@pytest.mark.parametrize("seed", range(96))
+def test_store_random_sweep(lb, seed):
+    """Seeded random producer steps crossing what the cases above take one at a time: batch size,
+    head counts, page size, 8-bit or bf16 cache, RMSNorm on or off, RoPE base (0 = off), Hadamard
+    on or off, eps and positions; q against the oracle with a guard row, every stored K/V value,
+    and nothing written outside the stored positions."""
+    from load_balanced_split_attn_amd.paged import unpack_request
+    g = np.random.default_rng([7, seed])
+    dev = torch.device("cuda")
+    max_pos = int(g.choice([100, 5000, 200000]))
+    B = int(g.integers(1, 300 if max_pos <= 5000 else 12))    # cache kept to a few GB
+    hq, hkv = [(64, 8), (8, 1), (6, 3), (12, 4), (16, 2), (32, 8)][int(g.integers(0, 6))]
+    page = int(g.choice([64, 128, 256]))
+    fp8 = bool(g.random() < 0.5)
+    norm = bool(g.random() < 0.5)
+    theta = float(g.choice([0.0, 10000.0, 1e6]))
+    had = bool(g.random() < 0.5)
+    eps = float(g.choice([1e-6, 1e-5]))
+    note(f"store sweep {seed}: B={B} heads={hq}/{hkv} page={page} fp8={fp8} norm={norm} theta={theta} "
+         f"hadamard={had} max_pos={max_pos}")
+    q, k, v, qw, kw = _inputs(500 + seed, B, Hq=hq, Hkv=hkv)
+    lens = [int(x) for x in g.integers(0, max_pos, size=B)]
+    kc, vc, bt = _empty_cache(lens, page, fp8, dev, Hkv=hkv)
+    pos = torch.tensor(lens, dtype=torch.int32, device=dev)
+    ks = vs = None
+    if fp8:
+        ks = torch.exp2(torch.rand(hkv, generator=torch.Generator().manual_seed(20 + seed)) * 2 - 5).float()
+        vs = torch.exp2(torch.rand(hkv, generator=torch.Generator().manual_seed(40 + seed)) * 2 - 6).float()
+    q_out = torch.full((B + 1, hq, 128), 7.0, dtype=torch.bfloat16, device=dev)   # one row of guard
+    lb.attn_store_kv(q.to(dev), k.to(dev), v.to(dev), pos, q_out[:B], kc, vc, bt,
+                     q_norm_w=qw.to(dev) if norm else None, k_norm_w=kw.to(dev) if norm else None, eps=eps,
+                     rope_theta=theta, hadamard=had, kv_scales=(ks.to(dev), vs.to(dev)) if fp8 else None)
+    torch.cuda.synchronize()
+    assert torch.all(q_out[B] == 7.0)
+    rq, rk, rv = SK.ref_store_kv(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                 np.array(lens, dtype=np.float64), qw.double().numpy() if norm else None,
+                                 kw.double().numpy() if norm else None, eps, theta, had,
+                                 ks.double().numpy() if fp8 else None, vs.double().numpy() if fp8 else None)
+    dq = np.abs(q_out[:B].float().cpu().numpy().astype(np.float64) - rq)
+    assert np.all(dq <= _tol(rq)), f"q: {int((dq > _tol(rq)).sum())} beyond tolerance"
+    table = e4m3_table()
+    for b, L in enumerate(lens):
+        kb, vb = unpack_request(kc, vc, bt, b, L + 1)
+        for got, ref in ((kb[L].cpu(), rk[b]), (vb[L].cpu(), rv[b])):
+            if fp8:
+                gc = got.numpy()
+                dv = np.abs(table[gc] - table[ref])
+                step = np.abs(table[np.minimum(ref.astype(np.int32) & 0x7F, 0x7D) + 1] - table[ref.astype(np.int32) & 0x7F])
+                assert np.all((gc == ref) | (dv <= step + 1e-12)), f"request {b}"
+            else:
+                assert np.all(np.abs(got.double().numpy() - ref) <= _tol(ref)), f"request {b}"
+    stored = sum(int(torch.count_nonzero(unpack_request(kc, vc, bt, b, L + 1)[0][L]).item()) for b, L in enumerate(lens))
+    written = sum(int(torch.count_nonzero(kc[p0:p0 + 256]).item()) for p0 in range(0, kc.shape[0], 256))
+    assert written == stored
