@@ -577,3 +577,122 @@ def pin_store_kv_scores_invariant(ref_store_kv):
     qo, ko, vo = ref_store_kv(q, k, k, pos, None, None, 1e-6, 10000.0, True)
     assert np.array_equal(qo, SK.round_bf16(SK.hadamard(a[0])))
     assert np.array_equal(ko, SK.round_bf16(SK.hadamard(a[1])))
+
+
+def _assert_bf16_nearest(got, exact, what):
+    """got holds bf16 values (torch's float32 -> bfloat16 round trip leaves them unchanged) within
+    half a bf16 step (8 significant bits) of the exact value: what round-to-nearest must give."""
+    got = np.asarray(got, dtype=np.float64)
+    exact = np.asarray(exact, dtype=np.float64)
+    rt = torch.from_numpy(got.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(rt, got), f"{what}: not bf16 values"
+    _, e = np.frexp(exact)
+    half_step = np.ldexp(1.0, e - 9)
+    bad = np.abs(got - exact) > half_step * (1 + 1e-9) + 1e-300
+    assert not bad.any(), f"{what}: {int(bad.sum())} values off by more than half a bf16 step"
+
+
+def _sylvester_sign(i, j):
+    """Entry (i, j) of the Sylvester-ordered Hadamard matrix: (-1)^popcount(i & j)."""
+    return -1.0 if bin(i & j).count("1") % 2 else 1.0
+
+
+def pin_store_kv_composition(ref_store_kv):
+    """Which vector takes which step, with which gain and scale, in which order — closed forms worked
+    out by hand and run through the whole producer step ([P3] §4.1: RoPE, RMSNorm, Hadamard,
+    quantisation and store fused; §8: q and k rotated before the 8-bit code).
+
+    (a) v is stored as given (rounded to bf16, or e4m3(v / v_scale[head])) whatever theta, gains
+        and Hadamard are: bf16 v comes back bit for bit; v = s 2^j v_scale[g] stores the code of
+        s 2^j (exponent field j + 7, mantissa 0, sign bit for s < 0).
+    (b) Gains reach their own kind only: x = c 1 with c = +-2^j and eps = 0 normalises to
+        sign(c) 1 exactly, so q comes out as sign(c) q_norm_w and k as sign(c) k_norm_w.
+    (c) eps sits under the root, added to the mean square: x = 1, eps = 3 gives w / 2.
+    (d) Position 0 is the identity of RoPE at any theta.
+    (e) A one-hot e_j through the Hadamard gives (-1)^popcount(i & j) / sqrt(128) at dim i.
+    (f) Order RMSNorm -> RoPE -> Hadamard: x = c 1 with gain e_0 normalises to sign(c) e_0; RoPE at
+        position p turns the pair (0, 64) at frequency 1, giving sign(c) (cos p e_0 + sin p e_64);
+        the Hadamard then gives sign(c) (cos p + sin p s_i) / sqrt(128), s_i = +1 below dim 64 and
+        -1 from it (column 64 of the Sylvester matrix).
+    (g) k takes k_scale: k = c 1 (c = +-2^j) with gain 2^-m 1, eps = 0, position 0 and the Hadamard
+        on becomes sign(c) 2^-m sqrt(128) e_0 (H 1 / sqrt(128) = sqrt(128) e_0); with k_scale[g] =
+        2^-m sqrt(128) / 2^(g+1) its code at dim 0 is that of sign(c) 2^(g+1), zero elsewhere."""
+    rng = np.random.default_rng(37)
+    D, N, Hq, Hkv = 128, 3, 16, 2
+    bf = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    pos_big = np.array([5.0, 4097.0, 123457.0])
+    zero_pos = np.zeros(N)
+    qw = bf(1 + 0.3 * rng.standard_normal(D))
+    kw = bf(-1 + 0.3 * rng.standard_normal(D))
+
+    def e4m3_pow2(s, j):
+        return np.where(s < 0, 0x80, 0x00) | ((j + 7) << 3)
+
+    # (a) v untouched by norm, RoPE and Hadamard; v_scale (not k_scale) sets its code
+    q = bf(rng.standard_normal((N, Hq, D)))
+    k = bf(rng.standard_normal((N, Hkv, D)))
+    v = bf(rng.standard_normal((N, Hkv, D)) * 3)
+    for theta, had in ((10000.0, True), (1e6, False), (0.0, True)):
+        _, _, vo = ref_store_kv(q, k, v, pos_big, qw, kw, 1e-6, theta, had)
+        assert np.array_equal(vo, v), "(a) v changed by the q/k steps"
+    k_scale = np.array([2.0 ** -3, 2.0 ** -1])
+    v_scale = np.array([2.0 ** -6, 2.0 ** 2])
+    jv = rng.integers(-3, 8, size=(N, Hkv, D))
+    sv = np.where(rng.random((N, Hkv, D)) < 0.5, -1.0, 1.0)
+    v8 = sv * np.ldexp(1.0, jv) * v_scale[None, :, None]
+    _, _, vc = ref_store_kv(q, k, v8, pos_big, qw, kw, 1e-6, 10000.0, True, k_scale, v_scale)
+    assert np.array_equal(vc.astype(np.int64), e4m3_pow2(sv, jv)), "(a) v code not e4m3(v / v_scale)"
+
+    # (b) gains reach their own kind only
+    cq = np.where(rng.random((N, Hq, 1)) < 0.5, -1.0, 1.0) * np.ldexp(1.0, rng.integers(-4, 5, (N, Hq, 1)))
+    ck = np.where(rng.random((N, Hkv, 1)) < 0.5, -1.0, 1.0) * np.ldexp(1.0, rng.integers(-4, 5, (N, Hkv, 1)))
+    qo, ko, _ = ref_store_kv(cq * np.ones(D), ck * np.ones(D), v, pos_big, qw, kw, 0.0, 0.0, False)
+    assert np.array_equal(qo, np.sign(cq) * qw), "(b) q does not carry sign(c) q_norm_w"
+    assert np.array_equal(ko, np.sign(ck) * kw), "(b) k does not carry sign(c) k_norm_w"
+    qo, ko, _ = ref_store_kv(cq * np.ones(D), ck * np.ones(D), v, pos_big, None, kw, 0.0, 0.0, False)
+    assert np.array_equal(qo, cq * np.ones(D)) and np.array_equal(ko, np.sign(ck) * kw), "(b) q normalised without a gain"
+
+    # (c) eps under the root
+    qo, ko, _ = ref_store_kv(np.ones((N, Hq, D)), np.ones((N, Hkv, D)), v, pos_big, qw, kw, 3.0, 0.0, False)
+    assert np.array_equal(qo, np.broadcast_to(qw / 2, qo.shape)) and np.array_equal(ko, np.broadcast_to(kw / 2, ko.shape)), "(c) eps"
+
+    # (d) position 0: RoPE is the identity for q and k
+    qo, ko, vo = ref_store_kv(q, k, v, zero_pos, None, None, 1e-6, 10000.0, False)
+    assert np.array_equal(qo, q) and np.array_equal(ko, k) and np.array_equal(vo, v), "(d) position 0"
+
+    # (e) one-hot vectors through the Hadamard, q and k alike
+    js = [0, 1, 5, 64, 127, 85]
+    for j in js:
+        e = np.zeros(D)
+        e[j] = 1.0
+        col = np.array([_sylvester_sign(i, j) for i in range(D)]) / math.sqrt(D)
+        qo, ko, _ = ref_store_kv(np.broadcast_to(e, (N, Hq, D)), np.broadcast_to(-e, (N, Hkv, D)), v, zero_pos,
+                                 None, None, 1e-6, 0.0, True)
+        _assert_bf16_nearest(qo, np.broadcast_to(col, qo.shape), f"(e) q one-hot {j}")
+        _assert_bf16_nearest(ko, np.broadcast_to(-col, ko.shape), f"(e) k one-hot {j}")
+
+    # (f) order: RMSNorm, then RoPE, then Hadamard
+    e0 = np.zeros(D)
+    e0[0] = 1.0
+    s = np.where(np.arange(D) < 64, 1.0, -1.0)
+    p = np.array([3.0, 1.0, 2.0])
+    for had in (False, True):
+        qo, ko, _ = ref_store_kv(cq * np.ones(D), ck * np.ones(D), v, p, e0, e0, 0.0, 10000.0, had)
+        for got, c, what in ((qo, cq, "q"), (ko, ck, "k")):
+            cos, sin = np.cos(p)[:, None, None], np.sin(p)[:, None, None]
+            if had:
+                exact = np.sign(c) * (cos + sin * s) / math.sqrt(D)
+            else:
+                exact = np.zeros(got.shape)
+                exact[..., 0:1] = np.sign(c) * cos
+                exact[..., 64:65] = np.sign(c) * sin
+            _assert_bf16_nearest(got, np.broadcast_to(exact, got.shape), f"(f) {what} order, hadamard={had}")
+
+    # (g) k takes k_scale (per head) after its own steps
+    m = 3
+    kg = np.full(D, 2.0 ** -m)
+    k_scale_g = np.array([2.0 ** -m * math.sqrt(D) / 2.0 ** (g + 1) for g in range(Hkv)])
+    _, kc, _ = ref_store_kv(q, ck * np.ones(D), v8, zero_pos, None, kg, 0.0, 10000.0, True, k_scale_g, v_scale)
+    want = np.zeros((N, Hkv, D), dtype=np.int64)
+    want[..., 0] = e4m3_pow2(np.sign(ck[..., 0]), np.arange(Hkv)[None, :] + 1)
+    assert np.array_equal(kc.astype(np.int64), want), "(g) k code not e4m3(k / k_scale) of the processed k"

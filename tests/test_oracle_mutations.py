@@ -72,6 +72,7 @@ def _store_pins(m):
         lambda: P.pin_hadamard(m.hadamard),
         lambda: P.pin_rope(m.rope),
         lambda: P.pin_rms_norm_library(m.rms_norm),
+        lambda: P.pin_store_kv_composition(m.ref_store_kv),
     ]
 
 
@@ -147,6 +148,46 @@ STORE_MUTANTS = {
     "bf16 truncates": ("return np.round(np.ldexp(x, -step_exp))", "return np.trunc(np.ldexp(x, -step_exp))"),
     "e4m3 ties away": ("((hi - a == a - lo) & ((pos_codes[j] & 1) == 0))", "(hi - a == a - lo)"),
     "e4m3 drops the sign": ("return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)", "return code.astype(np.uint8)"),
+    # the composition: which vector takes which step, gain and scale, in which order
+    "rope applied to v": ("        k = rope(k, positions, theta)\n", "        k = rope(k, positions, theta)\n        v = rope(v, positions, theta)\n"),
+    "hadamard applied to v": ("        k = hadamard(k)\n", "        k = hadamard(k)\n        v = hadamard(v)\n"),
+    "v normalised with the key gain": ("return q_out, round_bf16(k), round_bf16(v)",
+                                       "return q_out, round_bf16(k), round_bf16(v if k_norm_w is None else rms_norm(v, k_norm_w, eps))"),
+    "hadamard skipped on q": ("        q = hadamard(q)\n", "        q = q\n"),
+    "hadamard skipped on k": ("        k = hadamard(k)\n", "        k = k\n"),
+    "rope skipped on k": ("        k = rope(k, positions, theta)\n", "        k = k\n"),
+    "scales swapped": ("e4m3_round(k / ks), e4m3_round(v / vs)", "e4m3_round(k / vs), e4m3_round(v / ks)"),
+    "v quantised with the key scale": ("e4m3_round(v / vs)", "e4m3_round(v / ks)"),
+    "q takes the key gain": ("q = rms_norm(q, q_norm_w, eps)", "q = rms_norm(q, k_norm_w if k_norm_w is not None else q_norm_w, eps)"),
+    "k takes the query gain": ("k = rms_norm(k, k_norm_w, eps)", "k = rms_norm(k, q_norm_w if q_norm_w is not None else k_norm_w, eps)"),
+    "norm after rope": ("""    if q_norm_w is not None:
+        q = rms_norm(q, q_norm_w, eps)
+    if k_norm_w is not None:
+        k = rms_norm(k, k_norm_w, eps)
+    if theta > 0:
+        q = rope(q, positions, theta)
+        k = rope(k, positions, theta)
+""", """    if theta > 0:
+        q = rope(q, positions, theta)
+        k = rope(k, positions, theta)
+    if q_norm_w is not None:
+        q = rms_norm(q, q_norm_w, eps)
+    if k_norm_w is not None:
+        k = rms_norm(k, k_norm_w, eps)
+"""),
+    "hadamard before rope": ("""    if theta > 0:
+        q = rope(q, positions, theta)
+        k = rope(k, positions, theta)
+    if use_hadamard:
+        q = hadamard(q)
+        k = hadamard(k)
+""", """    if use_hadamard:
+        q = hadamard(q)
+        k = hadamard(k)
+    if theta > 0:
+        q = rope(q, positions, theta)
+        k = rope(k, positions, theta)
+"""),
 }
 
 PLAN_MUTANTS = {

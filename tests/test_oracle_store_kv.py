@@ -27,3 +27,7 @@ def test_rms_norm_library():
 
 def test_scores_invariant_under_hadamard():
     P.pin_store_kv_scores_invariant(SK.ref_store_kv)
+
+
+def test_composition_closed_forms():
+    P.pin_store_kv_composition(SK.ref_store_kv)
