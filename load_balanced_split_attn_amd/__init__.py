@@ -225,8 +225,21 @@ def _cache_geometry(k_cache: torch.Tensor, v_cache: torch.Tensor, head_dim: int)
     return P, Hkv, page
 
 
+def _check_partial_sizes(q, part_m, part_l, part_o, slots: int, rows_per_slot: int, what: str) -> None:
+    """Every partial buffer holds slots x rows_per_slot rows of Hq heads (o: x D).  Checked before any
+    device check, so an undersized buffer is refused whatever device it is on."""
+    if q.dim() != 3:
+        raise ValueError("q: need [rows, Hq, D]")
+    Hq, D = q.shape[1], q.shape[2]
+    n = slots * rows_per_slot * Hq
+    for name, t, need in (("part_m", part_m, n), ("part_l", part_l, n), ("part_o", part_o, n * D)):
+        if t.numel() < need:
+            raise ValueError(f"{name}: {t.numel()} elements, smaller than {what} ({need})")
+
+
 def _check_decode_args(q, k_cache, v_cache, block_table, seq_lens, map_dev, num_workers, num_segments, head_groups,
                        part_m, part_l, part_o, timing, cache_dtype):
+    _check_partial_sizes(q, part_m, part_l, part_o, num_segments, 1, "num_segments")
     dev = q.device
     _need(q, torch.bfloat16, "q", dev)
     _need(k_cache, cache_dtype, "k_cache", dev)
@@ -240,9 +253,6 @@ def _check_decode_args(q, k_cache, v_cache, block_table, seq_lens, map_dev, num_
     P, Hkv, page = _cache_geometry(k_cache, v_cache, D)
     if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.numel() != B:
         raise ValueError("block_table/seq_lens do not match the batch")
-    if part_m.numel() < num_segments * Hq or part_l.numel() < num_segments * Hq or \
-            part_o.numel() < num_segments * Hq * D:
-        raise ValueError("partial buffers smaller than num_segments")
     if timing is not None:
         _need(timing, torch.int64, "timing", dev)
         if timing.numel() < num_workers * head_groups * 4:
@@ -297,6 +307,7 @@ def attn_splitkv_mtp(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     """Multi-token decode: q [rows, Hq, D] with request b's q_lens[b] <= rows_per_unit rows from row
     q_start[b]; caches bf16, or uint8 E4M3 codes with kv_scales = (k_scale, v_scale); map from
     attn_plan_prefill(q_lens, kv_lens, W, q_tile=rows_per_unit); part_m/l [S, R, Hq], part_o [S, R, Hq, D]."""
+    _check_partial_sizes(q, part_m, part_l, part_o, num_segments, int(rows_per_unit), "num_segments x rows_per_unit")
     fp8 = k_cache.dtype == torch.uint8
     dev = q.device
     _need(q, torch.bfloat16, "q", dev)
@@ -313,9 +324,6 @@ def attn_splitkv_mtp(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
     if block_table.dim() != 2 or block_table.shape[0] != B or q_start.numel() != B or kv_lens.numel() != B:
         raise ValueError("block_table/q_start/kv_lens do not match the batch")
     R = int(rows_per_unit)
-    if part_m.numel() < num_segments * R * Hq or part_l.numel() < num_segments * R * Hq or \
-            part_o.numel() < num_segments * R * Hq * D:
-        raise ValueError("partial buffers smaller than num_segments x rows_per_unit")
     ks = vs = None
     if fp8:
         if kv_scales is None:
@@ -341,6 +349,7 @@ def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     """Launch the chunked-prefill split-KV kernel.  q [rows, Hq, D]; caches as in attn_splitkv;
     q_lens/q_start/kv_lens [B]; part_m/l [S, q_tile, Hq]; part_o [S, q_tile, Hq, D].
     exact_pv: bf16 P.V with hi/lo P (no fp16 range limit on V) instead of the fp16 P.V path."""
+    _check_partial_sizes(q, part_m, part_l, part_o, num_segments, int(q_tile), "num_segments x q_tile")
     dev = q.device
     _need(q, torch.bfloat16, "q", dev)
     _need(k_cache, torch.bfloat16, "k_cache", dev)
@@ -355,8 +364,6 @@ def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     B = q_lens.numel()
     if block_table.dim() != 2 or block_table.shape[0] != B or q_start.numel() != B or kv_lens.numel() != B:
         raise ValueError("block_table/q_start/kv_lens do not match the batch")
-    if part_m.numel() < num_segments * q_tile * Hq or part_o.numel() < num_segments * q_tile * Hq * D:
-        raise ValueError("partial buffers smaller than num_segments")
     st = lib().attn_splitkv_prefill(_dptr(q), _dptr(k_cache), _dptr(v_cache), _dptr(block_table),
                                     block_table.shape[1], P, _dptr(q_lens), _dptr(q_start), _dptr(kv_lens),
                                     _dptr(map_dev), num_workers, num_segments, B, Hq, Hkv, D, page, q_tile,

@@ -230,3 +230,27 @@ def test_lpt_plan_bit_exact():
         wl = WL.BY_NAME[name]()
         W = wl.workers or 128
         assert np.array_equal(lb.attn_plan_lpt(wl.kv_lens, W, 512), ref_plan_lpt(wl.kv_lens, W, 512)), name
+
+
+def test_binding_refuses_undersized_partials(L):
+    """The binding checks every partial buffer's size (part_l included) before anything reaches the
+    library: an undersized one is a ValueError, never a launch writing past its end.  CPU tensors
+    suffice, since the sizes are checked before the device."""
+    import torch
+    S, Hq, D = 3, 64, 128
+    q = torch.zeros((2, Hq, D), dtype=torch.bfloat16)
+    other = torch.zeros(1, dtype=torch.int32)
+    for rows, call in ((1, lambda m, l, o: L.attn_splitkv(q, q, q, other, other, other, 4, S, 8, 0.1, m, l, o)),
+                       (1, lambda m, l, o: L.attn_splitkv_fp8(q, q, q, other, other, other, other, other, 4, S, 8,
+                                                              0.1, m, l, o)),
+                       (4, lambda m, l, o: L.attn_splitkv_mtp(q, q, q, other, other, other, other, other, 4, S, 8,
+                                                              4, 0.1, m, l, o)),
+                       (128, lambda m, l, o: L.attn_splitkv_prefill(q, q, q, other, other, other, other, other, 4,
+                                                                    S, 0.1, m, l, o, q_tile=128))):
+        n = S * rows * Hq
+        full = (torch.zeros(n), torch.zeros(n), torch.zeros(n * D))
+        for i, name in enumerate(("part_m", "part_l", "part_o")):
+            bufs = list(full)
+            bufs[i] = torch.zeros(bufs[i].numel() - 1)
+            with pytest.raises(ValueError, match=name):
+                call(*bufs)

@@ -152,9 +152,11 @@ def test_store_head_counts(lb, fp8, hq, hkv):
                 assert np.all((g == ref) | (dv <= step + 1e-12)), f"request {b}"
             else:
                 assert np.all(np.abs(got.double().numpy() - ref) <= _tol(ref)), f"request {b}"
-    # exactly the B new tokens were written: nonzero elements only at the stored positions
-    stored = sum(int(torch.count_nonzero(unpack_request(kc, vc, bt, b, L + 1)[0][L]).item()) for b, L in enumerate(lens))
-    assert int(torch.count_nonzero(kc).item()) == stored
+    # exactly the B new tokens were written: nonzero elements only at the stored positions, K and V
+    for which, cache in ((0, kc), (1, vc)):
+        stored = sum(int(torch.count_nonzero(unpack_request(kc, vc, bt, b, L + 1)[which][L]).item())
+                     for b, L in enumerate(lens))
+        assert int(torch.count_nonzero(cache).item()) == stored, "KV"[which] + " cache: stray writes"
 
 
 def test_hardware_rounding_exact(lb):
@@ -201,10 +203,12 @@ def test_out_of_table_positions_not_stored(lb):
     lb.attn_store_kv(q.to(dev), k.to(dev), v.to(dev), pos, q_out, kc, vc, bt)
     torch.cuda.synchronize()
     from load_balanced_split_attn_amd.paged import unpack_request
-    kb, _ = unpack_request(kc, vc, bt, 0, 11)
+    kb, vb = unpack_request(kc, vc, bt, 0, 11)
     assert torch.equal(kb[10].cpu(), k[0])
-    nz = int(torch.count_nonzero(kc).item())
-    assert nz == int(torch.count_nonzero(k[0]).item())    # nothing else was written
+    assert torch.equal(vb[10].cpu(), v[0])
+    # nothing else was written, in either cache
+    assert int(torch.count_nonzero(kc).item()) == int(torch.count_nonzero(k[0]).item())
+    assert int(torch.count_nonzero(vc).item()) == int(torch.count_nonzero(v[0]).item())
 
 
 @pytest.mark.parametrize("fp8", [False, True])
@@ -308,6 +312,8 @@ def test_store_random_sweep(lb, seed):
                 assert np.all((gc == ref) | (dv <= step + 1e-12)), f"request {b}"
             else:
                 assert np.all(np.abs(got.double().numpy() - ref) <= _tol(ref)), f"request {b}"
-    stored = sum(int(torch.count_nonzero(unpack_request(kc, vc, bt, b, L + 1)[0][L]).item()) for b, L in enumerate(lens))
-    written = sum(int(torch.count_nonzero(kc[p0:p0 + 256]).item()) for p0 in range(0, kc.shape[0], 256))
-    assert written == stored
+    for which, cache in ((0, kc), (1, vc)):
+        stored = sum(int(torch.count_nonzero(unpack_request(kc, vc, bt, b, L + 1)[which][L]).item())
+                     for b, L in enumerate(lens))
+        written = sum(int(torch.count_nonzero(cache[p0:p0 + 256]).item()) for p0 in range(0, cache.shape[0], 256))
+        assert written == stored, "KV"[which] + " cache: stray writes"
