@@ -321,16 +321,23 @@ int attn_store_kv(const void* q_in, const void* k_in, const void* v_in,
  * written).  With causal != 0 row j sees keys [0, kv_lens[b] - q_lens[b] + j]; otherwise all keys.
  *   q_lens, q_start, kv_lens  device int32[B]
  *   map           device copy of the attn_plan_prefill map (same q_tile, kv_tile % 64 == 0)
- *   flags         0: P.V in fp16 (V converted exactly from bf16 while staged, P rounded to 11
- *                 significant bits; |v| above 65504 saturates); LBSA_PREFILL_EXACT_PV: bf16 V with
- *                 P as bf16 hi + lo parts (~16 bits, no range limit, ~15% slower)
+ *   flags         P.V precision.  0 or LBSA_PREFILL_EXACT_PV (the default): V stays bf16 and P
+ *                 enters as bf16 hi + lo parts (~16 significant bits), exact for every bf16 V.
+ *                 LBSA_PREFILL_F16_PV (faster, ~15% on the chunked-prefill batch): V converted to
+ *                 fp16 while staged and P rounded to fp16 (11 significant bits).  The conversion
+ *                 rounds toward zero, so V is carried exactly only where fp16 holds every bf16
+ *                 value: v = 0 and 2^-17 <= |v| <= 65504.  Below 2^-17 low bits are dropped (fp16
+ *                 subnormals, spacing 2^-24), below 2^-24 V becomes 0, above 65504 it saturates to
+ *                 +-65504.  For V known to lie in that range only.
  * Supported: head_dim 128, Hq/Hkv = 8, bf16, q_tile 128 (four waves of 32 rows per workgroup,
  * 256 threads) or 256 (eight waves, 512 threads), page_size a multiple of 64.  The map must come
  * from attn_plan_prefill with the same q_tile and num_workers (a map of another unit height or
  * worker count is skipped: nothing is written).
- * Errors: LBSA_ERR_INVALID (also unknown flag bits), LBSA_ERR_UNSUPPORTED, LBSA_ERR_HIP.
+ * Errors: LBSA_ERR_INVALID (also unknown flag bits, or both precision flags), LBSA_ERR_UNSUPPORTED,
+ * LBSA_ERR_HIP.
  */
 #define LBSA_PREFILL_EXACT_PV 1
+#define LBSA_PREFILL_F16_PV 2
 int attn_splitkv_prefill(const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
                          const int32_t* q_lens, const int32_t* q_start, const int32_t* kv_lens,

@@ -60,12 +60,14 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 // Tuning knobs (compile-time):
 //
 // P.V precision (runtime, template parameter PV):
-//   kPvF16   (default) each chunk's V^T is converted to fp16 once, in LDS, by the workgroup (each
-//            thread its own copied granules, before the chunk's barrier) and P is rounded to fp16
-//            (11 significant bits); the products run on v_mfma_f32_16x16x32_f16.  The bf16 -> fp16 conversion is exact for |v| in the
-//            fp16 normal range; larger magnitudes saturate at 65504.
-//   kPvExact bf16 V with P split into bf16 hi + lo parts (two MFMAs, ~16 significant bits), no
-//            range limit.
+//   kPvExact (default) bf16 V with P split into bf16 hi + lo parts (two MFMAs, ~16 significant
+//            bits): exact for every bf16 V.
+//   kPvF16   (opt-in, faster) each chunk's V^T is converted to fp16 once, in LDS, by the workgroup
+//            (each thread its own copied granules, before the chunk's barrier) and P is rounded to
+//            fp16 (11 significant bits); the products run on v_mfma_f32_16x16x32_f16.  The
+//            conversion rounds toward zero: exact for v = 0 and 2^-17 <= |v| <= 65504 (every bf16
+//            value there has at most fp16's bits); smaller magnitudes lose low bits in fp16's
+//            subnormals and vanish below 2^-24, larger ones saturate at 65504.
 //   LBSA_PREFILL_WPE     waves per SIMD the register budget is fitted to (1 or 2)
 
 #ifndef LBSA_PREFILL_WPE
@@ -83,8 +85,9 @@ __device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
                                                 0, 0);
 }
 
-// two bf16 values (one dword) -> two fp16 values, round toward zero (exact for the values bf16 and
-// fp16 share; saturates instead of overflowing)
+// two bf16 values (one dword) -> two fp16 values, round toward zero: exact for 0 and
+// 2^-17 <= |v| <= 65504; below that the fp16 subnormal spacing (2^-24) truncates, above it the value
+// saturates at +-65504 instead of overflowing
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(x), bf16_hi(x)));
 }
@@ -563,7 +566,8 @@ extern "C" int attn_splitkv_prefill(const void* q, const void* k_cache, const vo
   if (head_dim != kPD || num_q_heads != 8 * num_kv_heads || page_size % kPChunk != 0 ||
       (q_tile != 128 && q_tile != kMaxQTile))
     return LBSA_ERR_UNSUPPORTED;
-  if (flags & ~LBSA_PREFILL_EXACT_PV) return LBSA_ERR_INVALID;
+  if (flags & ~(LBSA_PREFILL_EXACT_PV | LBSA_PREFILL_F16_PV)) return LBSA_ERR_INVALID;
+  if ((flags & LBSA_PREFILL_EXACT_PV) && (flags & LBSA_PREFILL_F16_PV)) return LBSA_ERR_INVALID;
   PrefillParams p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k_cache);
@@ -590,7 +594,7 @@ extern "C" int attn_splitkv_prefill(const void* q, const void* k_cache, const vo
   const int64_t pairs = (int64_t)num_workers * num_kv_heads;
   const int64_t grid = ((pairs + 7) / 8) * 8 * 8;
   if (grid > INT32_MAX) return LBSA_ERR_INVALID;
-  const bool exact = flags & LBSA_PREFILL_EXACT_PV;
+  const bool exact = !(flags & LBSA_PREFILL_F16_PV);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const unsigned g = (unsigned)grid;
   if (q_tile == 128) {

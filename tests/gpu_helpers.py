@@ -136,3 +136,58 @@ def oracle_mtp(wl: WL.Workload, requests=None, fp8=False, scale=SCALE):
             k, v = kt.to(torch.float64).numpy(), vt.to(torch.float64).numpy()
         out[b] = ref_attention(q, k, v, scale, causal=True)
     return out
+
+
+LOG2E = 1.4426950408889634
+KERNEL_CHUNK = 64          # keys per online-softmax step of the split-KV kernels
+KERNEL_SLACK_LOG2 = 8.0    # the kernels move their reference maximum only past this margin
+
+
+def rescale_replay(q_rows, k, kv_begin, kv_end, vis_end, scale, chunk=KERNEL_CHUNK, slack=KERNEL_SLACK_LOG2):
+    """Replay, on the host, the split-KV kernels' lazy online-softmax rule for one segment, to show
+    that a test input drives the branch that rescales the accumulators from a finite reference.
+
+    The kernels walk the keys [kv_begin, kv_end) in chunks aligned to multiples of `chunk` and keep,
+    per (query row, query head) column, a reference maximum m_ref (log2 units, -inf at first): a
+    chunk whose largest visible score exceeds m_ref + slack moves m_ref to it and rescales o and l
+    by 2^(old - new).  q_rows [R, Hq, D] and k [L, Hkv, D] are float64 (k dequantised for an 8-bit
+    cache), vis_end [R] the exclusive causal key end of each row.
+
+    Returns (finite, first, frac): finite [R, Hq] counts of rescales from a finite m_ref, first
+    [R, Hq] counts of moves from -inf, and frac, the largest share of a column's final sum that
+    came before one of its finite rescales (how much a wrong rescale factor would move the result)."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    R, Hq, D = q_rows.shape
+    Hkv = k.shape[1]
+    group = Hq // Hkv
+    c0 = (kv_begin // chunk) * chunk
+    n = max(0, kv_end - c0)
+    nch = -(-n // chunk)
+    finite = np.zeros((R, Hq), dtype=np.int64)
+    first = np.zeros((R, Hq), dtype=np.int64)
+    frac = 0.0
+    if nch == 0:
+        return finite, first, frac
+    pos = c0 + np.arange(nch * chunk)
+    for g in range(Hkv):
+        kg = np.zeros((nch * chunk, D))
+        kg[:n] = k[c0:kv_end, g]
+        s = scale * LOG2E * np.einsum("rhd,td->rht", q_rows[:, g * group:(g + 1) * group], kg)
+        visible = (pos[None, :] >= kv_begin) & (pos[None, :] < np.minimum(kv_end, np.asarray(vis_end))[:, None])
+        s = np.where(visible[:, None, :], s, -np.inf).reshape(R, group, nch, chunk)
+        cmax = s.max(axis=3)                                          # [R, group, nch]
+        top = cmax.max(axis=2, keepdims=True)
+        safe = np.where(np.isfinite(top), top, 0.0)
+        mass = np.where(np.isfinite(s), np.exp2(s - safe[..., None]), 0.0).sum(axis=3)   # [R, group, nch]
+        total = mass.sum(axis=2)
+        before = np.cumsum(mass, axis=2) - mass
+        m_ref = np.full((R, group), -np.inf)
+        for i in range(nch):
+            need = cmax[:, :, i] > m_ref + slack
+            fin = need & np.isfinite(m_ref)
+            finite[:, g * group:(g + 1) * group] += fin
+            first[:, g * group:(g + 1) * group] += need & ~np.isfinite(m_ref)
+            if fin.any():
+                frac = max(frac, float(np.max(np.where(fin & (total > 0), before[:, :, i] / np.where(total > 0, total, 1), 0))))
+            m_ref = np.where(need, cmax[:, :, i], m_ref)
+    return finite, first, frac

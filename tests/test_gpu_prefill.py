@@ -13,7 +13,7 @@ from oracle.plan import ref_plan_prefill
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, W, causal=True, inputs=None, poison=False, kv_tile=512, exact_pv=False, q_tile=256):
+def _run(wl, W, causal=True, inputs=None, poison=False, kv_tile=512, exact_pv=True, q_tile=256):
     from load_balanced_split_attn_amd.prefill import PrefillStep
     q, kc, vc, bt = inputs if inputs is not None else prefill_inputs(wl, pad_value=float("nan"))
     step = PrefillStep(wl.q_lens, wl.kv_lens, q.device, num_workers=W, causal=causal, kv_tile=kv_tile,
@@ -52,7 +52,7 @@ def test_random_prefill(seed, batch, max_prefix, max_chunk, W, exact_pv, q_tile)
 def test_non_causal_and_small_tiles():
     wl = WL.random_prefill(7, 3, 900, 200)
     note(f"non-causal q_lens={wl.q_lens} kv_lens={wl.kv_lens}")
-    got, _ = _run(wl, 5, causal=False)
+    got, _ = _run(wl, 5, causal=False, exact_pv=False)
     _check_all(wl, got, causal=False)
     got, _ = _run(wl, 5, causal=False, exact_pv=True)
     _check_all(wl, got, causal=False)
@@ -86,7 +86,7 @@ def test_exact_pv_agrees_with_fp16_pv():
     """Both P.V precisions give the same attention to well inside the tolerance."""
     wl = WL.random_prefill(10, 3, 2500, 300)
     inputs = prefill_inputs(wl)
-    a, _ = _run(wl, 6, inputs=inputs)
+    a, _ = _run(wl, 6, inputs=inputs, exact_pv=False)
     b, _ = _run(wl, 6, inputs=inputs, exact_pv=True)
     assert errors(a.astype(np.float64), b.astype(np.float64))[1] <= 1e-3
 
@@ -103,6 +103,11 @@ def test_flags_rejected():
                                   st.W, st.S, 1, 64, 8, 128, 64, 128, 1, SCALE, lb._dptr(st.part_m),
                                   lb._dptr(st.part_l), lb._dptr(st.part_o), 4, None)
     assert rc == -1
+    rc = lib.attn_splitkv_prefill(lb._dptr(q), lb._dptr(kc), lb._dptr(vc), lb._dptr(bt), bt.shape[1], kc.shape[0],
+                                  lb._dptr(st.q_lens), lb._dptr(st.q_start), lb._dptr(st.kv_lens), lb._dptr(st.map),
+                                  st.W, st.S, 1, 64, 8, 128, 64, 128, 1, SCALE, lb._dptr(st.part_m),
+                                  lb._dptr(st.part_l), lb._dptr(st.part_o), 3, None)
+    assert rc == -1     # both precision flags at once
 
 
 def test_single_row_matches_decode():
@@ -119,7 +124,7 @@ def test_single_row_matches_decode():
     dec = dec.cpu().numpy().astype(np.float64)
     exact, _ = _run(wl, 3, inputs=(q, kc, vc, bt), exact_pv=True)
     assert errors(exact.astype(np.float64), dec)[1] <= 1e-5          # same arithmetic up to fp32 order
-    fast, _ = _run(wl, 3, inputs=(q, kc, vc, bt))
+    fast, _ = _run(wl, 3, inputs=(q, kc, vc, bt), exact_pv=False)
     assert errors(fast.astype(np.float64), dec)[1] <= 1e-3           # P rounded to fp16
 
 

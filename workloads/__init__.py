@@ -20,6 +20,21 @@ same bf16 values.  Seeds: ``seed_for(workload_id, stream, index)`` with streams
 scales of an 8-bit cache; K and V are drawn per request so a long batch can be
 generated and checked one request at a time.  An 8-bit (E4M3) cache holds the
 same K and V draws, quantised per KV head (``Workload.kv_fp8``).
+
+Score profiles (``Workload.profile``) reshape the same draws into inputs whose softmax is peaked or
+moves, so that the kernels' online softmax must move its running maximum part-way through a split
+(the exact merge of split partials, [P3] §3.1 方案 step 5 and §14 "Split-KV"):
+
+* ``q8`` / ``q16``: q multiplied by 8 or 16 (exact in bf16): scores with a spread of 8 or 16;
+* ``ramp``: q's dim 0 set to 64 and K's dim 0 to 0.02 t at token t: scores climb by about 7.2
+  per 64 tokens along every request;
+* ``spike``: q's dim 0 set to 8 and, at tokens t = 650 (mod 700), K's dim 0 set to 15 + 8.5 j
+  (the j-th such token): late dominant keys, each about 6 above the previous one;
+* ``vsmall`` / ``vlarge``: V multiplied by 1e-6 or 1e5 before its bf16 rounding (value range);
+  ``vlow`` / ``vhigh``: V times 2^-10 or 2^13 (small and large magnitudes that fp16 still holds).
+
+An 8-bit cache of a profile with larger K or V takes its per-head scales times a power of two (or
+the V factor) that keeps the values inside the E4M3 range.
 """
 
 from __future__ import annotations
@@ -42,7 +57,7 @@ E4M3_MAX = 448.0
 
 
 def seed_for(workload_id: int, stream: int, index: int = 0) -> int:
-    return workload_id * 1_000_000 + stream * 10_000 + index
+    return int(workload_id * 1_000_000 + stream * 10_000 + index)
 
 
 def randn_f32(shape, seed: int) -> torch.Tensor:
@@ -63,6 +78,12 @@ def to_e4m3_codes(x: torch.Tensor, scale: torch.Tensor) -> torch.Tensor:
     return y.to(torch.float8_e4m3fn).view(torch.uint8)
 
 
+PROFILES = ("normal", "q8", "q16", "ramp", "spike", "vsmall", "vlarge", "vlow", "vhigh")
+RAMP_Q, RAMP_SLOPE = 64.0, 0.02
+SPIKE_Q, SPIKE_PERIOD, SPIKE_AT, SPIKE_K0, SPIKE_STEP = 8.0, 700, 650, 15.0, 8.5
+V_FACTOR = {"vsmall": 1e-6, "vlarge": 1e5, "vlow": 2.0 ** -10, "vhigh": 2.0 ** 13}
+
+
 @dataclass
 class Workload:
     """One synthetic batch: KV lengths (and, for prefill, query-chunk lengths)."""
@@ -77,6 +98,7 @@ class Workload:
     hkv: int = HKV
     head_dim: int = HEAD_DIM
     meta: dict = field(default_factory=dict)
+    profile: str = "normal"           # score profile (module docstring)
 
     @property
     def batch(self) -> int:
@@ -86,32 +108,69 @@ class Workload:
         """Decode: all queries [B, Hq, D].  Prefill and multi-token decode: request b's rows
         [q_len_b, Hq, D]."""
         if self.kind == "decode":
-            return randn_bf16((self.batch, self.hq, self.head_dim), seed_for(self.workload_id, STREAM_Q))
-        return randn_bf16((self.q_lens[b], self.hq, self.head_dim), seed_for(self.workload_id, STREAM_Q, b))
+            x = randn_f32((self.batch, self.hq, self.head_dim), seed_for(self.workload_id, STREAM_Q))
+        else:
+            x = randn_f32((self.q_lens[b], self.hq, self.head_dim), seed_for(self.workload_id, STREAM_Q, b))
+        return self._shape_q(x).to(torch.bfloat16)
+
+    def _shape_q(self, x: torch.Tensor) -> torch.Tensor:
+        if self.profile == "q8":
+            return x * 8
+        if self.profile == "q16":
+            return x * 16
+        if self.profile in ("ramp", "spike"):
+            x[..., 0] = RAMP_Q if self.profile == "ramp" else SPIKE_Q
+        return x
+
+    def _kv_f32(self, b: int) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Request b's keys and values [L_b, Hkv, D] in float32, shaped by the profile."""
+        L = self.kv_lens[b]
+        k = randn_f32((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_K, b))
+        v = randn_f32((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_V, b))
+        if self.profile == "ramp":
+            k[:, :, 0] = RAMP_SLOPE * torch.arange(L, dtype=torch.float32)[:, None]
+        elif self.profile == "spike":
+            at = torch.arange(SPIKE_AT, L, SPIKE_PERIOD)
+            k[at, :, 0] = (SPIKE_K0 + SPIKE_STEP * torch.arange(len(at), dtype=torch.float32))[:, None]
+        elif self.profile in V_FACTOR:
+            v = v * V_FACTOR[self.profile]
+        return k, v
 
     def kv(self, b: int) -> Tuple[torch.Tensor, torch.Tensor]:
         """Request b's keys and values, each [L_b, Hkv, D] bf16, token-major."""
-        L = self.kv_lens[b]
-        k = randn_bf16((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_K, b))
-        v = randn_bf16((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_V, b))
-        return k, v
+        k, v = self._kv_f32(b)
+        return k.to(torch.bfloat16), v.to(torch.bfloat16)
+
+    def _k_range(self) -> float:
+        """Largest |K| the profile produces (over the batch), for the 8-bit cache's scales."""
+        L = max(self.kv_lens) if self.kv_lens else 0
+        if self.profile == "ramp":
+            return RAMP_SLOPE * L
+        if self.profile == "spike":
+            return SPIKE_K0 + SPIKE_STEP * max(0, (L - SPIKE_AT + SPIKE_PERIOD - 1) // SPIKE_PERIOD)
+        return 0.0
 
     def kv_scales(self) -> Tuple[torch.Tensor, torch.Tensor]:
         """Per-KV-head float32 scales of the 8-bit cache, K and V: 2^u with u ~ U[-6.5, -5.5], about
-        what an amax / 448 calibration gives for N(0, 1) values, and different for every head."""
+        what an amax / 448 calibration gives for N(0, 1) values, and different for every head; a
+        profile with larger K takes them times the power of two that covers its largest K, one with
+        scaled V times its V factor."""
         g = torch.Generator(device="cpu")
         g.manual_seed(seed_for(self.workload_id, STREAM_SCALES))
         u = torch.rand(2, self.hkv, generator=g, dtype=torch.float32) - 6.5
         s = torch.exp2(u)
+        kr = self._k_range()
+        if kr > 5.0:
+            s[0] *= 2.0 ** math.ceil(math.log2(kr / 5.0))
+        if self.profile in V_FACTOR:
+            s[1] *= V_FACTOR[self.profile]
         return s[0].clone(), s[1].clone()
 
     def kv_fp8(self, b: int) -> Tuple[torch.Tensor, torch.Tensor]:
-        """Request b's keys and values as E4M3 codes [L_b, Hkv, D] uint8: the same N(0, 1) draws as
-        ``kv`` (before their bf16 rounding), quantised with ``kv_scales``."""
-        L = self.kv_lens[b]
+        """Request b's keys and values as E4M3 codes [L_b, Hkv, D] uint8: the same draws as ``kv``
+        (before their bf16 rounding), quantised with ``kv_scales``."""
         ks, vs = self.kv_scales()
-        k = randn_f32((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_K, b))
-        v = randn_f32((L, self.hkv, self.head_dim), seed_for(self.workload_id, STREAM_V, b))
+        k, v = self._kv_f32(b)
         return to_e4m3_codes(k, ks), to_e4m3_codes(v, vs)
 
     def page_permutation(self, num_pages: int) -> torch.Tensor:
