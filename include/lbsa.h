@@ -372,6 +372,36 @@ int attn_combine(const float* part_m, const float* part_l, const float* part_o,
                  int32_t num_q_heads, int32_t head_dim,
                  void* out, int32_t out_dtype, int32_t max_splits, void* stream);
 
+/*
+ * Allocation-free decode step, for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It is attn_splitkv (or, with
+ * kv_dtype LBSA_KV_FP8_E4M3 and k_scale / v_scale, attn_splitkv_fp8) followed by attn_combine
+ * (num_units = B, one row per unit) on `stream`, same arguments, layouts and kernels, except that
+ * the partials live in a fixed array of the library, LBSA_NOALLOC_SCRATCH_BYTES of device memory
+ * per GPU that the library holds from its first use on that GPU until the process ends.  The caller
+ * passes inputs and `out` (fp32 or bf16 [B, Hq, D] by out_dtype, as attn_combine) only.
+ *   The partials of a call need S * Hq * (D + 2) * 4 bytes (S = num_segments): up to 1,008
+ *   segments at 64 query heads.  A larger call returns LBSA_ERR_CAPACITY and launches nothing.
+ *   Nothing in the array has to start cleared: the split kernel writes every slot the combine
+ *   reads in the same call.  Every call on one GPU shares that GPU's array: calls that may overlap
+ *   on one GPU (on different streams, or from several host threads without ordering) race and must
+ *   not be issued.
+ * The call allocates nothing, host or device.  On the first call on a device it takes the array's
+ * device address (hipGetSymbolAddress, with that device current); the device is the stream's
+ * (hipStreamGetDevice), or the current one for a NULL stream.
+ * Errors: as attn_splitkv / attn_splitkv_fp8 and attn_combine, plus LBSA_ERR_CAPACITY (above) and
+ * LBSA_ERR_INVALID for an unknown kv_dtype or scales that do not match it.
+ */
+#define LBSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
+                        const int32_t* seq_lens, const int32_t* map,
+                        int32_t num_workers, int32_t num_segments, int32_t head_groups,
+                        int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t page_size, float softmax_scale, int32_t max_splits,
+                        void* out, int32_t out_dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

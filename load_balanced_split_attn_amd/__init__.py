@@ -19,13 +19,15 @@ __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill", "attn_plan_device",
     "attn_plan_lpt", "attn_plan_weighted",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
-    "attn_combine", "attn_store_kv",
+    "attn_combine", "attn_store_kv", "attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
 ]
 
 # cache element types (LBSA_KV_* in include/lbsa.h)
 KV_BF16 = 0
 KV_FP8_E4M3 = 1
+# partial bytes attn_decode_noalloc holds per GPU (LBSA_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 # prefill P.V precision flags (LBSA_PREFILL_* in include/lbsa.h)
 PREFILL_EXACT_PV = 1
 PREFILL_F16_PV = 2
@@ -62,6 +64,9 @@ _SIGNATURES = {
     "attn_combine": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                     _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, _c_vp]),
     "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
+    "attn_decode_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
+                                           _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           ctypes.c_float, _c_i32, _c_vp, _c_i32, _c_vp]),
     "attn_splitkv_prefill": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
                                             _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                             _c_i32, _c_i32, ctypes.c_float, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp]),
@@ -438,6 +443,45 @@ def attn_combine(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tenso
                             _dptr(q_lens), _dptr(q_start), Hq, D, _dptr(out),
                             1 if out.dtype == torch.bfloat16 else 0, int(max_splits), _stream(stream))
     _check(st, "attn_combine")
+
+
+def attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                        seq_lens: torch.Tensor, map_dev: torch.Tensor, num_workers: int, num_segments: int,
+                        head_groups: int, softmax_scale: float, out: torch.Tensor, max_splits: int = 0,
+                        kv_scales=None, stream=None) -> None:
+    """Split-KV decode plus combine with the partials in the library's own fixed device array (no
+    allocation anywhere, this binding included): for callers that cannot allocate.  Caches bf16, or
+    uint8 E4M3 codes with kv_scales = (k_scale, v_scale); out fp32 or bf16 [B, Hq, D].  Calls that
+    may overlap on one GPU race (they share its array)."""
+    fp8 = k_cache.dtype == torch.uint8
+    dev = q.device
+    _need(q, torch.bfloat16, "q", dev)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, torch.uint8 if fp8 else torch.bfloat16, name, dev)
+    _need(block_table, torch.int32, "block_table", dev)
+    _need(seq_lens, torch.int32, "seq_lens", dev)
+    _need(map_dev, torch.int32, "map", dev)
+    if out.dtype not in (torch.float32, torch.bfloat16) or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out: need a contiguous fp32 or bf16 tensor on q's device")
+    B, Hq, D = q.shape
+    P, Hkv, page = _cache_geometry(k_cache, v_cache, D)
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.numel() != B or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("block_table/seq_lens/out do not match the batch")
+    ks = vs = None
+    if fp8:
+        if kv_scales is None:
+            raise ValueError("an 8-bit cache needs kv_scales=(k_scale, v_scale)")
+        ks, vs = kv_scales
+        for name, t in (("k_scale", ks), ("v_scale", vs)):
+            _need(t, torch.float32, name, dev)
+            if t.numel() != Hkv:
+                raise ValueError(f"{name}: need one scale per KV head ({Hkv})")
+    st = lib().attn_decode_noalloc(_dptr(q), _dptr(k_cache), _dptr(v_cache), KV_FP8_E4M3 if fp8 else KV_BF16,
+                                   _dptr(ks), _dptr(vs), _dptr(block_table), block_table.shape[1], P,
+                                   _dptr(seq_lens), _dptr(map_dev), num_workers, num_segments, head_groups, B, Hq,
+                                   Hkv, D, page, float(softmax_scale), int(max_splits), _dptr(out),
+                                   1 if out.dtype == torch.bfloat16 else 0, _stream(stream))
+    _check(st, "attn_decode_noalloc")
 
 
 def attn_probe_stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor, stream=None) -> None:

@@ -720,3 +720,81 @@ extern "C" int attn_query_workers(int device, int32_t head_groups, int32_t kv_dt
   *num_workers_out = w;
   return LBSA_OK;
 }
+
+// ---- allocation-free decode step ------------------------------------------------------------
+//
+// attn_decode_noalloc runs the split-KV kernel and the combine kernel of one decode step with the
+// partials kept in `scratch`, a fixed device array of this library, so the call allocates nothing.
+// Device code never names the array: host code takes its device address once per device with
+// hipGetSymbolAddress and passes that address to the kernels like any caller-owned buffer.
+
+namespace lbsa {
+
+static __device__ __align__(256) unsigned char scratch[LBSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::atomic<void*> g_scratch_addr[kMaxDevices];   // device address of scratch, per device
+
+// The device address of `scratch` on `device`, taken with that device current on first use.
+static int scratch_address(int device, unsigned char** out) {
+  if (device < 0 || device >= kMaxDevices) return LBSA_ERR_INVALID;
+  void* known = g_scratch_addr[device].load(std::memory_order_acquire);
+  if (!known) {
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess) return LBSA_ERR_HIP;
+    if (prev != device && hipSetDevice(device) != hipSuccess) return LBSA_ERR_HIP;
+    const hipError_t e = hipGetSymbolAddress(&known, HIP_SYMBOL(scratch));
+    if (prev != device && hipSetDevice(prev) != hipSuccess) return LBSA_ERR_HIP;
+    if (e != hipSuccess || !known) return LBSA_ERR_HIP;
+    g_scratch_addr[device].store(known, std::memory_order_release);   // same value from any thread
+  }
+  *out = static_cast<unsigned char*>(known);
+  return LBSA_OK;
+}
+
+}  // namespace lbsa
+
+extern "C" int attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                                   const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                   int32_t block_table_stride, int32_t num_pages, const int32_t* seq_lens,
+                                   const int32_t* map, int32_t num_workers, int32_t num_segments,
+                                   int32_t head_groups, int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t page_size, float softmax_scale, int32_t max_splits,
+                                   void* out, int32_t out_dtype, void* stream) {
+  if (num_segments < 0 || num_q_heads < 1 || head_dim < 1 || B < 0 || !out) return LBSA_ERR_INVALID;
+  // partials: o [S, Hq, D] at the start of scratch (16-byte aligned rows), then m [S, Hq], l [S, Hq]
+  const uint64_t items = (uint64_t)num_segments * (uint64_t)num_q_heads;
+  const uint64_t need = items * ((uint64_t)head_dim + 2) * sizeof(float);
+  if (need > LBSA_NOALLOC_SCRATCH_BYTES) return LBSA_ERR_CAPACITY;
+  int device = 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (st ? hipStreamGetDevice(st, &device) != hipSuccess : hipGetDevice(&device) != hipSuccess)
+    return LBSA_ERR_HIP;
+  unsigned char* base = nullptr;
+  const int rc = scratch_address(device, &base);
+  if (rc != LBSA_OK) return rc;
+  float* part_o = reinterpret_cast<float*>(base);
+  float* part_m = part_o + items * head_dim;
+  float* part_l = part_m + items;
+  int status;
+  if (kv_dtype == LBSA_KV_BF16) {
+    if (k_scale || v_scale) return LBSA_ERR_INVALID;
+    status = splitkv_launch<KvBf16>(q, k_cache, v_cache, nullptr, nullptr, block_table, block_table_stride,
+                                    num_pages, nullptr, nullptr, seq_lens, map, num_workers, num_segments,
+                                    head_groups, B, num_q_heads, num_kv_heads, head_dim, page_size, 1,
+                                    softmax_scale, part_m, part_l, part_o, nullptr, stream);
+  } else if (kv_dtype == LBSA_KV_FP8_E4M3) {
+    if (!k_scale || !v_scale) return LBSA_ERR_INVALID;
+    if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3) return LBSA_ERR_INVALID;
+    status = splitkv_launch<KvFp8>(q, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride,
+                                   num_pages, nullptr, nullptr, seq_lens, map, num_workers, num_segments,
+                                   head_groups, B, num_q_heads, num_kv_heads, head_dim, page_size, 1,
+                                   softmax_scale, part_m, part_l, part_o, nullptr, stream);
+  } else {
+    return LBSA_ERR_INVALID;
+  }
+  if (status != LBSA_OK) return status;
+  // decode maps have one unit per request
+  return attn_combine(part_m, part_l, part_o, map, B, 1, nullptr, nullptr, num_q_heads, head_dim, out, out_dtype,
+                      max_splits, stream);
+}
