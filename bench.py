@@ -236,9 +236,11 @@ def prefill_flops(wl) -> int:
     return 4 * wl.head_dim * wl.hq * total
 
 
-def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tile: int = 256) -> dict:
+def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256), exact_modes=(True, False)) -> dict:
     """Chunked prefill over cached prefixes: 8 requests x 2048-row causal chunks after prefixes drawn
-    log-uniform in [8K, 128K]; q tiles of `q_tile` rows x KV tiles of 512 on the same greedy planner."""
+    log-uniform in [8K, 128K]; q tiles of 128 or 256 rows x KV tiles of 512 on the same greedy
+    planner; P.V exact on bf16 V (the default) or on the fp16 path.  The section's roofline is the
+    configuration as stated (128-row q tiles, exact bf16 P.V)."""
     import numpy as np
     import torch
 
@@ -252,29 +254,122 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tile: int = 256)
     out = torch.empty(q.shape, dtype=torch.float32, device=dev)
     flops = prefill_flops(wl)
     rows = []
-    for W in workers_list:
-        st = PrefillStep(wl.q_lens, wl.kv_lens, dev, num_workers=W, q_tile=q_tile)
-        r = time_steps(lambda i, st=st: st.splitkv(q, kc, vc, bt, scale), lambda i, st=st: st.combine(out),
-                       steps, warmup)
-        split_ms = float(np.mean(r["split_ms"]))
-        rows.append({"workers": W, "q_tile": q_tile, "segments": st.S,
-                     "us_per_step": round(r["total_ms"] / steps * 1e3, 1),
-                     "splitkv_us": round(split_ms * 1e3, 1),
-                     "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 1),
-                     "splitkv_tflops": round(flops / (split_ms * 1e-3) / 1e12, 1)})
-        log(f"prefill W={W}: splitkv {split_ms * 1e3:.0f} us ({rows[-1]['splitkv_tflops']} TFLOP/s)")
-        del st
-    best = min(rows, key=lambda x: x["us_per_step"])
+    for q_tile in q_tiles:
+        for exact in exact_modes:
+            pv = "bf16 V, P as bf16 hi+lo (exact)" if exact else "fp16 V and P (fp16 path)"
+            for W in workers_list:
+                st = PrefillStep(wl.q_lens, wl.kv_lens, dev, num_workers=W, q_tile=q_tile, exact_pv=exact)
+                r = time_steps(lambda i, st=st: st.splitkv(q, kc, vc, bt, scale), lambda i, st=st: st.combine(out),
+                               steps, warmup)
+                split_ms = float(np.mean(r["split_ms"]))
+                tf = flops / (split_ms * 1e-3) / 1e12
+                rows.append({"q_tile": q_tile, "pv": pv, "exact_pv": exact, "workers": W, "segments": st.S,
+                             "us_per_step": round(r["total_ms"] / steps * 1e3, 1),
+                             "splitkv_us": round(split_ms * 1e3, 1),
+                             "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 1),
+                             "splitkv_tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+                log(f"prefill q_tile={q_tile} {'exact' if exact else 'fp16'} W={W}: splitkv {split_ms * 1e3:.0f} us "
+                    f"({rows[-1]['splitkv_tflops']} TFLOP/s)")
+                del st
     prefix = wl.meta["prefix"]
     cached = sum(prefix) / sum(wl.kv_lens)
+
+    def pick(q_tile, exact):
+        cand = [x for x in rows if x["q_tile"] == q_tile and x["exact_pv"] == exact]
+        return min(cand, key=lambda x: x["us_per_step"]) if cand else None
+
+    stated = pick(128, True) or min(rows, key=lambda x: x["us_per_step"])
+    fastest = min(rows, key=lambda x: x["us_per_step"])
     return {"workload": "chunked prefill: 8 x 2048-row causal chunks after prefixes log-uniform in [8K, 128K] "
-                        f"({prefix}), GQA 64q/8kv, d=128, bf16, q tile {q_tile} x KV tile 512",
+                        f"({prefix}), GQA 64q/8kv, d=128, bf16 Q/K/V, q tile {stated['q_tile']} x KV tile 512, "
+                        f"P.V: {stated['pv']}",
             "cached_fraction": round(cached, 4), "flops_per_step": flops,
-            "us_per_step": best["us_per_step"], "tflops_per_step": round(flops / (best["us_per_step"] * 1e-6) / 1e12, 1),
-            "roofline": {"bound": "mfma", "kernel": "splitkv_prefill_kernel",
-                         "achieved": best["splitkv_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(best["splitkv_tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None},
+            "us_per_step": stated["us_per_step"],
+            "tflops_per_step": round(flops / (stated["us_per_step"] * 1e-6) / 1e12, 1),
+            "roofline": {"bound": "mfma", "kernel": "splitkv_prefill_kernel", "dtype": "bf16",
+                         "achieved": stated["splitkv_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(stated["splitkv_tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None},
+            "fastest": {k: fastest[k] for k in ("q_tile", "pv", "workers", "us_per_step", "splitkv_us",
+                                                 "splitkv_tflops", "frac_of_bf16_peak")},
             "sweep": rows}
+
+
+def bench_decode_leg(dev, name: str, args) -> dict:
+    """Another decode batch timed the way the headline batch is: split-KV + combine per step on the
+    dynamic map, the split-KV kernel's roofline fraction, per-CU busy max/mean (median of five
+    instrumented launches, with their range), and the static split-KV baseline (plain and best S)."""
+    import numpy as np
+    import torch
+
+    import load_balanced_split_attn_amd as lb
+    import workloads as WL
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    from load_balanced_split_attn_amd.paged import pack_paged
+    wl = WL.BY_NAME[name]()
+    page = 64
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    nb = algorithmic_bytes(wl, page)
+    q = wl.q().to(dev)
+    kc, vc, bt = pack_paged(wl.kv, wl.kv_lens, page, wl.hkv, wl.head_dim, wl.page_permutation, dev)
+    copies = 1 if nb["kv"] >= 2e9 else min(8, int(math.ceil(2e9 / max(nb["kv"], 1))))
+    caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(copies - 1)]
+    workers = args.workers or lb.attn_query_workers(0, args.head_groups)
+    out = torch.empty((wl.batch, wl.hq, wl.head_dim), dtype=torch.float32, device=dev)
+
+    def run(step, steps, warmup):
+        def split(i):
+            k_, v_ = caches[i % copies]
+            step.splitkv(q, k_, v_, bt, scale)
+        return time_steps(split, lambda i: step.combine(out), steps, warmup)
+
+    def busy(step, n):
+        vals = []
+        for _ in range(n):
+            timing = torch.zeros((step.W * args.head_groups, 4), dtype=torch.int64, device=dev)
+            step.splitkv(q, kc, vc, bt, scale, timing=timing)
+            torch.cuda.synchronize()
+            vals.append(per_cu_busy(timing)["max_over_mean"])
+        return vals
+
+    step = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=workers, tile=args.tile,
+                      head_groups=args.head_groups)
+    r = run(step, args.steps, args.warmup)
+    ms = r["total_ms"] / args.steps
+    split_ms = float(np.mean(r["split_ms"]))
+    achieved = nb["splitkv"] / (split_ms * 1e-3) / 1e9
+    spread = busy(step, 5)
+    max_tiles = max(-(-L // args.tile) for L in wl.kv_lens)
+    plain = min(max(1, -(-step.W // wl.batch)), max_tiles)
+    rows = []
+    for S in sorted(set([plain] + [x for x in (1, 2, 4, 8, 16, 32, 64) if x <= max_tiles])):
+        st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, tile=args.tile, head_groups=args.head_groups,
+                        static_splits=S)
+        rs = run(st, args.static_steps, 2)
+        rows.append({"splits": S, "workgroups": st.W * args.head_groups,
+                     "us_per_step": round(rs["total_ms"] / args.static_steps * 1e3, 2),
+                     "per_cu_max_over_mean": round(float(np.median(busy(st, 1))), 3)})
+        del st
+    best = min(rows, key=lambda x: x["us_per_step"])
+    plain_row = next(x for x in rows if x["splits"] == plain)
+    log(f"{name}: step {ms * 1e3:.1f} us, splitkv {split_ms * 1e3:.1f} us ({achieved:.0f} GB/s), per-CU "
+        f"max/mean {np.median(spread):.3f}; static plain S={plain} {plain_row['us_per_step']} us, best "
+        f"S={best['splits']} {best['us_per_step']} us")
+    res = {"workload": DESCRIPTIONS[name], "us_per_step": round(ms * 1e3, 2),
+           "value": round(nb["step"] / (ms * 1e-3) / 1e12, 4), "unit": "TB/s",
+           "workers": step.W, "segments": step.S, "tiles": step.T, "cache_copies": copies,
+           "roofline": {"bound": "hbm", "kernel": "splitkv_decode_kernel", "achieved": round(achieved, 1),
+                        "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                        "bytes_per_launch": nb["splitkv"], "avg_launch_us": round(split_ms * 1e3, 2)},
+           "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 2),
+           "per_cu_busy": {"max_over_mean": round(float(np.median(spread)), 3),
+                           "range_of_5": [round(min(spread), 3), round(max(spread), 3)]},
+           "static_baseline": {"plain_splits": plain, "plain_us": plain_row["us_per_step"],
+                               "best_splits": best["splits"], "best_us": best["us_per_step"],
+                               "speedup_vs_plain": round(plain_row["us_per_step"] / (ms * 1e3), 3),
+                               "speedup_vs_best": round(best["us_per_step"] / (ms * 1e3), 3), "sweep": rows}}
+    del caches, kc, vc, step
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_fp8(dev, wl, args, bf16_us: float) -> dict:
@@ -588,9 +683,12 @@ def main() -> int:
                     help="run one plain 1 GiB copy first (reference for the HBM byte counters)")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill report")
-    ap.add_argument("--prefill-workers", default="64,128")
-    ap.add_argument("--prefill-q-tile", type=int, default=256, choices=(128, 256))
+    ap.add_argument("--prefill-workers", default="64")
+    ap.add_argument("--prefill-q-tiles", default="128,256", help="query rows per prefill unit (128 and/or 256)")
+    ap.add_argument("--prefill-pv", default="exact,fp16", help="prefill P.V paths to time: exact and/or fp16")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--legs", default="uniform,long_tail",
+                    help="other decode batches timed beside the headline one (comma list, '' for none)")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the chunked-prefill report (profiling runs); prints its JSON")
     ap.add_argument("--no-fp8", action="store_true", help="skip the 8-bit KV cache report")
@@ -619,9 +717,11 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.calibration_copy:
         calibration_copy(dev)
+    prefill_args = ([int(x) for x in args.prefill_workers.split(",")], args.prefill_steps, 1,
+                    tuple(int(x) for x in args.prefill_q_tiles.split(",")),
+                    tuple(x.strip() == "exact" for x in args.prefill_pv.split(",")))
     if args.only_prefill:
-        print(json.dumps(bench_prefill(dev, [int(x) for x in args.prefill_workers.split(",")],
-                                       args.prefill_steps, 1, q_tile=args.prefill_q_tile)), flush=True)
+        print(json.dumps(bench_prefill(dev, *prefill_args)), flush=True)
         return 0
     wl = WL.BY_NAME[args.workload]()
     if args.only_fp8:
@@ -862,9 +962,12 @@ def main() -> int:
     if not args.no_store and wl.name != "tiny":
         result["store_kv"] = bench_store_kv(dev, wl, args)
 
+    legs = [x for x in args.legs.split(",") if x and x != wl.name]
+    if legs:
+        result["legs"] = {name: bench_decode_leg(dev, name, args) for name in legs}
+
     if not args.no_prefill:
-        result["prefill"] = bench_prefill(dev, [int(x) for x in args.prefill_workers.split(",")],
-                                          args.prefill_steps, 1, q_tile=args.prefill_q_tile)
+        result["prefill"] = bench_prefill(dev, *prefill_args)
 
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a CPU sample")
