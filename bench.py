@@ -663,7 +663,99 @@ def bench_store_kv(dev, wl, args) -> dict:
                         "cache, for the batch's new tokens and for a 4096-token step (each token its own page)",
             "timing": f"HIP graph of {reps} launches, {replays} replays, events on the replay stream",
             "bound": "latency at the batch's size; at 4096 tokens the one-token V append, which touches one "
-                     "64-byte row per (dim, head)", "sweep": rows}
+                     "64-byte row per (dim, head)", "sweep": rows,
+            "chunk": bench_store_chunk(dev, reps, replays)}
+
+
+def _graph_us(f, reps: int, replays: int) -> float:
+    """Average time of f() captured `reps` times in one HIP graph, replayed `replays` times."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            f()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            f()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
+    return e0.elapsed_time(e1) / (reps * replays) * 1e3
+
+
+def bench_store_chunk(dev, reps: int, replays: int) -> dict:
+    """The producer step of a prefill chunk: the chunked-prefill batch's 8 x 2048 new tokens appended
+    after their cached prefixes, by attn_store_kv_chunk (V in whole 64-byte rows) and, on the same
+    tokens, by the one-token path (each token its own row of the block table)."""
+    import torch
+
+    import load_balanced_split_attn_amd as lb
+    import workloads as WL
+    from load_balanced_split_attn_amd.paged import cache_shapes
+    pw = WL.prefill()
+    n, prefix = list(pw.q_lens), list(pw.meta["prefix"])
+    B, rows_n, hq, hkv, D, page = len(n), sum(n), pw.hq, pw.hkv, pw.head_dim, 64
+    first = [p // page for p in prefix]
+    last = [(p + c - 1) // page for p, c in zip(prefix, n)]
+    stride = max(last) + 1
+    bt = torch.zeros((B, stride), dtype=torch.int32)
+    pid = 0
+    for b in range(B):
+        for lp in range(first[b], last[b] + 1):
+            bt[b, lp] = pid
+            pid += 1
+    num_pages = pid
+    bt = bt.to(dev)
+    g = torch.Generator().manual_seed(17)
+    q = torch.randn(rows_n, hq, D, generator=g).to(torch.bfloat16).to(dev)
+    k = torch.randn(rows_n, hkv, D, generator=g).to(torch.bfloat16).to(dev)
+    v = torch.randn(rows_n, hkv, D, generator=g).to(torch.bfloat16).to(dev)
+    qw = torch.ones(D, device=dev)
+    kw = torch.ones(D, device=dev)
+    q_lens = torch.tensor(n, dtype=torch.int32, device=dev)
+    starts = [0]
+    for c in n[:-1]:
+        starts.append(starts[-1] + c)
+    q_start = torch.tensor(starts, dtype=torch.int32, device=dev)
+    pos0 = torch.tensor(prefix, dtype=torch.int32, device=dev)
+    req = torch.repeat_interleave(torch.arange(B), torch.tensor(n))
+    pos_rows = torch.tensor([prefix[b] + j for b in range(B) for j in range(n[b])], dtype=torch.int32, device=dev)
+    bt_rows = bt[req.to(dev)].contiguous()
+    q_out = torch.empty_like(q)
+    out = []
+    for fp8 in (False, True):
+        dtype = torch.uint8 if fp8 else torch.bfloat16
+        ksh, vsh = cache_shapes(num_pages, hkv, page, D, dtype)
+        kc = torch.zeros(ksh, dtype=dtype, device=dev)
+        vc = torch.zeros(vsh, dtype=dtype, device=dev)
+        sc = (torch.full((hkv,), 0.02, device=dev), torch.full((hkv,), 0.02, device=dev)) if fp8 else None
+        common = dict(q_norm_w=qw, k_norm_w=kw, rope_theta=10000.0, hadamard=True, kv_scales=sc)
+        us_chunk = _graph_us(lambda: lb.attn_store_kv_chunk(q, k, v, q_lens, q_start, pos0, max(n), q_out, kc, vc, bt,
+                                                            **common), reps, replays)
+        us_token = _graph_us(lambda: lb.attn_store_kv(q, k, v, pos_rows, q_out, kc, vc, bt_rows, **common),
+                             reps, replays)
+        e = 1 if fp8 else 2
+        nbytes = rows_n * (hq + 2 * hkv) * D * 2 + rows_n * hq * D * 2 + rows_n * 2 * hkv * D * e + 3 * B * 4 + \
+            2 * D * 4 + sum(last[b] - first[b] + 1 for b in range(B)) * 4
+        out.append({"kv": "e4m3" if fp8 else "bf16", "tokens": rows_n, "chunk_us": round(us_chunk, 2),
+                    "one_token_path_us": round(us_token, 2), "speedup": round(us_token / us_chunk, 2),
+                    "algorithmic_bytes": nbytes, "GB_per_s": round(nbytes / (us_chunk * 1e-6) / 1e9, 1),
+                    "frac_of_hbm_peak": round(nbytes / (us_chunk * 1e-6) / 8e12, 4)})
+        log(f"store_kv chunk 8x2048 {'e4m3' if fp8 else 'bf16'}: chunk path {us_chunk:.1f} us, one-token path "
+            f"{us_token:.1f} us")
+        del kc, vc
+    return {"workload": "producer step of a prefill chunk: the chunked-prefill batch's 8 x 2048 new tokens after "
+                        f"their cached prefixes ({prefix}), 64 q / 8 kv heads, RMSNorm + RoPE + Hadamard",
+            "sweep": out}
 
 
 def main() -> int:
@@ -696,6 +788,8 @@ def main() -> int:
     ap.add_argument("--no-store", action="store_true", help="skip the producer-step report")
     ap.add_argument("--only-store", action="store_true",
                     help="run only the producer-step report on --workload (profiling runs); prints its JSON")
+    ap.add_argument("--only-store-chunk", action="store_true",
+                    help="run only the prefill-chunk producer-step report (profiling runs); prints its JSON")
     ap.add_argument("--only-fp8", action="store_true",
                     help="run only the 8-bit KV cache report on --workload (profiling runs); prints its JSON")
     args = ap.parse_args()
@@ -729,6 +823,9 @@ def main() -> int:
         return 0
     if args.only_store:
         print(json.dumps(bench_store_kv(dev, wl, args)), flush=True)
+        return 0
+    if args.only_store_chunk:
+        print(json.dumps(bench_store_chunk(dev, 20, 10)), flush=True)
         return 0
     scale = 1.0 / math.sqrt(wl.head_dim)
     page = 64

@@ -310,6 +310,35 @@ int attn_store_kv(const void* q_in, const void* k_in, const void* v_in,
                   int32_t page_size, void* stream);
 
 /*
+ * Producer step of a prefill chunk: the same per-vector steps as attn_store_kv ([P3] §4.1), for a
+ * chunk of consecutive new tokens per request (chunked prefill after a cached prefix, [P3] §6).
+ * Request b appends q_lens[b] tokens: rows q_start[b] .. q_start[b] + q_lens[b] - 1 of q_in / k_in /
+ * v_in / q_out, at positions positions[b] .. positions[b] + q_lens[b] - 1 of its pages.  q and k
+ * take steps 1-3 per row exactly as attn_store_kv does; V is staged per 64-byte cache row (32 bf16
+ * or 64 E4M3 tokens of one dim) so that every full row is written whole, and the rows the chunk
+ * only partly covers keep the cache's bytes for the other tokens (the cached prefix before the
+ * chunk, free slots after it).  The stored values are those of attn_store_kv token by token.
+ *   q_lens, q_start, positions  device int32[B]; max_q_len >= every q_lens[b] (rows past it are not
+ *                 processed); rows must lie inside q_in's [rows, Hq, 128] (not checked)
+ *   other arguments as attn_store_kv; v_in and v_cache 16-byte aligned
+ * A token at a position outside its block-table row, or in a page id outside [0, num_pages), is not
+ * stored; a request with positions[b] < 0 stores nothing (its q rows are still written).
+ * Launches B x max_q_len x ceil((ceil(Hq/4) + ceil(Hkv/4)) / 4) workgroups for q and k and
+ * B x (ceil(max_q_len / w) + 1) x Hkv for V (w = 32 bf16, 64 E4M3), 256 threads each.
+ * Errors: as attn_store_kv, plus LBSA_ERR_INVALID for NULL q_lens / q_start, max_q_len < 0 or a
+ * grid beyond INT32_MAX workgroups.
+ */
+int attn_store_kv_chunk(const void* q_in, const void* k_in, const void* v_in,
+                        const float* q_norm_w, const float* k_norm_w, float norm_eps,
+                        const int32_t* q_lens, const int32_t* q_start, const int32_t* positions,
+                        int32_t max_q_len, float rope_theta, int32_t hadamard,
+                        void* q_out, void* k_cache, void* v_cache, int32_t kv_dtype,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
+                        int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t page_size, void* stream);
+
+/*
  * Split-KV chunked-prefill kernel over a cached prefix (the greedy map of attn_plan_prefill
  * applied to prefill units; prefix reuse as in [P3] §6: a request's new chunk attends to its
  * cached prefix and, causally, to itself).  Request b has q_lens[b] query rows stored from row

@@ -19,7 +19,7 @@ __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill", "attn_plan_device",
     "attn_plan_lpt", "attn_plan_weighted",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
-    "attn_combine", "attn_store_kv", "attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "attn_combine", "attn_store_kv", "attn_store_kv_chunk", "attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
     "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
 ]
 
@@ -61,6 +61,9 @@ _SIGNATURES = {
     "attn_store_kv": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_float,
                                      _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp]),
+    "attn_store_kv_chunk": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp, _c_vp, _c_vp,
+                                           _c_i32, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp,
+                                           _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp]),
     "attn_combine": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                     _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, _c_vp]),
     "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
@@ -422,6 +425,51 @@ def attn_store_kv(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tensor, po
                              _dptr(v_cache), KV_FP8_E4M3 if fp8 else KV_BF16, _dptr(ks), _dptr(vs),
                              _dptr(block_table), block_table.shape[1], P, B, Hq, Hkv, D, page, _stream(stream))
     _check(st, "attn_store_kv")
+
+
+def attn_store_kv_chunk(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tensor, q_lens: torch.Tensor,
+                        q_start: torch.Tensor, positions: torch.Tensor, max_q_len: int, q_out: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                        q_norm_w: Optional[torch.Tensor] = None, k_norm_w: Optional[torch.Tensor] = None,
+                        eps: float = 1e-6, rope_theta: float = 0.0, hadamard: bool = False, kv_scales=None,
+                        stream=None) -> None:
+    """Producer step of a prefill chunk: request b's q_lens[b] new rows (from row q_start[b]) at
+    positions positions[b] + j; q and k as attn_store_kv, V written in whole 64-byte cache rows."""
+    dev = q_in.device
+    for name, t in (("q_in", q_in), ("k_in", k_in), ("v_in", v_in), ("q_out", q_out)):
+        _need(t, torch.bfloat16, name, dev)
+    fp8 = k_cache.dtype == torch.uint8
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(t, torch.uint8 if fp8 else torch.bfloat16, name, dev)
+    for name, t in (("q_lens", q_lens), ("q_start", q_start), ("positions", positions), ("block_table", block_table)):
+        _need(t, torch.int32, name, dev)
+    rows, Hq, D = q_in.shape
+    P, Hkv, page = _cache_geometry(k_cache, v_cache, D)
+    B = q_lens.numel()
+    if tuple(k_in.shape) != (rows, Hkv, D) or tuple(v_in.shape) != (rows, Hkv, D) or tuple(q_out.shape) != (rows, Hq, D):
+        raise ValueError("q_in/k_in/v_in/q_out shapes do not match [rows, Hq, D] / [rows, Hkv, D]")
+    if q_start.numel() != B or positions.numel() != B or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("q_start/positions/block_table do not match the batch")
+    for name, t in (("q_norm_w", q_norm_w), ("k_norm_w", k_norm_w)):
+        if t is not None:
+            _need(t, torch.float32, name, dev)
+            if t.numel() != D:
+                raise ValueError(f"{name}: need {D} gains")
+    ks = vs = None
+    if fp8:
+        if kv_scales is None:
+            raise ValueError("an 8-bit cache needs kv_scales=(k_scale, v_scale)")
+        ks, vs = kv_scales
+        for name, t in (("k_scale", ks), ("v_scale", vs)):
+            _need(t, torch.float32, name, dev)
+            if t.numel() != Hkv:
+                raise ValueError(f"{name}: need {Hkv} scales (one per KV head)")
+    st = lib().attn_store_kv_chunk(_dptr(q_in), _dptr(k_in), _dptr(v_in), _dptr(q_norm_w), _dptr(k_norm_w),
+                                   float(eps), _dptr(q_lens), _dptr(q_start), _dptr(positions), int(max_q_len),
+                                   float(rope_theta), 1 if hadamard else 0, _dptr(q_out), _dptr(k_cache),
+                                   _dptr(v_cache), KV_FP8_E4M3 if fp8 else KV_BF16, _dptr(ks), _dptr(vs),
+                                   _dptr(block_table), block_table.shape[1], P, B, Hq, Hkv, D, page, _stream(stream))
+    _check(st, "attn_store_kv_chunk")
 
 
 def attn_combine(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor, map_dev: torch.Tensor,

@@ -317,3 +317,95 @@ def test_store_random_sweep(lb, seed):
                      for b, L in enumerate(lens))
         written = sum(int(torch.count_nonzero(cache[p0:p0 + 256]).item()) for p0 in range(0, cache.shape[0], 256))
         assert written == stored, "KV"[which] + " cache: stray writes"
+
+
+def _prefilled_cache(totals, page, fp8, dev, seed, Hkv=8, D=128):
+    """A paged cache whose every slot (tokens, and pads up to the page end) holds random bytes, so
+    that a write outside the intended tokens shows; seeded page permutation."""
+    from load_balanced_split_attn_amd.paged import pack_paged
+    g = torch.Generator().manual_seed(seed)
+    dtype = torch.uint8 if fp8 else torch.bfloat16
+
+    def kv_of(b):
+        L = totals[b]
+        if fp8:
+            return (torch.randint(0, 256, (L, Hkv, D), generator=g, dtype=torch.uint8),
+                    torch.randint(0, 256, (L, Hkv, D), generator=g, dtype=torch.uint8))
+        return (torch.randn(L, Hkv, D, generator=g).to(torch.bfloat16), torch.randn(L, Hkv, D, generator=g).to(torch.bfloat16))
+
+    perm = lambda n: torch.randperm(n, generator=torch.Generator().manual_seed(seed + 1))
+    return pack_paged(kv_of, totals, page, Hkv, D, perm, dev, pad_value=77 if fp8 else 3.5, dtype=dtype)
+
+
+@pytest.mark.parametrize("page", [64, 256])
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("norm,theta,had", [(True, 10000.0, True), (False, 0.0, False)])
+def test_chunk_append(lb, fp8, norm, theta, had, page):
+    """attn_store_kv_chunk (chunked-prefill append: V written in whole 64-byte rows) stores exactly
+    what the one-token path stores for the same tokens, leaves every other byte of the cache as it
+    was (the prefix before each chunk and the slots after it share rows with the chunk's first and
+    last tokens), writes the same rotated q, and matches the fp64 oracle.  Chunks start on and off
+    row boundaries, span one token to several pages, and one request appends nothing."""
+    from load_balanced_split_attn_amd.paged import unpack_request
+    dev = torch.device("cuda")
+    prefix = [0, 31, 64, 100, 1000, 5, 4096]
+    n = [300, 1, 64, 0, 129, 2000, 33]
+    extra = [5, 0, 40, 7, 100, 3, 90]
+    totals = [p + c + e for p, c, e in zip(prefix, n, extra)]
+    B, rows = len(n), sum(n)
+    note(f"chunk append fp8={fp8} norm={norm} theta={theta} had={had} page={page}")
+    kc0, vc0, bt = _prefilled_cache(totals, page, fp8, dev, seed=90 + int(fp8))
+    q, k, v, qw, kw = _inputs(80 + int(fp8), rows)
+    starts = np.concatenate([[0], np.cumsum(n)[:-1]]).astype(np.int32)
+    q_lens = torch.tensor(n, dtype=torch.int32, device=dev)
+    q_start = torch.tensor(starts, dtype=torch.int32, device=dev)
+    pos0 = torch.tensor(prefix, dtype=torch.int32, device=dev)
+    ks = vs = None
+    if fp8:
+        ks = torch.tensor([0.02 * (1 + 0.1 * h) for h in range(8)], dtype=torch.float32, device=dev)
+        vs = torch.tensor([0.03 * (1 + 0.05 * h) for h in range(8)], dtype=torch.float32, device=dev)
+    kw_args = dict(q_norm_w=qw.to(dev) if norm else None, k_norm_w=kw.to(dev) if norm else None, eps=1e-6,
+                   rope_theta=theta, hadamard=had, kv_scales=(ks, vs) if fp8 else None)
+    kc1, vc1 = kc0.clone(), vc0.clone()
+    q1 = torch.full((rows, 64, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    lb.attn_store_kv_chunk(q.to(dev), k.to(dev), v.to(dev), q_lens, q_start, pos0, max(n), q1, kc1, vc1, bt, **kw_args)
+    # the one-token path over the same rows: row r of request b at position prefix[b] + j
+    req = np.repeat(np.arange(B), n)
+    pos_rows = torch.tensor([prefix[b] + j for b in range(B) for j in range(n[b])], dtype=torch.int32, device=dev)
+    bt_rows = bt[torch.from_numpy(req).to(dev)].contiguous()
+    kc2, vc2 = kc0.clone(), vc0.clone()
+    q2 = torch.full((rows, 64, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    lb.attn_store_kv(q.to(dev), k.to(dev), v.to(dev), pos_rows, q2, kc2, vc2, bt_rows, **kw_args)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2), "rotated q differs from the one-token path"
+    assert torch.equal(kc1, kc2), "K cache differs from the one-token path"
+    assert torch.equal(vc1, vc2), "V cache differs from the one-token path"
+    # every byte outside the chunks is the prefilled one
+    for b in range(B):
+        end = -(-totals[b] // page) * page
+        k_new, v_new = unpack_request(kc1, vc1, bt, b, end)
+        k_old, v_old = unpack_request(kc0, vc0, bt, b, end)
+        keep = torch.ones(end, dtype=torch.bool)
+        keep[prefix[b]:prefix[b] + n[b]] = False
+        assert torch.equal(k_new[keep], k_old[keep]) and torch.equal(v_new[keep], v_old[keep]), f"request {b}: stray writes"
+    # the stored values and q against the oracle
+    rq, rk, rv = SK.ref_store_kv(q.double().numpy(), k.double().numpy(), v.double().numpy(),
+                                 pos_rows.cpu().double().numpy(), qw.double().numpy() if norm else None,
+                                 kw.double().numpy() if norm else None, 1e-6, theta, had,
+                                 ks.cpu().double().numpy() if fp8 else None, vs.cpu().double().numpy() if fp8 else None)
+    dq = np.abs(q1.float().cpu().numpy().astype(np.float64) - rq)
+    assert np.all(dq <= _tol(rq)), f"q: {int((dq > _tol(rq)).sum())} beyond tolerance"
+    table = e4m3_table()
+    for b in range(B):
+        if n[b] == 0:
+            continue
+        kb, vb = unpack_request(kc1, vc1, bt, b, prefix[b] + n[b])
+        r0 = int(starts[b])
+        for got, ref in ((kb[prefix[b]:].cpu(), rk[r0:r0 + n[b]]), (vb[prefix[b]:].cpu(), rv[r0:r0 + n[b]])):
+            if fp8:
+                gc = got.numpy()
+                dv = np.abs(table[gc] - table[ref])
+                step = np.abs(table[np.minimum(ref.astype(np.int32) & 0x7F, 0x7D) + 1] - table[ref.astype(np.int32) & 0x7F])
+                assert np.all((gc == ref) | (dv <= step + 1e-12)), f"request {b}"
+            else:
+                assert np.all(np.abs(got.double().numpy() - ref) <= _tol(ref)), f"request {b}"
