@@ -128,26 +128,53 @@ def test_single_row_matches_decode():
     assert errors(fast.astype(np.float64), dec)[1] <= 1e-3           # P rounded to fp16
 
 
-def test_full_size_prefill_sampled():
-    """The chunked-prefill batch (8 x 2048-row chunks after log-uniform [8K, 128K] prefixes) in the
-    bench launch configuration; sampled rows of every request (every 37th row, both sides of each
-    256-row unit boundary and the last row) against the oracle."""
+@pytest.fixture(scope="module")
+def full_prefill():
+    """The chunked-prefill batch's inputs on the device and the fp64 oracle for (a) sampled rows of
+    every request and (b) every row of the two requests with the shortest prefixes."""
     wl = WL.prefill()
-    note(f"full-size prefill kv_lens={wl.kv_lens}")
-    W = 64
-    got, step = _run(wl, W, poison=True)
+    # every 37th row (all offsets inside a wave's 32 rows and a unit's 256 come up) plus both sides
+    # of each 128-row unit boundary and the last row
+    rows = sorted(set(range(0, 2048, 37)) | {u * 128 + d for u in range(1, 16) for d in (-1, 0)} | {2047})
+    prefix = wl.meta["prefix"]
+    whole = sorted(range(wl.batch), key=lambda b: prefix[b])[:2]
+    sampled, full = {}, {}
+    for b in range(wl.batch):
+        if b in whole:
+            k, v = wl.kv(b)
+            full[b] = ref_attention(wl.q(b).double().numpy(), k.double().numpy(), v.double().numpy(), SCALE)
+        else:
+            sampled[b] = oracle_prefill_rows(wl, b, rows)
+    note(f"full-size prefill oracle ready: every row of requests {whole} (prefixes "
+         f"{[prefix[b] for b in whole]}), {len(rows)} sampled rows of the others")
+    return wl, prefill_inputs(wl, pad_value=float("nan")), rows, sampled, full
+
+
+@pytest.mark.parametrize("q_tile,exact_pv", [(128, True), (256, True), (128, False), (256, False)])
+def test_full_size_prefill(full_prefill, q_tile, exact_pv):
+    """The chunked-prefill batch (8 x 2048-row chunks after log-uniform [8K, 128K] prefixes) in each
+    launch configuration the bench times (64 workers; 128- or 256-row units; exact or fp16 P.V):
+    every row of the two shortest-prefix requests and sampled rows of the others against the fp64
+    oracle."""
+    wl, inputs, rows, sampled, full = full_prefill
+    note(f"full-size prefill q_tile={q_tile} exact_pv={exact_pv}")
+    got, step = _run(wl, 64, inputs=inputs, poison=True, exact_pv=exact_pv, q_tile=q_tile)
     assert np.all(np.isfinite(got))
     starts = q_starts(wl)
-    # every 37th row (all offsets inside a wave's 32 rows and a unit's 256 come up) plus both sides
-    # of each unit boundary and the last row
-    rows = sorted(set(range(0, 2048, 37)) | {u * 256 + d for u in range(1, 8) for d in (-1, 0)} | {2047})
     for b in range(wl.batch):
-        ref = oracle_prefill_rows(wl, b, rows)
-        worst = 0.0
-        for j in rows:
-            ma, rr = assert_close(got[starts[b] + j], ref[j], f"prefill request {b} row {j}")
-            worst = max(worst, rr)
-        note(f"  request {b} kv_len={wl.kv_lens[b]}: {len(rows)} rows ok (worst rel_rms {worst:.2e})")
+        if b in full:
+            ma, rr = assert_close(got[starts[b]:starts[b] + wl.q_lens[b]], full[b], f"prefill request {b}, all rows")
+            worst = max(errors(got[starts[b] + j], full[b][j])[1] for j in range(wl.q_lens[b]))
+            note(f"  request {b} kv_len={wl.kv_lens[b]}: all {wl.q_lens[b]} rows, rel_rms {rr:.2e} "
+                 f"(worst row {worst:.2e})")
+            for j in range(wl.q_lens[b]):
+                assert_close(got[starts[b] + j], full[b][j], f"prefill request {b} row {j}")
+        else:
+            worst = 0.0
+            for j in rows:
+                ma, rr = assert_close(got[starts[b] + j], sampled[b][j], f"prefill request {b} row {j}")
+                worst = max(worst, rr)
+            note(f"  request {b} kv_len={wl.kv_lens[b]}: {len(rows)} rows ok (worst rel_rms {worst:.2e})")
 
 
 def test_million_token_prefix_sampled():
