@@ -294,6 +294,50 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256)
             "sweep": rows}
 
 
+def claim_sweep(dev, wl, q, caches, bt, out, args, base_us: float) -> dict:
+    """Run-time claiming (attn_splitkv_claimed) beside the static launch: one resident wave per SIMD
+    (one-wave workgroups) takes the (list, KV head) items of maps with m times the resident lists,
+    at 512- and 128-token tiles; beside each, the static launch over the same map (one workgroup per
+    item, the hardware dispatcher placing them).  speedup = the default static step / this step."""
+    import numpy as np
+    import torch
+
+    import load_balanced_split_attn_amd as lb
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    copies = len(caches)
+    kc, vc = caches[0]
+    resident = lb.attn_query_workers(0, 8) * 8          # one wave per SIMD
+    base_lists = resident // wl.hkv
+    rows = []
+    for mult in (1, 2, 4):
+        for tile in (512, 128):
+            for mode in ("claimed", "static"):
+                if mode == "static" and mult == 1 and tile == 512:
+                    continue   # the default launch itself
+                st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=base_lists * mult, tile=tile,
+                                head_groups=wl.hkv, resident_workgroups=resident if mode == "claimed" else None)
+
+                def split(i, st=st):
+                    k_, v_ = caches[i % copies]
+                    st.splitkv(q, k_, v_, bt, scale)
+
+                r = time_steps(split, lambda i, st=st: st.combine(out), args.static_steps, 2)
+                us = r["total_ms"] / args.static_steps * 1e3
+                n_wg = resident if mode == "claimed" else st.W * wl.hkv
+                timing = torch.zeros((n_wg, 4), dtype=torch.int64, device=dev)
+                st.splitkv(q, kc, vc, bt, scale, timing=timing)
+                torch.cuda.synchronize()
+                rows.append({"mode": mode, "lists": st.W, "tile": tile, "segments": st.S, "workgroups": n_wg,
+                             "us_per_step": round(us, 2), "splitkv_us": round(float(np.mean(r["split_ms"])) * 1e3, 2),
+                             "per_cu_max_over_mean": round(per_cu_busy(timing)["max_over_mean"], 3),
+                             "speedup": round(base_us / us, 3)})
+                log(f"{wl.name} {mode} lists={st.W} tile={tile}: {us:.1f} us")
+                del st
+    best = min(rows, key=lambda x: x["us_per_step"])
+    return {"resident_workgroups": resident, "default_us": round(base_us, 2), "best": best, "sweep": rows}
+
+
 def bench_decode_leg(dev, name: str, args) -> dict:
     """Another decode batch timed the way the headline batch is: split-KV + combine per step on the
     dynamic map, the split-KV kernel's roofline fraction, per-CU busy max/mean (median of five
@@ -313,7 +357,9 @@ def bench_decode_leg(dev, name: str, args) -> dict:
     kc, vc, bt = pack_paged(wl.kv, wl.kv_lens, page, wl.hkv, wl.head_dim, wl.page_permutation, dev)
     copies = 1 if nb["kv"] >= 2e9 else min(8, int(math.ceil(2e9 / max(nb["kv"], 1))))
     caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(copies - 1)]
-    workers = args.workers or lb.attn_query_workers(0, args.head_groups)
+    # one wave per (list, KV head) workgroup and one resident wave per SIMD: G = Hkv head groups
+    G = min(args.head_groups, wl.hkv)
+    workers = args.workers or lb.attn_query_workers(0, 8) * 8 // wl.hkv
     out = torch.empty((wl.batch, wl.hq, wl.head_dim), dtype=torch.float32, device=dev)
 
     def run(step, steps, warmup):
@@ -325,14 +371,13 @@ def bench_decode_leg(dev, name: str, args) -> dict:
     def busy(step, n):
         vals = []
         for _ in range(n):
-            timing = torch.zeros((step.W * args.head_groups, 4), dtype=torch.int64, device=dev)
+            timing = torch.zeros((step.W * G, 4), dtype=torch.int64, device=dev)
             step.splitkv(q, kc, vc, bt, scale, timing=timing)
             torch.cuda.synchronize()
             vals.append(per_cu_busy(timing)["max_over_mean"])
         return vals
 
-    step = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=workers, tile=args.tile,
-                      head_groups=args.head_groups)
+    step = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=workers, tile=args.tile, head_groups=G)
     r = run(step, args.steps, args.warmup)
     ms = r["total_ms"] / args.steps
     split_ms = float(np.mean(r["split_ms"]))
@@ -342,10 +387,9 @@ def bench_decode_leg(dev, name: str, args) -> dict:
     plain = min(max(1, -(-step.W // wl.batch)), max_tiles)
     rows = []
     for S in sorted(set([plain] + [x for x in (1, 2, 4, 8, 16, 32, 64) if x <= max_tiles])):
-        st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, tile=args.tile, head_groups=args.head_groups,
-                        static_splits=S)
+        st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, tile=args.tile, head_groups=G, static_splits=S)
         rs = run(st, args.static_steps, 2)
-        rows.append({"splits": S, "workgroups": st.W * args.head_groups,
+        rows.append({"splits": S, "workgroups": st.W * G,
                      "us_per_step": round(rs["total_ms"] / args.static_steps * 1e3, 2),
                      "per_cu_max_over_mean": round(float(np.median(busy(st, 1))), 3)})
         del st
@@ -367,6 +411,8 @@ def bench_decode_leg(dev, name: str, args) -> dict:
                                "best_splits": best["splits"], "best_us": best["us_per_step"],
                                "speedup_vs_plain": round(plain_row["us_per_step"] / (ms * 1e3), 3),
                                "speedup_vs_best": round(best["us_per_step"] / (ms * 1e3), 3), "sweep": rows}}
+    if not args.no_claim:
+        res["claimed"] = claim_sweep(dev, wl, q, caches, bt, out, args, ms * 1e3)
     del caches, kc, vc, step
     torch.cuda.empty_cache()
     return res
@@ -779,7 +825,8 @@ def main() -> int:
     ap.add_argument("--prefill-q-tiles", default="128,256", help="query rows per prefill unit (128 and/or 256)")
     ap.add_argument("--prefill-pv", default="exact,fp16", help="prefill P.V paths to time: exact and/or fp16")
     ap.add_argument("--prefill-steps", type=int, default=5)
-    ap.add_argument("--legs", default="uniform,long_tail",
+    ap.add_argument("--no-claim", action="store_true", help="skip the run-time claiming comparison")
+    ap.add_argument("--legs", default="uniform,long_tail,mixed_tp8",
                     help="other decode batches timed beside the headline one (comma list, '' for none)")
     ap.add_argument("--only-prefill", action="store_true",
                     help="run only the chunked-prefill report (profiling runs); prints its JSON")
@@ -1030,6 +1077,9 @@ def main() -> int:
                     "tile, tile to the worker whose equal cost share holds its midpoint; beside it the greedy "
                     "fill at smaller tiles; greedy_speedup = this step / the 512-token greedy-fill step",
             "sweep": rows}
+
+    if not args.no_claim and wl.hkv == args.head_groups:
+        result["claimed"] = claim_sweep(dev, wl, q, caches, bt, out, args, ms_per_step * 1e3)
 
     if not args.no_probe:
         # the device's streaming-read ceiling, measured on the same run (the KV cache itself)

@@ -252,6 +252,36 @@ int attn_splitkv_fp8(const void* q, const void* k_cache, const void* v_cache,
                      uint64_t* timing, void* stream);
 
 /*
+ * Split-KV decode with run-time claiming of the map's lists ([P4] §二.1: the workers take their
+ * tasks from the map at run time; [P3] §3.1 方案 step 4).  The map is attn_plan's (or attn_plan_static's,
+ * attn_plan_weighted's, attn_plan_lpt's) for num_workers lists, typically several times the lists a
+ * resident launch would get; instead of one workgroup per (list, KV head), resident_workgroups
+ * workgroups of one wave each take items (list w, KV head g) in the order i = w * Hkv + g from a
+ * device counter until every item is taken, so a list goes to whichever workgroup is free first.
+ * Each item is run exactly once and writes the partial slots the static launch writes, with the
+ * same arithmetic: the partials, and the attn_combine output, are bitwise those of attn_splitkv /
+ * attn_splitkv_fp8 over the same map.
+ *   kv_dtype      LBSA_KV_BF16 (k_scale, v_scale NULL) or LBSA_KV_FP8_E4M3 (scales as attn_splitkv_fp8)
+ *   resident_workgroups  workgroups launched (>= 1; attn_query_workers(dev, 8, kv_dtype) * 8 fills
+ *                 the device once)
+ *   claim_state   device int32[2], 4-byte aligned, zero before the first launch; every launch
+ *                 leaves it zero (the last workgroup to finish resets it).  Launches that share one
+ *                 claim_state must not overlap (same stream, or ordered by events).
+ *   timing        optional, device uint64[resident_workgroups * 4] (as attn_splitkv)
+ * One wave per workgroup: head_groups is Hkv (every KV head its own item).  Other arguments, layouts
+ * and errors as attn_splitkv; LBSA_ERR_INVALID also for a NULL or misaligned claim_state or
+ * resident_workgroups < 1.
+ */
+int attn_splitkv_claimed(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                         const float* k_scale, const float* v_scale,
+                         const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
+                         const int32_t* seq_lens, const int32_t* map, int32_t num_workers, int32_t num_segments,
+                         int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t page_size, float softmax_scale, int32_t resident_workgroups,
+                         int32_t* claim_state, float* part_m, float* part_l, float* part_o,
+                         uint64_t* timing, void* stream);
+
+/*
  * Multi-token decode (the verify step of multi-token prediction, [P3] §7: a step checks several
  * drafted tokens at once, so a request carries a few query tokens instead of one).  Request b has
  * q_lens[b] <= rows_per_unit query rows stored from row q_start[b] of q [rows, Hq, D]; they are the

@@ -19,7 +19,7 @@ __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill", "attn_plan_device",
     "attn_plan_lpt", "attn_plan_weighted",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
-    "attn_combine", "attn_store_kv", "attn_store_kv_chunk", "attn_decode_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "attn_combine", "attn_store_kv", "attn_store_kv_chunk", "attn_decode_noalloc", "attn_splitkv_claimed", "NOALLOC_SCRATCH_BYTES",
     "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
 ]
 
@@ -61,6 +61,9 @@ _SIGNATURES = {
     "attn_store_kv": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp, ctypes.c_float,
                                      _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp]),
+    "attn_splitkv_claimed": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
+                                            _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                            ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
     "attn_store_kv_chunk": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp, _c_vp, _c_vp,
                                            _c_i32, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp,
                                            _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp]),
@@ -308,6 +311,42 @@ def attn_splitkv_fp8(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tens
                                 num_workers, num_segments, head_groups, B, Hq, Hkv, D, page, float(softmax_scale),
                                 _dptr(part_m), _dptr(part_l), _dptr(part_o), _dptr(timing), _stream(stream))
     _check(st, "attn_splitkv_fp8")
+
+
+def attn_splitkv_claimed(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, map_dev: torch.Tensor, num_workers: int, num_segments: int,
+                         resident_workgroups: int, claim_state: torch.Tensor, softmax_scale: float,
+                         part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor, kv_scales=None,
+                         timing: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Split-KV decode with run-time claiming: resident_workgroups one-wave workgroups take the map's
+    (list, KV head) items from claim_state (device int32[2], zero before the first launch and left
+    zero by every launch).  Same partials as attn_splitkv / attn_splitkv_fp8 over the same map."""
+    fp8 = k_cache.dtype == torch.uint8
+    B, Hq, D, P, Hkv, page = _check_decode_args(q, k_cache, v_cache, block_table, seq_lens, map_dev, num_workers,
+                                                num_segments, 1, part_m, part_l, part_o, None,
+                                                torch.uint8 if fp8 else torch.bfloat16)
+    _need(claim_state, torch.int32, "claim_state", q.device)
+    if claim_state.numel() < 2:
+        raise ValueError("claim_state: need 2 int32")
+    if timing is not None:
+        _need(timing, torch.int64, "timing", q.device)
+        if timing.numel() < resident_workgroups * 4:
+            raise ValueError("timing buffer too small")
+    ks = vs = None
+    if fp8:
+        if kv_scales is None:
+            raise ValueError("an 8-bit cache needs kv_scales=(k_scale, v_scale)")
+        ks, vs = kv_scales
+        for name, t in (("k_scale", ks), ("v_scale", vs)):
+            _need(t, torch.float32, name, q.device)
+            if t.numel() != Hkv:
+                raise ValueError(f"{name}: need one scale per KV head ({Hkv})")
+    st = lib().attn_splitkv_claimed(_dptr(q), _dptr(k_cache), _dptr(v_cache), KV_FP8_E4M3 if fp8 else KV_BF16,
+                                    _dptr(ks), _dptr(vs), _dptr(block_table), block_table.shape[1], P,
+                                    _dptr(seq_lens), _dptr(map_dev), num_workers, num_segments, B, Hq, Hkv, D, page,
+                                    float(softmax_scale), int(resident_workgroups), _dptr(claim_state),
+                                    _dptr(part_m), _dptr(part_l), _dptr(part_o), _dptr(timing), _stream(stream))
+    _check(st, "attn_splitkv_claimed")
 
 
 def attn_splitkv_mtp(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_table: torch.Tensor,

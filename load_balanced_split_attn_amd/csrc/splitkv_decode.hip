@@ -61,7 +61,9 @@ struct DecodeParams {
   const int32_t* q_lens;        // multi-token decode: [B] query rows of request b (else null)
   const int32_t* q_start;       // multi-token decode: [B] first row of request b in q (else null)
   uint64_t* timing;             // [grid, 4] or null
+  int32_t* claim;               // run-time claiming: device int32[2] (next item, workgroups done), else null
   int32_t bt_stride, num_pages, W, S, B, Hq, Hkv, page;
+  int32_t G;                    // KV-head groups per list (workgroups per list in the static launch)
   int32_t R;                    // partial rows per slot (1 for plain decode)
   float scale_log2;             // softmax scale * log2(e)
 };
@@ -340,23 +342,27 @@ __device__ __forceinline__ void compute_chunk(typename KV::Chunk& ch, State (&st
 // q_start[b] of q and are the last q_lens[b] positions of its context, row j seeing keys
 // [0, kv_len - q_len + j]; the map comes from attn_plan_prefill with q_tile = R >= q_lens[b], and
 // the partials have R rows per slot.
-template <class KV, int WAVES, int ROWS>
+//
+// CLAIM = false: workgroup (w, g) of a W x G grid walks list w for head group g.  CLAIM = true (one
+// wave per workgroup): a grid of resident workgroups runs items (list w, KV head g) = (i / G, i % G),
+// workgroup b item b first and then, one at a time, the next item from a device counter until
+// none is left; every item is run exactly once and writes the same partial slots as in the static
+// launch, so the results are bitwise those of the static launch.  The last workgroup to finish
+// puts the counter state back to zero.
+template <class KV, int WAVES, int ROWS, bool CLAIM = false>
 __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams p) {
   using Chunk = typename KV::Chunk;
   constexpr int NQB = ROWS <= 2 ? 1 : 2;   // 16-column blocks: 8 heads x 2 rows each
+  static_assert(!CLAIM || WAVES == 1, "run-time claiming runs one wave per workgroup");
   const int lane = threadIdx.x & 63;
   // wave index is uniform across the wave; say so, so page addressing stays in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int G = gridDim.x / p.W;
-  const int w = blockIdx.x / G;
-  const int h = (blockIdx.x % G) * WAVES + wave;   // KV head of this wave
+  const int G = p.G;
   Lane ln;
   ln.r = lane & 15;                                 // MFMA row / column index
   ln.grp = lane >> 4;                               // MFMA k group
   KV::setup(ln);
   const int block_bytes = p.page * kD * KV::kElem;
-  const float s_log2 = p.k_scale ? p.scale_log2 * p.k_scale[h] : p.scale_log2;
-  const float o_scale = p.v_scale ? p.v_scale[h] : 1.f;
 
   uint64_t t_start = 0;
   if (p.timing && threadIdx.x == 0) t_start = realtime();
@@ -371,10 +377,14 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
   const int32_t* segs = p.map + 8 + (p.W + 1) + (U + 1) + 2 * U;
   // version 2: worker w runs the segments order[worker_ptr[w] ..), by slot index
   const int32_t* order = version == LBSA_MAP_VERSION_ORDERED ? segs + 4 * p.map[4] : nullptr;
-  const int s_begin = worker_ptr[w];
-  const int s_end = min(worker_ptr[w + 1], p.S);
   const size_t head_bytes = (size_t)block_bytes;   // bytes per (page, KV head) block
 
+  // list w for KV head h (this wave)
+  auto run_list = [&](int w, int h) __attribute__((always_inline)) {
+  const float s_log2 = p.k_scale ? p.scale_log2 * p.k_scale[h] : p.scale_log2;
+  const float o_scale = p.v_scale ? p.v_scale[h] : 1.f;
+  const int s_begin = worker_ptr[w];
+  const int s_end = min(worker_ptr[w + 1], p.S);
   for (int j = s_begin; j < s_end; ++j) {
     const int s = order ? order[j] : j;
     if (s < 0 || s >= p.S) continue;
@@ -516,6 +526,30 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
       }
     }
   }
+  };
+
+  if constexpr (!CLAIM) {
+    run_list(blockIdx.x / G, (blockIdx.x % G) * WAVES + wave);
+  } else {
+    // workgroup b starts with item b; each further item takes one device-scope atomic on the
+    // counter (issued by lane 0 as a vector memory atomic, broadcast), numbered after the grid's
+    // first items, so no atomics at all are issued while the grid starts
+    const int items = p.W * G;
+    auto claim = [&]() __attribute__((always_inline)) {
+      int v = 0;
+      if (lane == 0) v = atomicAdd(p.claim, 1);
+      return (int)gridDim.x + __builtin_amdgcn_readlane(v, 0);
+    };
+    for (int item = blockIdx.x; item < items; item = claim()) run_list(item / G, item % G);
+    // every claim of this workgroup has returned; the last workgroup to get here resets the state
+    if (lane == 0) {
+      const int done = atomicAdd(p.claim + 1, 1);
+      if (done == (int)gridDim.x - 1) {
+        atomicExch(p.claim, 0);
+        atomicExch(p.claim + 1, 0);
+      }
+    }
+  }
 
   // loads of an empty last chunk may still be outstanding; drain them before the wave ends
   // (gfx9 s_waitcnt encoding: vmcnt 0, expcnt and lgkmcnt at their maximum)
@@ -535,6 +569,12 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
 
 template <class KV, int WAVES, int ROWS>
 hipError_t launch_decode(const DecodeParams& p, int grid, hipStream_t stream) {
+  if constexpr (WAVES == 1 && ROWS == 1) {
+    if (p.claim) {
+      hipLaunchKernelGGL((splitkv_decode_kernel<KV, 1, 1, true>), dim3(grid), dim3(64), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((splitkv_decode_kernel<KV, WAVES, ROWS>), dim3(grid), dim3(64 * WAVES), 0, stream, p);
   return hipGetLastError();
 }
@@ -567,7 +607,7 @@ int splitkv_launch(const void* q, const void* k_cache, const void* v_cache, cons
                    int32_t num_workers, int32_t num_segments, int32_t head_groups, int32_t B, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t rows_per_unit,
                    float softmax_scale, float* part_m, float* part_l, float* part_o, uint64_t* timing,
-                   void* stream) {
+                   void* stream, int32_t* claim = nullptr, int32_t resident = 0) {
   if (num_workers < 1 || num_segments < 0 || B < 0 || head_groups < 1 || num_kv_heads < 1 ||
       num_pages < 1 || block_table_stride < 0 || page_size < 1 || rows_per_unit < 1)
     return LBSA_ERR_INVALID;
@@ -601,6 +641,8 @@ int splitkv_launch(const void* q, const void* k_cache, const void* v_cache, cons
   p.q_lens = q_lens;
   p.q_start = q_start;
   p.timing = timing;
+  p.claim = claim;
+  p.G = head_groups;
   p.bt_stride = block_table_stride;
   p.num_pages = num_pages;
   p.W = num_workers;
@@ -612,8 +654,9 @@ int splitkv_launch(const void* q, const void* k_cache, const void* v_cache, cons
   p.R = rows_per_unit;
   p.scale_log2 = softmax_scale * kLog2e;
 
-  const int64_t grid = (int64_t)num_workers * head_groups;
-  if (grid > INT32_MAX) return LBSA_ERR_INVALID;
+  if (claim && (waves != 1 || q_lens || resident < 1)) return LBSA_ERR_INVALID;
+  const int64_t grid = claim ? (int64_t)resident : (int64_t)num_workers * head_groups;
+  if (grid > INT32_MAX || (int64_t)num_workers * head_groups > INT32_MAX) return LBSA_ERR_INVALID;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
   if (!q_lens)
@@ -690,6 +733,31 @@ extern "C" int attn_splitkv_mtp(const void* q, const void* k_cache, const void* 
                                q_lens, q_start, kv_lens, map, num_workers, num_segments, head_groups, B,
                                num_q_heads, num_kv_heads, head_dim, page_size, rows_per_unit, softmax_scale, part_m,
                                part_l, part_o, nullptr, stream);
+}
+
+extern "C" int attn_splitkv_claimed(const void* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                                    const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                    int32_t block_table_stride, int32_t num_pages, const int32_t* seq_lens,
+                                    const int32_t* map, int32_t num_workers, int32_t num_segments,
+                                    int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t page_size, float softmax_scale, int32_t resident_workgroups,
+                                    int32_t* claim_state, float* part_m, float* part_l, float* part_o,
+                                    uint64_t* timing, void* stream) {
+  if (!claim_state || (reinterpret_cast<uintptr_t>(claim_state) & 3) || resident_workgroups < 1)
+    return LBSA_ERR_INVALID;
+  if (kv_dtype == LBSA_KV_BF16) {
+    if (k_scale || v_scale) return LBSA_ERR_INVALID;
+    return splitkv_launch<KvBf16>(q, k_cache, v_cache, nullptr, nullptr, block_table, block_table_stride,
+                                  num_pages, nullptr, nullptr, seq_lens, map, num_workers, num_segments, num_kv_heads,
+                                  B, num_q_heads, num_kv_heads, head_dim, page_size, 1, softmax_scale, part_m,
+                                  part_l, part_o, timing, stream, claim_state, resident_workgroups);
+  }
+  if (kv_dtype != LBSA_KV_FP8_E4M3 || !k_scale || !v_scale) return LBSA_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3) return LBSA_ERR_INVALID;
+  return splitkv_launch<KvFp8>(q, k_cache, v_cache, k_scale, v_scale, block_table, block_table_stride, num_pages,
+                               nullptr, nullptr, seq_lens, map, num_workers, num_segments, num_kv_heads, B,
+                               num_q_heads, num_kv_heads, head_dim, page_size, 1, softmax_scale, part_m, part_l,
+                               part_o, timing, stream, claim_state, resident_workgroups);
 }
 
 extern "C" int attn_query_workers(int device, int32_t head_groups, int32_t kv_dtype, int32_t* num_workers_out) {

@@ -15,14 +15,17 @@ import torch
 
 from . import (KV_BF16, KV_FP8_E4M3, attn_combine, attn_plan, attn_plan_lpt, attn_plan_static, attn_plan_weighted,
                attn_query_workers,
-               attn_splitkv, attn_splitkv_fp8, map_header, max_splits_of)
+               attn_splitkv, attn_splitkv_claimed, attn_splitkv_fp8, map_header, max_splits_of)
 
 
 class DecodeStep:
     def __init__(self, seq_lens: Sequence[int], device, num_workers: Optional[int] = None, tile: int = 512,
                  head_groups: int = 8, num_q_heads: int = 64, head_dim: int = 128,
                  static_splits: Optional[int] = None, kv_dtype: int = KV_BF16, planner: str = "greedy",
-                 split_cost: int = 0):
+                 split_cost: int = 0, resident_workgroups: Optional[int] = None):
+        """resident_workgroups: run the split-KV kernel with run-time claiming (that many one-wave
+        workgroups take the map's (list, KV head) items from a device counter) instead of one
+        workgroup per (list, head group); needs head_groups equal to the KV head count."""
         device = torch.device(device)
         self.seq_lens_host = [int(x) for x in seq_lens]
         if static_splits is not None:
@@ -51,10 +54,18 @@ class DecodeStep:
         self.part_m = torch.empty((S, num_q_heads), dtype=torch.float32, device=device)
         self.part_l = torch.empty((S, num_q_heads), dtype=torch.float32, device=device)
         self.part_o = torch.empty((S, num_q_heads, head_dim), dtype=torch.float32, device=device)
+        self.resident = resident_workgroups
+        self.claim_state = torch.zeros(2, dtype=torch.int32, device=device) if resident_workgroups else None
 
     def splitkv(self, q, k_cache, v_cache, block_table, scale: float, timing=None, stream=None,
                 kv_scales=None) -> None:
         """bf16 cache, or (kv_dtype KV_FP8_E4M3) uint8 codes with kv_scales = (k_scale, v_scale)."""
+        if self.resident:
+            attn_splitkv_claimed(q, k_cache, v_cache, block_table, self.seq_lens, self.map, self.W, self.S,
+                                 self.resident, self.claim_state, scale, self.part_m, self.part_l, self.part_o,
+                                 kv_scales=kv_scales if self.kv_dtype == KV_FP8_E4M3 else None, timing=timing,
+                                 stream=stream)
+            return
         if self.kv_dtype == KV_FP8_E4M3:
             if kv_scales is None:
                 raise ValueError("an 8-bit cache needs kv_scales=(k_scale, v_scale)")
