@@ -25,8 +25,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_JSON = os.path.join(PKG, "measured_traffic.json")
 GIB = 1 << 30
 KERNELS = {
-    "splitkv_decode_kernel": "splitkv_decode_kernel<lbsa::KvBf16, 1, 1>",
-    "splitkv_decode_kernel_fp8": "splitkv_decode_kernel<lbsa::KvFp8, 1, 1>",
+    "splitkv_decode_kernel": "splitkv_decode_kernel<lbsa::KvBf16, 1, 1, false>",
+    "splitkv_decode_kernel_fp8": "splitkv_decode_kernel<lbsa::KvFp8, 1, 1, false>",
 }
 
 

@@ -10,8 +10,8 @@ import pytest
 
 from load_balanced_split_attn_amd import record_traffic as RT
 
-BF16 = "void lbsa::splitkv_decode_kernel<lbsa::KvBf16, 1, 1>(lbsa::DecodeParams)"
-FP8 = "void lbsa::splitkv_decode_kernel<lbsa::KvFp8, 1, 1>(lbsa::DecodeParams)"
+BF16 = "void lbsa::splitkv_decode_kernel<lbsa::KvBf16, 1, 1, false>(lbsa::DecodeParams)"
+FP8 = "void lbsa::splitkv_decode_kernel<lbsa::KvFp8, 1, 1, false>(lbsa::DecodeParams)"
 COPY = "__amd_rocclr_copyBuffer"
 
 
