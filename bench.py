@@ -236,11 +236,15 @@ def prefill_flops(wl) -> int:
     return 4 * wl.head_dim * wl.hq * total
 
 
-def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256), exact_modes=(True, False)) -> dict:
+PV_LABELS = {None: "fp16 P.V on checked V chunks, bf16 hi+lo P for chunks fp16 does not hold (default; V exact)",
+             True: "bf16 V, P as bf16 hi+lo (every chunk)", False: "fp16 V and P, unchecked (V range-limited)"}
+
+
+def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256), exact_modes=(None, True, False)) -> dict:
     """Chunked prefill over cached prefixes: 8 requests x 2048-row causal chunks after prefixes drawn
     log-uniform in [8K, 128K]; q tiles of 128 or 256 rows x KV tiles of 512 on the same greedy
-    planner; P.V exact on bf16 V (the default) or on the fp16 path.  The section's roofline is the
-    configuration as stated (128-row q tiles, exact bf16 P.V)."""
+    planner; P.V in the default checked mode, exact on bf16 V, or on the unchecked fp16 path.  The
+    section's roofline is the configuration as stated (128-row q tiles, default P.V)."""
     import numpy as np
     import torch
 
@@ -256,7 +260,7 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256)
     rows = []
     for q_tile in q_tiles:
         for exact in exact_modes:
-            pv = "bf16 V, P as bf16 hi+lo (exact)" if exact else "fp16 V and P (fp16 path)"
+            pv = PV_LABELS[exact]
             for W in workers_list:
                 st = PrefillStep(wl.q_lens, wl.kv_lens, dev, num_workers=W, q_tile=q_tile, exact_pv=exact)
                 r = time_steps(lambda i, st=st: st.splitkv(q, kc, vc, bt, scale), lambda i, st=st: st.combine(out),
@@ -268,7 +272,8 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256)
                              "splitkv_us": round(split_ms * 1e3, 1),
                              "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 1),
                              "splitkv_tflops": round(tf, 1), "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
-                log(f"prefill q_tile={q_tile} {'exact' if exact else 'fp16'} W={W}: splitkv {split_ms * 1e3:.0f} us "
+                log(f"prefill q_tile={q_tile} {'checked' if exact is None else ('exact' if exact else 'fp16')} W={W}: "
+                    f"splitkv {split_ms * 1e3:.0f} us "
                     f"({rows[-1]['splitkv_tflops']} TFLOP/s)")
                 del st
     prefix = wl.meta["prefix"]
@@ -278,7 +283,7 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256)
         cand = [x for x in rows if x["q_tile"] == q_tile and x["exact_pv"] == exact]
         return min(cand, key=lambda x: x["us_per_step"]) if cand else None
 
-    stated = pick(128, True) or min(rows, key=lambda x: x["us_per_step"])
+    stated = pick(128, None) or min(rows, key=lambda x: x["us_per_step"])
     fastest = min(rows, key=lambda x: x["us_per_step"])
     return {"workload": "chunked prefill: 8 x 2048-row causal chunks after prefixes log-uniform in [8K, 128K] "
                         f"({prefix}), GQA 64q/8kv, d=128, bf16 Q/K/V, q tile {stated['q_tile']} x KV tile 512, "
@@ -823,7 +828,8 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true", help="skip the chunked-prefill report")
     ap.add_argument("--prefill-workers", default="64")
     ap.add_argument("--prefill-q-tiles", default="128,256", help="query rows per prefill unit (128 and/or 256)")
-    ap.add_argument("--prefill-pv", default="exact,fp16", help="prefill P.V paths to time: exact and/or fp16")
+    ap.add_argument("--prefill-pv", default="checked,exact,fp16",
+                    help="prefill P.V paths to time: checked (the default), exact and/or fp16")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-claim", action="store_true", help="skip the run-time claiming comparison")
     ap.add_argument("--legs", default="uniform,long_tail,mixed_tp8",
@@ -860,7 +866,7 @@ def main() -> int:
         calibration_copy(dev)
     prefill_args = ([int(x) for x in args.prefill_workers.split(",")], args.prefill_steps, 1,
                     tuple(int(x) for x in args.prefill_q_tiles.split(",")),
-                    tuple(x.strip() == "exact" for x in args.prefill_pv.split(",")))
+                    tuple({"checked": None, "exact": True, "fp16": False}[x.strip()] for x in args.prefill_pv.split(",")))
     if args.only_prefill:
         print(json.dumps(bench_prefill(dev, *prefill_args)), flush=True)
         return 0

@@ -380,14 +380,18 @@ int attn_store_kv_chunk(const void* q_in, const void* k_in, const void* v_in,
  * written).  With causal != 0 row j sees keys [0, kv_lens[b] - q_lens[b] + j]; otherwise all keys.
  *   q_lens, q_start, kv_lens  device int32[B]
  *   map           device copy of the attn_plan_prefill map (same q_tile, kv_tile % 64 == 0)
- *   flags         P.V precision.  0 or LBSA_PREFILL_EXACT_PV (the default): V stays bf16 and P
- *                 enters as bf16 hi + lo parts (~16 significant bits), exact for every bf16 V.
- *                 LBSA_PREFILL_F16_PV (faster, ~15% on the chunked-prefill batch): V converted to
- *                 fp16 while staged and P rounded to fp16 (11 significant bits).  The conversion
- *                 rounds toward zero, so V is carried exactly only where fp16 holds every bf16
- *                 value: v = 0 and 2^-17 <= |v| <= 65504.  Below 2^-17 low bits are dropped (fp16
- *                 subnormals, spacing 2^-24), below 2^-24 V becomes 0, above 65504 it saturates to
- *                 +-65504.  For V known to lie in that range only.
+ *   flags         P.V precision.
+ *                 0 (the default): V converted to fp16 while staged and P rounded to fp16 (11
+ *                 significant bits), with every staged V value checked: a 64-key chunk holding a
+ *                 value fp16 does not carry exactly (nonzero |v| < 2^-17, |v| > 65280, inf, NaN)
+ *                 takes the exact path below instead, so V is carried exactly for every bf16 input.
+ *                 LBSA_PREFILL_EXACT_PV: V stays bf16 and P enters as bf16 hi + lo parts (~16
+ *                 significant bits), for every chunk (~15-20% slower than 0 on N(0,1) inputs).
+ *                 LBSA_PREFILL_F16_PV: the fp16 path with no check (~10% faster than 0).  The
+ *                 conversion rounds toward zero, so V is carried exactly only where fp16 holds every
+ *                 bf16 value: v = 0 and 2^-17 <= |v| <= 65504.  Below 2^-17 low bits are dropped
+ *                 (fp16 subnormals, spacing 2^-24), below 2^-24 V becomes 0, above 65504 it
+ *                 saturates to +-65504.  For V known to lie in that range only.
  * Supported: head_dim 128, Hq/Hkv = 8, bf16, q_tile 128 (four waves of 32 rows per workgroup,
  * 256 threads) or 256 (eight waves, 512 threads), page_size a multiple of 64.  The map must come
  * from attn_plan_prefill with the same q_tile and num_workers (a map of another unit height or

@@ -395,11 +395,13 @@ def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                          q_lens: torch.Tensor, q_start: torch.Tensor, kv_lens: torch.Tensor, map_dev: torch.Tensor,
                          num_workers: int, num_segments: int, softmax_scale: float, part_m: torch.Tensor,
                          part_l: torch.Tensor, part_o: torch.Tensor, causal: bool = True, q_tile: int = 128,
-                         exact_pv: bool = True, stream=None) -> None:
+                         exact_pv: Optional[bool] = None, stream=None) -> None:
     """Launch the chunked-prefill split-KV kernel.  q [rows, Hq, D]; caches as in attn_splitkv;
     q_lens/q_start/kv_lens [B]; part_m/l [S, q_tile, Hq]; part_o [S, q_tile, Hq, D].
-    exact_pv: True (default) runs P.V on bf16 V with P as hi + lo bf16 parts, exact for every bf16 V;
-    False takes the faster fp16 P.V path, exact only for V = 0 and 2^-17 <= |V| <= 65504."""
+    exact_pv: None (default) runs P.V in fp16 with every staged 64-key chunk of V checked, a chunk that
+    fp16 does not hold exactly taking the bf16 path (V exact for every input); True runs every chunk
+    on bf16 V with P as hi + lo bf16 parts; False takes the unchecked fp16 path, exact only for V = 0
+    and 2^-17 <= |V| <= 65504."""
     _check_partial_sizes(q, part_m, part_l, part_o, num_segments, int(q_tile), "num_segments x q_tile")
     dev = q.device
     _need(q, torch.bfloat16, "q", dev)
@@ -419,7 +421,8 @@ def attn_splitkv_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
                                     block_table.shape[1], P, _dptr(q_lens), _dptr(q_start), _dptr(kv_lens),
                                     _dptr(map_dev), num_workers, num_segments, B, Hq, Hkv, D, page, q_tile,
                                     int(bool(causal)), float(softmax_scale), _dptr(part_m), _dptr(part_l),
-                                    _dptr(part_o), PREFILL_EXACT_PV if exact_pv else PREFILL_F16_PV,
+                                    _dptr(part_o),
+                                    0 if exact_pv is None else (PREFILL_EXACT_PV if exact_pv else PREFILL_F16_PV),
                                     _stream(stream))
     _check(st, "attn_splitkv_prefill")
 

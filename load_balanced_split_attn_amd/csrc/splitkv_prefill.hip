@@ -60,14 +60,18 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 // Tuning knobs (compile-time):
 //
 // P.V precision (runtime, template parameter PV):
-//   kPvExact (default) bf16 V with P split into bf16 hi + lo parts (two MFMAs, ~16 significant
-//            bits): exact for every bf16 V.
-//   kPvF16   (opt-in, faster) each chunk's V^T is converted to fp16 once, in LDS, by the workgroup
-//            (each thread its own copied granules, before the chunk's barrier) and P is rounded to
-//            fp16 (11 significant bits); the products run on v_mfma_f32_16x16x32_f16.  The
-//            conversion rounds toward zero: exact for v = 0 and 2^-17 <= |v| <= 65504 (every bf16
-//            value there has at most fp16's bits); smaller magnitudes lose low bits in fp16's
-//            subnormals and vanish below 2^-24, larger ones saturate at 65504.
+//   kPvF16   each chunk's V^T is converted to fp16 once, in LDS, by the workgroup (each thread its
+//            own copied granules, before the chunk's barrier) and P is rounded to fp16 (11
+//            significant bits); the products run on v_mfma_f32_16x16x32_f16.  The conversion
+//            rounds toward zero: exact for v = 0 and 2^-17 <= |v| <= 65504 (every bf16 value there
+//            has at most fp16's bits); smaller magnitudes lose low bits in fp16's subnormals and
+//            vanish below 2^-24, larger ones saturate at 65504.
+//   kPvExact bf16 V with P split into bf16 hi + lo parts (two MFMAs, ~16 significant bits): exact
+//            for every bf16 V.
+//   kPvGuard (default) the fp16 path, except that the conversion also checks every V value of the
+//            chunk: a chunk holding any value fp16 does not carry exactly is stamped, and its P.V
+//            takes the exact path with V^T read from the cache.  V is then carried exactly for
+//            every bf16 input, at the fp16 path's speed whenever the values fit.
 //   LBSA_PREFILL_WPE     waves per SIMD the register budget is fitted to (1 or 2)
 
 #ifndef LBSA_PREFILL_WPE
@@ -75,10 +79,12 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 #endif
 
 constexpr int kPvExact = 0;
+constexpr int kPvGuard = 1;
 constexpr int kPvF16 = 2;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
@@ -238,6 +244,16 @@ void splitkv_prefill_kernel(PrefillParams p) {
     v_src[t] = ((vp >> 2) * kPD + d) * kRow + 16 * (vp & 3);
   }
 
+  // guarded fp16 P.V: stamp[stage] = running chunk number of the chunk in that stage whose V is not
+  // held exactly by fp16 (set while converting it), so that the chunk's P.V takes the exact path
+  __shared__ int stamp_mem[2];
+  volatile int* stamp = stamp_mem;
+  int gbase = 0;   // chunks staged by this workgroup in earlier segments
+  if constexpr (PV == kPvGuard) {
+    if (tid == 0) stamp[0] = stamp[1] = -1;
+    __syncthreads();
+  }
+
   for (int s = s_begin; s < s_end; ++s) {
     const int b = segs[4 * s];
     const int qt = segs[4 * s + 1];
@@ -378,7 +394,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
     // operand of the P.V products (fp16; or bf16 hi + lo parts)
     // (fp16 path: the row sums add the fp16-rounded probabilities, the very values the P.V products
     // take, two per v_dot2_f32_f16 against (1, 1) with fp32 accumulation)
-    auto exp_pack = [&](const float (&sc)[2][kColBlocks][8], u32x4 (&pf)[2][kColBlocks][2]) __attribute__((always_inline)) {
+    auto exp_pack = [&](const float (&sc)[2][kColBlocks][8], u32x4 (&pf)[2][kColBlocks][2], bool f16) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -386,7 +402,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
           float ps[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) ps[e] = fast_exp2(fmaf(sc[kb][cb][e], c, neg_mc[cb]));
-          if constexpr (PV == kPvF16) {
+          if (f16) {
             const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -410,21 +426,33 @@ void splitkv_prefill_kernel(PrefillParams p) {
       }
     };
     // one online-softmax update over the 64 scores of a chunk
-    auto softmax_chunk = [&](const float (&sc)[2][kColBlocks][8], u32x4 (&pf)[2][kColBlocks][2]) __attribute__((always_inline)) {
+    auto softmax_chunk = [&](const float (&sc)[2][kColBlocks][8], u32x4 (&pf)[2][kColBlocks][2], bool f16) __attribute__((always_inline)) {
       float mxs[kColBlocks];
       if (__builtin_amdgcn_ballot_w64(chunk_max(sc, mxs))) rescale_to(mxs);
-      exp_pack(sc, pf);
+      exp_pack(sc, pf, f16);
     };
     // O^T += V^T . P^T for the chunk in stage st
     // (vedge: the chunk holds keys outside [kv_begin, kv_end), whose V must be masked)
     auto v_edge = [&](int c0) __attribute__((always_inline)) { return (c0 < kv_begin) || (c0 + kPChunk > kv_end); };
     // O^T += V^T . P^T for 32-key block kb of the chunk in stage st
-    auto pv_block = [&](int c0, bool vedge, const uint8_t* st, int kb, const u32x4 (&pb)[kColBlocks][2]) __attribute__((always_inline)) {
+    auto pv_block = [&](int c0, bool vedge, const uint8_t* st, int kb, const u32x4 (&pb)[kColBlocks][2], bool f16) __attribute__((always_inline)) {
       const int kbase = c0 + 32 * kb;
       // V^T fragments of this 32-key block: dim 16n + r, keys kbase + 8grp .. +7
       u32x4 vf[8];
+      if (PV == kPvGuard && !f16) {
+        // the exact path of a guarded chunk: bf16 V^T straight from the cache (rare; the staged copy
+        // holds the fp16 conversion): row (32-key tile, dim) of the chunk's (page, KV head) block
+        const int pg = c0 / p.page;
+        int pid = bt_row[pg];
+        pid = min(max(pid, 0), p.num_pages - 1);
+        const uint8_t* blk = reinterpret_cast<const uint8_t*>(p.v) + ((size_t)pid * p.Hkv + g) * (size_t)block_bytes;
+        const int tile = (c0 - pg * p.page + 32 * kb) / 32;
 #pragma unroll
-      for (int n = 0; n < 8; ++n) vf[n] = lds_ld16(st, v_base[kb] + 16 * n * kVRow);
+        for (int n = 0; n < 8; ++n) vf[n] = ld16(blk + (size_t)(tile * kPD + 16 * n + r) * kRow + 16 * grp);
+      } else {
+#pragma unroll
+        for (int n = 0; n < 8; ++n) vf[n] = lds_ld16(st, v_base[kb] + 16 * n * kVRow);
+      }
       if (vedge) {
         // keys outside [kv_begin, kv_end) may hold any bits; p = 0 does not cancel a NaN
 #pragma unroll
@@ -438,7 +466,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
       }
 #pragma unroll
       for (int cb = 0; cb < kColBlocks; ++cb) {
-        if constexpr (PV == kPvF16) {
+        if (f16) {
 #pragma unroll
           for (int n = 0; n < 8; ++n) o[cb][n] = mfma16x16x32_f16(vf[n], pb[cb][0], o[cb][n]);
         } else {
@@ -451,9 +479,9 @@ void splitkv_prefill_kernel(PrefillParams p) {
       }
     };
     // O^T += V^T . P^T for the chunk in stage st
-    auto pv_chunk = [&](int c0, bool vedge, const uint8_t* st, const u32x4 (&pf)[2][kColBlocks][2]) __attribute__((always_inline)) {
-      pv_block(c0, vedge, st, 0, pf[0]);
-      pv_block(c0, vedge, st, 1, pf[1]);
+    auto pv_chunk = [&](int c0, bool vedge, const uint8_t* st, const u32x4 (&pf)[2][kColBlocks][2], bool f16) __attribute__((always_inline)) {
+      pv_block(c0, vedge, st, 0, pf[0], f16);
+      pv_block(c0, vedge, st, 1, pf[1], f16);
     };
     // the whole chunk i in one wave: S^T, softmax, P.V
     auto compute = [&](int i, const uint8_t* st) __attribute__((always_inline)) {
@@ -463,9 +491,36 @@ void splitkv_prefill_kernel(PrefillParams p) {
       float sc[2][kColBlocks][8];
       scores(c0, edge, st, 0, sc[0]);
       scores(c0, edge, st, 1, sc[1]);
-      u32x4 pf[2][kColBlocks][2];
-      softmax_chunk(sc, pf);
-      pv_chunk(c0, v_edge(c0), st, pf);
+      // P.V in fp16 on the fp16 path, and on the guarded path unless the chunk's V was stamped
+      const bool f16 = PV == kPvF16 || (PV == kPvGuard && stamp[st == stage0 ? 0 : 1] != gbase + i);
+      if (PV != kPvGuard || f16) {
+        u32x4 pf[2][kColBlocks][2];
+        softmax_chunk(sc, pf, PV != kPvExact);
+        pv_chunk(c0, v_edge(c0), st, pf, PV != kPvExact);
+      } else {
+        // exact P.V of a stamped chunk, one 32-key block at a time (hi + lo P of one block live)
+        float mxs[kColBlocks];
+        if (__builtin_amdgcn_ballot_w64(chunk_max(sc, mxs))) rescale_to(mxs);
+        const bool vedge = v_edge(c0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          u32x4 pb[kColBlocks][2];
+#pragma unroll
+          for (int cb = 0; cb < kColBlocks; ++cb) {
+            float ps[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ps[e] = fast_exp2(fmaf(sc[kb][cb][e], c, neg_mc[cb]));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              lsum[cb] += ps[2 * e] + ps[2 * e + 1];
+              const uint32_t hv = pack_bf16(ps[2 * e], ps[2 * e + 1]);
+              pb[cb][0][e] = hv;
+              pb[cb][1][e] = pack_bf16(ps[2 * e] - bf16_lo(hv), ps[2 * e + 1] - bf16_hi(hv));
+            }
+          }
+          pv_block(c0, vedge, st, kb, pb, false);
+        }
+      }
     };
 
 
@@ -473,14 +528,28 @@ void splitkv_prefill_kernel(PrefillParams p) {
     // fragments mask them); on the fp16 path the values are converted to fp16 in place.  Each
     // thread converts the granules its own buffer->LDS loads wrote, so only its own loads need to
     // have landed.
-    auto to_f16 = [&](uint8_t* st) __attribute__((always_inline)) {
+    auto to_f16 = [&](uint8_t* st, int chunk) __attribute__((always_inline)) {
+      // guarded path: the largest and the smallest nonzero |v| as packed 16-bit bf16 patterns
+      u16x2 mx = {0, 0}, mn = {0xffff, 0xffff};
 #pragma unroll
       for (int t = 0; t < Shape::kTpw; ++t) {
         u32x4* gp = reinterpret_cast<u32x4*>(st + kKBytes + 1024 * (Shape::kTpw * wave + t) + 16 * lane);
         u32x4 x = *gp;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = bf16x2_to_f16x2(x[e]);
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (PV == kPvGuard) {
+            const u16x2 a = __builtin_bit_cast(u16x2, x[e] & 0x7fff7fffu);
+            mx = __builtin_elementwise_max(mx, a);
+            mn = __builtin_elementwise_min(mn, a - (u16x2){1, 1});   // |v| = 0 wraps to 0xffff
+          }
+          x[e] = bf16x2_to_f16x2(x[e]);
+        }
         *gp = x;
+      }
+      if constexpr (PV == kPvGuard) {
+        // fp16 holds every bf16 value v = 0 or 2^-17 <= |v| <= 65280 (bf16 0x3700 .. 0x477f) exactly
+        const bool bad = mx[0] > 0x477f || mx[1] > 0x477f || mn[0] < 0x36ff || mn[1] < 0x36ff;
+        if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) stamp[st == stage0 ? 0 : 1] = gbase + chunk;
       }
     };
     // one pipeline step: start chunk i+1's DMA into the other stage (last read by chunk i-1,
@@ -491,29 +560,32 @@ void splitkv_prefill_kernel(PrefillParams p) {
       const bool more = i + 1 < n_chunks;
       if (more) dma(i + 1, ahead);
       compute(i, cur);
-      if constexpr (PV == kPvF16) {
+      if constexpr (PV != kPvExact) {
         if (more) {
           LBSA_WAIT_VM_LGKM(0, 15);
-          to_f16(ahead);
+          to_f16(ahead, i + 1);
         }
       }
       LBSA_WAIT_VM_LGKM(0, 0);
       __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");   // the stamps and staged chunks read after the barrier stay after it
     };
 
     if (n_chunks > 0) {
       dma(0, stage0);
-      if constexpr (PV == kPvF16) {
+      if constexpr (PV != kPvExact) {
         LBSA_WAIT_VM_LGKM(0, 15);
-        to_f16(stage0);
+        to_f16(stage0, 0);
       }
       LBSA_WAIT_VM_LGKM(0, 0);
       __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
       for (int i = 0; i < n_chunks; i += 2) {
         step(i, stage0, stage1);
         if (i + 1 >= n_chunks) break;
         step(i + 1, stage1, stage0);
       }
+      gbase += n_chunks;
     }
 
     // write the partials of this wave's rows (rows past the chunk's end are not stored)
@@ -594,15 +666,17 @@ extern "C" int attn_splitkv_prefill(const void* q, const void* k_cache, const vo
   const int64_t pairs = (int64_t)num_workers * num_kv_heads;
   const int64_t grid = ((pairs + 7) / 8) * 8 * 8;
   if (grid > INT32_MAX) return LBSA_ERR_INVALID;
-  const bool exact = !(flags & LBSA_PREFILL_F16_PV);
+  const int mode = (flags & LBSA_PREFILL_EXACT_PV) ? kPvExact : (flags & LBSA_PREFILL_F16_PV) ? kPvF16 : kPvGuard;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const unsigned g = (unsigned)grid;
   if (q_tile == 128) {
-    if (exact) launch_prefill<kPvExact, 4>(g, st, p);
-    else launch_prefill<kPvF16, 4>(g, st, p);
+    if (mode == kPvExact) launch_prefill<kPvExact, 4>(g, st, p);
+    else if (mode == kPvF16) launch_prefill<kPvF16, 4>(g, st, p);
+    else launch_prefill<kPvGuard, 4>(g, st, p);
   } else {
-    if (exact) launch_prefill<kPvExact, 8>(g, st, p);
-    else launch_prefill<kPvF16, 8>(g, st, p);
+    if (mode == kPvExact) launch_prefill<kPvExact, 8>(g, st, p);
+    else if (mode == kPvF16) launch_prefill<kPvF16, 8>(g, st, p);
+    else launch_prefill<kPvGuard, 8>(g, st, p);
   }
   return hipGetLastError() == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;
 }

@@ -3,8 +3,9 @@
 Prefill units are 256-row (or 128-row) blocks of each request's query chunk; their 512-token KV tiles are packed
 onto workers by the same greedy equal-budget planner as decode ([P3] "Hy3 Preview AI Infra 推理优化
 精读笔记" §3.1 方案), then the split-KV kernel and the combine kernel run on the current stream.
-exact_pv=True (default) keeps P.V exact for every bf16 V; False takes the faster fp16 P.V path,
-exact only for V = 0 and 2^-17 <= |V| <= 65504.
+P.V precision (exact_pv): None (default) runs fp16 P.V on checked chunks of V, falling back to
+bf16 V for a chunk fp16 does not hold exactly; True always bf16 V with hi + lo P; False the
+unchecked fp16 path, exact only for V = 0 and 2^-17 <= |V| <= 65504.
 """
 
 from __future__ import annotations
@@ -21,12 +22,12 @@ Q_TILE = 256   # rows per unit: eight waves of 32 rows share each staged K/V chu
 class PrefillStep:
     def __init__(self, q_lens: Sequence[int], kv_lens: Sequence[int], device, num_workers: int = 128,
                  kv_tile: int = 512, causal: bool = True, num_q_heads: int = 64, head_dim: int = 128,
-                 exact_pv: bool = True, q_tile: int = Q_TILE):
+                 exact_pv: Optional[bool] = None, q_tile: int = Q_TILE):
         device = torch.device(device)
         self.q_lens_host = [int(x) for x in q_lens]
         self.kv_lens_host = [int(x) for x in kv_lens]
         self.causal = bool(causal)
-        self.exact_pv = bool(exact_pv)
+        self.exact_pv = None if exact_pv is None else bool(exact_pv)
         if q_tile not in (128, 256):
             raise ValueError("q_tile must be 128 or 256 (32 rows per wave, 4 or 8 waves)")
         self.q_tile = q_tile

@@ -89,7 +89,7 @@ def test_mtp_page_sizes(lb, page, fp8):
         assert_close(got[starts[b]:starts[b] + wl.q_lens[b]], r, f"page {page} request {b}")
 
 
-@pytest.mark.parametrize("exact_pv", [False, True])
+@pytest.mark.parametrize("exact_pv", [None, False, True])
 @pytest.mark.parametrize("page", [128, 256])
 def test_prefill_page_sizes(page, exact_pv):
     from load_balanced_split_attn_amd.prefill import PrefillStep

@@ -13,7 +13,7 @@ from oracle.plan import ref_plan_prefill
 pytestmark = pytest.mark.gpu
 
 
-def _run(wl, W, causal=True, inputs=None, poison=False, kv_tile=512, exact_pv=True, q_tile=256):
+def _run(wl, W, causal=True, inputs=None, poison=False, kv_tile=512, exact_pv=None, q_tile=256):
     from load_balanced_split_attn_amd.prefill import PrefillStep
     q, kc, vc, bt = inputs if inputs is not None else prefill_inputs(wl, pad_value=float("nan"))
     step = PrefillStep(wl.q_lens, wl.kv_lens, q.device, num_workers=W, causal=causal, kv_tile=kv_tile,
@@ -38,7 +38,7 @@ def _check_all(wl, got, causal=True):
 
 
 @pytest.mark.parametrize("q_tile", [256, 128])
-@pytest.mark.parametrize("exact_pv", [False, True])
+@pytest.mark.parametrize("exact_pv", [None, False, True])
 @pytest.mark.parametrize("seed,batch,max_prefix,max_chunk,W", [
     (0, 3, 1500, 300, 3), (1, 4, 700, 200, 1), (2, 2, 3000, 260, 8), (3, 5, 100, 140, 16),
 ])
@@ -67,7 +67,7 @@ def test_no_prefix_is_textbook_causal():
     _check_all(wl, got)
 
 
-@pytest.mark.parametrize("exact_pv", [False, True])
+@pytest.mark.parametrize("exact_pv", [None, False, True])
 def test_segment_boundary_inside_a_wave(exact_pv):
     """Regression: a 128-row chunk after a 1000-token prefix sees keys up to 1000..1127, so the
     worker boundary at key 1024 (three 512-key tiles, one per worker) falls inside the rows of the
@@ -150,10 +150,11 @@ def full_prefill():
     return wl, prefill_inputs(wl, pad_value=float("nan")), rows, sampled, full
 
 
-@pytest.mark.parametrize("q_tile,exact_pv", [(128, True), (256, True), (128, False), (256, False)])
+@pytest.mark.parametrize("q_tile,exact_pv", [(128, None), (256, None), (128, True), (256, True), (128, False),
+                                             (256, False)])
 def test_full_size_prefill(full_prefill, q_tile, exact_pv):
     """The chunked-prefill batch (8 x 2048-row chunks after log-uniform [8K, 128K] prefixes) in each
-    launch configuration the bench times (64 workers; 128- or 256-row units; exact or fp16 P.V):
+    launch configuration the bench times (64 workers; 128- or 256-row units; checked-fp16, exact or fp16 P.V):
     every row of the two shortest-prefix requests and sampled rows of the others against the fp64
     oracle."""
     wl, inputs, rows, sampled, full = full_prefill

@@ -96,7 +96,7 @@ def test_prefill_sweep(seed):
     q_tile = int(g.choice([128, 256]))
     kv_tile = int(g.choice([64, 256, 512]))
     page = int(g.choice([64, 128]))
-    exact_pv = bool(g.random() < 0.5)
+    exact_pv = [None, True, False][int(g.integers(0, 3))]
     causal = bool(g.random() < 0.75)
     note(f"prefill sweep {seed}: q={wl.q_lens} kv={wl.kv_lens} W={W} q_tile={q_tile} kv_tile={kv_tile} "
          f"page={page} exact_pv={exact_pv} causal={causal}")

@@ -201,7 +201,7 @@ def _run_prefill(lb, wl, W, q_tile, exact_pv, kvs, q_rows, replay=True):
 
 
 @pytest.mark.parametrize("q_tile", [128, 256])
-@pytest.mark.parametrize("exact_pv", [True, False])
+@pytest.mark.parametrize("exact_pv", [None, True, False])
 @pytest.mark.parametrize("profile", PEAKED)
 def test_prefill_rescale(lb, profile, exact_pv, q_tile):
     wl = WL.random_prefill(41, 3, 2500, 300)
@@ -286,5 +286,36 @@ def test_prefill_f16_value_range(lb, profile, q_tile):
     for b in range(wl.batch):
         v = kvs[b][1] if profile in ("vlow", "vhigh") else _as_fp16_pv(kvs[b][1])
         ref = ref_attention(q_rows[b], kvs[b][0], v, SCALE, causal=True)
+        assert_close(got[starts[b]:starts[b] + wl.q_lens[b]], ref, f"{profile} request {b}",
+                     max_abs=1e-2 * float(np.max(np.abs(ref))))
+
+
+@pytest.mark.parametrize("q_tile", [128, 256])
+@pytest.mark.parametrize("profile", ["vsmall", "vlarge", "vlow", "vhigh", "outlier"])
+def test_prefill_checked_value_range(lb, profile, q_tile):
+    """The default P.V path (fp16 on checked chunks, bf16 for a chunk fp16 does not hold exactly)
+    carries V exactly for every input: V scaled by 1e-6, 1e5, 2^-10, 2^13, and N(0, 1) values with a
+    single 1e5 among them, each against the oracle on V itself (not on V as fp16 would hold it)."""
+    wl = WL.random_prefill(42, 3, 2500, 300)
+    if profile == "outlier":
+        base = wl.kv
+
+        def kv(b, base=base):
+            k, v = base(b)
+            if b == 1:
+                v = v.clone()
+                v[700, 3, 17] = 1e5
+            return k, v
+
+        wl.kv = kv
+    else:
+        wl.profile = profile
+    note(f"prefill checked P.V value range {profile} q_tile={q_tile}")
+    q_rows = [wl.q(b).double().numpy() for b in range(wl.batch)]
+    kvs = _host_kv(wl, False)
+    got, _ = _run_prefill(lb, wl, 5, q_tile, None, kvs, q_rows, replay=False)
+    starts = q_starts(wl)
+    for b in range(wl.batch):
+        ref = ref_attention(q_rows[b], kvs[b][0], kvs[b][1], SCALE, causal=True)
         assert_close(got[starts[b]:starts[b] + wl.q_lens[b]], ref, f"{profile} request {b}",
                      max_abs=1e-2 * float(np.max(np.abs(ref))))
