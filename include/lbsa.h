@@ -383,8 +383,9 @@ int attn_store_kv_chunk(const void* q_in, const void* k_in, const void* v_in,
  *   flags         P.V precision.
  *                 0 (the default): V converted to fp16 while staged and P rounded to fp16 (11
  *                 significant bits), with every staged V value checked: a 64-key chunk holding a
- *                 value fp16 does not carry exactly (nonzero |v| < 2^-17, |v| > 65280, inf, NaN)
- *                 takes the exact path below instead, so V is carried exactly for every bf16 input.
+ *                 value outside 2^-17 <= |v| <= 65280 (where fp16 carries bf16 exactly; inf, NaN
+ *                 and exact zeros included) takes the exact path below instead, so V is carried
+ *                 exactly for every bf16 input.
  *                 LBSA_PREFILL_EXACT_PV: V stays bf16 and P enters as bf16 hi + lo parts (~16
  *                 significant bits), for every chunk (~15-20% slower than 0 on N(0,1) inputs).
  *                 LBSA_PREFILL_F16_PV: the fp16 path with no check (~10% faster than 0).  The

@@ -69,9 +69,10 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 //   kPvExact bf16 V with P split into bf16 hi + lo parts (two MFMAs, ~16 significant bits): exact
 //            for every bf16 V.
 //   kPvGuard (default) the fp16 path, except that the conversion also checks every V value of the
-//            chunk: a chunk holding any value fp16 does not carry exactly is stamped, and its P.V
-//            takes the exact path with V^T read from the cache.  V is then carried exactly for
-//            every bf16 input, at the fp16 path's speed whenever the values fit.
+//            chunk: a chunk holding any value outside 2^-17 <= |v| <= 65280 (where fp16 carries
+//            bf16 exactly; exact zeros are sent along with them) is stamped, and its P.V takes the
+//            exact path with V^T read from the cache.  V is then carried exactly for every bf16
+//            input, at the fp16 path's speed whenever the values fit.
 //   LBSA_PREFILL_WPE     waves per SIMD the register budget is fitted to (1 or 2)
 
 #ifndef LBSA_PREFILL_WPE
@@ -529,8 +530,8 @@ void splitkv_prefill_kernel(PrefillParams p) {
     // thread converts the granules its own buffer->LDS loads wrote, so only its own loads need to
     // have landed.
     auto to_f16 = [&](uint8_t* st, int chunk) __attribute__((always_inline)) {
-      // guarded path: the largest and the smallest nonzero |v| as packed 16-bit bf16 patterns
-      u16x2 mx = {0, 0}, mn = {0xffff, 0xffff};
+      // guarded path: the largest (|v| - 2^-17) as packed 16-bit bf16 patterns, wrapping below 2^-17
+      u16x2 mx = {0, 0};
 #pragma unroll
       for (int t = 0; t < Shape::kTpw; ++t) {
         u32x4* gp = reinterpret_cast<u32x4*>(st + kKBytes + 1024 * (Shape::kTpw * wave + t) + 16 * lane);
@@ -539,16 +540,17 @@ void splitkv_prefill_kernel(PrefillParams p) {
         for (int e = 0; e < 4; ++e) {
           if constexpr (PV == kPvGuard) {
             const u16x2 a = __builtin_bit_cast(u16x2, x[e] & 0x7fff7fffu);
-            mx = __builtin_elementwise_max(mx, a);
-            mn = __builtin_elementwise_min(mn, a - (u16x2){1, 1});   // |v| = 0 wraps to 0xffff
+            mx = __builtin_elementwise_max(mx, a - (u16x2){0x3700, 0x3700});
           }
           x[e] = bf16x2_to_f16x2(x[e]);
         }
         *gp = x;
       }
       if constexpr (PV == kPvGuard) {
-        // fp16 holds every bf16 value v = 0 or 2^-17 <= |v| <= 65280 (bf16 0x3700 .. 0x477f) exactly
-        const bool bad = mx[0] > 0x477f || mx[1] > 0x477f || mn[0] < 0x36ff || mn[1] < 0x36ff;
+        // fp16 holds every bf16 value with 2^-17 <= |v| <= 65280 (bf16 0x3700 .. 0x477f) exactly:
+        // |v| - 0x3700 lands in 0 .. 0x107f for those and above it for any other value, 0 included
+        // (one comparison per value; a chunk holding an exact 0 takes the exact path too)
+        const bool bad = mx[0] > 0x107f || mx[1] > 0x107f;
         if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) stamp[st == stage0 ? 0 : 1] = gbase + chunk;
       }
     };
