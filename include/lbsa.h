@@ -75,6 +75,12 @@ extern "C" {
 #define LBSA_ERR_CAPACITY (-2)    /* map buffer too small; *map_words_out holds the size needed */
 #define LBSA_ERR_UNSUPPORTED (-3) /* a shape the kernels are not built for (see each call)     */
 #define LBSA_ERR_HIP (-4)         /* HIP runtime error at launch                              */
+/* the same codes under the attn_ prefix of the entry points */
+#define ATTN_OK LBSA_OK
+#define ATTN_ERR_INVALID LBSA_ERR_INVALID
+#define ATTN_ERR_CAPACITY LBSA_ERR_CAPACITY
+#define ATTN_ERR_UNSUPPORTED LBSA_ERR_UNSUPPORTED
+#define ATTN_ERR_HIP LBSA_ERR_HIP
 
 #define LBSA_MAP_VERSION 1
 #define LBSA_MAP_HEADER_WORDS 8
@@ -367,6 +373,24 @@ int attn_store_kv_chunk(const void* q_in, const void* k_in, const void* v_in,
                         const int32_t* block_table, int32_t block_table_stride, int32_t num_pages,
                         int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                         int32_t page_size, void* stream);
+
+/*
+ * KV-cache layout conversion between the token-major paged layout (each (page, KV head) block is
+ * page_size rows of head_dim elements: a cache [num_pages, num_kv_heads, page_size, head_dim], the
+ * layout most paged caches keep) and the blocked layout above that the attention kernels read.
+ *   direction 0: src token-major -> dst blocked;  1: src blocked -> dst token-major
+ *   kv_dtype  LBSA_KV_BF16 (2-byte elements) or LBSA_KV_FP8_E4M3 (1-byte codes, converted as bytes)
+ *   src_k, src_v, dst_k, dst_v  device, 16-byte aligned, num_pages * num_kv_heads * page_size *
+ *             head_dim elements each; dst must not overlap src (out of place)
+ * Launches num_pages x num_kv_heads x page_size / 64 workgroups of 256 threads (one 64-token slice
+ * of one block each: K as a permutation of 16-byte pieces, V transposed through LDS).
+ * Errors: LBSA_ERR_INVALID (NULL or misaligned pointers, overlapping src and dst, unknown kv_dtype
+ * or direction, negative sizes), LBSA_ERR_UNSUPPORTED (head_dim != 128, page_size not a multiple of
+ * 64), LBSA_ERR_HIP.
+ */
+int attn_kv_layout(const void* src_k, const void* src_v, void* dst_k, void* dst_v, int32_t num_pages,
+                   int32_t num_kv_heads, int32_t page_size, int32_t head_dim, int32_t kv_dtype,
+                   int32_t direction, void* stream);
 
 /*
  * Split-KV chunked-prefill kernel over a cached prefix (the greedy map of attn_plan_prefill

@@ -19,7 +19,7 @@ __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill", "attn_plan_device",
     "attn_plan_lpt", "attn_plan_weighted",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
-    "attn_combine", "attn_store_kv", "attn_store_kv_chunk", "attn_decode_noalloc", "attn_splitkv_claimed", "NOALLOC_SCRATCH_BYTES",
+    "attn_combine", "attn_store_kv", "attn_store_kv_chunk", "attn_kv_layout", "attn_decode_noalloc", "attn_splitkv_claimed", "NOALLOC_SCRATCH_BYTES",
     "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
 ]
 
@@ -64,6 +64,8 @@ _SIGNATURES = {
     "attn_splitkv_claimed": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
                                             _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                             ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]),
+    "attn_kv_layout": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                      _c_vp]),
     "attn_store_kv_chunk": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, ctypes.c_float, _c_vp, _c_vp, _c_vp,
                                            _c_i32, ctypes.c_float, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp,
                                            _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_vp]),
@@ -512,6 +514,31 @@ def attn_store_kv_chunk(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tens
                                    _dptr(v_cache), KV_FP8_E4M3 if fp8 else KV_BF16, _dptr(ks), _dptr(vs),
                                    _dptr(block_table), block_table.shape[1], P, B, Hq, Hkv, D, page, _stream(stream))
     _check(st, "attn_store_kv_chunk")
+
+
+def attn_kv_layout(src_k: torch.Tensor, src_v: torch.Tensor, dst_k: torch.Tensor, dst_v: torch.Tensor,
+                   to_blocked: bool = True, stream=None) -> None:
+    """Convert a paged KV cache between the token-major layout [P, Hkv, page, D] and the blocked layout
+    the attention kernels read ([P, Hkv, D/w, page, w] and [P, Hkv, page/w, D, w]); to_blocked=False
+    converts back.  bf16 or uint8 (E4M3 codes); out of place."""
+    tm, bl = (src_k, dst_k) if to_blocked else (dst_k, src_k)
+    dev = src_k.device
+    dtype = src_k.dtype
+    for name, t in (("src_k", src_k), ("src_v", src_v), ("dst_k", dst_k), ("dst_v", dst_v)):
+        _need(t, dtype, name, dev)
+    if dtype not in (torch.bfloat16, torch.uint8) or tm.dim() != 4:
+        raise ValueError("token-major caches: bf16 or uint8 [P, Hkv, page, D]")
+    P, Hkv, page, D = tm.shape
+    want_k = (P, Hkv, D // (64 // tm.element_size()), page, 64 // tm.element_size())
+    want_v = (P, Hkv, page // (64 // tm.element_size()), D, 64 // tm.element_size())
+    bl_v = dst_v if to_blocked else src_v
+    tm_v = src_v if to_blocked else dst_v
+    if tuple(bl.shape) != want_k or tuple(bl_v.shape) != want_v or tuple(tm_v.shape) != tuple(tm.shape):
+        raise ValueError(f"blocked caches must be {want_k} / {want_v} for a token-major {tuple(tm.shape)}")
+    st = lib().attn_kv_layout(_dptr(src_k), _dptr(src_v), _dptr(dst_k), _dptr(dst_v), P, Hkv, page, D,
+                              KV_FP8_E4M3 if dtype == torch.uint8 else KV_BF16, 0 if to_blocked else 1,
+                              _stream(stream))
+    _check(st, "attn_kv_layout")
 
 
 def attn_combine(part_m: torch.Tensor, part_l: torch.Tensor, part_o: torch.Tensor, map_dev: torch.Tensor,

@@ -17,7 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblbsa.so")
 
-SOURCES = ["plan.cpp", "plan_device.hip", "splitkv_decode.hip", "splitkv_prefill.hip", "combine.hip", "store_kv.hip", "probe.hip"]
+SOURCES = ["plan.cpp", "plan_device.hip", "splitkv_decode.hip", "splitkv_prefill.hip", "combine.hip", "store_kv.hip",
+           "layout.hip", "probe.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",
