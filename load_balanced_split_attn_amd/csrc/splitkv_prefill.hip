@@ -83,14 +83,9 @@ constexpr int kPvExact = 0;
 constexpr int kPvGuard = 1;
 constexpr int kPvF16 = 2;
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ f32x4 mfma16x16x32_f16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
-                                                0, 0);
-}
 
 // two bf16 values (one dword) -> two fp16 values, round toward zero: exact for 0 and
 // 2^-17 <= |v| <= 65504; below that the fp16 subnormal spacing (2^-24) truncates, above it the value
