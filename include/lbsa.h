@@ -417,8 +417,8 @@ int attn_kv_layout(const void* src_k, const void* src_v, void* dst_k, void* dst_
  *                 bf16 value: v = 0 and 2^-17 <= |v| <= 65504.  Below 2^-17 low bits are dropped
  *                 (fp16 subnormals, spacing 2^-24), below 2^-24 V becomes 0, above 65504 it
  *                 saturates to +-65504.  For V known to lie in that range only.
- * Supported: head_dim 128, Hq/Hkv = 8, bf16, q_tile 128 (four waves of 32 rows per workgroup,
- * 256 threads) or 256 (eight waves, 512 threads), page_size a multiple of 64.  The map must come
+ * Supported: head_dim 128, Hq/Hkv = 8, bf16, q_tile 128 (workgroups of eight waves of 32 rows,
+ * two query heads each) or 256 (eight waves, one query head), page_size a multiple of 64.  The map must come
  * from attn_plan_prefill with the same q_tile and num_workers (a map of another unit height or
  * worker count is skipped: nothing is written).
  * Errors: LBSA_ERR_INVALID (also unknown flag bits, or both precision flags), LBSA_ERR_UNSUPPORTED,

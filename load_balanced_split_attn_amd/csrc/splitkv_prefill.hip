@@ -7,15 +7,16 @@
 // attends to a long cached prefix plus itself under a causal mask: row j of a q_len-row chunk sits at
 // position kv_len - q_len + j and sees keys [0, that position].
 //
-// gfx950 design.  Workgroup = (worker w, KV head g, query head h of the group), WAVES = 8 (or 4)
-// waves; wave v owns the 32 query rows 32v .. 32v+31 of the unit.  Each 64-key chunk of K and V
-// (blocked cache layout) goes from HBM straight into LDS with buffer->LDS loads (no registers), in
-// XOR-swizzled layouts that the MFMA fragment reads take without bank conflicts, and is read by
-// every wave: 256 (128) query rows per K/V load, so the staging and the fp16 conversion of V are
-// shared by all of them; the eight query heads of a KV head run as eight workgroups on one XCD so
-// K/V come from one L2.  Two 32 KiB LDS stages (the next chunk streams in while the current one is
-// computed) and a register budget of 256 give two waves per SIMD (one 8-wave workgroup or two
-// 4-wave ones per CU), so one wave's softmax VALU work can overlap another wave's MFMAs.
+// gfx950 design.  Workgroup = (worker w, KV head g, HPW query heads of the group), 8 waves, each
+// owning 32 query rows of one head: 256-row units run one head per workgroup (wave v has rows
+// 32v .. 32v+31), 128-row units two heads (waves 0-3 the first, 4-7 the second).  Each 64-key chunk
+// of K and V (blocked cache layout) goes from HBM straight into LDS with buffer->LDS loads (no
+// registers), in XOR-swizzled layouts that the MFMA fragment reads take without bank conflicts, and
+// is read by every wave: 256 (query row, head) columns per K/V load at either unit height, so the
+// staging and the fp16 conversion of V are shared by all of them; the workgroups covering the eight
+// query heads of a KV head run on one XCD so K/V come from one L2.  Two 32 KiB LDS stages (the next
+// chunk streams in while the current one is computed) and a register budget of 256 give two waves
+// per SIMD (one workgroup per CU), so one wave's softmax VALU work can overlap another wave's MFMAs.
 // Per wave, with the query rows as the MFMA columns:
 //   S^T (keys x rows) = K . Q^T       v_mfma_f32_16x16x32_bf16, Q^T fragments held in VGPRs
 //   O^T (dims x rows) += V^T . P^T    fp16 operands (V converted in LDS), or bf16 with P as
@@ -48,7 +49,7 @@ struct PrefillParams {
 constexpr int kPD = 128;          // head dim
 constexpr int kRow = 64;          // bytes per row of the blocked cache layout
 constexpr int kPChunk = 64;       // keys per staged chunk
-constexpr int kMaxQTile = 256;    // query rows per unit: 32 per wave, 4 or 8 waves
+constexpr int kMaxQTile = 256;    // query rows per unit: 32 per wave, 4 or 8 waves per query head
 constexpr int kColBlocks = 2;     // 16-row column blocks per wave (32 rows)
 constexpr int kKRow = kPD * 2;             // LDS bytes per key row of K (16 granules, XOR-swizzled)
 constexpr int kVRow = kPChunk * 2;         // LDS bytes per dim row of V^T (8 granules, XOR-swizzled)
@@ -162,16 +163,18 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;
 
 // Unit height and DMA share of a workgroup of WAVES waves (a struct, not function-local constants:
 // the host pass of the kernel template needs them as constant expressions).
-template <int WAVES>
+template <int WAVES, int HPW>
 struct PrefillShape {
-  static constexpr int kQTile = 32 * WAVES;   // query rows per unit
-  static constexpr int kTpw = 16 / WAVES;     // 1 KiB DMA slots per wave in each half of a stage
+  static constexpr int kWavesPerHead = WAVES / HPW;
+  static constexpr int kQTile = 32 * kWavesPerHead;   // query rows per unit
+  static constexpr int kTpw = 16 / WAVES;             // 1 KiB DMA slots per wave in each half of a stage
+  static constexpr int kGroups = 8 / HPW;             // workgroups per (worker, KV head)
 };
 
-template <int PV, int WAVES>
+template <int PV, int WAVES, int HPW = 1>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(LBSA_PREFILL_WPE, LBSA_PREFILL_WPE)))
 void splitkv_prefill_kernel(PrefillParams p) {
-  using Shape = PrefillShape<WAVES>;
+  using Shape = PrefillShape<WAVES, HPW>;
   // the pipeline stages, separate objects so the compiler can tell their DMA writes apart
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
@@ -181,19 +184,20 @@ void splitkv_prefill_kernel(PrefillParams p) {
   const int r = lane & 15;
   const int grp = lane >> 4;
 
-  // block -> (worker, KV head, query head of the group); the eight workgroups of one
+  // block -> (worker, KV head, query heads of the group); the 8 / HPW workgroups of one
   // (worker, KV head) land on the same XCD (dispatch is round-robin over 8 XCDs) and are
   // dispatched together, so the K/V they share comes from one L2
   const int f = blockIdx.x;
   const int xcd = f & 7;
   const int kq = f >> 3;
-  const int hq = kq & 7;
-  const int wg_index = (kq >> 3) * 8 + xcd;      // (w * Hkv + g)
+  const int hq = kq % Shape::kGroups;
+  const int wg_index = (kq / Shape::kGroups) * 8 + xcd;      // (w * Hkv + g)
   const int w = wg_index / p.Hkv;
   const int g = wg_index - w * p.Hkv;
   if (w >= p.W) return;
-  const int h = g * 8 + hq;                        // query head of this workgroup
-  const int rbase = 32 * wave;                     // first row (inside the unit) of this wave
+  // query head of this wave (a workgroup runs HPW query heads of the group, WAVES / HPW waves each)
+  const int h = g * 8 + hq * HPW + wave / Shape::kWavesPerHead;
+  const int rbase = 32 * (wave % Shape::kWavesPerHead);   // first row (inside the unit) of this wave
 
   const_i32* map = (const_i32*)p.map;
   if (map[0] != LBSA_MAP_VERSION) return;   // a device-built map that reported an error
@@ -607,9 +611,9 @@ void splitkv_prefill_kernel(PrefillParams p) {
   }
 }
 
-template <int PV, int WAVES>
+template <int PV, int WAVES, int HPW = 1>
 void launch_prefill(unsigned grid, hipStream_t stream, const PrefillParams& p) {
-  hipLaunchKernelGGL((splitkv_prefill_kernel<PV, WAVES>), dim3(grid), dim3(64 * WAVES), 0, stream, p);
+  hipLaunchKernelGGL((splitkv_prefill_kernel<PV, WAVES, HPW>), dim3(grid), dim3(64 * WAVES), 0, stream, p);
 }
 
 }  // namespace lbsa
@@ -661,15 +665,17 @@ extern "C" int attn_splitkv_prefill(const void* q, const void* k_cache, const vo
   p.scale_log2 = softmax_scale * kLog2e;
   // (worker, KV head) pairs padded to a multiple of 8, times the 8 query heads of a group
   const int64_t pairs = (int64_t)num_workers * num_kv_heads;
+  const int64_t grid128 = ((pairs + 7) / 8) * 8 * 4;   // 128-row units: two query heads per workgroup
   const int64_t grid = ((pairs + 7) / 8) * 8 * 8;
   if (grid > INT32_MAX) return LBSA_ERR_INVALID;
   const int mode = (flags & LBSA_PREFILL_EXACT_PV) ? kPvExact : (flags & LBSA_PREFILL_F16_PV) ? kPvF16 : kPvGuard;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   const unsigned g = (unsigned)grid;
   if (q_tile == 128) {
-    if (mode == kPvExact) launch_prefill<kPvExact, 4>(g, st, p);
-    else if (mode == kPvF16) launch_prefill<kPvF16, 4>(g, st, p);
-    else launch_prefill<kPvGuard, 4>(g, st, p);
+    const unsigned g2 = (unsigned)grid128;
+    if (mode == kPvExact) launch_prefill<kPvExact, 8, 2>(g2, st, p);
+    else if (mode == kPvF16) launch_prefill<kPvF16, 8, 2>(g2, st, p);
+    else launch_prefill<kPvGuard, 8, 2>(g2, st, p);
   } else {
     if (mode == kPvExact) launch_prefill<kPvExact, 8>(g, st, p);
     else if (mode == kPvF16) launch_prefill<kPvF16, 8>(g, st, p);

@@ -16,7 +16,7 @@ import torch
 
 from . import attn_combine, attn_plan_prefill, attn_splitkv_prefill, map_header, max_splits_of
 
-Q_TILE = 256   # rows per unit: eight waves of 32 rows share each staged K/V chunk (128: four waves)
+Q_TILE = 256   # rows per unit: eight waves of 32 rows share each staged K/V chunk (128: two heads per workgroup)
 
 
 class PrefillStep:
@@ -29,7 +29,7 @@ class PrefillStep:
         self.causal = bool(causal)
         self.exact_pv = None if exact_pv is None else bool(exact_pv)
         if q_tile not in (128, 256):
-            raise ValueError("q_tile must be 128 or 256 (32 rows per wave, 4 or 8 waves)")
+            raise ValueError("q_tile must be 128 or 256 (32 rows per wave, 4 or 8 waves per query head)")
         self.q_tile = q_tile
         self.map_host = attn_plan_prefill(self.q_lens_host, self.kv_lens_host, num_workers, q_tile, kv_tile,
                                           self.causal)
