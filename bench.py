@@ -134,12 +134,12 @@ def time_steps(fn_split, fn_combine, steps: int, warmup: int):
             "combine_ms": [c.elapsed_time(d) for _, _, c, d in ev]}
 
 
-def kernel_source_digest() -> str:
+def kernel_source_digest(family: str = "decode") -> str:
     from load_balanced_split_attn_amd.record_traffic import kernel_source_digest as digest
-    return digest()
+    return digest(family)
 
 
-def recorded_traffic(kernel: str, workload: str):
+def recorded_traffic(kernel: str, workload: str, family: str = "decode"):
     """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs, if they were taken on
     the current kernel source (None otherwise)."""
     path = os.path.join(ROOT, "load_balanced_split_attn_amd", "measured_traffic.json")
@@ -148,7 +148,7 @@ def recorded_traffic(kernel: str, workload: str):
             rec = json.load(f).get(kernel, {}).get(workload)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_digest") != kernel_source_digest():
+    if not rec or rec.get("source_digest") != kernel_source_digest(family):
         return None
     return rec.get("bytes_per_launch")
 
@@ -240,6 +240,16 @@ PV_LABELS = {None: "fp16 P.V on checked V chunks, bf16 hi+lo P for chunks fp16 d
              True: "bf16 V, P as bf16 hi+lo (every chunk)", False: "fp16 V and P, unchecked (V range-limited)"}
 
 
+def prefill_unique_bytes(wl, segments: int, q_tile: int) -> int:
+    """Bytes a prefill launch must move at least: Q, every request's K and V once, the partial slots
+    written (m, l and 128 output values per (row, query head), fp32)."""
+    rows = sum(wl.q_lens)
+    q_bytes = rows * wl.hq * wl.head_dim * 2
+    kv_bytes = sum(wl.kv_lens) * wl.hkv * wl.head_dim * 2 * 2
+    part_bytes = segments * q_tile * wl.hq * (wl.head_dim + 2) * 4
+    return q_bytes + kv_bytes + part_bytes
+
+
 def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256), exact_modes=(None, True, False)) -> dict:
     """Chunked prefill over cached prefixes: 8 requests x 2048-row causal chunks after prefixes drawn
     log-uniform in [8K, 128K]; q tiles of 128 or 256 rows x KV tiles of 512 on the same greedy
@@ -293,7 +303,13 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256)
             "tflops_per_step": round(flops / (stated["us_per_step"] * 1e-6) / 1e12, 1),
             "roofline": {"bound": "mfma", "kernel": "splitkv_prefill_kernel", "dtype": "bf16",
                          "achieved": stated["splitkv_tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(stated["splitkv_tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                         "frac": round(stated["splitkv_tflops"] / PEAK_BF16_TFLOPS, 4),
+                         # HBM bytes per launch from the counter runs (128-row units, checked P.V,
+                         # 64 workers, on this kernel source), beside the bytes read or written once
+                         "traffic": (recorded_traffic("splitkv_prefill_kernel", "chunked_q128_checked", "prefill")
+                                     if (stated["q_tile"], stated["exact_pv"], stated["workers"]) == (128, None, 64)
+                                     else None),
+                         "unique_bytes": prefill_unique_bytes(wl, stated["segments"], stated["q_tile"])},
             "fastest": {k: fastest[k] for k in ("q_tile", "pv", "workers", "us_per_step", "splitkv_us",
                                                  "splitkv_tflops", "frac_of_bf16_peak")},
             "sweep": rows}

@@ -1,6 +1,6 @@
 """The traffic recorder on synthetic rocprofv3 counter files: calibration by the largest copy,
 mean over the kernel's dispatches, rows of one dispatch summed, the workload's algorithmic bytes
-kept, the decode source's digest stamped."""
+kept, the decode source's digest stamped; the prefill family beside it."""
 
 import csv
 import json
@@ -55,3 +55,21 @@ def test_missing_pieces(tmp_path):
         RT.record(str(tmp_path / "f"), str(tmp_path / "w"), json_path=str(js))
     with pytest.raises(FileNotFoundError):
         RT.read_counter(str(tmp_path / "none"), "FETCH_SIZE")
+
+
+def test_record_prefill_keeps_decode(tmp_path):
+    # the prefill family rewrites only its own entry, stamped with the prefill sources' digest
+    pf = "void lbsa::splitkv_prefill_kernel<1, 8, 2>(lbsa::PrefillParams)"
+    other = "void lbsa::splitkv_prefill_kernel<1, 8, 1>(lbsa::PrefillParams)"
+    _write(tmp_path / "f", "FETCH_SIZE", [(1, COPY, 512 * 1024), (2, pf, 300.0), (3, pf, 100.0), (4, other, 7.0)])
+    _write(tmp_path / "w", "WRITE_SIZE", [(1, COPY, 1024 * 1024), (2, pf, 8.0), (3, pf, 8.0), (4, other, 1.0)])
+    js = tmp_path / "t.json"
+    decode = {"splitkv_decode_kernel": {"mixed": {"algorithmic_bytes": 111, "bytes_per_launch": 5}}}
+    js.write_text(json.dumps(decode))
+    out = RT.record(str(tmp_path / "f"), str(tmp_path / "w"), family="prefill", json_path=str(js))
+    e = out["splitkv_prefill_kernel"]["chunked_q128_checked"]
+    assert e["fetch_bytes"] == 200 * 1024 * 2 and e["write_bytes"] == 8 * 1024   # the 8-wave, 2-head launches only
+    assert e["algorithmic_bytes"] is None
+    assert e["source_digest"] == RT.kernel_source_digest("prefill") != RT.kernel_source_digest("decode")
+    assert out["splitkv_decode_kernel"] == decode["splitkv_decode_kernel"]
+    assert json.loads(js.read_text()) == out
