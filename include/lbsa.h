@@ -397,19 +397,21 @@ int attn_kv_layout(const void* src_k, const void* src_v, void* dst_k, void* dst_
  * applied to prefill units; prefix reuse as in [P3] §6: a request's new chunk attends to its
  * cached prefix and, causally, to itself).  Request b has q_lens[b] query rows stored from row
  * q_start[b] of q [rows, Hq, D]; they are the last q_lens[b] positions of a kv_lens[b]-token
- * context held in the paged caches.  Launches 8 x ceil(W x Hkv / 8) x 8 workgroups of q_tile / 32
- * waves: workgroup (w, g, h) walks worker w's segments for query head h of KV head g, 32 rows per
- * wave.  Writes, for every segment s and row i < q_tile of its unit that lies inside the chunk,
- * part_m/part_l [S, q_tile, Hq] and part_o [S, q_tile, Hq, D] (rows past the chunk are not
- * written).  With causal != 0 row j sees keys [0, kv_lens[b] - q_lens[b] + j]; otherwise all keys.
+ * context held in the paged caches.  Launches 8 x ceil(W x Hkv / 8) x (q_tile / 32) workgroups of
+ * eight waves: a workgroup walks worker w's segments for KV head g and 256 / q_tile of its query
+ * heads (one for q_tile 256, two for 128), 32 rows of one head per wave.  Writes, for every segment
+ * s and row i < q_tile of its unit that lies inside the chunk, part_m/part_l [S, q_tile, Hq] and
+ * part_o [S, q_tile, Hq, D] (rows past the chunk are not written).  With causal != 0 row j sees
+ * keys [0, kv_lens[b] - q_lens[b] + j]; otherwise all keys.
  *   q_lens, q_start, kv_lens  device int32[B]
  *   map           device copy of the attn_plan_prefill map (same q_tile, kv_tile % 64 == 0)
  *   flags         P.V precision.
- *                 0 (the default): V converted to fp16 while staged and P rounded to fp16 (11
- *                 significant bits), with every staged V value checked: a 64-key chunk holding a
- *                 value outside 2^-17 <= |v| <= 65280 (where fp16 carries bf16 exactly; inf, NaN
- *                 and exact zeros included) takes the exact path below instead, so V is carried
- *                 exactly for every bf16 input.
+ *                 0 (the default): V * 2^6 converted to fp16 while staged and P * 2^-6 rounded
+ *                 to fp16 (11 significant bits; P below 2^-8 of the reference maximum in fp16's
+ *                 subnormals, spacing 2^-18), with every staged V value checked: a 64-key chunk
+ *                 holding a value outside 2^-23 <= |v| <= 1020 (where fp16 carries bf16 * 2^6
+ *                 exactly; inf, NaN and exact zeros included) takes the exact path below instead,
+ *                 so V is carried exactly for every bf16 input.
  *                 LBSA_PREFILL_EXACT_PV: V stays bf16 and P enters as bf16 hi + lo parts (~16
  *                 significant bits), for every chunk (~15-20% slower than 0 on N(0,1) inputs).
  *                 LBSA_PREFILL_F16_PV: the fp16 path with no check (~10% faster than 0).  The

@@ -69,16 +69,21 @@ constexpr float kPRescaleSlack = 8.0f;   // log2 units
 //            vanish below 2^-24, larger ones saturate at 65504.
 //   kPvExact bf16 V with P split into bf16 hi + lo parts (two MFMAs, ~16 significant bits): exact
 //            for every bf16 V.
-//   kPvGuard (default) the fp16 path, except that the conversion also checks every V value of the
-//            chunk: a chunk holding any value outside 2^-17 <= |v| <= 65280 (where fp16 carries
-//            bf16 exactly; exact zeros are sent along with them) is stamped, and its P.V takes the
-//            exact path with V^T read from the cache.  V is then carried exactly for every bf16
-//            input, at the fp16 path's speed whenever the values fit.
+//   kPvGuard (default) the fp16 path on V * 2^6 and P * 2^-6 (the products are unchanged), except
+//            that the conversion also checks every V value of the chunk: a chunk holding any value
+//            outside 2^-23 <= |v| <= 1020 (where fp16 carries bf16 * 2^6 exactly; exact zeros are
+//            sent along with them) is stamped, and its P.V takes the exact path with V^T read from
+//            the cache.  V is then carried exactly for every bf16 input, at the fp16 path's speed
+//            whenever the values fit.  The shift centres fp16's window on activation magnitudes:
+//            unshifted, any chunk holding a |v| below 2^-17 is stamped, ~5% of the chunks of
+//            N(0, 1) V and nearly all of N(0, 0.02^2) V; shifted, ~0.1% and ~4%.
 //   LBSA_PREFILL_WPE     waves per SIMD the register budget is fitted to (1 or 2)
 
 #ifndef LBSA_PREFILL_WPE
 #define LBSA_PREFILL_WPE 2
 #endif
+
+constexpr int kGuardShift = 6;   // guarded path: V carried as V * 2^6 in fp16, P as P * 2^-6
 
 constexpr int kPvExact = 0;
 constexpr int kPvGuard = 1;
@@ -175,6 +180,8 @@ template <int PV, int WAVES, int HPW = 1>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(LBSA_PREFILL_WPE, LBSA_PREFILL_WPE)))
 void splitkv_prefill_kernel(PrefillParams p) {
   using Shape = PrefillShape<WAVES, HPW>;
+  // exponent shift of the fp16 operands: V * 2^kShift and P * 2^-kShift (guarded path only)
+  constexpr int kShift = PV == kPvGuard ? kGuardShift : 0;
   // the pipeline stages, separate objects so the compiler can tell their DMA writes apart
   __shared__ __attribute__((aligned(16))) uint8_t stage0[kStage];
   __shared__ __attribute__((aligned(16))) uint8_t stage1[kStage];
@@ -384,7 +391,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
         const float m_new = move ? mxs[cb] : m_ref[cb];
         const float alpha = move ? fast_exp2((m_ref[cb] - m_new) * c) : 1.f;
         m_ref[cb] = m_new;
-        neg_mc[cb] = move ? -m_new * c : neg_mc[cb];
+        neg_mc[cb] = move ? -m_new * c - (float)kShift : neg_mc[cb];
         lsum[cb] *= alpha;
 #pragma unroll
         for (int n = 0; n < 8; ++n) o[cb][n] *= alpha;
@@ -512,10 +519,12 @@ void splitkv_prefill_kernel(PrefillParams p) {
             for (int e = 0; e < 8; ++e) ps[e] = fast_exp2(fmaf(sc[kb][cb][e], c, neg_mc[cb]));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+              // the row sums stay in the shifted units; the bf16 V products take P itself
               lsum[cb] += ps[2 * e] + ps[2 * e + 1];
-              const uint32_t hv = pack_bf16(ps[2 * e], ps[2 * e + 1]);
+              const float p0 = ps[2 * e] * (float)(1 << kShift), p1 = ps[2 * e + 1] * (float)(1 << kShift);
+              const uint32_t hv = pack_bf16(p0, p1);
               pb[cb][0][e] = hv;
-              pb[cb][1][e] = pack_bf16(ps[2 * e] - bf16_lo(hv), ps[2 * e + 1] - bf16_hi(hv));
+              pb[cb][1][e] = pack_bf16(p0 - bf16_lo(hv), p1 - bf16_hi(hv));
             }
           }
           pv_block(c0, vedge, st, kb, pb, false);
@@ -529,7 +538,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
     // thread converts the granules its own buffer->LDS loads wrote, so only its own loads need to
     // have landed.
     auto to_f16 = [&](uint8_t* st, int chunk) __attribute__((always_inline)) {
-      // guarded path: the largest (|v| - 2^-17) as packed 16-bit bf16 patterns, wrapping below 2^-17
+      // guarded path: the largest (|v| - 2^-23) as packed 16-bit bf16 patterns, wrapping below 2^-23
       u16x2 mx = {0, 0};
 #pragma unroll
       for (int t = 0; t < Shape::kTpw; ++t) {
@@ -539,16 +548,21 @@ void splitkv_prefill_kernel(PrefillParams p) {
         for (int e = 0; e < 4; ++e) {
           if constexpr (PV == kPvGuard) {
             const u16x2 a = __builtin_bit_cast(u16x2, x[e] & 0x7fff7fffu);
-            mx = __builtin_elementwise_max(mx, a - (u16x2){0x3700, 0x3700});
+            constexpr unsigned short lo = 0x3700 - (kShift << 7);
+            mx = __builtin_elementwise_max(mx, a - (u16x2){lo, lo});
           }
-          x[e] = bf16x2_to_f16x2(x[e]);
+          // V * 2^kShift: the shift added to both exponent fields (a value outside the window,
+          // whose field could carry over, is in a stamped chunk whose fp16 copy is not used)
+          constexpr uint32_t up = (uint32_t)(kShift << 7) * 0x00010001u;
+          x[e] = bf16x2_to_f16x2(x[e] + up);
         }
         *gp = x;
       }
       if constexpr (PV == kPvGuard) {
-        // fp16 holds every bf16 value with 2^-17 <= |v| <= 65280 (bf16 0x3700 .. 0x477f) exactly:
-        // |v| - 0x3700 lands in 0 .. 0x107f for those and above it for any other value, 0 included
-        // (one comparison per value; a chunk holding an exact 0 takes the exact path too)
+        // fp16 holds every bf16 value with 2^-17 <= |v| <= 65280 (bf16 0x3700 .. 0x477f) exactly, so
+        // V * 2^6 for 2^-23 <= |v| <= 1020 (0x3400 .. 0x447f): |v| - 0x3400 lands in 0 .. 0x107f
+        // for those and above it for any other value, 0 included (one comparison per value; a
+        // chunk holding an exact 0 takes the exact path too)
         const bool bad = mx[0] > 0x107f || mx[1] > 0x107f;
         if (__builtin_amdgcn_ballot_w64(bad) && lane == 0) stamp[st == stage0 ? 0 : 1] = gbase + chunk;
       }
@@ -593,7 +607,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int cb = 0; cb < kColBlocks; ++cb) {
       const float to_true = (m_true[cb] == -INFINITY) ? 0.f : fast_exp2((m_ref[cb] - m_true[cb]) * c);
-      float l = lsum[cb] * to_true;
+      float l = lsum[cb] * (to_true * (float)(1 << kShift));   // row sums back from the shifted units
       l += xor_lane(l, 16);
       l += xor_lane(l, 32);
       const int row_in_unit = rbase + 16 * cb + r;

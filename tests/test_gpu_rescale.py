@@ -290,6 +290,49 @@ def test_prefill_f16_value_range(lb, profile, q_tile):
                      max_abs=1e-2 * float(np.max(np.abs(ref))))
 
 
+def _window_v(v: torch.Tensor, case: str, b: int) -> torch.Tensor:
+    """V for the window test: magnitudes drawn from the case's range, signs from v (bf16)."""
+    g = torch.Generator().manual_seed(1234 + b)
+    u = torch.rand(v.shape, generator=g, dtype=torch.float32)
+    sign = torch.where(v.float() < 0, -1.0, 1.0)
+    if case == "lo_in":        # [2^-23, 2^-22): the smallest magnitudes the fp16 copy holds
+        mag = 2.0 ** -23 * (1.0 + u)
+    elif case == "lo_out":     # [2^-24, 2^-23): every chunk stamped
+        mag = 2.0 ** -24 * (1.0 + u)
+    elif case == "hi_in":      # [510, 1015]: up to the largest magnitudes the fp16 copy holds
+        mag = 510.0 * (1.0 + 0.99 * u)
+    elif case == "hi_out":     # [1024, 2048): every chunk stamped
+        mag = 1024.0 * (1.0 + u)
+    else:                      # "sigma": N(0, 0.02^2), the shift's reason
+        return (v.float() * 0.02).to(torch.bfloat16)
+    return (sign * mag).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("q_tile", [128, 256])
+@pytest.mark.parametrize("case", ["lo_in", "lo_out", "hi_in", "hi_out", "sigma"])
+def test_prefill_checked_window_edges(lb, case, q_tile):
+    """The default P.V carries V * 2^6 in fp16 for 2^-23 <= |v| <= 1020 and stamps any chunk with a
+    value outside: V just inside and just outside each end of that window, and N(0, 0.02^2) V,
+    against the oracle on V itself."""
+    wl = WL.random_prefill(43, 3, 2500, 300)
+    base = wl.kv
+
+    def kv(b, base=base):
+        k, v = base(b)
+        return k, _window_v(v, case, b)
+
+    wl.kv = kv
+    note(f"prefill checked P.V window {case} q_tile={q_tile}")
+    q_rows = [wl.q(b).double().numpy() for b in range(wl.batch)]
+    kvs = _host_kv(wl, False)
+    got, _ = _run_prefill(lb, wl, 5, q_tile, None, kvs, q_rows, replay=False)
+    starts = q_starts(wl)
+    for b in range(wl.batch):
+        ref = ref_attention(q_rows[b], kvs[b][0], kvs[b][1], SCALE, causal=True)
+        assert_close(got[starts[b]:starts[b] + wl.q_lens[b]], ref, f"{case} request {b}",
+                     max_abs=1e-2 * float(np.max(np.abs(ref))))
+
+
 @pytest.mark.parametrize("q_tile", [128, 256])
 @pytest.mark.parametrize("profile", ["vsmall", "vlarge", "vlow", "vhigh", "outlier"])
 def test_prefill_checked_value_range(lb, profile, q_tile):
