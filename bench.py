@@ -236,7 +236,8 @@ def prefill_flops(wl) -> int:
     return 4 * wl.head_dim * wl.hq * total
 
 
-PV_LABELS = {None: "fp16 P.V on checked V chunks, bf16 hi+lo P for chunks fp16 does not hold (default; V exact)",
+PV_LABELS = {None: "fp16 P.V (V*2^6, P*2^-6) on checked V chunks, bf16 hi+lo P for chunks fp16 does not hold "
+                   "(default; V exact)",
              True: "bf16 V, P as bf16 hi+lo (every chunk)", False: "fp16 V and P, unchecked (V range-limited)"}
 
 
