@@ -222,8 +222,9 @@ void splitkv_prefill_kernel(PrefillParams p) {
   const float c = p.scale_log2;                 // raw score -> log2 units
   const float slack_raw = kPRescaleSlack / c;
 
-  // DMA layout: wave v fills LDS granules 64*(4v + t) + lane, t = 0..3, of the K half and of the
-  // V^T half of a stage; the lane fetches whichever global granule belongs in that swizzled slot
+  // DMA layout: wave v fills LDS granules 64*(kTpw*v + t) + lane, t < kTpw (2 with eight waves), of
+  // the K half and of the V^T half of a stage; the lane fetches whichever global granule belongs in
+  // that swizzled slot
   // LDS fragment addresses.  K: key 32kb + 4j + key0 at granule 4ks + grp; the swizzle of those keys
   // is swz(key0) for every (kb, j), so each read is k_base[ks] + (32kb + 4j) * 256.  V^T: dim
   // 16n + r at granule 4kb + grp; the swizzle depends on r only, so each read is v_base[kb] + 2048n.
@@ -311,7 +312,7 @@ void splitkv_prefill_kernel(PrefillParams p) {
     const int c_first = kv_begin & ~(kPChunk - 1);
     const int n_chunks = kv_end > c_first ? (kv_end - c_first + kPChunk - 1) / kPChunk : 0;
 
-    // chunk i -> stage: each wave issues 8 buffer->LDS loads of 1 KiB (4 of K, 4 of V^T)
+    // chunk i -> stage: each wave issues 2 * kTpw buffer->LDS loads of 1 KiB (kTpw of K, kTpw of V^T)
     auto dma = [&](int i, uint8_t* st) __attribute__((always_inline)) {
       const int c0 = c_first + kPChunk * i;
       const int pg = c0 / p.page;
