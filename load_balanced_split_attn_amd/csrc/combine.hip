@@ -139,15 +139,16 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 }
 
 // Row-wide form for units of many rows with 64 query heads (prefill): one workgroup per
-// (unit, row), thread t owns query head t / 4 and output dims 32 (t % 4) .. +31, so a slot's
-// partial row (64 heads x 128 dims, 32 KiB) and the output row are read and written as whole
-// contiguous rows, and the four threads of a head keep the same running maximum.  Two slots' loads
-// are in flight at a time.
+// (unit, row), the four waves taking heads 16w .. 16w + 15 of the row.  A slot's partial row (64
+// heads x 128 dims, 32 KiB) is read, and the output row written, with every load and store of a
+// wave covering 1 KiB of contiguous bytes: lane l's k-th float4 is dims 4 (l % 32) .. +3 of head
+// 16w + 2k + l / 32, so a lane keeps eight heads' running maxima and sums.  Two slots' loads are
+// in flight at a time.
 __global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
   const int64_t ur = blockIdx.x;   // u * R + r
   const int t = threadIdx.x;
-  const int h = t >> 2;
-  const int d0 = 32 * (t & 3);
+  const int wv = t >> 6;
+  const int lane = t & 63;
   if (ur >= (int64_t)p.U * p.R) return;
   if (p.map[0] != LBSA_MAP_VERSION && p.map[0] != LBSA_MAP_VERSION_ORDERED) return;
   const int W = p.map[2];
@@ -164,33 +165,42 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
   const int s0 = unit_ptr[u];
   const int n = unit_ptr[u + 1] - s0;
   if (s0 < 0 || n < 0 || s0 + n > p.map[4]) return;
-  auto ml_index = [&](int i) -> int64_t { return ((int64_t)(s0 + i) * p.R + r) * 64 + h; };
+  const int h0 = 16 * wv + (lane >> 5);      // head of the lane's first float4; +2 per k
+  const int q0 = 512 * wv + lane;            // float4 index of that float4 inside the row
 
-  float M = -INFINITY, L = 0.f;
+  float M[8], L[8];
   f32x4 a[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) a[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // the same branch-free online update as the per-head form, on eight float4 per slot
-  auto absorb = [&](float m, float l, const f32x4 (&o)[8]) {
-    const float Mn = fmaxf(M, m);
-    const float sc = Mn == -INFINITY ? 1.f : fast_exp2((M - Mn) * kLog2e);
-    const float w = m == -INFINITY ? 0.f : fast_exp2((m - Mn) * kLog2e);
+  for (int k = 0; k < 8; ++k) {
+    M[k] = -INFINITY;
+    L[k] = 0.f;
+    a[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // the same branch-free online update as the per-head form, per head of the lane
+  auto absorb = [&](const float (&m)[8], const float (&l)[8], const f32x4 (&o)[8]) {
 #pragma unroll
-    for (int k = 0; k < 8; ++k) a[k] = w * o[k] + a[k] * sc;
-    L = fmaf(w, l, L * sc);
-    M = Mn;
+    for (int k = 0; k < 8; ++k) {
+      const float Mn = fmaxf(M[k], m[k]);
+      const float sc = Mn == -INFINITY ? 1.f : fast_exp2((M[k] - Mn) * kLog2e);
+      const float w = m[k] == -INFINITY ? 0.f : fast_exp2((m[k] - Mn) * kLog2e);
+      a[k] = w * o[k] + a[k] * sc;
+      L[k] = fmaf(w, l[k], L[k] * sc);
+      M[k] = Mn;
+    }
   };
-  auto load = [&](int i, float& m, float& l, f32x4 (&o)[8]) {
-    const int64_t mi = ml_index(i);
-    m = p.part_m[mi];
-    l = p.part_l[mi];
-    const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o + mi * 128 + d0);
+  auto load = [&](int i, float (&m)[8], float (&l)[8], f32x4 (&o)[8]) {
+    const int64_t row = (int64_t)(s0 + i) * p.R + r;   // (slot, row) of the partials
+    const f32x4* src = reinterpret_cast<const f32x4*>(p.part_o) + row * 2048 + q0;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) o[k] = src[k];
+    for (int k = 0; k < 8; ++k) {
+      o[k] = src[64 * k];
+      m[k] = p.part_m[row * 64 + h0 + 2 * k];
+      l[k] = p.part_l[row * 64 + h0 + 2 * k];
+    }
   };
   int i = 0;
   for (; i + 1 < n; i += 2) {
-    float m0, l0, m1, l1;
+    float m0[8], l0[8], m1[8], l1[8];
     f32x4 o0[8], o1[8];
     load(i, m0, l0, o0);
     load(i + 1, m1, l1, o1);
@@ -198,24 +208,27 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
     absorb(m1, l1, o1);
   }
   if (i < n) {
-    float m0, l0;
+    float m0[8], l0[8];
     f32x4 o0[8];
     load(i, m0, l0, o0);
     absorb(m0, l0, o0);
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;   // a row with no visible key gets 0
-  const int64_t obase = (orow * 64 + h) * 128 + d0;
+  const int64_t obase = orow * 2048 + q0;   // float4 index
   if (p.out_bf16) {
-    uint32_t* dst = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.out) + obase);
+    uint2* dst = reinterpret_cast<uint2*>(p.out) + obase;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+      const float inv = L[k] > 0.f ? 1.f / L[k] : 0.f;   // a row with no visible key gets 0
       const f32x4 v = a[k] * inv;
-      *reinterpret_cast<uint2*>(dst + 2 * k) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+      dst[64 * k] = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
     }
   } else {
-    f32x4* dst = reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + obase);
+    f32x4* dst = reinterpret_cast<f32x4*>(p.out) + obase;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) dst[k] = a[k] * inv;
+    for (int k = 0; k < 8; ++k) {
+      const float inv = L[k] > 0.f ? 1.f / L[k] : 0.f;   // a row with no visible key gets 0
+      dst[64 * k] = a[k] * inv;
+    }
   }
 }
 
