@@ -255,3 +255,51 @@ def test_worker_count_mismatch_writes_nothing(launch_workers):
                             pm, pl, po)
     torch.cuda.synchronize()
     assert bool((pm == 7.0).all()) and bool((pl == 7.0).all()) and bool((po == 7.0).all())
+
+
+@pytest.mark.parametrize("q_tile", [128, 256])
+def test_graph_captured_prefill_step(q_tile):
+    """The prefill step (split-KV and combine on one stream) captured in a HIP graph: four replays
+    with new query and key values written in place between them, and eager work of the program in
+    between, each replay bit for bit equal to the eager step on the same inputs and within the gates
+    of the fp64 oracle."""
+    from load_balanced_split_attn_amd.prefill import PrefillStep
+    wl = WL.random_prefill(77, 3, 2000, 300)
+    q, kc, vc, bt = prefill_inputs(wl, pad_value=float("nan"))
+    dev = q.device
+    step = PrefillStep(wl.q_lens, wl.kv_lens, dev, num_workers=6, q_tile=q_tile)
+    out = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                           # warm-up outside the capture
+        step(q, kc, vc, bt, scale=SCALE, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(q, kc, vc, bt, scale=SCALE, out=out)
+    torch.cuda.synchronize()
+    q0 = q.clone()
+    gen = torch.Generator(device="cpu").manual_seed(11)
+    starts = q_starts(wl)
+    for replay in range(4):
+        # new query rows (the scaled first rows; replay 0 keeps them) and the eager step beside the graph
+        factor = 1.0 + 0.25 * replay
+        q.copy_((q0.float() * factor).to(torch.bfloat16))
+        eager = torch.empty_like(out)
+        step(q, kc, vc, bt, scale=SCALE, out=eager)
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 16, generator=gen).to(dev).sum()      # the program's own eager work
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(out, eager), f"replay {replay}: graph output differs from the eager step"
+        got = out.cpu().numpy()
+        qh = q.cpu()
+        for b in range(wl.batch):
+            k, v = wl.kv(b)
+            rows = qh[starts[b]:starts[b] + wl.q_lens[b]].double().numpy()
+            ref = ref_attention(rows, k.double().numpy(), v.double().numpy(), SCALE, causal=True)
+            assert_close(got[starts[b]:starts[b] + wl.q_lens[b]], ref, f"replay {replay} request {b}")
+        note(f"prefill graph replay {replay} (q x {factor}) ok")
