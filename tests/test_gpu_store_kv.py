@@ -409,3 +409,43 @@ def test_chunk_append(lb, fp8, norm, theta, had, page):
                 assert np.all((gc == ref) | (dv <= step + 1e-12)), f"request {b}"
             else:
                 assert np.all(np.abs(got.double().numpy() - ref) <= _tol(ref)), f"request {b}"
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_graph_captured_store(lb, fp8):
+    """The producer step captured in a HIP graph: four replays with new q/k/v values and new
+    positions written in place between them, and the program's own eager work in between; after
+    every replay q_out and both caches equal, byte for byte, what the eager step writes into a copy of
+    the caches taken before the replay."""
+    lens = [37, 300, 1, 129, 64]
+    dev = torch.device("cuda")
+    B = len(lens)
+    q, k, v, qw, kw = (t.to(dev) for t in _inputs(91, B))
+    kc, vc, bt = _empty_cache([L + 3 for L in lens], 64, fp8, dev)
+    scales = (torch.full((8,), 0.75, device=dev), torch.full((8,), 1.5, device=dev)) if fp8 else None
+    pos = torch.tensor(lens, dtype=torch.int32, device=dev)
+    q_out = torch.empty_like(q)
+    args = dict(q_norm_w=qw, k_norm_w=kw, rope_theta=10000.0, hadamard=True, kv_scales=scales)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                           # warm-up outside the capture
+        lb.attn_store_kv(q, k, v, pos, q_out, kc, vc, bt, **args)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lb.attn_store_kv(q, k, v, pos, q_out, kc, vc, bt, **args)
+    torch.cuda.synchronize()
+    for replay in range(4):
+        nq, nk, nv, _, _ = (t.to(dev) for t in _inputs(200 + replay, B))
+        q.copy_(nq), k.copy_(nk), v.copy_(nv)
+        pos.copy_(torch.tensor([L + replay % 3 for L in lens], dtype=torch.int32))
+        kc_e, vc_e, qo_e = kc.clone(), vc.clone(), torch.empty_like(q_out)
+        lb.attn_store_kv(q, k, v, pos, qo_e, kc_e, vc_e, bt, **args)
+        junk = torch.randn(1 << 16, device=dev).sum()   # the program's own eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(q_out, qo_e), f"replay {replay}: q_out"
+        assert torch.equal(kc, kc_e) and torch.equal(vc, vc_e), f"replay {replay}: caches"
