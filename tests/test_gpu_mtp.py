@@ -100,3 +100,45 @@ def test_full_size_mtp4_mixed(lb, fp8):
         ma, rr = assert_close(got[starts[b]:starts[b] + 4], r, f"mtp4 request {b} (L={wl.kv_lens[b]})")
         worst = (max(worst[0], ma), max(worst[1], rr))
     note(f"  all {wl.batch} requests: worst max_abs={worst[0]:.2e} rel_rms={worst[1]:.2e}")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_graph_captured_mtp_step(lb, fp8):
+    """The multi-token decode step (split-KV and combine) captured in a HIP graph: four replays with
+    new query rows written in place and the program's own eager work between them, each bit for bit
+    equal to the eager step on the same inputs; the first replay also against the fp64 oracle."""
+    from load_balanced_split_attn_amd.mtp import MtpDecodeStep
+    wl = WL.random_mtp(41, 7, 2600)
+    wl.q_lens[-1] = 4
+    q, kc, vc, bt, scales = mtp_inputs(wl, fp8=fp8, pad=NAN_CODE if fp8 else NAN_BF16)
+    step = MtpDecodeStep(wl.q_lens, wl.kv_lens, q.device, num_workers=9,
+                         kv_dtype=lb.KV_FP8_E4M3 if fp8 else lb.KV_BF16)
+    out = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                           # warm-up outside the capture
+        step(q, kc, vc, bt, scale=SCALE, out=out, kv_scales=scales)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(q, kc, vc, bt, scale=SCALE, out=out, kv_scales=scales)
+    torch.cuda.synchronize()
+    q0 = q.clone()
+    starts = q_starts(wl)
+    for replay in range(4):
+        q.copy_((q0.float() * (1.0 + 0.5 * replay)).to(torch.bfloat16))
+        eager = torch.empty_like(out)
+        step(q, kc, vc, bt, scale=SCALE, out=eager, kv_scales=scales)
+        junk = torch.randn(1 << 16, device=q.device).sum()   # the program's own eager work
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
+        assert torch.equal(out, eager), f"replay {replay}: graph output differs from the eager step"
+        if replay == 0:
+            got = out.cpu().numpy()
+            for b, r in oracle_mtp(wl, fp8=fp8).items():
+                assert_close(got[starts[b]:starts[b] + wl.q_lens[b]], r, f"request {b}")
+        note(f"mtp graph replay {replay} ok")
