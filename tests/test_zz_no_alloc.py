@@ -66,6 +66,47 @@ def test_noalloc_two_calls_second_smaller(lb, fp8):
             assert_close(got[b], ref[b], f"request {b}")
 
 
+def test_noalloc_graph_replays(lb):
+    """The allocation-free step captured in a HIP graph (its first call, which resolves the array's
+    device address, made before the capture): three replays with new query values, each bit for
+    bit equal to the allocating path on the same inputs."""
+    wl = WL.random_decode(64, 6, 5000, min_len=1)
+    W = 24
+    words = lb.attn_plan(wl.kv_lens, W, 512)
+    hdr = lb.map_header(words)
+    q, kc, vc, bt = decode_inputs(wl)
+    dev = q.device
+    mp = torch.from_numpy(words).to(dev)
+    lens = torch.tensor(wl.kv_lens, dtype=torch.int32, device=dev)
+    S, ms = hdr["S"], lb.max_splits_of(words)
+    out = torch.zeros(q.shape, dtype=torch.float32, device=dev)
+    pm = torch.empty((S, wl.hq), device=dev)
+    pl = torch.empty((S, wl.hq), device=dev)
+    po = torch.empty((S, wl.hq, wl.head_dim), device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        lb.attn_decode_noalloc(q, kc, vc, bt, lens, mp, W, S, 8, SCALE, out, max_splits=ms)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lb.attn_decode_noalloc(q, kc, vc, bt, lens, mp, W, S, 8, SCALE, out, max_splits=ms)
+    torch.cuda.synchronize()
+    q0 = q.clone()
+    for replay in range(3):
+        q.copy_((q0.float() * (1.0 + 0.5 * replay)).to(torch.bfloat16))
+        ref_out = torch.full(q.shape, float("nan"), device=dev)
+        lb.attn_splitkv(q, kc, vc, bt, lens, mp, W, S, 8, SCALE, pm, pl, po)
+        lb.attn_combine(pm, pl, po, mp, hdr["U"], ref_out, max_splits=ms)
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out), f"replay {replay}: noalloc graph output differs"
+        note(f"noalloc graph replay {replay} ok")
+
+
 def test_noalloc_refuses_oversized_partials(lb):
     """More segments than the array holds: LBSA_ERR_CAPACITY, nothing launched."""
     wl = WL.random_decode(63, 2, 600, min_len=1)
