@@ -251,6 +251,54 @@ def prefill_unique_bytes(wl, segments: int, q_tile: int) -> int:
     return q_bytes + kv_bytes + part_bytes
 
 
+def mfma_ceiling(dev, prefill_tflops: float) -> dict:
+    """The bf16 rate this device's matrix cores sustain, measured beside the prefill kernel: the
+    register-only probe (v_mfma_f32_16x16x32_bf16 flat out, 1,024 workgroups of four waves, eight
+    launches back to back after two) and a library GEMM (torch.mm, 16384^3 bf16, A . B^T)."""
+    import torch
+
+    import load_balanced_split_attn_amd as lb
+
+    def timed(fn, reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        work = sum(fn() for _ in range(reps))
+        e1.record()
+        torch.cuda.synchronize()
+        return work / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+    blocks, iters = 1024, 32768
+    sink = torch.zeros(blocks * 256, dtype=torch.int32, device=dev)
+    probe = lambda: lb.attn_probe_mfma_rate(iters, blocks, sink)
+    timed(probe, 2)
+    probe_tf = timed(probe, 8)
+    # the library's fastest square case on this device: A . B^T with both operands row-major
+    # (~1.6 PFLOP/s at 16384^3, against ~1.37 for A . B)
+    n = 16384
+    g = torch.Generator(device=dev).manual_seed(5)
+    a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+
+    def gemm():
+        torch.mm(a, b.t(), out=c)
+        return 2 * n ** 3
+
+    timed(gemm, 3)
+    gemm_tf = timed(gemm, 10)
+    del a, b, c
+    torch.cuda.empty_cache()
+    # 16 cycles per 16x16x32 product on each of the 1,024 SIMDs: 1,048,576 flops per clock
+    clock = probe_tf * 1e12 / (1024 * 1024) / 1e9
+    log(f"matrix cores: probe {probe_tf:.0f} TFLOP/s (~{clock:.2f} GHz), library GEMM {gemm_tf:.0f} TFLOP/s")
+    return {"probe_tflops": round(probe_tf, 1), "probe_implied_clock_GHz": round(clock, 3),
+            "probe": f"v_mfma_f32_16x16x32_bf16 on register operands, {blocks} x 4 waves x {iters} x 8 products",
+            "library_gemm_tflops": round(gemm_tf, 1), "library_gemm": f"torch.mm bf16 {n}x{n}x{n}, A . B^T",
+            "prefill_frac_of_probe": round(prefill_tflops / probe_tf, 4),
+            "prefill_frac_of_library_gemm": round(prefill_tflops / gemm_tf, 4)}
+
+
 def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256), exact_modes=(None, True, False)) -> dict:
     """Chunked prefill over cached prefixes: 8 requests x 2048-row causal chunks after prefixes drawn
     log-uniform in [8K, 128K]; q tiles of 128 or 256 rows x KV tiles of 512 on the same greedy
@@ -313,6 +361,7 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256)
                          "unique_bytes": prefill_unique_bytes(wl, stated["segments"], stated["q_tile"])},
             "fastest": {k: fastest[k] for k in ("q_tile", "pv", "workers", "us_per_step", "splitkv_us",
                                                  "splitkv_tflops", "frac_of_bf16_peak")},
+            "mfma_ceiling": mfma_ceiling(dev, stated["splitkv_tflops"]),
             "sweep": rows}
 
 

@@ -7,6 +7,15 @@
  * measured streaming-read ceiling of the device, the yardstick for the decode kernel's HBM
  * rate.  Returns LBSA_OK, LBSA_ERR_INVALID (null pointer, misaligned, bytes % 16 != 0,
  * blocks < 1) or LBSA_ERR_HIP.  Asynchronous on `stream`.
+ *
+ * attn_probe_mfma_rate: `blocks` workgroups of 256 threads (four waves) in which every wave runs
+ * `iters` rounds of eight independent v_mfma_f32_16x16x32_bf16 products on register operands
+ * (random finite bf16 values, no memory reads), then writes the sum of each thread's accumulators
+ * (fp32 bits) to `sink` (device uint32[blocks * 256]).  One launch performs
+ * blocks * 4 * iters * 8 * 16384 flops; divided by its duration, that is the bf16 matrix-core rate
+ * the device sustains at the clock it holds under that load, the yardstick for the prefill
+ * kernel's MFMA rate beside the 2.5 PFLOP/s dense figure.  Returns LBSA_OK, LBSA_ERR_INVALID (null or
+ * misaligned sink, iters < 1, blocks < 1) or LBSA_ERR_HIP.  Asynchronous on `stream`.
  */
 #ifndef LBSA_PROBE_H
 #define LBSA_PROBE_H
@@ -18,6 +27,7 @@ extern "C" {
 #endif
 
 int attn_probe_stream_read(const void* buf, int64_t bytes, int32_t blocks, uint32_t* sink, void* stream);
+int attn_probe_mfma_rate(int32_t iters, int32_t blocks, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

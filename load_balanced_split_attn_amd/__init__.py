@@ -20,7 +20,7 @@ __all__ = [
     "attn_plan_lpt", "attn_plan_weighted",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
     "attn_combine", "attn_store_kv", "attn_store_kv_chunk", "attn_kv_layout", "attn_decode_noalloc", "attn_splitkv_claimed", "NOALLOC_SCRATCH_BYTES",
-    "attn_status_string", "attn_probe_stream_read", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
+    "attn_status_string", "attn_probe_stream_read", "attn_probe_mfma_rate", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
 ]
 
 # cache element types (LBSA_KV_* in include/lbsa.h)
@@ -72,6 +72,7 @@ _SIGNATURES = {
     "attn_combine": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp, _c_vp,
                                     _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, _c_vp]),
     "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
+    "attn_probe_mfma_rate": (ctypes.c_int, [_c_i32, _c_i32, _c_vp, _c_vp]),
     "attn_decode_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
                                            _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                            ctypes.c_float, _c_i32, _c_vp, _c_i32, _c_vp]),
@@ -608,3 +609,11 @@ def attn_probe_stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor, s
     nbytes = buf.numel() * buf.element_size()
     _check(lib().attn_probe_stream_read(_dptr(buf), nbytes - nbytes % 16, blocks, _dptr(sink), _stream(stream)),
            "attn_probe_stream_read")
+
+
+def attn_probe_mfma_rate(iters: int, blocks: int, sink: torch.Tensor, stream=None) -> int:
+    """Run the matrix-core rate probe (measurement helper); returns the flops of the launch."""
+    if not sink.is_cuda or sink.dtype != torch.int32 or not sink.is_contiguous() or sink.numel() < blocks * 256:
+        raise ValueError("attn_probe_mfma_rate: need a contiguous int32 GPU sink of blocks*256")
+    _check(lib().attn_probe_mfma_rate(int(iters), int(blocks), _dptr(sink), _stream(stream)), "attn_probe_mfma_rate")
+    return int(blocks) * 4 * int(iters) * 8 * 16384

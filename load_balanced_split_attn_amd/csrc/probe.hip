@@ -1,5 +1,7 @@
-// Streaming-read probe: the device's practical HBM read ceiling, measured beside the kernels.
+// Measurement probes, run beside the kernels: the device's practical HBM read ceiling and the rate
+// its matrix cores sustain.
 //
+// Streaming read:
 // Each wave reads UNROLL consecutive KiB (one 16-byte non-temporal load per lane per KiB) per step,
 // steps spread over the grid; all loads of a step are issued before any is used.  Non-temporal
 // loads of whole lines are the fastest plain read stream measured on gfx950 (~10% above default
@@ -34,7 +36,57 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// Matrix-core rate: each wave issues `iters` rounds of eight independent v_mfma_f32_16x16x32_bf16
+// products whose operands sit in registers (nothing is read from memory), so the launch measures the
+// matrix pipes at the clock the chip holds while they run flat out.  The operands cycle over four
+// register sets of random finite bf16 values (|x| in [0.5, 1)) so the multiplier inputs change on
+// every product, as in a real contraction; eight accumulators put 128 cycles between dependent
+// products, more than the instruction's latency.  The sum of a thread's accumulators goes to sink.
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// The register budget is pinned (two waves per SIMD): left free, the compiler keeps the accumulators
+// in AGPRs and copies them between register tuples on every round, which would time the copies.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_rate_kernel(
+    int32_t iters, uint32_t* __restrict__ sink) {
+  const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+  u32x4 a[4], b[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[k][e] = (probe_hash(t * 32u + 8u * k + e) & 0x807f807fu) | 0x3f003f00u;
+      b[k][e] = (probe_hash(t * 32u + 8u * k + 4u + e) & 0x807f807fu) | 0x3f003f00u;
+    }
+  f32x4 c0{}, c1{}, c2{}, c3{}, c4{}, c5{}, c6{}, c7{};
+  for (int i = 0; i < iters; ++i) {
+    c0 = mfma16x16x32(a[0], b[0], c0);
+    c1 = mfma16x16x32(a[1], b[0], c1);
+    c2 = mfma16x16x32(a[2], b[1], c2);
+    c3 = mfma16x16x32(a[3], b[1], c3);
+    c4 = mfma16x16x32(a[0], b[2], c4);
+    c5 = mfma16x16x32(a[1], b[2], c5);
+    c6 = mfma16x16x32(a[2], b[3], c6);
+    c7 = mfma16x16x32(a[3], b[3], c7);
+  }
+  const f32x4 s4 = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+  sink[t] = __float_as_uint((s4[0] + s4[1]) + (s4[2] + s4[3]));
+}
+
 }  // namespace lbsa
+
+extern "C" int attn_probe_mfma_rate(int32_t iters, int32_t blocks, uint32_t* sink, void* stream) {
+  if (!sink || iters < 1 || blocks < 1 || (reinterpret_cast<uintptr_t>(sink) & 3)) return LBSA_ERR_INVALID;
+  hipLaunchKernelGGL(lbsa::mfma_rate_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters,
+                     sink);
+  return hipGetLastError() == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;
+}
 
 extern "C" int attn_probe_stream_read(const void* buf, int64_t bytes, int32_t blocks, uint32_t* sink,
                                       void* stream) {

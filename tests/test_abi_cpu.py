@@ -178,6 +178,14 @@ def test_errors_and_capacity(L):
     assert lib.attn_query_workers(0, 3, 0, ctypes.byref(out)) == -1
     assert lib.attn_combine(None, None, None, dummy, 1, 1, None, None, 64, 128, None, 0, 0, None) == -1
     assert lib.attn_combine(dummy, dummy, dummy, dummy, 1, 1, None, None, 64, 128, dummy, 0, -1, None) == -1
+    # measurement probes: argument checks before any launch
+    assert lib.attn_probe_stream_read(None, 16, 1, dummy, None) == -1
+    assert lib.attn_probe_stream_read(dummy, 15, 1, dummy, None) == -1
+    assert lib.attn_probe_stream_read(dummy, 16, 0, dummy, None) == -1
+    assert lib.attn_probe_mfma_rate(0, 1, dummy, None) == -1
+    assert lib.attn_probe_mfma_rate(1, 0, dummy, None) == -1
+    assert lib.attn_probe_mfma_rate(1, 1, None, None) == -1
+    assert lib.attn_probe_mfma_rate(1, 1, ctypes.c_void_p(18), None) == -1
 
 
 def test_weighted_plan_bit_exact():
