@@ -47,6 +47,11 @@ Version 2 (the LPT comparison planner below): a worker's segments need not be
 contiguous in unit-major order, so the segments stay unit-major (segment i owns
 partial slot i) and an extra ``order[S]`` follows ``seg``: worker w runs the
 segments ``order[worker_ptr[w] .. worker_ptr[w+1])``.
+
+Version 3 (the rate-proportional planner below): the words of version 1; the
+version only tells the split-KV launch to run worker w's list for every head
+group on workgroups b with b mod W = w (list-major order), so that a list's
+workgroups share one placement on the device.
 """
 
 from __future__ import annotations
@@ -58,6 +63,8 @@ import numpy as np
 
 MAP_VERSION = 1
 MAP_VERSION_ORDERED = 2   # version 1 plus order[S]: the segments each worker runs, by slot index
+MAP_VERSION_PLACED = 3    # version 1's words, list-major workgroup order in the split-KV launch
+RATE_MAX = 1 << 20        # largest per-worker rate the rate-proportional planner accepts
 HEADER_WORDS = 8
 
 
@@ -135,7 +142,7 @@ def _runs(units: Sequence[Unit], taken: Sequence[Tuple[int, int]], tile: int) ->
 
 
 def _serialise(B: int, units: Sequence[Unit], lists: Sequence[Sequence[Segment]],
-               kv_tile: int, q_tile: int, total_tiles: int) -> np.ndarray:
+               kv_tile: int, q_tile: int, total_tiles: int, version: int = MAP_VERSION) -> np.ndarray:
     W = len(lists)
     U = len(units)
     segs = [s for lst in lists for s in lst]
@@ -156,7 +163,7 @@ def _serialise(B: int, units: Sequence[Unit], lists: Sequence[Sequence[Segment]]
     unit_ptr = [0]
     for c in counts:
         unit_ptr.append(unit_ptr[-1] + c)
-    words = [MAP_VERSION, B, W, kv_tile, S, total_tiles, q_tile, U]
+    words = [version, B, W, kv_tile, S, total_tiles, q_tile, U]
     words += worker_ptr
     words += unit_ptr
     for u in units:
@@ -341,6 +348,51 @@ def ref_plan_weighted(seq_lens: Sequence[int], num_workers: int, tile: int, spli
     return _serialise(len(seq_lens), units, lists, tile, 1, len(stream))
 
 
+def ref_plan_rated(seq_lens: Sequence[int], num_workers: int, tile: int, split_cost: int,
+                   rates: Sequence[int]) -> np.ndarray:
+    """Rate-proportional contiguous fill: ``ref_plan_weighted`` with worker w's share of the cost
+    line proportional to ``rates[w]`` instead of equal.  The pages' scheduler gives every worker the
+    same budget ([P3] §3.1 方案 step 3), which balances finish times when every worker streams at
+    the same rate; here the workers' rates may differ (on the device they depend on where a
+    worker's workgroups run), and the aim, equal finish times, is kept by giving each worker the cost
+    it can stream in the same time.
+
+    With R_w = rates[0] + ... + rates[w - 1] and R = R_W, worker w's share of the cost line is
+    [C R_w / R, C R_(w+1) / R).  Tile i (cost c_i, P_i the cost before it; costs as in
+    ``ref_plan_weighted``: KV tokens, plus ``split_cost`` on a request's first tile) goes to the
+    worker whose share holds its midpoint P_i + c_i / 2: the last worker w with
+    C R_w / R <= P_i + c_i / 2, i.e. 2 C R_w <= R (2 P_i + c_i) in integers.  A worker of rate 0
+    holds an empty share and gets nothing.  With equal rates the rule is ``ref_plan_weighted``'s
+    floor(W (2 P_i + c_i) / (2 C)).  Every worker's stretch of the stream stays contiguous and its
+    cost within one tile's cost of C rates[w] / R.  Serialised as a version-3 map.
+    """
+    _check_common(num_workers, tile)
+    if split_cost < 0:
+        raise ValueError("split_cost must be >= 0")
+    rates = [int(r) for r in rates]
+    if len(rates) != num_workers or any(r < 0 or r > RATE_MAX for r in rates) or sum(rates) == 0:
+        raise ValueError(f"need num_workers rates in [0, {RATE_MAX}], not all zero")
+    units = decode_units(seq_lens)
+    tiles = []                                    # (unit index, tile index, cost)
+    for ui, u in enumerate(units):
+        for t in range(tiles_of(u.extent, tile)):
+            tokens = min(tile, u.extent - t * tile)
+            tiles.append((ui, t, tokens + split_cost * (t == 0)))
+    C = sum(c for _, _, c in tiles)
+    R = sum(rates)
+    share_start = [0]                             # R_w for w = 0 .. W
+    for r in rates:
+        share_start.append(share_start[-1] + r)
+    mine: List[List[Tuple[int, int]]] = [[] for _ in range(num_workers)]
+    P = 0
+    for ui, t, c in tiles:
+        w = max(v for v in range(num_workers) if 2 * C * share_start[v] <= R * (2 * P + c))
+        mine[w].append((ui, t))
+        P += c
+    lists = [_runs(units, taken, tile) for taken in mine]
+    return _serialise(len(seq_lens), units, lists, tile, 1, len(tiles), version=MAP_VERSION_PLACED)
+
+
 # ----------------------------------------------------------------------------------------------
 # Reading a map back (used by tests and by the attention oracle's split helpers)
 
@@ -382,7 +434,7 @@ def parse_map(words: np.ndarray) -> WorkMap:
     order = None
     if version == MAP_VERSION_ORDERED:
         order = words[o:o + S]; o += S
-    elif version != MAP_VERSION:
+    elif version not in (MAP_VERSION, MAP_VERSION_PLACED):
         raise ValueError(f"unknown map version {version}")
     if o != len(words):
         raise ValueError(f"map has {len(words)} words, layout implies {o}")

@@ -491,6 +491,99 @@ def pin_weighted_hand_examples(ref_plan_weighted, parse_map):
 
 
 # ------------------------------------------------------------------------------------------------
+# Rate-proportional planner.
+
+def _rated_worker_tiles(ref_plan_rated, parse_map, lens, W, tile, split_cost, rates):
+    mp = parse_map(ref_plan_rated(lens, W, tile, split_cost, rates))
+    assert mp.version == 3
+    per = []
+    for w in range(W):
+        tiles = []
+        for b, qt, a, e in mp.worker_segments(w).tolist():
+            assert qt == 0 and 0 <= a < e <= lens[b] and a % tile == 0 and (e % tile == 0 or e == lens[b])
+            tiles += [(b, t) for t in range(a // tile, -(-e // tile))]
+        per.append(tiles)
+    return mp, per
+
+
+def pin_rated_equal_rates_are_weighted(ref_plan_rated, ref_plan_weighted, trials=120, seed=13):
+    """Equal rates, whatever their common value, give the cost-weighted map word for word apart from
+    the version word: the share boundaries C w r / (W r) are the equal shares."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        B = int(rng.integers(0, 10))
+        W = int(rng.integers(1, 12))
+        tile = int(rng.choice([64, 128, 512]))
+        sc = int(rng.choice([0, 1, 64, 300, 2000]))
+        r = int(rng.choice([1, 7, 1000, 1 << 20]))
+        lens = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 4000, size=B)]
+        got = ref_plan_rated(lens, W, tile, sc, [r] * W)
+        want = ref_plan_weighted(lens, W, tile, sc)
+        assert got[0] == 3 and want[0] == 1
+        assert np.array_equal(got[1:], want[1:]), (lens, W, tile, sc, r)
+
+
+def pin_rated_contiguous_and_proportional(ref_plan_rated, parse_map, trials=150, seed=17):
+    """The workers' tiles read in worker order are the task stream itself (no tile lost, repeated or
+    reordered); each worker holds one segment per request it touches; a worker of rate 0 gets no
+    tile; and every worker's cost is within the largest tile cost of C r_w / R — its share of the
+    cost line is covered by its own tiles up to half a tile at each end, and its tiles reach at most
+    half a tile beyond it on each side."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        B = int(rng.integers(0, 10))
+        W = int(rng.integers(1, 10))
+        tile = int(rng.choice([64, 128, 512]))
+        sc = int(rng.choice([0, 1, 64, 300, 2000]))
+        rates = [int(x) if rng.random() > 0.2 else 0 for x in rng.integers(1, 100, size=W)]
+        if sum(rates) == 0:
+            rates[int(rng.integers(0, W))] = 1
+        lens = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 4000, size=B)]
+        mp, per = _rated_worker_tiles(ref_plan_rated, parse_map, lens, W, tile, sc, rates)
+        stream = [(b, t) for b, L in enumerate(lens) for t in range(-(-L // tile))]
+        assert [x for tiles in per for x in tiles] == stream
+        assert mp.T == len(stream)
+        assert mp.S == sum(len({b for b, _ in tiles}) for tiles in per)
+        assert all(not tiles for tiles, r in zip(per, rates) if r == 0)
+        if not stream:
+            continue
+        cost = lambda bt: min(tile, lens[bt[0]] - bt[1] * tile) + (sc if bt[1] == 0 else 0)
+        C = sum(cost(x) for x in stream)
+        cmax = max(cost(x) for x in stream)
+        R = sum(rates)
+        for tiles, r in zip(per, rates):
+            cw = sum(cost(x) for x in tiles)
+            assert abs(R * cw - C * r) <= R * cmax, (lens, W, tile, sc, rates)
+
+
+def pin_rated_hand_examples(ref_plan_rated, parse_map):
+    """Worked by hand (c = tile cost, mid = cost before the tile + c / 2, worker w's share
+    [C R_w / R, C R_(w+1) / R)):
+    (a) the worked example's lengths 1024, 5120, 2048 (512-token tiles) on rates 1 and 3: C = 8192,
+        worker 1's share starts at 2048, mids 256 + 512 i -> tiles 0-3 of the stream on worker 0,
+        the other 12 on worker 1;
+    (b) six 512-token requests on rates 1, 0, 2: C = 3072, shares [0, 1024), empty, [1024, 3072)
+        -> requests 0-1 on worker 0, none on worker 1, 2-5 on worker 2;
+    (c) two 4096-token requests, 64-token tiles, rates 20, 19, 20, 19: C = 8192, R = 78, shares
+        start at 0, 2100.5, 4096, 6196.5; mids 32 + 64 i -> 33, 31, 33, 31 tiles;
+    (d) 512, 512, 10, 10 with split cost 500 on rates 1 and 2: c = 1012, 1012, 510, 510, C = 3044,
+        worker 1 from 1014.7, mids 506, 1518, 2279, 2789 -> 0, 1, 1, 1 (equal rates: 0, 0, 1, 1);
+    (e) a midpoint exactly on a share boundary goes to the later worker: one 1536-token request on
+        two workers of rate 5, C = 1536, boundary 768, mids 256, 768, 1280 -> 0, 1, 1."""
+    f = lambda lens, W, tile, sc, rates: _rated_worker_tiles(ref_plan_rated, parse_map, lens, W, tile, sc, rates)[1]
+    stream = [(0, 0), (0, 1)] + [(1, t) for t in range(10)] + [(2, t) for t in range(4)]
+    assert f([1024, 5120, 2048], 2, 512, 0, [1, 3]) == [stream[:4], stream[4:]]
+    assert f([512] * 6, 3, 512, 0, [1, 0, 2]) == [[(0, 0), (1, 0)], [], [(b, 0) for b in range(2, 6)]]
+    assert [len(t) for t in f([4096, 4096], 4, 64, 0, [20, 19, 20, 19])] == [33, 31, 33, 31]
+    assert f([512, 512, 10, 10], 2, 512, 500, [1, 2]) == [[(0, 0)], [(1, 0), (2, 0), (3, 0)]]
+    assert f([512, 512, 10, 10], 2, 512, 500, [1, 1]) == [[(0, 0), (1, 0)], [(2, 0), (3, 0)]]
+    assert f([1536], 2, 512, 0, [5, 5]) == [[(0, 0)], [(0, 1), (0, 2)]]
+    mp, _ = _rated_worker_tiles(ref_plan_rated, parse_map, [1024, 5120, 2048], 2, 512, 0, [1, 3])
+    assert mp.segs.tolist() == [[0, 0, 0, 1024], [1, 0, 0, 1024], [1, 0, 1024, 5120], [2, 0, 0, 2048]]
+    assert mp.worker_ptr.tolist() == [0, 2, 4]
+
+
+# ------------------------------------------------------------------------------------------------
 # Producer step (normalise, rotate, quantise, store).
 
 def pin_round_bf16_library(round_bf16):

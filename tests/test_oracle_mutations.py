@@ -56,6 +56,14 @@ def _lpt_pins(m):
     ]
 
 
+def _rated_pins(m):
+    return [
+        lambda: P.pin_rated_hand_examples(m.ref_plan_rated, m.parse_map),
+        lambda: P.pin_rated_equal_rates_are_weighted(m.ref_plan_rated, m.ref_plan_weighted, trials=40),
+        lambda: P.pin_rated_contiguous_and_proportional(m.ref_plan_rated, m.parse_map, trials=60),
+    ]
+
+
 def _weighted_pins(m):
     return [
         lambda: P.pin_weighted_hand_examples(m.ref_plan_weighted, m.parse_map),
@@ -137,6 +145,21 @@ WEIGHTED_MUTANTS = {
                                   "stream.append((ui, t, tile +"),
     "worker index rounded up": ("w = (num_workers * (2 * before + c)) // (2 * total_cost)",
                                 "w = min(num_workers - 1, -(-(num_workers * (2 * before + c)) // (2 * total_cost)))"),
+}
+
+RATED_MUTANTS = {
+    "tile start instead of its midpoint": ("if 2 * C * share_start[v] <= R * (2 * P + c))",
+                                           "if 2 * C * share_start[v] <= R * (2 * P))"),
+    "share boundary owned by the earlier worker": ("if 2 * C * share_start[v] <= R * (2 * P + c))",
+                                                   "if 2 * C * share_start[v] < R * (2 * P + c))"),
+    "shares start one worker late": ("if 2 * C * share_start[v] <= R * (2 * P + c))",
+                                     "if 2 * C * share_start[v + 1] <= R * (2 * P + c))"),
+    "own rate instead of the running sum": ("share_start.append(share_start[-1] + r)", "share_start.append(r)"),
+    "first worker instead of the last": ("w = max(v for v in range(num_workers) if 2 * C",
+                                         "w = min(v for v in range(num_workers) if 2 * C"),
+    "split cost ignored": ("tiles.append((ui, t, tokens + split_cost * (t == 0)))", "tiles.append((ui, t, tokens))"),
+    "tiles counted, not tokens": ("tokens = min(tile, u.extent - t * tile)", "tokens = tile"),
+    "rates reversed": ("    for r in rates:\n        share_start.append", "    for r in rates[::-1]:\n        share_start.append"),
 }
 
 STORE_MUTANTS = {
@@ -227,6 +250,13 @@ def test_weighted_mutant_is_caught(name):
     assert _caught(_weighted_pins(m)), f"no pin catches: {name}"
 
 
+@pytest.mark.parametrize("name", sorted(RATED_MUTANTS))
+def test_rated_mutant_is_caught(name):
+    old, new = RATED_MUTANTS[name]
+    m = _load_mutant("plan", old, new, count=1)
+    assert _caught(_rated_pins(m)), f"no pin catches: {name}"
+
+
 @pytest.mark.parametrize("name", sorted(STORE_MUTANTS))
 def test_store_mutant_is_caught(name):
     old, new = STORE_MUTANTS[name]
@@ -246,5 +276,6 @@ def test_unmutated_oracle_passes_all_pins():
     import oracle.fp8 as F
     import oracle.plan as Pl
     import oracle.store_kv as SK
-    for pin in _attention_pins(A) + _plan_pins(Pl) + _fp8_pins(F) + _lpt_pins(Pl) + _weighted_pins(Pl) + _store_pins(SK):
+    for pin in (_attention_pins(A) + _plan_pins(Pl) + _fp8_pins(F) + _lpt_pins(Pl) + _weighted_pins(Pl)
+                + _rated_pins(Pl) + _store_pins(SK)):
         pin()

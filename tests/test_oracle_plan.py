@@ -180,3 +180,28 @@ def test_weighted_rejects_negative_split_cost():
     from oracle.plan import ref_plan_weighted
     with pytest.raises(ValueError):
         ref_plan_weighted([100], 2, 64, -1)
+
+
+def test_rated_equal_rates_are_weighted():
+    from oracle.plan import ref_plan_rated, ref_plan_weighted
+    P.pin_rated_equal_rates_are_weighted(ref_plan_rated, ref_plan_weighted)
+
+
+def test_rated_contiguous_and_proportional():
+    from oracle.plan import parse_map, ref_plan_rated
+    P.pin_rated_contiguous_and_proportional(ref_plan_rated, parse_map)
+
+
+def test_rated_hand_examples():
+    from oracle.plan import parse_map, ref_plan_rated
+    P.pin_rated_hand_examples(ref_plan_rated, parse_map)
+
+
+def test_rated_rejects_bad_rates():
+    from oracle.plan import RATE_MAX, ref_plan_rated
+    for rates in ([1, 2], [0, 0, 0], [1, -1, 1], [1, RATE_MAX + 1, 1]):
+        with pytest.raises(ValueError):
+            ref_plan_rated([100, 200], 3, 512, 0, rates)
+    with pytest.raises(ValueError):
+        ref_plan_rated([100, 200], 3, 512, -1, [1, 1, 1])
+
