@@ -26,7 +26,7 @@
  * ---------------------------------------------------------------------------
  * Work map: one flat little-endian int32 buffer
  *
- *   [0] version (=1)   [1] B  (requests)     [2] W (workers)      [3] kv_tile
+ *   [0] version (1; 2 and 3 below)           [1] B  (requests)     [2] W (workers)      [3] kv_tile
  *   [4] S (segments)   [5] T  (total tiles)  [6] q_tile (1 for decode)
  *   [7] U (query units: one per request in decode, one per q_tile rows in prefill)
  *   worker_ptr[W+1]    segments of worker w:  [worker_ptr[w], worker_ptr[w+1])
@@ -149,6 +149,30 @@ int attn_plan_device(const int32_t* seq_lens, int32_t B, int32_t num_workers, in
  */
 int attn_plan_weighted(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile,
                        int32_t split_cost, int32_t* map, int32_t map_capacity, int32_t* map_words_out);
+
+/*
+ * Rate-proportional contiguous fill: attn_plan_weighted's stream and tile costs, with worker w's
+ * share of the cost line proportional to worker_rates[w] instead of equal.  The pages' scheduler
+ * ([P3] "Hy3 Preview AI Infra 推理优化精读笔记" §3.1 方案 steps 3-4) gives every worker the same
+ * budget, which equalises finish times when the workers stream at one rate; on a device whose
+ * workgroups stream at different rates depending on where they run, equal finish times need budgets
+ * in proportion to the rates.  With R_w the sum of the rates of workers 0 .. w-1 and R their total,
+ * tile i (cost c_i, P_i the cost before it) goes to the last worker w with 2 C R_w <= R (2 P_i + c_i):
+ * the worker whose share [C R_w / R, C R_(w+1) / R) holds the tile's midpoint.  A worker of rate 0
+ * gets nothing; equal rates give attn_plan_weighted's lists exactly.
+ *   worker_rates  host int32[num_workers], each in [0, LBSA_RATE_MAX], not all zero
+ * The map is written in version 3 (LBSA_MAP_VERSION_PLACED): version 1's words, and the split-KV
+ * launch (attn_splitkv, attn_splitkv_fp8) then runs workgroup b on list b mod W and
+ * head group b div W, so with W a multiple of 8 every workgroup of list w runs on XCD w mod 8 (the
+ * dispatcher places workgroup b on XCD b mod 8) and per-XCD rates can be given per worker.
+ * attn_combine and the run-time claiming launch (whose order comes from its counter) accept it; the
+ * prefill kernel takes version 1 only.  O(B + T + W) time, no allocation.  Errors and capacity reporting as attn_plan_weighted
+ * (LBSA_ERR_INVALID also for a NULL worker_rates, a rate outside the range, or all rates zero).
+ */
+#define LBSA_MAP_VERSION_PLACED 3
+#define LBSA_RATE_MAX (1 << 20)
+int attn_plan_rated(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile, int32_t split_cost,
+                    const int32_t* worker_rates, int32_t* map, int32_t map_capacity, int32_t* map_words_out);
 
 /*
  * LPT comparison map ([P5] "大模型推理性能优化揭秘：从算子到系统的全链路技术解析" §五(一): tiles

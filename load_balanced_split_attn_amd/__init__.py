@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "LbsaError", "lib", "attn_map_words", "attn_plan", "attn_plan_static", "attn_plan_prefill", "attn_plan_device",
-    "attn_plan_lpt", "attn_plan_weighted",
+    "attn_plan_lpt", "attn_plan_weighted", "attn_plan_rated", "MAP_VERSION_PLACED", "RATE_MAX",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
     "attn_combine", "attn_store_kv", "attn_store_kv_chunk", "attn_kv_layout", "attn_decode_noalloc", "attn_splitkv_claimed", "NOALLOC_SCRATCH_BYTES",
     "attn_status_string", "attn_probe_stream_read", "attn_probe_mfma_rate", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
@@ -45,6 +45,8 @@ _SIGNATURES = {
     "attn_plan_static": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
     "attn_plan_lpt": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
     "attn_plan_weighted": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32, _c_i32p]),
+    "attn_plan_rated": (ctypes.c_int, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32p, _c_i32,
+                                       _c_i32p]),
     "attn_plan_prefill": (ctypes.c_int, [_c_i32p, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                          _c_i32p, _c_i32, _c_i32p]),
     "attn_query_workers": (ctypes.c_int, [ctypes.c_int, _c_i32, _c_i32, _c_i32p]),
@@ -166,6 +168,22 @@ def attn_plan_weighted(seq_lens: Sequence[int], num_workers: int, tile: int = 51
     lens = _i32_host(seq_lens)
     return _plan_call(lib().attn_plan_weighted, "attn_plan_weighted", _ptr_i32(lens), len(lens), num_workers, tile,
                       split_cost)
+
+
+MAP_VERSION_PLACED = 3     # lbsa.h LBSA_MAP_VERSION_PLACED
+RATE_MAX = 1 << 20         # lbsa.h LBSA_RATE_MAX
+
+
+def attn_plan_rated(seq_lens: Sequence[int], num_workers: int, rates: Sequence[int], tile: int = 512,
+                    split_cost: int = 0) -> np.ndarray:
+    """Rate-proportional contiguous fill (version-3 map, list-major workgroup order): worker w's
+    share of the cost line is proportional to rates[w] (ints in [0, RATE_MAX], not all zero)."""
+    lens = _i32_host(seq_lens)
+    r = _i32_host(rates)
+    if len(r) != num_workers:
+        raise ValueError(f"attn_plan_rated: need {num_workers} rates, got {len(r)}")
+    return _plan_call(lib().attn_plan_rated, "attn_plan_rated", _ptr_i32(lens), len(lens), num_workers, tile,
+                      split_cost, _ptr_i32(r))
 
 
 def attn_plan_prefill(q_lens: Sequence[int], kv_lens: Sequence[int], num_workers: int, q_tile: int = 128,

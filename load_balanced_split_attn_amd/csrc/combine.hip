@@ -40,7 +40,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   const int64_t total = (int64_t)p.U * p.R * p.Hq;
   if (item >= total) return;
   // a device-built map that reported an error, or an unknown layout
-  if (p.map[0] != LBSA_MAP_VERSION && p.map[0] != LBSA_MAP_VERSION_ORDERED) return;
+  if (p.map[0] != LBSA_MAP_VERSION && p.map[0] != LBSA_MAP_VERSION_ORDERED && p.map[0] != LBSA_MAP_VERSION_PLACED)
+    return;
   const int W = p.map[2];
   const int32_t* unit_ptr = p.map + 8 + (W + 1);
   const int32_t* units = unit_ptr + (p.U + 1);
@@ -150,7 +151,8 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(CombineParams p) {
   const int wv = t >> 6;
   const int lane = t & 63;
   if (ur >= (int64_t)p.U * p.R) return;
-  if (p.map[0] != LBSA_MAP_VERSION && p.map[0] != LBSA_MAP_VERSION_ORDERED) return;
+  if (p.map[0] != LBSA_MAP_VERSION && p.map[0] != LBSA_MAP_VERSION_ORDERED && p.map[0] != LBSA_MAP_VERSION_PLACED)
+    return;
   const int W = p.map[2];
   const int32_t* unit_ptr = p.map + 8 + (W + 1);
   const int32_t* units = unit_ptr + (p.U + 1);

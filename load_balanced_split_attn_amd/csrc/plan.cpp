@@ -160,9 +160,17 @@ int plan_units(const Units& units, int32_t B, int32_t W, int32_t kv_tile, int32_
 // request's first tile.  Tile i goes to worker floor(W (2 P_i + c_i) / (2 C)) — P_i the cost before
 // it, C the total — so workers take contiguous stretches whose costs are within one tile's cost of
 // C / W.  One walk over the tiles per pass, no allocation; the map is version 1.
+//
+// With per-worker rates (attn_plan_rated) worker w's share of the cost line is [C R_w / R, C R_(w+1) / R)
+// (R_w the rates of the workers before w, R their total) and tile i goes to the last worker whose
+// share starts at or before its midpoint: 2 C R_w <= R (2 P_i + c_i).  The midpoints increase along
+// the stream, so the worker index only moves forward; zero-rate workers are stepped over.
 int64_t weighted_fill(const int32_t* lens, int32_t B, int32_t W, int64_t tile, int64_t split_cost, int64_t C,
-                      const Writer* wr) {
+                      const Writer* wr, const int32_t* rates = nullptr, int64_t R = 0) {
   int64_t segs = 0, before = 0;
+  int32_t w_rated = 0;       // current worker of the rated walk
+  int64_t share_next = 0;    // R_(w_rated + 1)
+  if (rates) share_next = rates[0];
   int32_t w_open = 0;   // workers <= w_open have their worker_ptr set
   bool have = false;
   int32_t run_b = 0, run_w = 0;
@@ -192,7 +200,14 @@ int64_t weighted_fill(const int32_t* lens, int32_t B, int32_t W, int64_t tile, i
     const int64_t n = tiles_for(L, tile);
     for (int64_t t = 0; t < n; ++t) {
       const int64_t c = (L - t * tile < tile ? L - t * tile : tile) + (t == 0 ? split_cost : 0);
-      const int32_t w = (int32_t)((__int128)W * (2 * before + c) / (2 * (__int128)C));
+      int32_t w;
+      if (rates) {
+        const __int128 mid2 = (__int128)R * (2 * before + c);
+        while (w_rated + 1 < W && 2 * (__int128)C * share_next <= mid2) share_next += rates[++w_rated];
+        w = w_rated;
+      } else {
+        w = (int32_t)((__int128)W * (2 * before + c) / (2 * (__int128)C));
+      }
       before += c;
       if (have && w != run_w) close();
       if (have) {
@@ -339,6 +354,43 @@ int attn_plan_weighted(const int32_t* seq_lens, int32_t B, int32_t num_workers, 
   map[6] = 1;
   map[7] = B;
   return weighted_fill(seq_lens, B, num_workers, tile, split_cost, C, &wr) == S ? LBSA_OK : LBSA_ERR_INVALID;
+}
+
+int attn_plan_rated(const int32_t* seq_lens, int32_t B, int32_t num_workers, int32_t tile, int32_t split_cost,
+                    const int32_t* worker_rates, int32_t* map, int32_t map_capacity, int32_t* map_words_out) {
+  if (B < 0 || num_workers < 1 || tile < 1 || split_cost < 0 || !worker_rates || !map || map_capacity < 0)
+    return LBSA_ERR_INVALID;
+  if (B > 0 && !seq_lens) return LBSA_ERR_INVALID;
+  int64_t R = 0;
+  for (int32_t w = 0; w < num_workers; ++w) {
+    if (worker_rates[w] < 0 || worker_rates[w] > LBSA_RATE_MAX) return LBSA_ERR_INVALID;
+    R += worker_rates[w];
+  }
+  if (R == 0) return LBSA_ERR_INVALID;
+  int64_t T = 0, C = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (seq_lens[b] < 0) return LBSA_ERR_INVALID;
+    T += tiles_for(seq_lens[b], tile);
+    C += (int64_t)seq_lens[b] + (seq_lens[b] > 0 ? split_cost : 0);
+  }
+  if (T > INT32_MAX) return LBSA_ERR_INVALID;
+  Writer probe{nullptr, num_workers, B};
+  const int64_t S = weighted_fill(seq_lens, B, num_workers, tile, split_cost, C, nullptr, worker_rates, R);
+  const int64_t words = probe.seg_base() + 4 * S;
+  if (words > INT32_MAX) return LBSA_ERR_INVALID;
+  if (map_words_out) *map_words_out = (int32_t)words;
+  if (words > map_capacity) return LBSA_ERR_CAPACITY;
+  Writer wr{map, num_workers, B};
+  map[0] = LBSA_MAP_VERSION_PLACED;
+  map[1] = B;
+  map[2] = num_workers;
+  map[3] = tile;
+  map[4] = (int32_t)S;
+  map[5] = (int32_t)T;
+  map[6] = 1;
+  map[7] = B;
+  return weighted_fill(seq_lens, B, num_workers, tile, split_cost, C, &wr, worker_rates, R) == S ? LBSA_OK
+                                                                                                  : LBSA_ERR_INVALID;
 }
 
 // LPT bucket packing ([P5] "大模型推理性能优化揭秘：从算子到系统的全链路技术解析" §五(一)), the

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
 
   const int version = p.map[0];
   // a device-built map that reported an error, or an unknown layout
-  if (version != LBSA_MAP_VERSION && version != LBSA_MAP_VERSION_ORDERED) return;
+  if (version != LBSA_MAP_VERSION && version != LBSA_MAP_VERSION_ORDERED && version != LBSA_MAP_VERSION_PLACED) return;
   // a map planned for another worker count (its lists would be read past their end)
   if (p.map[2] != p.W) return;
   const int U = p.map[7];
@@ -529,7 +529,11 @@ __global__ __launch_bounds__(64 * WAVES) void splitkv_decode_kernel(DecodeParams
   };
 
   if constexpr (!CLAIM) {
-    run_list(blockIdx.x / G, (blockIdx.x % G) * WAVES + wave);
+    // version 3 asks for list-major order: every workgroup of list w on XCD w mod 8 (b mod 8)
+    if (version == LBSA_MAP_VERSION_PLACED)
+      run_list(blockIdx.x % p.W, (blockIdx.x / p.W) * WAVES + wave);
+    else
+      run_list(blockIdx.x / G, (blockIdx.x % G) * WAVES + wave);
   } else {
     // workgroup b starts with item b; each further item takes one device-scope atomic on the
     // counter (issued by lane 0 as a vector memory atomic, broadcast), numbered after the grid's

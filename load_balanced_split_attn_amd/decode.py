@@ -9,23 +9,29 @@ combine kernel on the current stream, reusing the map and the partial buffers.
 
 from __future__ import annotations
 
-from typing import Optional, Sequence
+from typing import List, Optional, Sequence
 
+import numpy as np
 import torch
 
-from . import (KV_BF16, KV_FP8_E4M3, attn_combine, attn_plan, attn_plan_lpt, attn_plan_static, attn_plan_weighted,
-               attn_query_workers,
+from . import (KV_BF16, KV_FP8_E4M3, MAP_VERSION_PLACED, attn_combine, attn_plan, attn_plan_lpt, attn_plan_rated,
+               attn_plan_static, attn_plan_weighted, attn_query_workers,
                attn_splitkv, attn_splitkv_claimed, attn_splitkv_fp8, map_header, max_splits_of)
+
+XCDS = 8   # accelerator complex dies; the dispatcher places workgroup b on XCD b mod 8
 
 
 class DecodeStep:
     def __init__(self, seq_lens: Sequence[int], device, num_workers: Optional[int] = None, tile: int = 512,
                  head_groups: int = 8, num_q_heads: int = 64, head_dim: int = 128,
                  static_splits: Optional[int] = None, kv_dtype: int = KV_BF16, planner: str = "greedy",
-                 split_cost: int = 0, resident_workgroups: Optional[int] = None):
+                 split_cost: int = 0, resident_workgroups: Optional[int] = None,
+                 xcd_rates: Optional[Sequence[int]] = None):
         """resident_workgroups: run the split-KV kernel with run-time claiming (that many one-wave
         workgroups take the map's (list, KV head) items from a device counter) instead of one
-        workgroup per (list, head group); needs head_groups equal to the KV head count."""
+        workgroup per (list, head group); needs head_groups equal to the KV head count.
+        planner "rated": attn_plan_rated with worker w's rate xcd_rates[w mod 8] (the XCD its
+        workgroups run on in the map's list-major order; see ``calibrate_xcd_rates``)."""
         device = torch.device(device)
         self.seq_lens_host = [int(x) for x in seq_lens]
         if static_splits is not None:
@@ -39,8 +45,13 @@ class DecodeStep:
                 self.map_host = attn_plan_lpt(self.seq_lens_host, num_workers, tile)
             elif planner == "weighted":
                 self.map_host = attn_plan_weighted(self.seq_lens_host, num_workers, tile, split_cost)
+            elif planner == "rated":
+                if xcd_rates is None or len(xcd_rates) != XCDS:
+                    raise ValueError("planner 'rated' needs xcd_rates, one rate per XCD")
+                rates = [int(xcd_rates[w % XCDS]) for w in range(num_workers)]
+                self.map_host = attn_plan_rated(self.seq_lens_host, num_workers, rates, tile, split_cost)
             else:
-                raise ValueError(f"unknown planner {planner!r} (greedy, lpt or weighted)")
+                raise ValueError(f"unknown planner {planner!r} (greedy, lpt, weighted or rated)")
         hdr = map_header(self.map_host)
         self.W, self.S, self.U, self.T = hdr["W"], hdr["S"], hdr["U"], hdr["T"]
         self.max_splits = max_splits_of(self.map_host)
@@ -91,6 +102,53 @@ class DecodeStep:
         self.splitkv(q, k_cache, v_cache, block_table, scale, timing=timing, stream=stream, kv_scales=kv_scales)
         self.combine(out, stream=stream)
         return out
+
+
+def xcd_rates_from_timing(timing: torch.Tensor, map_host: np.ndarray, head_groups: int,
+                          scale_to: int = 1 << 16) -> List[int]:
+    """Per-XCD streaming rates from one or more instrumented split-KV launches over ``map_host``
+    (``timing`` rows as the kernel writes them: start, end, HW_ID, XCC_ID per workgroup; several
+    launches stacked along the first axis): on each XCD, the KV tokens its workgroups streamed over
+    the sum of their durations.  Scaled so the fastest XCD has ``scale_to``."""
+    t = timing.cpu().numpy().astype(np.int64).reshape(-1, 4)
+    hdr = map_header(map_host)
+    W, U = hdr["W"], hdr["U"]
+    wptr = np.asarray(map_host[8:8 + W + 1], dtype=np.int64)
+    segs = np.asarray(map_host[8 + (W + 1) + (U + 1) + 2 * U:], dtype=np.int64)[:4 * hdr["S"]].reshape(-1, 4)
+    if hdr["version"] == 2:
+        order = np.asarray(map_host[8 + (W + 1) + (U + 1) + 2 * U + 4 * hdr["S"]:], dtype=np.int64)
+        segs = segs[order[:hdr["S"]]]
+    seg_tokens = np.maximum(segs[:, 3] - segs[:, 2], 0)
+    list_tokens = np.array([seg_tokens[wptr[w]:wptr[w + 1]].sum() for w in range(W)], dtype=np.float64)
+    per_launch = W * head_groups
+    b = np.arange(t.shape[0]) % per_launch
+    w = b % W if hdr["version"] == MAP_VERSION_PLACED else b // head_groups
+    xcc = t[:, 3] & 0xF
+    dur = (t[:, 1] - t[:, 0]).astype(np.float64)
+    rate = np.zeros(XCDS)
+    for x in range(XCDS):
+        sel = xcc == x
+        if dur[sel].sum() <= 0:
+            raise ValueError(f"no timed workgroup ran on XCD {x}")
+        rate[x] = list_tokens[w[sel]].sum() / dur[sel].sum()
+    return [max(1, int(round(scale_to * r / rate.max()))) for r in rate]
+
+
+def calibrate_xcd_rates(step: "DecodeStep", q, k_cache, v_cache, block_table, scale: float, launches: int = 3,
+                        kv_scales=None) -> List[int]:
+    """Run ``step``'s split-KV launch ``launches`` times with the kernel's timestamps on (after one
+    untimed launch) and return the per-XCD rates of ``xcd_rates_from_timing``: the input of
+    ``DecodeStep(..., planner="rated", xcd_rates=...)``.  With eight head groups every XCD runs one
+    head group of every list, so the XCDs stream equal work and only their rates differ."""
+    if step.resident:
+        raise ValueError("calibrate on a static launch (no run-time claiming)")
+    step.splitkv(q, k_cache, v_cache, block_table, scale, kv_scales=kv_scales)
+    n = step.W * step.head_groups
+    timing = torch.zeros((launches, n, 4), dtype=torch.int64, device=step.device)
+    for i in range(launches):
+        step.splitkv(q, k_cache, v_cache, block_table, scale, timing=timing[i], kv_scales=kv_scales)
+    torch.cuda.synchronize(step.device)
+    return xcd_rates_from_timing(timing, step.map_host, step.head_groups)
 
 
 class DeviceDecodeStep:

@@ -222,6 +222,83 @@ def test_weighted_plan_errors():
             lb.attn_plan_weighted(*args)
 
 
+def test_rated_plan_bit_exact():
+    """attn_plan_rated (C++) reproduces the oracle's rate-proportional map word for word: random
+    batches with empty requests and partial tiles, random rates with zeros (leading, trailing and
+    inside), split costs, the bench workloads at per-XCD rates like the device's, and lengths and
+    rates at their limits."""
+    import load_balanced_split_attn_amd as lb
+    from oracle.plan import RATE_MAX, ref_plan_rated
+    rng = np.random.default_rng(29)
+    for _ in range(600):
+        B = int(rng.integers(0, 14))
+        W = int(rng.integers(1, 24))
+        tile = int(rng.choice([16, 64, 128, 512]))
+        sc = int(rng.choice([0, 1, 64, 256, 5000]))
+        lens = [int(x) if rng.random() > 0.2 else 0 for x in rng.integers(1, 5000, size=B)]
+        hi = int(rng.choice([2, 100, RATE_MAX]))
+        rates = [int(x) if rng.random() > 0.25 else 0 for x in rng.integers(1, hi + 1, size=W)]
+        if sum(rates) == 0:
+            rates[-1] = 1
+        got = lb.attn_plan_rated(lens, W, rates, tile, sc)
+        assert np.array_equal(got, ref_plan_rated(lens, W, tile, sc, rates)), (lens, W, tile, sc, rates)
+    import workloads as WL
+    xcd = [65536, 61440, 65000, 61900, 64800, 62000, 65536, 61000]
+    for name in ("tiny", "uniform", "mixed", "long_tail", "mixed_tp8"):
+        wl = WL.BY_NAME[name]()
+        W = wl.workers or 128
+        rates = [xcd[w % 8] for w in range(W)]
+        for tile, sc in ((512, 0), (128, 0), (64, 256)):
+            assert np.array_equal(lb.attn_plan_rated(wl.kv_lens, W, rates, tile, sc),
+                                  ref_plan_rated(wl.kv_lens, W, tile, sc, rates)), (name, tile, sc)
+    big = [2**31 - 1, 2**31 - 1, 5]
+    rates = [RATE_MAX, 1, 0, RATE_MAX - 1, 7, 0, RATE_MAX]
+    assert np.array_equal(lb.attn_plan_rated(big, 7, rates, 2**20, 2**30),
+                          ref_plan_rated(big, 7, 2**20, 2**30, rates))
+
+
+def test_rated_plan_errors():
+    import load_balanced_split_attn_amd as lb
+    for args in (([10], 2, [1, 1], 64, -1), ([10], 2, [0, 0], 64, 0), ([10], 2, [1, -1], 64, 0),
+                 ([10], 2, [1, lb.RATE_MAX + 1], 64, 0), ([10], 2, [1, 1], 0, 0), ([-1], 2, [1, 1], 64, 0)):
+        with pytest.raises(lb.LbsaError):
+            lb.attn_plan_rated(*args)
+    with pytest.raises(ValueError):
+        lb.attn_plan_rated([10], 2, [1, 1, 1])
+    L = lb.lib()
+    i32 = ctypes.c_int32
+    buf = (i32 * 64)()
+    assert L.attn_plan_rated((i32 * 1)(10), 1, 2, 64, 0, None, buf, 64, None) == -1
+
+
+def test_xcd_rates_from_timing():
+    """Per-XCD rates from synthetic timestamp records: XCD x's workgroups take d_x per token, so its
+    rate is 1 / d_x, for a version-1 map with eight head groups (workgroup b on list b // 8, every
+    XCD one head group of every list) and for a version-3 map (list b mod W, lists on XCD w mod 8)."""
+    import torch
+
+    import load_balanced_split_attn_amd as lb
+    from load_balanced_split_attn_amd.decode import xcd_rates_from_timing
+    lens = [1000, 3000, 512, 7000, 0, 2222, 4096, 100, 9000, 333]
+    speed = np.array([1.0, 0.95, 1.0, 0.93, 0.99, 0.94, 1.0, 0.96])
+    for words in (lb.attn_plan(lens, 16, 128), lb.attn_plan_rated(lens, 16, [3] * 16, 128)):
+        hdr = lb.map_header(words)
+        W = hdr["W"]
+        wptr = words[8:8 + W + 1]
+        segs = words[8 + (W + 1) + (hdr["U"] + 1) + 2 * hdr["U"]:].reshape(-1, 4)
+        tokens = [int((segs[wptr[w]:wptr[w + 1], 3] - segs[wptr[w]:wptr[w + 1], 2]).sum()) for w in range(W)]
+        rows = []
+        for rep in range(2):
+            for b in range(W * 8):
+                w = b % W if hdr["version"] == 3 else b // 8
+                x = b % 8
+                start = 1000 * rep + b
+                rows.append([start, start + int(round(tokens[w] / speed[x] * 1000)) + 1, 0, x])
+        got = xcd_rates_from_timing(torch.tensor(rows, dtype=torch.int64), words, 8)
+        want = np.round(65536 * speed / speed.max())
+        assert np.max(np.abs(np.array(got) - want)) <= 40, (got, want)
+
+
 def test_lpt_plan_bit_exact():
     """attn_plan_lpt (C++) reproduces the oracle's version-2 LPT map word for word."""
     import load_balanced_split_attn_amd as lb
