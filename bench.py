@@ -409,6 +409,48 @@ def claim_sweep(dev, wl, q, caches, bt, out, args, base_us: float) -> dict:
     return {"resident_workgroups": resident, "default_us": round(base_us, 2), "best": best, "sweep": rows}
 
 
+def rated_compare(dev, wl, base, q, caches, bt, out, args, base_us: float, split_bytes: int) -> dict:
+    """The rate-proportional map beside the default (equal-budget) one, on the same workers and tile:
+    per-XCD rates from the default launch's own timestamps (calibrate_xcd_rates: three instrumented
+    launches, every XCD running one head group of every list), then attn_plan_rated with worker w at
+    the rate of XCD w mod 8 (a version-3 map: list-major launch, every workgroup of list w on XCD
+    w mod 8).  Beside it, equal rates in the same list-major order, to separate the order from the
+    rates.  speedup = default step / this step."""
+    import numpy as np
+    import torch
+
+    from load_balanced_split_attn_amd.decode import DecodeStep, calibrate_xcd_rates
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    kc, vc = caches[0]
+    copies = len(caches)
+    G = base.head_groups
+    rates = calibrate_xcd_rates(base, q, kc, vc, bt, scale)
+    rows = []
+    for label, r in (("list-major, equal rates", [1] * 8), ("list-major, calibrated rates", rates)):
+        st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=base.W, tile=base.tile, head_groups=G,
+                        planner="rated", xcd_rates=r)
+
+        def split(i, st=st):
+            k_, v_ = caches[i % copies]
+            st.splitkv(q, k_, v_, bt, scale)
+
+        rs = time_steps(split, lambda i, st=st: st.combine(out), args.steps, args.warmup)
+        us = rs["total_ms"] / args.steps * 1e3
+        split_us = float(np.mean(rs["split_ms"])) * 1e3
+        timing = torch.zeros((st.W * G, 4), dtype=torch.int64, device=dev)
+        st.splitkv(q, kc, vc, bt, scale, timing=timing)
+        torch.cuda.synchronize()
+        rows.append({"map": label, "segments": st.S, "us_per_step": round(us, 2), "splitkv_us": round(split_us, 2),
+                     "splitkv_frac_hbm": round(split_bytes / (split_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                     "per_cu_max_over_mean": round(per_cu_busy(timing)["max_over_mean"], 3),
+                     "speedup": round(base_us / us, 4)})
+        log(f"{wl.name} rated map ({label}): {us:.1f} us/step vs {base_us:.1f} default")
+        del st
+    return {"what": "rate-proportional map (attn_plan_rated, version 3: list-major launch) against the "
+                    "default equal-budget map on the same workers and tile",
+            "xcd_rates": rates, "default_us": round(base_us, 2), "sweep": rows}
+
+
 def bench_decode_leg(dev, name: str, args) -> dict:
     """Another decode batch timed the way the headline batch is: split-KV + combine per step on the
     dynamic map, the split-KV kernel's roofline fraction, per-CU busy max/mean (median of five
@@ -484,6 +526,8 @@ def bench_decode_leg(dev, name: str, args) -> dict:
                                "speedup_vs_best": round(best["us_per_step"] / (ms * 1e3), 3), "sweep": rows}}
     if not args.no_claim:
         res["claimed"] = claim_sweep(dev, wl, q, caches, bt, out, args, ms * 1e3)
+    if not args.no_rated:
+        res["xcd_rated"] = rated_compare(dev, wl, step, q, caches, bt, out, args, ms * 1e3, nb["splitkv"])
     del caches, kc, vc, step
     torch.cuda.empty_cache()
     return res
@@ -898,6 +942,7 @@ def main() -> int:
                     help="prefill P.V paths to time: checked (the default), exact and/or fp16")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-claim", action="store_true", help="skip the run-time claiming comparison")
+    ap.add_argument("--no-rated", action="store_true", help="skip the rate-proportional map comparison")
     ap.add_argument("--legs", default="uniform,long_tail,mixed_tp8",
                     help="other decode batches timed beside the headline one (comma list, '' for none)")
     ap.add_argument("--only-prefill", action="store_true",
@@ -1048,6 +1093,10 @@ def main() -> int:
     step.splitkv(q, kc, vc, bt, scale, timing=timing)
     torch.cuda.synchronize()
     result["per_cu_busy"] = per_cu_busy(timing)
+
+    if not args.no_rated and wl.name != "tiny":
+        result["xcd_rated"] = rated_compare(dev, wl, step, q, caches, bt, out, args, ms_per_step * 1e3,
+                                            nbytes["splitkv"])
 
     if not args.no_static and wl.name != "tiny":
         max_tiles = max(-(-L // args.tile) for L in wl.kv_lens)
