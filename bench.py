@@ -410,12 +410,13 @@ def claim_sweep(dev, wl, q, caches, bt, out, args, base_us: float) -> dict:
 
 
 def rated_compare(dev, wl, base, q, caches, bt, out, args, base_us: float, split_bytes: int) -> dict:
-    """The rate-proportional map beside the default (equal-budget) one, on the same workers and tile:
-    per-XCD rates from the default launch's own timestamps (calibrate_xcd_rates: three instrumented
-    launches, every XCD running one head group of every list), then attn_plan_rated with worker w at
-    the rate of XCD w mod 8 (a version-3 map: list-major launch, every workgroup of list w on XCD
-    w mod 8).  Beside it, equal rates in the same list-major order, to separate the order from the
-    rates.  speedup = default step / this step."""
+    """The rate-proportional map beside the default (equal-budget) one, on the same workers: per-XCD
+    rates from the default launch's own timestamps (calibrate_xcd_rates: three instrumented launches,
+    every XCD running one head group of every list), then attn_plan_rated with worker w at the rate
+    of XCD w mod 8 (a version-3 map: list-major launch, every workgroup of list w on XCD w mod 8), at
+    the default tile and at 128-token tiles (short lists need the finer steps).  Beside them, equal
+    rates in the same list-major order (the order alone) and the equal-budget map at 128-token tiles
+    (the tile alone).  speedup = default step / this step."""
     import numpy as np
     import torch
 
@@ -426,9 +427,12 @@ def rated_compare(dev, wl, base, q, caches, bt, out, args, base_us: float, split
     G = base.head_groups
     rates = calibrate_xcd_rates(base, q, kc, vc, bt, scale)
     rows = []
-    for label, r in (("list-major, equal rates", [1] * 8), ("list-major, calibrated rates", rates)):
-        st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=base.W, tile=base.tile, head_groups=G,
-                        planner="rated", xcd_rates=r)
+    for label, tile, r in (("list-major, equal rates", base.tile, [1] * 8),
+                           ("list-major, calibrated rates", base.tile, rates),
+                           ("equal budgets, 128-token tiles", 128, None),
+                           ("list-major, calibrated rates, 128-token tiles", 128, rates)):
+        kw = dict(planner="rated", xcd_rates=r) if r is not None else {}
+        st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=base.W, tile=tile, head_groups=G, **kw)
 
         def split(i, st=st):
             k_, v_ = caches[i % copies]
@@ -440,11 +444,12 @@ def rated_compare(dev, wl, base, q, caches, bt, out, args, base_us: float, split
         timing = torch.zeros((st.W * G, 4), dtype=torch.int64, device=dev)
         st.splitkv(q, kc, vc, bt, scale, timing=timing)
         torch.cuda.synchronize()
-        rows.append({"map": label, "segments": st.S, "us_per_step": round(us, 2), "splitkv_us": round(split_us, 2),
+        rows.append({"map": label, "tile": tile, "segments": st.S, "us_per_step": round(us, 2),
+                     "splitkv_us": round(split_us, 2),
                      "splitkv_frac_hbm": round(split_bytes / (split_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                      "per_cu_max_over_mean": round(per_cu_busy(timing)["max_over_mean"], 3),
                      "speedup": round(base_us / us, 4)})
-        log(f"{wl.name} rated map ({label}): {us:.1f} us/step vs {base_us:.1f} default")
+        log(f"{wl.name} {label}: {us:.1f} us/step vs {base_us:.1f} default")
         del st
     return {"what": "rate-proportional map (attn_plan_rated, version 3: list-major launch) against the "
                     "default equal-budget map on the same workers and tile",
