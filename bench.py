@@ -1225,6 +1225,30 @@ def main() -> int:
             best = gbs if best is None else max(best, gbs)
         result["stream_read_ceiling"] = {"GB/s": round(best, 1), "buffer_GB": round(kc.numel() * 2 / 1e9, 2),
                                          "splitkv_frac_of_ceiling": round(achieved / best, 4)}
+        rated = result.get("xcd_rated")
+        if rated:
+            # the same read with each XCD's share in proportion to the rates calibrated above: the
+            # ceiling for work shared out by XCD rate (equal shares leave the faster XCDs idle at the end)
+            best_r = None
+            for blocks in (1024, 2048, 4096):
+                for _ in range(2):
+                    lb.attn_probe_stream_read_rated(kc, blocks, rated["xcd_rates"], sink)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(10):
+                    lb.attn_probe_stream_read_rated(kc, blocks, rated["xcd_rates"], sink)
+                e1.record()
+                torch.cuda.synchronize()
+                gbs = kc.numel() * 2 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+                best_r = gbs if best_r is None else max(best_r, gbs)
+            row = next(x for x in rated["sweep"] if x["map"] == "list-major, calibrated rates")
+            rated_gbs = nbytes["splitkv"] / (row["splitkv_us"] * 1e-6) / 1e9
+            result["stream_read_ceiling"].update({
+                "xcd_rated_GB/s": round(best_r, 1),
+                "splitkv_frac_of_xcd_rated_ceiling": round(achieved / best_r, 4),
+                "rated_map_splitkv_frac_of_xcd_rated_ceiling": round(rated_gbs / best_r, 4)})
+            log(f"streaming-read ceiling {best:.0f} GB/s, with per-XCD shares {best_r:.0f} GB/s")
 
     if not args.no_fp8:
         result["fp8_kv"] = bench_fp8(dev, wl, args, ms_per_step * 1e3)

@@ -20,7 +20,7 @@ __all__ = [
     "attn_plan_lpt", "attn_plan_weighted", "attn_plan_rated", "MAP_VERSION_PLACED", "RATE_MAX",
     "attn_query_workers", "attn_splitkv", "attn_splitkv_fp8", "attn_splitkv_mtp", "attn_splitkv_prefill",
     "attn_combine", "attn_store_kv", "attn_store_kv_chunk", "attn_kv_layout", "attn_decode_noalloc", "attn_splitkv_claimed", "NOALLOC_SCRATCH_BYTES",
-    "attn_status_string", "attn_probe_stream_read", "attn_probe_mfma_rate", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
+    "attn_status_string", "attn_probe_stream_read", "attn_probe_stream_read_rated", "attn_probe_mfma_rate", "map_header", "LIB_PATH", "KV_BF16", "KV_FP8_E4M3",
 ]
 
 # cache element types (LBSA_KV_* in include/lbsa.h)
@@ -75,6 +75,7 @@ _SIGNATURES = {
                                     _c_i32, _c_i32, _c_vp, _c_i32, _c_i32, _c_vp]),
     "attn_probe_stream_read": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_vp, _c_vp]),
     "attn_probe_mfma_rate": (ctypes.c_int, [_c_i32, _c_i32, _c_vp, _c_vp]),
+    "attn_probe_stream_read_rated": (ctypes.c_int, [_c_vp, ctypes.c_int64, _c_i32, _c_i32p, _c_vp, _c_vp]),
     "attn_decode_noalloc": (ctypes.c_int, [_c_vp, _c_vp, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_vp,
                                            _c_vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                            ctypes.c_float, _c_i32, _c_vp, _c_i32, _c_vp]),
@@ -627,6 +628,20 @@ def attn_probe_stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor, s
     nbytes = buf.numel() * buf.element_size()
     _check(lib().attn_probe_stream_read(_dptr(buf), nbytes - nbytes % 16, blocks, _dptr(sink), _stream(stream)),
            "attn_probe_stream_read")
+
+
+def attn_probe_stream_read_rated(buf: torch.Tensor, blocks: int, xcd_rates: Sequence[int], sink: torch.Tensor,
+                                 stream=None) -> None:
+    """Read all of ``buf`` once, XCD x's workgroups taking a share in proportion to xcd_rates[x]
+    (measurement helper: the streaming-read ceiling when work follows the XCDs' rates)."""
+    if not buf.is_cuda or not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < blocks * 256:
+        raise ValueError("attn_probe_stream_read_rated: need a contiguous GPU buffer and an int32 sink of blocks*256")
+    r = _i32_host(xcd_rates)
+    if len(r) != 8:
+        raise ValueError("attn_probe_stream_read_rated: need eight rates, one per XCD")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().attn_probe_stream_read_rated(_dptr(buf), nbytes - nbytes % 16, blocks, _ptr_i32(r), _dptr(sink),
+                                              _stream(stream)), "attn_probe_stream_read_rated")
 
 
 def attn_probe_mfma_rate(iters: int, blocks: int, sink: torch.Tensor, stream=None) -> int:

@@ -36,6 +36,51 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
   sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+// Streaming read with per-XCD shares: workgroup b runs on XCD b mod 8 (the dispatcher's order).
+// The buffer is cut into steps of UNROLL KiB, dealt to the XCDs in repeating cycles of
+// L = q[0] + ... + q[7] steps, XCD x owning q[x] consecutive steps of each cycle; XCD x's waves take
+// its steps in turn.  All XCDs move through the buffer together, as in stream_read_kernel, each at
+// its own share; with q in proportion to the XCDs' streaming rates every XCD finishes at once, which
+// equal shares do not give when the XCDs differ.  The sub-step tail is read by workgroup 0.
+struct XcdShares {
+  int32_t q[8];
+};
+
+template <int UNROLL>
+__global__ __launch_bounds__(256) void stream_read_rated_kernel(const u32x4* __restrict__ buf, int64_t n16,
+                                                                XcdShares sh, uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int x = blockIdx.x & 7;
+  const int64_t wx = (int64_t)(blockIdx.x >> 3) * 4 + (threadIdx.x >> 6);   // wave index inside XCD x
+  const int64_t waves_x = (int64_t)(gridDim.x >> 3) * 4;
+  int L = 0, pre = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pre += i < x ? sh.q[i] : 0;
+    L += sh.q[i];
+  }
+  const int qx = sh.q[x];
+  const int64_t step_elems = 64 * UNROLL;
+  const int64_t n_steps = n16 / step_elems;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  if (qx > 0) {
+    for (int64_t k = wx;; k += waves_x) {
+      const int64_t c = k / qx;
+      const int64_t step = c * L + pre + (k - c * qx);   // increases with k
+      if (step >= n_steps) break;
+      const u32x4* src = buf + step * step_elems + lane;
+      u32x4 v[UNROLL];
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) v[u] = __builtin_nontemporal_load(src + 64 * u);
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u) acc ^= v[u];
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x < 64)
+    for (int64_t i = n_steps * step_elems + lane; i < n16; i += 64) acc ^= buf[i];
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
 // Matrix-core rate: each wave issues `iters` rounds of eight independent v_mfma_f32_16x16x32_bf16
 // products whose operands sit in registers (nothing is read from memory), so the launch measures the
 // matrix pipes at the clock the chip holds while they run flat out.  The operands cycle over four
@@ -85,6 +130,28 @@ extern "C" int attn_probe_mfma_rate(int32_t iters, int32_t blocks, uint32_t* sin
   if (!sink || iters < 1 || blocks < 1 || (reinterpret_cast<uintptr_t>(sink) & 3)) return LBSA_ERR_INVALID;
   hipLaunchKernelGGL(lbsa::mfma_rate_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream), iters,
                      sink);
+  return hipGetLastError() == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;
+}
+
+extern "C" int attn_probe_stream_read_rated(const void* buf, int64_t bytes, int32_t blocks, const int32_t* xcd_rates,
+                                            uint32_t* sink, void* stream) {
+  if (!buf || !sink || !xcd_rates || bytes < 0 || (bytes & 15) || blocks < 8 || (blocks & 7) ||
+      (reinterpret_cast<uintptr_t>(buf) & 15))
+    return LBSA_ERR_INVALID;
+  int32_t top = 0;
+  for (int i = 0; i < 8; ++i) {
+    if (xcd_rates[i] < 0 || xcd_rates[i] > LBSA_RATE_MAX) return LBSA_ERR_INVALID;
+    top = xcd_rates[i] > top ? xcd_rates[i] : top;
+  }
+  if (top == 0) return LBSA_ERR_INVALID;
+  // steps per cycle: the rates scaled so the fastest XCD owns 64 (a positive rate owns at least one)
+  lbsa::XcdShares sh;
+  for (int i = 0; i < 8; ++i) {
+    const int64_t q = ((int64_t)xcd_rates[i] * 64 + top / 2) / top;
+    sh.q[i] = xcd_rates[i] > 0 && q == 0 ? 1 : (int32_t)q;
+  }
+  hipLaunchKernelGGL(lbsa::stream_read_rated_kernel<LBSA_PROBE_UNROLL>, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const lbsa::u32x4*>(buf), bytes / 16, sh, sink);
   return hipGetLastError() == hipSuccess ? LBSA_OK : LBSA_ERR_HIP;
 }
 

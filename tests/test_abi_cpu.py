@@ -182,6 +182,13 @@ def test_errors_and_capacity(L):
     assert lib.attn_probe_stream_read(None, 16, 1, dummy, None) == -1
     assert lib.attn_probe_stream_read(dummy, 15, 1, dummy, None) == -1
     assert lib.attn_probe_stream_read(dummy, 16, 0, dummy, None) == -1
+    rates8 = (ctypes.c_int32 * 8)(1, 1, 1, 1, 1, 1, 1, 1)
+    zeros8 = (ctypes.c_int32 * 8)()
+    assert lib.attn_probe_stream_read_rated(dummy, 16, 12, rates8, dummy, None) == -1     # not a multiple of 8
+    assert lib.attn_probe_stream_read_rated(dummy, 16, 0, rates8, dummy, None) == -1
+    assert lib.attn_probe_stream_read_rated(dummy, 16, 8, zeros8, dummy, None) == -1
+    assert lib.attn_probe_stream_read_rated(dummy, 16, 8, None, dummy, None) == -1
+    assert lib.attn_probe_stream_read_rated(None, 16, 8, rates8, dummy, None) == -1
     assert lib.attn_probe_mfma_rate(0, 1, dummy, None) == -1
     assert lib.attn_probe_mfma_rate(1, 0, dummy, None) == -1
     assert lib.attn_probe_mfma_rate(1, 1, None, None) == -1

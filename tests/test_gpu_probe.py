@@ -1,8 +1,9 @@
 """The measurement probes do the work their rates are computed from.
 
-* attn_probe_stream_read reads every 16-byte element of its buffer exactly once: the XOR of all
-  per-thread digests equals the XOR of all 32-bit words of the buffer (an element read twice or
-  skipped would cancel or drop its bits), for sizes with and without a ragged tail.
+* attn_probe_stream_read and attn_probe_stream_read_rated read every 16-byte element of their buffer
+  exactly once: the XOR of all per-thread digests equals the XOR of all 32-bit words of the buffer
+  (an element read twice or skipped would cancel or drop its bits), for sizes with and without a
+  ragged tail, and (rated) for uneven per-XCD shares, zero shares and all of it on one XCD.
 * attn_probe_mfma_rate performs all blocks * 4 * iters * 8 products of 16 x 16 x 32: each thread's
   digest equals the sum, over its eight accumulators, of the entries of A.B that the matrix core
   leaves in that lane (A and B rebuilt on the host from the probe's hash, in fp64), times `iters` —
@@ -34,6 +35,24 @@ def test_stream_read_touches_every_element_once(lb, nbytes, blocks):
     sink = torch.zeros(blocks * 256, dtype=torch.int32, device="cuda")
     note(f"stream probe {nbytes} B over {blocks} blocks")
     lb.attn_probe_stream_read(buf, blocks, sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
+    assert got == want
+
+
+@pytest.mark.parametrize("nbytes,blocks,rates", [
+    (16 * 1000003, 64, [65536, 61000, 65536, 60000, 64000, 62000, 65000, 61500]),
+    (1 << 24, 1024, [1, 0, 3, 0, 1, 1, 7, 2]),
+    (16 * 4097, 8, [0, 0, 0, 5, 0, 0, 0, 0]),
+])
+def test_rated_stream_read_touches_every_element_once(lb, nbytes, blocks, rates):
+    g = torch.Generator().manual_seed(nbytes + blocks)
+    host = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), generator=g, dtype=torch.int32)
+    buf = host.cuda()
+    sink = torch.zeros(blocks * 256, dtype=torch.int32, device="cuda")
+    note(f"rated stream probe {nbytes} B over {blocks} blocks, rates {rates}")
+    lb.attn_probe_stream_read_rated(buf, blocks, rates, sink)
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
     want = np.bitwise_xor.reduce(host.numpy().view(np.uint32))
