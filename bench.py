@@ -409,7 +409,8 @@ def claim_sweep(dev, wl, q, caches, bt, out, args, base_us: float) -> dict:
     return {"resident_workgroups": resident, "default_us": round(base_us, 2), "best": best, "sweep": rows}
 
 
-def rated_compare(dev, wl, base, q, caches, bt, out, args, base_us: float, split_bytes: int) -> dict:
+def rated_compare(dev, wl, base, q, caches, bt, out, args, base_us: float, split_bytes: int,
+                  kv_scales=None) -> dict:
     """The rate-proportional map beside the default (equal-budget) one, on the same workers: per-XCD
     rates from the default launch's own timestamps (calibrate_xcd_rates: three instrumented launches,
     every XCD running one head group of every list), then attn_plan_rated with worker w at the rate
@@ -425,24 +426,25 @@ def rated_compare(dev, wl, base, q, caches, bt, out, args, base_us: float, split
     kc, vc = caches[0]
     copies = len(caches)
     G = base.head_groups
-    rates = calibrate_xcd_rates(base, q, kc, vc, bt, scale)
+    rates = calibrate_xcd_rates(base, q, kc, vc, bt, scale, kv_scales=kv_scales)
     rows = []
     for label, tile, r in (("list-major, equal rates", base.tile, [1] * 8),
                            ("list-major, calibrated rates", base.tile, rates),
                            ("equal budgets, 128-token tiles", 128, None),
                            ("list-major, calibrated rates, 128-token tiles", 128, rates)):
         kw = dict(planner="rated", xcd_rates=r) if r is not None else {}
-        st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=base.W, tile=tile, head_groups=G, **kw)
+        st = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=base.W, tile=tile, head_groups=G,
+                        kv_dtype=base.kv_dtype, **kw)
 
         def split(i, st=st):
             k_, v_ = caches[i % copies]
-            st.splitkv(q, k_, v_, bt, scale)
+            st.splitkv(q, k_, v_, bt, scale, kv_scales=kv_scales)
 
         rs = time_steps(split, lambda i, st=st: st.combine(out), args.steps, args.warmup)
         us = rs["total_ms"] / args.steps * 1e3
         split_us = float(np.mean(rs["split_ms"])) * 1e3
         timing = torch.zeros((st.W * G, 4), dtype=torch.int64, device=dev)
-        st.splitkv(q, kc, vc, bt, scale, timing=timing)
+        st.splitkv(q, kc, vc, bt, scale, timing=timing, kv_scales=kv_scales)
         torch.cuda.synchronize()
         rows.append({"map": label, "tile": tile, "segments": st.S, "us_per_step": round(us, 2),
                      "splitkv_us": round(split_us, 2),
@@ -588,7 +590,10 @@ def bench_fp8(dev, wl, args, bf16_us: float) -> dict:
     step.splitkv(q, kc, vc, bt, scale, timing=timing, kv_scales=(ks, vs))
     torch.cuda.synchronize()
     log(f"fp8 cache: step {ms * 1e3:.1f} us, splitkv {split_ms * 1e3:.1f} us ({achieved:.0f} GB/s)")
-    return {"workload": DESCRIPTIONS[wl.name].replace("bf16, paged", "bf16 q, E4M3 KV with per-head fp32 scales, "
+    rated = None
+    if not args.no_rated and wl.name != "tiny":
+        rated = rated_compare(dev, wl, step, q, caches, bt, out, args, ms * 1e3, nb["splitkv"], kv_scales=(ks, vs))
+    res = {"workload": DESCRIPTIONS[wl.name].replace("bf16, paged", "bf16 q, E4M3 KV with per-head fp32 scales, "
                                                                      "paged"),
             "algorithmic_bytes": nb["step"], "us_per_step": round(ms * 1e3, 2),
             "value": round(nb["step"] / (ms * 1e-3) / 1e12, 4), "unit": "TB/s",
@@ -600,6 +605,9 @@ def bench_fp8(dev, wl, args, bf16_us: float) -> dict:
                          "bytes_per_launch": nb["splitkv"], "avg_launch_us": round(split_ms * 1e3, 2)},
             "combine_us": round(float(np.mean(r["combine_ms"])) * 1e3, 2),
             "per_cu_busy": per_cu_busy(timing)}
+    if rated:
+        res["xcd_rated"] = rated
+    return res
 
 
 def bench_mtp(dev, base: str, args, decode_us: float) -> dict:
