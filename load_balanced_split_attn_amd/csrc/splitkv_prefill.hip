@@ -149,13 +149,14 @@ __device__ __forceinline__ u32x4 raw_rsrc(const void* p, int bytes) {
 // compiler's wait-count pass no longer tells the LDS stages apart and would make every LDS read wait
 // for all outstanding copies.  The kernel waits for its own copies (vmcnt) and publishes them with
 // a barrier before any wave reads them; the memory clobber keeps LDS accesses in program order
-// around the copy.
+// around the copy.  The LDS address goes in as an operand bound to M0, so the compiler sets M0
+// itself and knows its value; the s_nop gives the M0 write the wait state the copy needs.
 __device__ __forceinline__ void lds_dma16(u32x4 rsrc, const uint8_t* lds, int voff, int soff) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LBSA_LDS(lds)));
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                :
-               : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+               : "memory");
 }
 
 // Read-only kernel inputs read at wave-uniform addresses (block table): the constant address
