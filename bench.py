@@ -251,6 +251,17 @@ def prefill_unique_bytes(wl, segments: int, q_tile: int) -> int:
     return q_bytes + kv_bytes + part_bytes
 
 
+def optional_section(name: str, fn):
+    """Run a comparison section that the headline does not depend on; a Python error in it (say, a
+    device partitioned into fewer XCDs than the rated map assumes) is recorded in the line instead
+    of ending the run."""
+    try:
+        return fn()
+    except Exception as e:   # noqa: BLE001 - recorded in the output, never silent
+        log(f"{name}: skipped ({type(e).__name__}: {e})")
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
 def mfma_ceiling(dev, prefill_tflops: float) -> dict:
     """The bf16 rate this device's matrix cores sustain, measured beside the prefill kernel: the
     register-only probe (v_mfma_f32_16x16x32_bf16 flat out, 1,024 workgroups of four waves, eight
@@ -361,7 +372,7 @@ def bench_prefill(dev, workers_list, steps: int, warmup: int, q_tiles=(128, 256)
                          "unique_bytes": prefill_unique_bytes(wl, stated["segments"], stated["q_tile"])},
             "fastest": {k: fastest[k] for k in ("q_tile", "pv", "workers", "us_per_step", "splitkv_us",
                                                  "splitkv_tflops", "frac_of_bf16_peak")},
-            "mfma_ceiling": mfma_ceiling(dev, stated["splitkv_tflops"]),
+            "mfma_ceiling": optional_section("mfma_ceiling", lambda: mfma_ceiling(dev, stated["splitkv_tflops"])),
             "sweep": rows}
 
 
@@ -534,7 +545,8 @@ def bench_decode_leg(dev, name: str, args) -> dict:
     if not args.no_claim:
         res["claimed"] = claim_sweep(dev, wl, q, caches, bt, out, args, ms * 1e3)
     if not args.no_rated:
-        res["xcd_rated"] = rated_compare(dev, wl, step, q, caches, bt, out, args, ms * 1e3, nb["splitkv"])
+        res["xcd_rated"] = optional_section(
+            "xcd_rated", lambda: rated_compare(dev, wl, step, q, caches, bt, out, args, ms * 1e3, nb["splitkv"]))
     del caches, kc, vc, step
     torch.cuda.empty_cache()
     return res
@@ -592,7 +604,8 @@ def bench_fp8(dev, wl, args, bf16_us: float) -> dict:
     log(f"fp8 cache: step {ms * 1e3:.1f} us, splitkv {split_ms * 1e3:.1f} us ({achieved:.0f} GB/s)")
     rated = None
     if not args.no_rated and wl.name != "tiny":
-        rated = rated_compare(dev, wl, step, q, caches, bt, out, args, ms * 1e3, nb["splitkv"], kv_scales=(ks, vs))
+        rated = optional_section("xcd_rated", lambda: rated_compare(dev, wl, step, q, caches, bt, out, args, ms * 1e3,
+                                                                    nb["splitkv"], kv_scales=(ks, vs)))
     res = {"workload": DESCRIPTIONS[wl.name].replace("bf16, paged", "bf16 q, E4M3 KV with per-head fp32 scales, "
                                                                      "paged"),
             "algorithmic_bytes": nb["step"], "us_per_step": round(ms * 1e3, 2),
@@ -1108,8 +1121,9 @@ def main() -> int:
     result["per_cu_busy"] = per_cu_busy(timing)
 
     if not args.no_rated and wl.name != "tiny":
-        result["xcd_rated"] = rated_compare(dev, wl, step, q, caches, bt, out, args, ms_per_step * 1e3,
-                                            nbytes["splitkv"])
+        result["xcd_rated"] = optional_section(
+            "xcd_rated", lambda: rated_compare(dev, wl, step, q, caches, bt, out, args, ms_per_step * 1e3,
+                                               nbytes["splitkv"]))
 
     if not args.no_static and wl.name != "tiny":
         max_tiles = max(-(-L // args.tile) for L in wl.kv_lens)
@@ -1234,7 +1248,7 @@ def main() -> int:
         result["stream_read_ceiling"] = {"GB/s": round(best, 1), "buffer_GB": round(kc.numel() * 2 / 1e9, 2),
                                          "splitkv_frac_of_ceiling": round(achieved / best, 4)}
         rated = result.get("xcd_rated")
-        if rated:
+        if rated and "error" not in rated:
             # the same read with each XCD's share in proportion to the rates calibrated above: the
             # ceiling for work shared out by XCD rate (equal shares leave the faster XCDs idle at the end)
             best_r = None

@@ -1,6 +1,7 @@
 """CPU checks of the measurement arithmetic in bench.py: algorithmic bytes per step (against totals
 worked out by hand from the workload definitions), prefill flops (against a brute-force count of
-visible (row, key) pairs) and the per-CU busy union (against synthetic timestamp records)."""
+visible (row, key) pairs), the per-CU busy union (against synthetic timestamp records), and that an
+optional comparison section records its error instead of ending the run."""
 
 import numpy as np
 import pytest
@@ -74,3 +75,15 @@ def test_per_cu_busy_union():
     assert r["max_over_mean"] == pytest.approx(busy.max() / busy.mean())
     assert r["tail_fraction"] == pytest.approx((busy.max() - busy.mean()) / busy.max())
     assert r["mean_busy_over_span"] == pytest.approx(busy.mean() / 40)
+
+
+def test_optional_section_records_errors():
+    """A comparison section that fails records its error in the line; one that works returns its
+    result unchanged."""
+    assert bench.optional_section("ok", lambda: {"x": 1}) == {"x": 1}
+
+    def broken():
+        raise ValueError("no timed workgroup ran on XCD 3")
+
+    got = bench.optional_section("broken", broken)
+    assert got == {"error": "ValueError: no timed workgroup ran on XCD 3"}
