@@ -1,7 +1,7 @@
 """Seeded random sweep of the GPU paths against the fp64 oracle.  Each case draws its own
 configuration from its seed, so the sweep crosses options the hand-picked cases take one at a time:
-decode (planner greedy / LPT / cost-weighted, workers, head groups, tile 64-1024, page 64-256,
-bf16 or E4M3 cache, empty requests), chunked prefill (unit height, P.V mode, causal or not, KV tile,
+decode (planner greedy / LPT / cost-weighted, and rate-proportional with random rates, workers, head
+groups, tile 64-1024, page 64-256, bf16 or E4M3 cache, empty requests), chunked prefill (unit height, P.V mode, causal or not, KV tile,
 page) and multi-token decode (0-4 rows, bf16 or E4M3, page).  Pads and partial buffers hold NaN, so a
 read outside a request's keys or a slot the combine should not touch shows up in the output."""
 
@@ -13,7 +13,7 @@ import workloads as WL
 from gpu_helpers import (SCALE, assert_close, decode_inputs, decode_inputs_fp8, mtp_inputs, note, oracle_decode,
                          oracle_decode_fp8, oracle_mtp, prefill_inputs, q_starts)
 from oracle.attention import ref_attention
-from oracle.plan import ref_plan, ref_plan_lpt, ref_plan_prefill, ref_plan_weighted
+from oracle.plan import ref_plan, ref_plan_lpt, ref_plan_prefill, ref_plan_rated, ref_plan_weighted
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,6 @@ def _rng(kind: int, seed: int) -> np.random.Generator:
 
 @pytest.mark.parametrize("seed", range(64))
 def test_decode_sweep(lb, seed):
-    from load_balanced_split_attn_amd import map_header
     g = _rng(1, seed)
     batch = int(g.integers(1, 10))
     max_len = int(g.choice([200, 1000, 3000, 6000]))
@@ -57,6 +56,37 @@ def test_decode_sweep(lb, seed):
         words = lb.attn_plan_weighted(wl.kv_lens, W, tile, cost)
         ref_words = ref_plan_weighted(wl.kv_lens, W, tile, cost)
     assert np.array_equal(words, ref_words)
+    _run_decode_case(lb, wl, words, G, page, fp8, f"decode sweep {seed}")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_decode_sweep_rated(lb, seed):
+    """Rate-proportional (version-3, list-major) maps with random rates, zeros included."""
+    g = _rng(4, seed)
+    batch = int(g.integers(1, 10))
+    max_len = int(g.choice([200, 1000, 3000, 6000]))
+    wl = WL.random_decode(900 + seed, batch, max_len)
+    if g.random() < 0.3:
+        wl.kv_lens[int(g.integers(0, batch))] = 0
+    W = int(g.choice([8, 16, 24, int(g.integers(1, 41))]))
+    G = int(g.choice([1, 2, 4, 8]))
+    tile = int(g.choice([64, 128, 256, 512, 1024]))
+    page = int(g.choice([64, 128, 256]))
+    fp8 = bool(g.random() < 0.5)
+    cost = int(g.choice([0, 64, 512]))
+    rates = [int(r) if g.random() > 0.2 else 0 for r in g.integers(1, 1 << 16, size=W)]
+    if sum(rates) == 0:
+        rates[0] = 1
+    note(f"rated sweep {seed}: lens={wl.kv_lens} W={W} G={G} tile={tile} page={page} fp8={fp8} cost={cost} "
+         f"rates={rates}")
+    words = lb.attn_plan_rated(wl.kv_lens, W, rates, tile, cost)
+    assert np.array_equal(words, ref_plan_rated(wl.kv_lens, W, tile, cost, rates))
+    _run_decode_case(lb, wl, words, G, page, fp8, f"rated sweep {seed}")
+
+
+def _run_decode_case(lb, wl, words, G, page, fp8, what):
+    """One decode step over `words` with NaN in the pads and partial buffers, against the oracle."""
+    from load_balanced_split_attn_amd import map_header
     if fp8:
         inputs = decode_inputs_fp8(wl, page=page, pad_code=NAN_CODE)
         ref = oracle_decode_fp8(wl)
@@ -81,7 +111,7 @@ def test_decode_sweep(lb, seed):
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     for b in range(wl.batch):
-        assert_close(got[b], ref[b], f"decode sweep {seed} request {b} (L={wl.kv_lens[b]})")
+        assert_close(got[b], ref[b], f"{what} request {b} (L={wl.kv_lens[b]})")
 
 
 @pytest.mark.parametrize("seed", range(32))
