@@ -1097,6 +1097,7 @@ def main() -> int:
         "config": {"workload": DESCRIPTIONS[wl.name], "name": wl.name, "batch": wl.batch,
                    "kv_tokens": sum(wl.kv_lens), "q_heads": wl.hq, "kv_heads": wl.hkv, "head_dim": wl.head_dim,
                    "page": page, "tile": args.tile, "workers": step.W, "head_groups": args.head_groups,
+                   "launch_order": "list-major" if step.list_major else "head-major",
                    "segments": step.S, "tiles": step.T, "cache_copies": copies},
         "us_per_step": round(ms_per_step * 1e3, 2),
         "splitkv_us_p10_p50_p90": [round(float(np.percentile(r["split_ms"], p)) * 1e3, 2) for p in (10, 50, 90)],

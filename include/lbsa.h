@@ -166,7 +166,10 @@ int attn_plan_weighted(const int32_t* seq_lens, int32_t B, int32_t num_workers, 
  * head group b div W, so with W a multiple of 8 every workgroup of list w runs on XCD w mod 8 (the
  * dispatcher places workgroup b on XCD b mod 8) and per-XCD rates can be given per worker.
  * attn_combine and the run-time claiming launch (whose order comes from its counter) accept it; the
- * prefill kernel takes version 1 only.  O(B + T + W) time, no allocation.  Errors and capacity reporting as attn_plan_weighted
+ * prefill kernel takes version 1 only.  Any version-1 decode map may be launched in the same
+ * list-major order by setting its word 0 to LBSA_MAP_VERSION_PLACED (its other words unchanged; the
+ * partials are bitwise the same): that pays when the token totals of the lists on each XCD
+ * (w mod 8) are nearly equal, and costs when they are not.  O(B + T + W) time, no allocation.  Errors and capacity reporting as attn_plan_weighted
  * (LBSA_ERR_INVALID also for a NULL worker_rates, a rate outside the range, or all rates zero).
  */
 #define LBSA_MAP_VERSION_PLACED 3

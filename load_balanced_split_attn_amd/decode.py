@@ -19,6 +19,28 @@ from . import (KV_BF16, KV_FP8_E4M3, MAP_VERSION_PLACED, attn_combine, attn_plan
                attn_splitkv, attn_splitkv_claimed, attn_splitkv_fp8, map_header, max_splits_of)
 
 XCDS = 8   # accelerator complex dies; the dispatcher places workgroup b on XCD b mod 8
+LIST_MAJOR_BALANCE = 1.01   # largest per-XCD token max/mean at which "auto" launches list-major
+
+
+def list_tokens(map_host: np.ndarray) -> np.ndarray:
+    """KV tokens of each worker's list in a host work map (versions 1-3)."""
+    hdr = map_header(map_host)
+    W, U = hdr["W"], hdr["U"]
+    wptr = np.asarray(map_host[8:8 + W + 1], dtype=np.int64)
+    segs = np.asarray(map_host[8 + (W + 1) + (U + 1) + 2 * U:], dtype=np.int64)[:4 * hdr["S"]].reshape(-1, 4)
+    if hdr["version"] == 2:
+        order = np.asarray(map_host[8 + (W + 1) + (U + 1) + 2 * U + 4 * hdr["S"]:], dtype=np.int64)
+        segs = segs[order[:hdr["S"]]]
+    seg_tokens = np.maximum(segs[:, 3] - segs[:, 2], 0)
+    return np.array([seg_tokens[wptr[w]:wptr[w + 1]].sum() for w in range(W)], dtype=np.float64)
+
+
+def xcd_token_balance(map_host: np.ndarray) -> float:
+    """Largest over mean of the per-XCD token totals when list w runs on XCD w mod 8 (1.0 for a map
+    with no tokens)."""
+    tok = list_tokens(map_host)
+    per_xcd = np.array([tok[x::XCDS].sum() for x in range(XCDS)])
+    return float(per_xcd.max() / per_xcd.mean()) if per_xcd.mean() > 0 else 1.0
 
 
 class DecodeStep:
@@ -26,12 +48,21 @@ class DecodeStep:
                  head_groups: int = 8, num_q_heads: int = 64, head_dim: int = 128,
                  static_splits: Optional[int] = None, kv_dtype: int = KV_BF16, planner: str = "greedy",
                  split_cost: int = 0, resident_workgroups: Optional[int] = None,
-                 xcd_rates: Optional[Sequence[int]] = None):
+                 xcd_rates: Optional[Sequence[int]] = None, launch_order: str = "auto"):
         """resident_workgroups: run the split-KV kernel with run-time claiming (that many one-wave
         workgroups take the map's (list, KV head) items from a device counter) instead of one
         workgroup per (list, head group); needs head_groups equal to the KV head count.
         planner "rated": attn_plan_rated with worker w's rate xcd_rates[w mod 8] (the XCD its
-        workgroups run on in the map's list-major order; see ``calibrate_xcd_rates``)."""
+        workgroups run on in the map's list-major order; see ``calibrate_xcd_rates``).
+        launch_order: the order in which the split-KV launch runs a version-1 map's (list, head
+        group) workgroups.  "head": workgroup b takes list b div G, head group b mod G, so every XCD
+        runs one head group of every list and streams exactly the same tokens.  "list": workgroup b
+        takes list b mod W, head group b div W, so all of list w's workgroups run on XCD w mod 8 and
+        stream its pages' heads together (requested by writing the version-3 word into the device
+        copy of the map; the host map stays as planned).  "auto": list-major when the head groups
+        are more than one, W is a multiple of 8 and the per-XCD token totals under it are within 1%
+        of each other (``xcd_token_balance``): it measured 0.4-1.3% faster on such batches and up to
+        1.6% slower where whole lists leave the XCDs 2% apart.  The partials are the same either way."""
         device = torch.device(device)
         self.seq_lens_host = [int(x) for x in seq_lens]
         if static_splits is not None:
@@ -59,7 +90,17 @@ class DecodeStep:
         self.head_groups = head_groups
         self.kv_dtype = kv_dtype
         self.device = device
-        self.map = torch.from_numpy(self.map_host).to(device)
+        if launch_order not in ("auto", "head", "list"):
+            raise ValueError(f"unknown launch_order {launch_order!r} (auto, head or list)")
+        version = int(self.map_host[0])
+        self.list_major = version == MAP_VERSION_PLACED
+        if version == 1 and head_groups > 1 and self.W % XCDS == 0 and resident_workgroups is None:
+            self.list_major = launch_order == "list" or (
+                launch_order == "auto" and xcd_token_balance(self.map_host) <= LIST_MAJOR_BALANCE)
+        device_words = self.map_host.copy()
+        if self.list_major:
+            device_words[0] = MAP_VERSION_PLACED
+        self.map = torch.from_numpy(device_words).to(device)
         self.seq_lens = torch.tensor(self.seq_lens_host, dtype=torch.int32, device=device)
         S = max(self.S, 1)
         self.part_m = torch.empty((S, num_q_heads), dtype=torch.float32, device=device)
@@ -105,24 +146,21 @@ class DecodeStep:
 
 
 def xcd_rates_from_timing(timing: torch.Tensor, map_host: np.ndarray, head_groups: int,
-                          scale_to: int = 1 << 16) -> List[int]:
+                          scale_to: int = 1 << 16, list_major: Optional[bool] = None) -> List[int]:
     """Per-XCD streaming rates from one or more instrumented split-KV launches over ``map_host``
     (``timing`` rows as the kernel writes them: start, end, HW_ID, XCC_ID per workgroup; several
     launches stacked along the first axis): on each XCD, the KV tokens its workgroups streamed over
-    the sum of their durations.  Scaled so the fastest XCD has ``scale_to``."""
+    the sum of their durations.  Scaled so the fastest XCD has ``scale_to``.  ``list_major``: the
+    order the launches ran in (default: the map's own, list-major for version 3)."""
     t = timing.cpu().numpy().astype(np.int64).reshape(-1, 4)
     hdr = map_header(map_host)
-    W, U = hdr["W"], hdr["U"]
-    wptr = np.asarray(map_host[8:8 + W + 1], dtype=np.int64)
-    segs = np.asarray(map_host[8 + (W + 1) + (U + 1) + 2 * U:], dtype=np.int64)[:4 * hdr["S"]].reshape(-1, 4)
-    if hdr["version"] == 2:
-        order = np.asarray(map_host[8 + (W + 1) + (U + 1) + 2 * U + 4 * hdr["S"]:], dtype=np.int64)
-        segs = segs[order[:hdr["S"]]]
-    seg_tokens = np.maximum(segs[:, 3] - segs[:, 2], 0)
-    list_tokens = np.array([seg_tokens[wptr[w]:wptr[w + 1]].sum() for w in range(W)], dtype=np.float64)
+    W = hdr["W"]
+    tokens = list_tokens(map_host)
+    if list_major is None:
+        list_major = hdr["version"] == MAP_VERSION_PLACED
     per_launch = W * head_groups
     b = np.arange(t.shape[0]) % per_launch
-    w = b % W if hdr["version"] == MAP_VERSION_PLACED else b // head_groups
+    w = b % W if list_major else b // head_groups
     xcc = t[:, 3] & 0xF
     dur = (t[:, 1] - t[:, 0]).astype(np.float64)
     rate = np.zeros(XCDS)
@@ -130,7 +168,7 @@ def xcd_rates_from_timing(timing: torch.Tensor, map_host: np.ndarray, head_group
         sel = xcc == x
         if dur[sel].sum() <= 0:
             raise ValueError(f"no timed workgroup ran on XCD {x}")
-        rate[x] = list_tokens[w[sel]].sum() / dur[sel].sum()
+        rate[x] = tokens[w[sel]].sum() / dur[sel].sum()
     return [max(1, int(round(scale_to * r / rate.max()))) for r in rate]
 
 
@@ -138,8 +176,8 @@ def calibrate_xcd_rates(step: "DecodeStep", q, k_cache, v_cache, block_table, sc
                         kv_scales=None) -> List[int]:
     """Run ``step``'s split-KV launch ``launches`` times with the kernel's timestamps on (after one
     untimed launch) and return the per-XCD rates of ``xcd_rates_from_timing``: the input of
-    ``DecodeStep(..., planner="rated", xcd_rates=...)``.  With eight head groups every XCD runs one
-    head group of every list, so the XCDs stream equal work and only their rates differ."""
+    ``DecodeStep(..., planner="rated", xcd_rates=...)``.  Each XCD's rate is its tokens over its
+    workgroups' time, whichever order the step launches in."""
     if step.resident:
         raise ValueError("calibrate on a static launch (no run-time claiming)")
     step.splitkv(q, k_cache, v_cache, block_table, scale, kv_scales=kv_scales)
@@ -148,7 +186,7 @@ def calibrate_xcd_rates(step: "DecodeStep", q, k_cache, v_cache, block_table, sc
     for i in range(launches):
         step.splitkv(q, k_cache, v_cache, block_table, scale, timing=timing[i], kv_scales=kv_scales)
     torch.cuda.synchronize(step.device)
-    return xcd_rates_from_timing(timing, step.map_host, step.head_groups)
+    return xcd_rates_from_timing(timing, step.map_host, step.head_groups, list_major=step.list_major)
 
 
 class DeviceDecodeStep:

@@ -306,6 +306,25 @@ def test_xcd_rates_from_timing():
         assert np.max(np.abs(np.array(got) - want)) <= 40, (got, want)
 
 
+def test_xcd_token_balance():
+    """Per-XCD token totals under list-major placement (list w on XCD w mod 8), against sums taken
+    directly from the oracle's segments: equal on the uniform and mixed batches (whole tiles, budgets
+    that differ by one tile spread over the XCDs alike), 1.9% apart on the long-tail batch."""
+    import workloads as WL
+    from load_balanced_split_attn_amd.decode import LIST_MAJOR_BALANCE, list_tokens, xcd_token_balance
+    from oracle.plan import parse_map, ref_plan
+    for name, want in (("uniform", 1.0), ("mixed", 1.0), ("long_tail", 1.0190)):
+        words = ref_plan(WL.BY_NAME[name]().kv_lens, 128, 512)
+        mp = parse_map(words)
+        direct = np.array([sum(e - a for _, _, a, e in mp.worker_segments(w).tolist()) for w in range(mp.W)])
+        assert np.array_equal(list_tokens(words), direct)
+        per_xcd = np.array([direct[x::8].sum() for x in range(8)])
+        assert xcd_token_balance(words) == pytest.approx(per_xcd.max() / per_xcd.mean())
+        assert xcd_token_balance(words) == pytest.approx(want, abs=5e-4)
+    assert xcd_token_balance(ref_plan(WL.BY_NAME["long_tail"]().kv_lens, 128, 512)) > LIST_MAJOR_BALANCE
+    assert xcd_token_balance(ref_plan([0, 0], 16, 512)) == 1.0
+
+
 def test_lpt_plan_bit_exact():
     """attn_plan_lpt (C++) reproduces the oracle's version-2 LPT map word for word."""
     import load_balanced_split_attn_amd as lb

@@ -9,6 +9,8 @@ b mod W and head group b div W.
 * Calibrated: per-XCD rates from the kernel's own timestamps on the mixed batch, then the rated step
   at full size against the default step (an exact re-association: rel-RMS 1e-5) and the oracle on a
   sample of requests.
+* Launch order of a version-1 map (DecodeStep's launch_order): head-major and list-major give the
+  same partials bit for bit, and "auto" picks list-major only where the per-XCD totals are balanced.
 """
 
 import numpy as np
@@ -118,3 +120,41 @@ def test_calibrated_rates_full_size_mixed(lb):
         assert errors(got[b], want[b])[1] <= 1e-5, f"request {b}"
     for b in (0, 7, 21, 39):
         assert_close(got[b], oracle_decode(wl, [b])[b], f"rated mixed request {b} (L={wl.kv_lens[b]})")
+
+
+@pytest.mark.parametrize("G", [8, 4, 2])
+def test_launch_order_bitwise(lb, G):
+    """A version-1 map launched head-major and list-major (its device word 0 set to 3): the same
+    partials and output bit for bit; the host map stays the oracle's."""
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    from oracle.plan import ref_plan
+    wl = WL.random_decode(123 + G, 11, 7000, min_len=1)
+    q, kc, vc, bt = decode_inputs(wl)
+    note(f"launch order G={G}")
+    outs, parts = [], []
+    for order in ("head", "list"):
+        st = DecodeStep(wl.kv_lens, q.device, num_workers=16, head_groups=G, launch_order=order)
+        assert np.array_equal(st.map_host, ref_plan(wl.kv_lens, 16, 512))
+        assert st.list_major == (order == "list")
+        assert int(st.map[0].item()) == (3 if order == "list" else 1)
+        for t in (st.part_m, st.part_l, st.part_o):
+            t.fill_(float("nan"))
+        outs.append(st(q, kc, vc, bt, scale=SCALE))
+        parts.append([t.clone() for t in (st.part_m, st.part_l, st.part_o)])
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    for a, b in zip(*parts):
+        assert torch.equal(a, b)
+
+
+def test_launch_order_auto_choice(lb):
+    """"auto" launches list-major where the per-XCD token totals under it are within 1% (the mixed
+    batch) and head-major where they are not (the long-tail batch), at the device's worker count."""
+    from load_balanced_split_attn_amd.decode import DecodeStep
+    mixed = DecodeStep(WL.mixed().kv_lens, "cuda", head_groups=8)
+    tail = DecodeStep(WL.long_tail().kv_lens, "cuda", head_groups=8)
+    note(f"auto order: mixed W={mixed.W} list-major={mixed.list_major}, long tail W={tail.W} "
+         f"list-major={tail.list_major}")
+    if mixed.W % 8 == 0:
+        assert mixed.list_major and int(mixed.map[0].item()) == 3 and int(mixed.map_host[0]) == 1
+    assert not tail.list_major and int(tail.map[0].item()) == 1
