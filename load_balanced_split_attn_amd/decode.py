@@ -43,6 +43,31 @@ def xcd_token_balance(map_host: np.ndarray) -> float:
     return float(per_xcd.max() / per_xcd.mean()) if per_xcd.mean() > 0 else 1.0
 
 
+def choose_list_major(map_host: np.ndarray, head_groups: int, launch_order: str = "auto",
+                      claiming: bool = False) -> bool:
+    """Whether a step's split-KV launch runs the map list-major (see ``DecodeStep``'s launch_order):
+    always for a version-3 map; for a version-1 map with more than one head group and W a multiple of
+    8 when asked ("list") or when its per-XCD token totals are within 1% ("auto"); never otherwise
+    (a run-time claiming launch takes its order from its counter)."""
+    if launch_order not in ("auto", "head", "list"):
+        raise ValueError(f"unknown launch_order {launch_order!r} (auto, head or list)")
+    hdr = map_header(map_host)
+    if hdr["version"] == MAP_VERSION_PLACED:
+        return True
+    if hdr["version"] != 1 or head_groups <= 1 or hdr["W"] % XCDS or claiming:
+        return False
+    return launch_order == "list" or (launch_order == "auto" and xcd_token_balance(map_host) <= LIST_MAJOR_BALANCE)
+
+
+def device_map(map_host: np.ndarray, list_major: bool, device) -> torch.Tensor:
+    """The map's device copy; a version-1 map launched list-major carries the version-3 word there
+    (the host map is left as planned)."""
+    words = map_host.copy()
+    if list_major:
+        words[0] = MAP_VERSION_PLACED
+    return torch.from_numpy(words).to(device)
+
+
 class DecodeStep:
     def __init__(self, seq_lens: Sequence[int], device, num_workers: Optional[int] = None, tile: int = 512,
                  head_groups: int = 8, num_q_heads: int = 64, head_dim: int = 128,
@@ -90,17 +115,9 @@ class DecodeStep:
         self.head_groups = head_groups
         self.kv_dtype = kv_dtype
         self.device = device
-        if launch_order not in ("auto", "head", "list"):
-            raise ValueError(f"unknown launch_order {launch_order!r} (auto, head or list)")
-        version = int(self.map_host[0])
-        self.list_major = version == MAP_VERSION_PLACED
-        if version == 1 and head_groups > 1 and self.W % XCDS == 0 and resident_workgroups is None:
-            self.list_major = launch_order == "list" or (
-                launch_order == "auto" and xcd_token_balance(self.map_host) <= LIST_MAJOR_BALANCE)
-        device_words = self.map_host.copy()
-        if self.list_major:
-            device_words[0] = MAP_VERSION_PLACED
-        self.map = torch.from_numpy(device_words).to(device)
+        self.list_major = choose_list_major(self.map_host, head_groups, launch_order,
+                                            claiming=resident_workgroups is not None)
+        self.map = device_map(self.map_host, self.list_major, device)
         self.seq_lens = torch.tensor(self.seq_lens_host, dtype=torch.int32, device=device)
         S = max(self.S, 1)
         self.part_m = torch.empty((S, num_q_heads), dtype=torch.float32, device=device)

@@ -16,6 +16,7 @@ import torch
 
 from . import (KV_BF16, KV_FP8_E4M3, attn_combine, attn_plan_prefill, attn_query_workers, attn_splitkv_mtp,
                map_header, max_splits_of)
+from .decode import choose_list_major, device_map
 
 MAX_ROWS = 4
 
@@ -23,7 +24,9 @@ MAX_ROWS = 4
 class MtpDecodeStep:
     def __init__(self, q_lens: Sequence[int], kv_lens: Sequence[int], device, num_workers: Optional[int] = None,
                  tile: int = 512, head_groups: int = 8, kv_dtype: int = KV_BF16, num_q_heads: int = 64,
-                 head_dim: int = 128):
+                 head_dim: int = 128, launch_order: str = "auto"):
+        """launch_order as in ``decode.DecodeStep``: list-major when the per-XCD token totals of the
+        map's lists are within 1% ("auto"), or as asked; the partials are the same either way."""
         device = torch.device(device)
         self.q_lens_host = [int(x) for x in q_lens]
         self.kv_lens_host = [int(x) for x in kv_lens]
@@ -41,7 +44,8 @@ class MtpDecodeStep:
         self.head_groups = head_groups
         self.kv_dtype = kv_dtype
         self.device = device
-        self.map = torch.from_numpy(self.map_host).to(device)
+        self.list_major = choose_list_major(self.map_host, head_groups, launch_order)
+        self.map = device_map(self.map_host, self.list_major, device)
         self.q_lens = torch.tensor(self.q_lens_host, dtype=torch.int32, device=device)
         self.kv_lens = torch.tensor(self.kv_lens_host, dtype=torch.int32, device=device)
         starts = [0]

@@ -142,3 +142,27 @@ def test_graph_captured_mtp_step(lb, fp8):
             for b, r in oracle_mtp(wl, fp8=fp8).items():
                 assert_close(got[starts[b]:starts[b] + wl.q_lens[b]], r, f"request {b}")
         note(f"mtp graph replay {replay} ok")
+
+
+@pytest.mark.parametrize("R,G", [(2, 8), (4, 8), (3, 4)])
+def test_launch_order_bitwise(lb, R, G):
+    """The multi-token step's map launched head-major and list-major: the same output bit for bit
+    (the host map is the oracle's either way)."""
+    from load_balanced_split_attn_amd.mtp import MtpDecodeStep
+    wl = WL.random_mtp(300 + R, 13, 6000, max_q=R)
+    inputs = mtp_inputs(wl)
+    q, kc, vc, bt, scales = inputs
+    note(f"mtp launch order R={R} G={G}")
+    outs = []
+    for order in ("head", "list"):
+        step = MtpDecodeStep(wl.q_lens, wl.kv_lens, q.device, num_workers=16, head_groups=G, launch_order=order)
+        assert np.array_equal(step.map_host, ref_plan_prefill(wl.q_lens, wl.kv_lens, 16, step.R, 512, True))
+        assert step.list_major == (order == "list")
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device)
+        outs.append(step(q, kc, vc, bt, scale=SCALE, out=out))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    ref = oracle_mtp(wl)
+    starts = q_starts(wl)
+    for b, rows in ref.items():
+        assert_close(outs[1][starts[b]:starts[b] + wl.q_lens[b]].cpu().numpy(), rows, f"mtp request {b}")
