@@ -508,7 +508,8 @@ def bench_decode_leg(dev, name: str, args) -> dict:
             vals.append(per_cu_busy(timing)["max_over_mean"])
         return vals
 
-    step = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=workers, tile=args.tile, head_groups=G)
+    step = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=workers, tile=args.tile, head_groups=G,
+                      launch_order=args.launch_order)
     r = run(step, args.steps, args.warmup)
     ms = r["total_ms"] / args.steps
     split_ms = float(np.mean(r["split_ms"]))
@@ -969,6 +970,8 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--no-claim", action="store_true", help="skip the run-time claiming comparison")
     ap.add_argument("--no-rated", action="store_true", help="skip the rate-proportional map comparison")
+    ap.add_argument("--launch-order", default="auto", choices=("auto", "head", "list"),
+                    help="order of the decode steps' split-KV workgroups (DecodeStep's launch_order)")
     ap.add_argument("--legs", default="uniform,long_tail,mixed_tp8",
                     help="other decode batches timed beside the headline one (comma list, '' for none)")
     ap.add_argument("--only-prefill", action="store_true",
@@ -1034,7 +1037,7 @@ def main() -> int:
     workers = args.workers or (wl.workers if wl.workers else lb.attn_query_workers(0, args.head_groups))
     plan_t = time.perf_counter()
     step = DecodeStep(wl.kv_lens, dev, num_q_heads=wl.hq, num_workers=workers, tile=args.tile,
-                      head_groups=args.head_groups)
+                      head_groups=args.head_groups, launch_order=args.launch_order)
     plan_s = time.perf_counter() - plan_t
     t = time.perf_counter()
     for _ in range(100):
