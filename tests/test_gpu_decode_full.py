@@ -1,5 +1,6 @@
 """Full-size decode workloads in the launch configuration bench.py times (workers from the device
-occupancy query, 512-token tiles, one workgroup per KV head): every request against the fp64
+occupancy query, 512-token tiles, one workgroup per KV head, the launch order the step picks:
+list-major for the balanced mixed and uniform batches): every request against the fp64
 oracle, and all requests against the static split-KV map (an exact re-association, so the two must agree to fp32
 rounding)."""
 
@@ -24,6 +25,7 @@ def test_full_size(name):
     W = lb.attn_query_workers(0, 8)
     step = DecodeStep(wl.kv_lens, q.device, num_workers=W, head_groups=8)
     assert np.array_equal(step.map_host, ref_plan(wl.kv_lens, W, 512))
+    note(f"  W={W}, launch order {'list' if step.list_major else 'head'}-major")
     out = step(q, kc, vc, bt, scale=SCALE)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
