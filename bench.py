@@ -833,7 +833,8 @@ def bench_store_kv(dev, wl, args) -> dict:
             e1.record()
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) / (reps * replays) * 1e3
-            unfused = bench_unfused_store(dev, wl, q, k, v, pos, bt, qw, kw, sc, q_out, kc, vc, reps)
+            unfused = (None if getattr(args, "no_unfused", False)
+                       else bench_unfused_store(dev, wl, q, k, v, pos, bt, qw, kw, sc, q_out, kc, vc, reps))
             e = 1 if fp8 else 2
             nbytes = B * (wl.hq + 2 * wl.hkv) * wl.head_dim * 2 + B * wl.hq * wl.head_dim * 2 + \
                 B * 2 * wl.hkv * wl.head_dim * e + B * 8 + 2 * wl.head_dim * 4
@@ -843,9 +844,10 @@ def bench_store_kv(dev, wl, args) -> dict:
                          "algorithmic_bytes": nbytes, "GB_per_s": round(nbytes / (us * 1e-6) / 1e9, 1),
                          "frac_of_hbm_peak": round(nbytes / (us * 1e-6) / 8e12, 4), "v_rows_touched_bytes": v_rows,
                          "unfused": unfused,
-                         "fused_speedup_graph": (round(unfused["graph_us"] / us, 2) if unfused["graph_us"] else None)})
-            log(f"store_kv B={B} {'e4m3' if fp8 else 'bf16'}: {us:.1f} us; unfused ops: graph "
-                f"{unfused['graph_us']} us, eager {unfused['eager_us']} us")
+                         "fused_speedup_graph": (round(unfused["graph_us"] / us, 2)
+                                                 if unfused and unfused["graph_us"] else None)})
+            log(f"store_kv B={B} {'e4m3' if fp8 else 'bf16'}: {us:.1f} us"
+                + (f"; unfused ops: graph {unfused['graph_us']} us, eager {unfused['eager_us']} us" if unfused else ""))
             del graph, kc, vc
     return {"workload": "producer step: RMSNorm + RoPE + Hadamard on q and k, K/V stored in the blocked paged "
                         "cache, for the batch's new tokens and for a 4096-token step (each token its own page)",
@@ -941,9 +943,28 @@ def bench_store_chunk(dev, reps: int, replays: int) -> dict:
         log(f"store_kv chunk 8x2048 {'e4m3' if fp8 else 'bf16'}: chunk path {us_chunk:.1f} us, one-token path "
             f"{us_token:.1f} us")
         del kc, vc
+    # the step reads and writes about equal bytes; a plain copy of half its bytes is the read+write
+    # rate HBM gives such a mix
+    ceiling = copy_ceiling(dev, out[0]["algorithmic_bytes"] // 2, reps, replays)
+    for row in out:
+        row["frac_of_copy_ceiling"] = round(row["GB_per_s"] / ceiling["GB_per_s"], 4)
+    log(f"store_kv chunk: copy ceiling {ceiling['GB_per_s']:.0f} GB/s read + write")
     return {"workload": "producer step of a prefill chunk: the chunked-prefill batch's 8 x 2048 new tokens after "
                         f"their cached prefixes ({prefix}), 64 q / 8 kv heads, RMSNorm + RoPE + Hadamard",
-            "sweep": out}
+            "sweep": out, "copy_ceiling": ceiling}
+
+
+def copy_ceiling(dev, nbytes: int, reps: int, replays: int) -> dict:
+    """Read + write rate of a plain device copy of nbytes (torch's copy kernel, a HIP graph of reps
+    copies replayed): what HBM sustains for a kernel that reads and writes equal amounts."""
+    import torch
+    src = torch.ones(nbytes // 16 * 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    us = _graph_us(lambda: dst.copy_(src), reps, replays)
+    moved = 2 * src.numel() * 4
+    del src, dst
+    return {"what": "torch copy_ of a device buffer, read + write bytes / time", "bytes_each_way": moved // 2,
+            "us": round(us, 2), "GB_per_s": round(moved / (us * 1e-6) / 1e9, 1)}
 
 
 def main() -> int:
@@ -981,6 +1002,8 @@ def main() -> int:
     ap.add_argument("--no-store", action="store_true", help="skip the producer-step report")
     ap.add_argument("--only-store", action="store_true",
                     help="run only the producer-step report on --workload (profiling runs); prints its JSON")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="producer-step report without the separate-tensor-ops comparison (counter runs)")
     ap.add_argument("--only-store-chunk", action="store_true",
                     help="run only the prefill-chunk producer-step report (profiling runs); prints its JSON")
     ap.add_argument("--only-fp8", action="store_true",

@@ -106,42 +106,72 @@ __device__ __forceinline__ void rope_angle(const StoreParams& p, int lane, int p
   cs = __builtin_amdgcn_cosf(f);
 }
 
-// One task: four head vectors of one kind (task < nq: q heads 4 task ..; then k; then v) of the token
-// in `row` of request b at position pos, RoPE angles (sn, cs) of pair `lane` already formed.
-__device__ __forceinline__ void store_task(const StoreParams& p, int task, int nq, int nk, int b, int row, int pos,
-                                           float sn, float cs) {
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15;   // lane within the vector's row: dims 4r..4r+3 and 64+4r..64+4r+3
+// One task: four head vectors of one kind (task < nq: q heads 4 task ..; then k; then v) of one
+// token, one per 16-lane row of the wave.  Rows past the last head take the last head's vector and
+// store nothing.
+struct TaskHead {
+  int kind;   // 0 q, 1 k, 2 v
+  int head;
+  bool live;
+};
+__device__ __forceinline__ TaskHead task_head(const StoreParams& p, int task, int nq, int nk, int lane) {
   const int kind = task < nq ? 0 : (task < nq + nk ? 1 : 2);
   const int hb = kind == 0 ? task : (kind == 1 ? task - nq : task - nq - nk);
   const int H = kind == 0 ? p.Hq : p.Hkv;
   const int head_raw = hb * 4 + (lane >> 4);
-  const bool live = head_raw < H;
-  const int head = live ? head_raw : H - 1;   // rows past the last head load a valid vector, store nothing
+  return TaskHead{kind, head_raw < H ? head_raw : H - 1, head_raw < H};
+}
 
-  // every load first
-  const uint16_t* src = (kind == 0 ? p.q_in : (kind == 1 ? p.k_in : p.v_in)) + ((size_t)row * H + head) * kSD;
-  const uint2 raw_lo = *reinterpret_cast<const uint2*>(src + 4 * r);
-  const uint2 raw_hi = *reinterpret_cast<const uint2*>(src + 64 + 4 * r);
-  const float* w = kind == 0 ? p.q_norm_w : (kind == 1 ? p.k_norm_w : nullptr);
-  float4 w_lo = {}, w_hi = {};
-  if (w) {
-    w_lo = *reinterpret_cast<const float4*>(w + 4 * r);
-    w_hi = *reinterpret_cast<const float4*>(w + 64 + 4 * r);
-  }
-  const bool rope = kind < 2 && p.theta > 0.f;
-  int pid = -1, t = 0;
-  if (kind > 0 && pos >= 0 && pos < p.bt_stride * p.page) {
+// The lane's pieces of its head vector in `row` (dims 4r..4r+3 and 64+4r..64+4r+3, bf16 pairs) and,
+// for k and v over an 8-bit cache, the head's scale (1 otherwise).
+struct TaskIn {
+  uint2 lo, hi;
+  float scale;
+};
+__device__ __forceinline__ TaskIn load_task(const StoreParams& p, const TaskHead& th, int row, int r) {
+  const int H = th.kind == 0 ? p.Hq : p.Hkv;
+  const uint16_t* src = (th.kind == 0 ? p.q_in : (th.kind == 1 ? p.k_in : p.v_in)) + ((size_t)row * H + th.head) * kSD;
+  const float scale = th.kind > 0 && p.fp8 ? (th.kind == 1 ? p.k_scale : p.v_scale)[th.head] : 1.f;
+  return TaskIn{*reinterpret_cast<const uint2*>(src + 4 * r), *reinterpret_cast<const uint2*>(src + 64 + 4 * r), scale};
+}
+
+// RMSNorm gains of the lane's dims (zeros when w is null: no norm)
+struct Gains {
+  float4 lo, hi;
+};
+__device__ __forceinline__ Gains load_gains(const float* w, int r) {
+  if (!w) return Gains{};
+  return Gains{*reinterpret_cast<const float4*>(w + 4 * r), *reinterpret_cast<const float4*>(w + 64 + 4 * r)};
+}
+
+// Cache slot of the token at pos in request b: page block_table[b][pos / page] and offset pos % page;
+// pid = -1 for a position outside the table (not stored)
+__device__ __forceinline__ void cache_slot(const StoreParams& p, int b, int pos, int& pid, int& t) {
+  pid = -1;
+  t = 0;
+  if (pos >= 0 && pos < p.bt_stride * p.page) {
     pid = p.block_table[(size_t)b * p.bt_stride + pos / p.page];
     t = pos % p.page;
   }
-  const float scale = kind > 0 && p.fp8 ? (kind == 1 ? p.k_scale : p.v_scale)[head] : 1.f;
+}
+
+// The arithmetic and the stores of one task whose loads (vector, gains, cache slot) are done; RoPE
+// angles (sn, cs) of pair `lane` already formed.  norm: the task's kind has RMSNorm gains.
+__device__ __forceinline__ void store_task(const StoreParams& p, const TaskHead& th, const TaskIn& in, bool norm,
+                                           const Gains& gn, int row, int pid, int t, float sn, float cs) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;   // lane within the vector's row: dims 4r..4r+3 and 64+4r..64+4r+3
+  const int kind = th.kind, head = th.head;
+  const bool rope = kind < 2 && p.theta > 0.f;
+  const uint2 raw_lo = in.lo, raw_hi = in.hi;
+  const float4 w_lo = gn.lo, w_hi = gn.hi;
+  const float scale = in.scale;
 
   float x[8] = {bf16_lo(raw_lo.x), bf16_hi(raw_lo.x), bf16_lo(raw_lo.y), bf16_hi(raw_lo.y),
                 bf16_lo(raw_hi.x), bf16_hi(raw_hi.x), bf16_lo(raw_hi.y), bf16_hi(raw_hi.y)};
 
   if (kind < 2) {
-    if (w) {
+    if (norm) {
       float ss = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) ss = fmaf(x[j], x[j], ss);
@@ -192,7 +222,7 @@ __device__ __forceinline__ void store_task(const StoreParams& p, int task, int n
     }
   }
 
-  if (!live) return;
+  if (!th.live) return;
   if (kind == 0) {
     uint16_t* dst = p.q_out + ((size_t)row * p.Hq + head) * kSD;
     *reinterpret_cast<uint2*>(dst + 4 * r) = make_uint2(pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]));
@@ -237,12 +267,15 @@ __device__ __forceinline__ void store_task(const StoreParams& p, int task, int n
 }
 
 // CHUNK = false: one new token per request, row b at positions[b]; one task (q, k or v heads) per
-// wave.  CHUNK = true: request b's q_lens[b] rows from row q_start[b] at positions positions[b] + j;
-// one workgroup per row, each wave looping over every fourth q/k task with the row's RoPE angles
-// formed once (the chunk's V goes through store_v_chunk_kernel, which writes whole 64-byte rows).
+// wave, every load issued before the arithmetic.  CHUNK = true: request b's q_lens[b] rows from row
+// q_start[b] at positions positions[b] + j; one workgroup per row, each wave looping over every
+// fourth q/k task with the row's RoPE angles, gains and cache slot formed once, and the next task's
+// loads in flight while the current task is computed (the chunk's V goes through
+// store_v_chunk_kernel, which writes whole 64-byte rows).
 template <bool CHUNK>
 __global__ __launch_bounds__(256) void store_kv_kernel(StoreParams p) {
   const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nq = (p.Hq + 3) >> 2, nk = (p.Hkv + 3) >> 2;
   const bool rope = p.theta > 0.f;
@@ -251,17 +284,34 @@ __global__ __launch_bounds__(256) void store_kv_kernel(StoreParams p) {
     const int b = blockIdx.x / p.max_rows;
     const int j = blockIdx.x - b * p.max_rows;
     if (j >= p.q_lens[b]) return;
+    const int ntask = nq + nk;
+    int task = wave;
+    if (task >= ntask) return;
     const int row = p.q_start[b] + j;
     const int pos = p.positions[b] < 0 ? -1 : p.positions[b] + j;   // a chunk starting before 0 is not stored
+    int pid, t;
+    cache_slot(p, b, pos, pid, t);
     if (rope) rope_angle(p, lane, pos, sn, cs);
-    for (int task = wave; task < nq + nk; task += 4) store_task(p, task, nq, nk, b, row, pos, sn, cs);
+    for (; task < ntask; task += 4) {
+      const TaskHead th = task_head(p, task, nq, nk, lane);
+      const TaskIn in = load_task(p, th, row, r);
+      const float* w = th.kind == 0 ? p.q_norm_w : p.k_norm_w;
+      const Gains gn = load_gains(w, r);
+      store_task(p, th, in, w != nullptr, gn, row, pid, t, sn, cs);
+    }
   } else {
     const int b = blockIdx.x;
     const int pos = p.positions[b];
     const int task = blockIdx.y * 4 + wave;   // 4 heads of one kind: q blocks, then k blocks, then v blocks
     if (task >= nq + 2 * nk) return;
-    if (rope && task < nq + nk) rope_angle(p, lane, pos, sn, cs);
-    store_task(p, task, nq, nk, b, b, pos, sn, cs);
+    const TaskHead th = task_head(p, task, nq, nk, lane);
+    const TaskIn in = load_task(p, th, b, r);
+    const float* w = th.kind == 0 ? p.q_norm_w : (th.kind == 1 ? p.k_norm_w : nullptr);
+    const Gains gn = load_gains(w, r);
+    int pid = -1, t = 0;
+    if (th.kind > 0) cache_slot(p, b, pos, pid, t);
+    if (rope && th.kind < 2) rope_angle(p, lane, pos, sn, cs);
+    store_task(p, th, in, w != nullptr, gn, b, pid, t, sn, cs);
   }
 }
 

@@ -346,6 +346,19 @@ def test_chunk_append(lb, fp8, norm, theta, had, page):
     was (the prefix before each chunk and the slots after it share rows with the chunk's first and
     last tokens), writes the same rotated q, and matches the fp64 oracle.  Chunks start on and off
     row boundaries, span one token to several pages, and one request appends nothing."""
+    _check_chunk_append(lb, fp8, norm, theta, had, page)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 1), (6, 3), (12, 4), (20, 2), (32, 8), (68, 12)])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_chunk_append_head_counts(lb, fp8, hq, hkv):
+    """The chunk append's q/k workgroups loop over four-head tasks per wave with the next task's
+    loads in flight: head counts that leave a wave without a task or give it one to five (some with
+    rows past the last head), bitwise the one-token path and against the oracle, as above."""
+    _check_chunk_append(lb, fp8, True, 10000.0, True, 64, hq=hq, hkv=hkv)
+
+
+def _check_chunk_append(lb, fp8, norm, theta, had, page, hq=64, hkv=8):
     from load_balanced_split_attn_amd.paged import unpack_request
     dev = torch.device("cuda")
     prefix = [0, 31, 64, 100, 1000, 5, 4096]
@@ -353,28 +366,28 @@ def test_chunk_append(lb, fp8, norm, theta, had, page):
     extra = [5, 0, 40, 7, 100, 3, 90]
     totals = [p + c + e for p, c, e in zip(prefix, n, extra)]
     B, rows = len(n), sum(n)
-    note(f"chunk append fp8={fp8} norm={norm} theta={theta} had={had} page={page}")
-    kc0, vc0, bt = _prefilled_cache(totals, page, fp8, dev, seed=90 + int(fp8))
-    q, k, v, qw, kw = _inputs(80 + int(fp8), rows)
+    note(f"chunk append fp8={fp8} norm={norm} theta={theta} had={had} page={page} heads={hq}/{hkv}")
+    kc0, vc0, bt = _prefilled_cache(totals, page, fp8, dev, seed=90 + int(fp8), Hkv=hkv)
+    q, k, v, qw, kw = _inputs(80 + int(fp8), rows, Hq=hq, Hkv=hkv)
     starts = np.concatenate([[0], np.cumsum(n)[:-1]]).astype(np.int32)
     q_lens = torch.tensor(n, dtype=torch.int32, device=dev)
     q_start = torch.tensor(starts, dtype=torch.int32, device=dev)
     pos0 = torch.tensor(prefix, dtype=torch.int32, device=dev)
     ks = vs = None
     if fp8:
-        ks = torch.tensor([0.02 * (1 + 0.1 * h) for h in range(8)], dtype=torch.float32, device=dev)
-        vs = torch.tensor([0.03 * (1 + 0.05 * h) for h in range(8)], dtype=torch.float32, device=dev)
+        ks = torch.tensor([0.02 * (1 + 0.1 * h) for h in range(hkv)], dtype=torch.float32, device=dev)
+        vs = torch.tensor([0.03 * (1 + 0.05 * h) for h in range(hkv)], dtype=torch.float32, device=dev)
     kw_args = dict(q_norm_w=qw.to(dev) if norm else None, k_norm_w=kw.to(dev) if norm else None, eps=1e-6,
                    rope_theta=theta, hadamard=had, kv_scales=(ks, vs) if fp8 else None)
     kc1, vc1 = kc0.clone(), vc0.clone()
-    q1 = torch.full((rows, 64, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    q1 = torch.full((rows, hq, 128), float("nan"), dtype=torch.bfloat16, device=dev)
     lb.attn_store_kv_chunk(q.to(dev), k.to(dev), v.to(dev), q_lens, q_start, pos0, max(n), q1, kc1, vc1, bt, **kw_args)
     # the one-token path over the same rows: row r of request b at position prefix[b] + j
     req = np.repeat(np.arange(B), n)
     pos_rows = torch.tensor([prefix[b] + j for b in range(B) for j in range(n[b])], dtype=torch.int32, device=dev)
     bt_rows = bt[torch.from_numpy(req).to(dev)].contiguous()
     kc2, vc2 = kc0.clone(), vc0.clone()
-    q2 = torch.full((rows, 64, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    q2 = torch.full((rows, hq, 128), float("nan"), dtype=torch.bfloat16, device=dev)
     lb.attn_store_kv(q.to(dev), k.to(dev), v.to(dev), pos_rows, q2, kc2, vc2, bt_rows, **kw_args)
     torch.cuda.synchronize()
     assert torch.equal(q1, q2), "rotated q differs from the one-token path"
