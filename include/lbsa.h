@@ -386,8 +386,9 @@ int attn_store_kv(const void* q_in, const void* k_in, const void* v_in,
  *   other arguments as attn_store_kv; v_in and v_cache 16-byte aligned
  * A token at a position outside its block-table row, or in a page id outside [0, num_pages), is not
  * stored; a request with positions[b] < 0 stores nothing (its q rows are still written).
- * Launches B x max_q_len x ceil((ceil(Hq/4) + ceil(Hkv/4)) / 4) workgroups for q and k and
- * B x (ceil(max_q_len / w) + 1) x Hkv for V (w = 32 bf16, 64 E4M3), 256 threads each.
+ * Launches B x max_q_len workgroups for q and k (one per row; its four waves take every fourth
+ * group of four q or k heads) and B x (ceil(max_q_len / w) + 1) x Hkv for V (w = 32 bf16, 64 E4M3),
+ * 256 threads each.
  * Errors: as attn_store_kv, plus LBSA_ERR_INVALID for NULL q_lens / q_start, max_q_len < 0 or a
  * grid beyond INT32_MAX workgroups.
  */
