@@ -385,7 +385,8 @@ int attn_store_kv(const void* q_in, const void* k_in, const void* v_in,
  *                 processed); rows must lie inside q_in's [rows, Hq, 128] (not checked)
  *   other arguments as attn_store_kv; v_in and v_cache 16-byte aligned
  * A token at a position outside its block-table row, or in a page id outside [0, num_pages), is not
- * stored; a request with positions[b] < 0 stores nothing (its q rows are still written).
+ * stored; a request with positions[b] < 0 stores nothing (its q rows are still written, rotated as
+ * a token at position -1).
  * Launches B x max_q_len workgroups for q and k (one per row; its four waves take every fourth
  * group of four q or k heads) and B x (ceil(max_q_len / w) + 1) x Hkv for V (w = 32 bf16, 64 E4M3),
  * 256 threads each.

@@ -424,6 +424,73 @@ def _check_chunk_append(lb, fp8, norm, theta, had, page, hq=64, hkv=8):
                 assert np.all(np.abs(got.double().numpy() - ref) <= _tol(ref)), f"request {b}"
 
 
+@pytest.mark.parametrize("seed", range(32))
+def test_chunk_random_sweep(lb, seed):
+    """Seeded random chunk appends crossing what the cases above take one at a time: batch size,
+    prefix and chunk lengths (empty chunks included), a max_q_len above the longest chunk, a request
+    with a negative start position (q written, nothing stored), head counts, page size, cache type,
+    RMSNorm, RoPE base, Hadamard and eps.  q_out and both caches (prefilled with random bytes) bit
+    for bit against the one-token path over the same tokens, and q against the fp64 oracle."""
+    g = np.random.default_rng([11, seed])
+    dev = torch.device("cuda")
+    B = int(g.integers(1, 7))
+    hq, hkv = [(64, 8), (8, 1), (6, 3), (12, 4), (16, 2), (32, 8), (68, 12)][int(g.integers(0, 7))]
+    page = int(g.choice([64, 128, 256]))
+    fp8 = bool(g.random() < 0.5)
+    norm = bool(g.random() < 0.5)
+    theta = float(g.choice([0.0, 10000.0, 1e6]))
+    had = bool(g.random() < 0.5)
+    eps = float(g.choice([1e-6, 1e-5]))
+    prefix = [int(x) for x in g.integers(0, 3000, size=B)]
+    n = [int(x) for x in g.integers(0, 300, size=B)]
+    n[int(g.integers(0, B))] = int(g.integers(1, 300))
+    extra = [int(x) for x in g.integers(0, 100, size=B)]
+    neg = int(g.integers(0, B)) if g.random() < 0.2 else -1
+    max_q = max(n) + int(g.integers(0, 3))
+    note(f"chunk sweep {seed}: B={B} heads={hq}/{hkv} page={page} fp8={fp8} norm={norm} theta={theta} "
+         f"hadamard={had} n={n} prefix={prefix} negative={neg}")
+    totals = [p_ + c + e for p_, c, e in zip(prefix, n, extra)]
+    rows = sum(n)
+    kc0, vc0, bt = _prefilled_cache(totals, page, fp8, dev, seed=300 + seed, Hkv=hkv)
+    q, k, v, qw, kw = _inputs(700 + seed, rows, Hq=hq, Hkv=hkv)
+    starts = np.concatenate([[0], np.cumsum(n)[:-1]]).astype(np.int32)
+    pos_list = [(-1 - p_ if b == neg else p_) for b, p_ in enumerate(prefix)]
+    q_lens = torch.tensor(n, dtype=torch.int32, device=dev)
+    q_start = torch.tensor(starts, dtype=torch.int32, device=dev)
+    pos0 = torch.tensor(pos_list, dtype=torch.int32, device=dev)
+    ks = vs = None
+    if fp8:
+        ks = torch.exp2(torch.rand(hkv, generator=torch.Generator().manual_seed(50 + seed)) * 2 - 5).float().to(dev)
+        vs = torch.exp2(torch.rand(hkv, generator=torch.Generator().manual_seed(60 + seed)) * 2 - 6).float().to(dev)
+    kw_args = dict(q_norm_w=qw.to(dev) if norm else None, k_norm_w=kw.to(dev) if norm else None, eps=eps,
+                   rope_theta=theta, hadamard=had, kv_scales=(ks, vs) if fp8 else None)
+    kc1, vc1 = kc0.clone(), vc0.clone()
+    q1 = torch.full((rows, hq, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    lb.attn_store_kv_chunk(q.to(dev), k.to(dev), v.to(dev), q_lens, q_start, pos0, max_q, q1, kc1, vc1, bt, **kw_args)
+    # the one-token path: row j of request b at position pos_list[b] + j (all negative for the
+    # request that starts below zero, so none of its tokens is stored)
+    req = np.repeat(np.arange(B), n)
+    pos_rows_l = [(pos_list[b] + j if pos_list[b] >= 0 else -1) for b in range(B) for j in range(n[b])]
+    pos_rows = torch.tensor(pos_rows_l, dtype=torch.int32, device=dev)
+    bt_rows = bt[torch.from_numpy(req).to(dev)].contiguous()
+    kc2, vc2 = kc0.clone(), vc0.clone()
+    q2 = torch.full((rows, hq, 128), float("nan"), dtype=torch.bfloat16, device=dev)
+    lb.attn_store_kv(q.to(dev), k.to(dev), v.to(dev), pos_rows, q2, kc2, vc2, bt_rows, **kw_args)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2), "rotated q differs from the one-token path"
+    assert torch.equal(kc1, kc2), "K cache differs from the one-token path"
+    assert torch.equal(vc1, vc2), "V cache differs from the one-token path"
+    # q against the oracle at the positions the rows were rotated by: a request that starts below
+    # zero takes position -1 for every row, as the one-token path does for a token at -1
+    qpos = np.array(pos_rows_l, dtype=np.float64)
+    rq, _, _ = SK.ref_store_kv(q.double().numpy(), k.double().numpy(), v.double().numpy(), qpos,
+                               qw.double().numpy() if norm else None, kw.double().numpy() if norm else None,
+                               eps, theta, had, ks.cpu().double().numpy() if fp8 else None,
+                               vs.cpu().double().numpy() if fp8 else None)
+    dq = np.abs(q1.float().cpu().numpy().astype(np.float64) - rq)
+    assert np.all(dq <= _tol(rq)), f"q: {int((dq > _tol(rq)).sum())} beyond tolerance"
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 def test_graph_captured_store(lb, fp8):
     """The producer step captured in a HIP graph: four replays with new q/k/v values and new
